@@ -1,0 +1,12 @@
+"""Float64 CPU oracle for the TTT-Linear scan (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It shares no code with the GPU path.
+"""
+from .ttt_oracle import (EPS, LN_EXACT, LN_NONE, LN_ST, inner_grad_vector,
+                         layer_norm, ln_jacobian, rel_max_err, sigmoid,
+                         ttt_linear_forward)
+
+__all__ = ["EPS", "LN_EXACT", "LN_NONE", "LN_ST", "inner_grad_vector",
+           "layer_norm", "ln_jacobian", "rel_max_err", "sigmoid",
+           "ttt_linear_forward"]

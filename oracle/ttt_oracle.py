@@ -1,0 +1,178 @@
+"""Plain CPU oracle for the TTT-Linear fast-weight scan.
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, obviously correct
+reference that the GPU path is checked against.  Only the test suite, the
+smoke check and the CPU-baseline leg of the benchmark may import it; the
+product path never calls it, and it imports nothing from the GPU package.
+
+Arithmetic is float64 NumPy (a ``dtype`` argument exists only so that the
+conditioning of a workload can be probed by re-running in float32).  The
+code is vectorised over the independent (batch, head) axis only; the time
+axis is an explicit Python loop in the order the pages state the method.
+
+Sources (web pages, cited by title and section):
+
+* "Edifice.Recurrent.TTT" (hexdocs), sections "Paper-Faithful
+  Implementation", "Equations (TTT-Linear)" and "Architecture": the
+  per-token recurrence, the 1/d scaling of the inner learning rate, the
+  learnable inner LayerNorm, the sigmoid output gate applied to the output
+  of the *updated* inner weight, and the straight-through inner gradient
+  ``grad_W = error_t k_t^T``.
+* "Error Correction in Trained TTT Layers" (aiqbench), abstract: the inner
+  gradient of the LayerNorm squared-error objective with the LayerNorm
+  Jacobian retained ("exact" mode).
+* "PonderTTT", section "Technical Architecture" (dual-form updates) and
+  "cortex_rust ... layers/ttt.rs", ``forward_chunkwise`` (every token of a
+  chunk takes its gradient at the chunk-start weight, last chunk may be
+  short): the mini-batch / dual mode.
+* "cortex_rust ... layers/ttt.rs", ``TTT_NORM_EPS``: epsilon 1e-6.
+
+Readings taken where the pages are silent (each is listed in the design
+notes): epsilon sits inside the square root, the LayerNorm variance is the
+biased (1/d) one, gamma/beta are per head, eta is one scalar per
+(batch, head, token), the gate is elementwise, the output uses the updated
+weight, the loss is 0.5*||.||^2, the dual-mode causal sum is inclusive, and
+a final short chunk uses the same rule.
+
+Parity status of each public function is stated in its docstring; every
+function here is pinned by ``tests/test_oracle.py``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+#: LayerNorm epsilon.  The cortex_rust page fixes 1e-6 as its normalisation
+#: epsilon (``TTT_NORM_EPS``); it is used here inside the square root.
+EPS = 1e-6
+
+#: Inner-gradient choices.
+LN_ST = "st"        # gradient of 0.5||pred - v||^2 w.r.t. pred, times k^T
+LN_EXACT = "exact"  # LayerNorm Jacobian applied (Error Correction ... abstract)
+LN_NONE = "none"    # inner LayerNorm removed (diagnostic: delta rule)
+
+
+def sigmoid(x: np.ndarray) -> np.ndarray:
+    """Logistic function, written so that +-inf map to exactly 1 and 0."""
+    x = np.asarray(x)
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    ex = np.exp(x[~pos])
+    out[~pos] = ex / (1.0 + ex)
+    return out
+
+
+def layer_norm(z: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float = EPS):
+    """Learnable LayerNorm over the last axis.
+
+    "Edifice.Recurrent.TTT", "Paper-Faithful Implementation" item 3 and
+    "Equations (TTT-Linear)": ``pred_t = LayerNorm(W_{t-1} k_t)``.
+    Returns ``(pred, xhat, s)`` with ``s = sqrt(var + eps)`` (biased variance).
+    Pinned against ``torch.nn.functional.layer_norm``.
+    """
+    d = z.shape[-1]
+    mu = z.sum(axis=-1, keepdims=True) / d
+    c = z - mu
+    var = (c * c).sum(axis=-1, keepdims=True) / d
+    s = np.sqrt(var + eps)
+    xhat = c / s
+    return gamma * xhat + beta, xhat, s
+
+
+def ln_jacobian(xhat: np.ndarray, s: np.ndarray, gamma: np.ndarray) -> np.ndarray:
+    """Explicit Jacobian d pred / d z of the learnable LayerNorm.
+
+    J[..., i, m] = gamma_i / s * (delta_im - 1/d - xhat_i xhat_m / d).
+    Used by the exact inner gradient ("Error Correction in Trained TTT
+    Layers", abstract: the inner gradient of the LayerNorm squared-error
+    objective).  Pinned by finite differences and by autograd through
+    ``torch.nn.functional.layer_norm``.
+    """
+    d = xhat.shape[-1]
+    eye = np.eye(d, dtype=xhat.dtype)
+    core = eye - 1.0 / d - xhat[..., :, None] * xhat[..., None, :] / d
+    return (gamma[..., :, None] / s[..., None]) * core
+
+
+def inner_grad_vector(z, v, gamma, beta, ln: str, eps: float = EPS):
+    """The vector delta such that the inner update is ``W -= eta * delta k^T``.
+
+    * ``st``: delta = LN(z) - v  ("Equations (TTT-Linear)": grad_W = error k^T)
+    * ``exact``: delta = J^T (LN(z) - v), the gradient of
+      0.5*||LN(z) - v||^2 with respect to z ("Error Correction ..." abstract)
+    * ``none``: delta = z - v (LayerNorm removed; the delta rule of the
+      "Key Innovations" equivalence with linear attention)
+    """
+    if ln == LN_NONE:
+        return z - v
+    pred, xhat, s = layer_norm(z, gamma, beta, eps)
+    err = pred - v
+    if ln == LN_ST:
+        return err
+    if ln == LN_EXACT:
+        jac = ln_jacobian(xhat, s, gamma)
+        return np.matmul(np.swapaxes(jac, -1, -2), err[..., None])[..., 0]
+    raise ValueError(f"unknown ln mode {ln!r}")
+
+
+def ttt_linear_forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None,
+                       *, ln: str = LN_ST, dual: bool = False, chunk: int = 16,
+                       eps: float = EPS, dtype=np.float64):
+    """The TTT-Linear scan, token by token.
+
+    Shapes (row-major): q, k, v, gate_logit [B,H,T,d]; eta_logit [B,H,T];
+    W0 [B,H,d,d] with z = W k meaning z_i = sum_j W[i,j] k_j; gamma, beta
+    [H,d] (ignored when ``ln == "none"``).  Returns ``(out [B,H,T,d],
+    W_final [B,H,d,d])`` in ``dtype``.
+
+    For each token t ("Equations (TTT-Linear)" and "Architecture" of
+    "Edifice.Recurrent.TTT"):
+
+      eta_t   = sigmoid(eta_logit_t) / d           (1/d: "Paper-Faithful" item 2)
+      z_t     = P k_t, with P = W (per-token) or P = W_c, the weight at the
+                start of t's chunk (dual mode: "PonderTTT" dual-form updates,
+                "cortex_rust" forward_chunkwise)
+      delta_t = inner_grad_vector(z_t, v_t)        (LN then error; see above)
+      W       = W - eta_t * delta_t k_t^T
+      o_t     = (W q_t) * sigmoid(gate_logit_t)    (updated W, sigmoid gate)
+
+    Parity: pinned (eta -> 0 closed form, delta-rule unrolled product,
+    autograd inner-gradient steps, finite differences, dual-form special
+    cases, overwrite and cancellation identities, resume, independence).
+    """
+    f = lambda a: None if a is None else np.asarray(a, dtype=dtype)
+    q, k, v, eta_logit, gate_logit, W0 = map(f, (q, k, v, eta_logit, gate_logit, W0))
+    B, H, T, d = q.shape
+    if ln != LN_NONE:
+        gamma = f(gamma)[None, :, :]   # [1,H,d], broadcast over batch
+        beta = f(beta)[None, :, :]
+    if dual and chunk < 1:
+        raise ValueError("chunk must be >= 1 in dual mode")
+
+    W = W0.copy()
+    out = np.zeros((B, H, T, d), dtype=dtype)
+    eta_all = sigmoid(eta_logit) / dtype(d)
+    gate_all = sigmoid(gate_logit)
+    Wc = W
+    for t in range(T):
+        if dual and t % chunk == 0:
+            Wc = W.copy()
+        P = Wc if dual else W
+        kt = k[:, :, t, :]
+        z = np.matmul(P, kt[..., None])[..., 0]
+        delta = inner_grad_vector(z, v[:, :, t, :], gamma, beta, ln, eps)
+        eta = eta_all[:, :, t][..., None, None]
+        W = W - eta * (delta[..., :, None] * kt[..., None, :])
+        out[:, :, t, :] = np.matmul(W, q[:, :, t, :][..., None])[..., 0] * gate_all[:, :, t, :]
+    return out, W
+
+
+def rel_max_err(got, ref) -> float:
+    """Relative max error of one output tensor: max|got - ref| / max|ref|."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.max(np.abs(ref)) if ref.size else 0.0
+    num = np.max(np.abs(got - ref)) if ref.size else 0.0
+    if den == 0.0:
+        return float(num)
+    return float(num / den)

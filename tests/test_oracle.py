@@ -1,0 +1,410 @@
+"""Pins of the float64 oracle against facts that do not come from the oracle.
+
+Every check here is independent of the oracle's own code: closed forms the
+pages imply, a hand-worked example, library routines (torch autograd and
+``torch.nn.functional.layer_norm``), finite differences and invariants.  A
+dropped term, a wrong sign, a transposed W or a misplaced epsilon in the
+oracle fails at least one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from test_rnn_layer_ttt_amd.inputs import make_case
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def run(x, **kw):
+    kw.setdefault("ln", x.ln)
+    kw.setdefault("dual", x.dual)
+    kw.setdefault("chunk", x.chunk)
+    return oracle.ttt_linear_forward(x.q, x.k, x.v, x.eta_logit, x.gate_logit, x.W0,
+                                     x.gamma, x.beta, **kw)
+
+
+def small(seed=0, B=2, H=3, T=9, d=5, **kw):
+    return make_case(B, H, T, d, seed, random_affine=True, **kw)
+
+
+# --------------------------------------------------------------------------
+# page constants
+# --------------------------------------------------------------------------
+def test_page_constants():
+    c = json.load(open(os.path.join(GOLDEN, "page_constants.json")))
+    assert oracle.EPS == c["norm_eps"]["value"]
+    # eta scaling by 1/d: sigmoid(0)/d for d = inner_size
+    d = c["default_inner_size"]["value"]
+    assert c["eta_unscaled_overshoot"]["value"] == d
+    x = make_case(1, 1, 1, d, 0)
+    x.eta_logit[:] = 0.0
+    x.v[:] = 0.0
+    # no LN, v = 0: W1 k = W0 k - eta (W0 k)(k.k), so the step recovers eta = sigmoid(0)/d
+    out, W1 = run(x, ln="none")
+    k = x.k[0, 0, 0].astype(np.float64)
+    z = x.W0[0, 0].astype(np.float64) @ k
+    step = (x.W0[0, 0] - W1[0, 0]) @ k / (z * (k @ k))
+    assert np.allclose(step, 0.5 / d, rtol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# the inner LayerNorm
+# --------------------------------------------------------------------------
+def test_layer_norm_matches_torch():
+    rng = np.random.default_rng(3)
+    z = rng.standard_normal((4, 7, 16)) * 0.3 + 0.1
+    g = 1 + 0.1 * rng.standard_normal(16)
+    b = 0.1 * rng.standard_normal(16)
+    pred, xhat, s = oracle.layer_norm(z, g, b)
+    ref = F.layer_norm(torch.tensor(z), (16,), torch.tensor(g), torch.tensor(b), eps=oracle.EPS)
+    assert np.allclose(pred, ref.numpy(), rtol=0, atol=1e-13)
+    # and the normalised part alone
+    ref0 = F.layer_norm(torch.tensor(z), (16,), eps=oracle.EPS)
+    assert np.allclose(xhat, ref0.numpy(), rtol=0, atol=1e-13)
+
+
+def test_layer_norm_moments():
+    rng = np.random.default_rng(4)
+    z = rng.standard_normal((50, 64)) * 0.05
+    _, xhat, s = oracle.layer_norm(z, np.ones(64), np.zeros(64))
+    var = z.var(axis=-1)                       # numpy's biased variance
+    assert np.allclose(xhat.mean(-1), 0.0, atol=1e-14)
+    assert np.allclose((xhat ** 2).mean(-1), var / (var + oracle.EPS), rtol=1e-12)
+    assert np.allclose(s[..., 0], np.sqrt(var + oracle.EPS), rtol=1e-14)
+
+
+def test_degenerate_layer_norm_gives_beta():
+    z = np.full((3, 8), 0.7)
+    g = np.arange(8.0)
+    b = np.linspace(-1, 1, 8)
+    pred, xhat, _ = oracle.layer_norm(z, g, b)
+    assert np.all(xhat == 0.0) and np.allclose(pred, b)
+
+
+# --------------------------------------------------------------------------
+# a hand-worked two-token example, d = 2, eps = 0
+# --------------------------------------------------------------------------
+def test_hand_worked_example():
+    # W0 = [[2,0],[0,1]], eta_logit = 0 -> eta = sigmoid(0)/2 = 0.25, gate 0 -> 0.5
+    # t=1: k=(1,1) z=(2,1) mu=1.5 s=0.5 xhat=(1,-1) pred=(1,-1) v=0 e=(1,-1)
+    #      W1 = W0 - 0.25 e k^T = [[1.75,-0.25],[0.25,1.25]]; q=(1,0) -> o=(0.875,0.125)
+    # t=2: k=(1,0) z=(1.75,0.25) mu=1 s=0.75 xhat=(1,-1) pred=(1,-1) v=(1,1) e=(0,-2)
+    #      W2 = W1 - 0.25 e k^T = [[1.75,-0.25],[0.75,1.25]]; q=(0,1) -> o=(-0.125,0.625)
+    W0 = np.array([[[[2.0, 0.0], [0.0, 1.0]]]])
+    k = np.array([[[[1.0, 1.0], [1.0, 0.0]]]])
+    v = np.array([[[[0.0, 0.0], [1.0, 1.0]]]])
+    q = np.array([[[[1.0, 0.0], [0.0, 1.0]]]])
+    eta = np.zeros((1, 1, 2))
+    gate = np.zeros((1, 1, 2, 2))
+    g, b = np.ones((1, 2)), np.zeros((1, 2))
+    out, W = oracle.ttt_linear_forward(q, k, v, eta, gate, W0, g, b, ln="st", eps=0.0)
+    assert np.allclose(W[0, 0], [[1.75, -0.25], [0.75, 1.25]], atol=1e-15)
+    assert np.allclose(out[0, 0], [[0.875, 0.125], [-0.125, 0.625]], atol=1e-15)
+    # exact mode at d = 2, eps = 0: LN output is the constant +-1, its Jacobian is 0,
+    # so the weight never moves and the output is the gated W0 q.
+    out_e, W_e = oracle.ttt_linear_forward(q, k, v, eta, gate, W0, g, b, ln="exact", eps=0.0)
+    assert np.allclose(W_e, W0, atol=1e-15)
+    assert np.allclose(out_e[0, 0], [[1.0, 0.0], [0.0, 0.5]], atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# eta -> 0 (eta_logit = -inf) and gate limits
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("ln", ["st", "exact", "none"])
+@pytest.mark.parametrize("dual", [False, True])
+def test_eta_zero_closed_form(ln, dual):
+    x = small(1)
+    x.eta_logit[:] = -np.inf
+    out, W = run(x, ln=ln, dual=dual, chunk=4)
+    assert np.array_equal(W, x.W0.astype(np.float64))
+    B, H, T, d = x.q.shape
+    for b in range(B):
+        for h in range(H):
+            for t in range(T):
+                u = [sum(float(x.W0[b, h, i, j]) * float(x.q[b, h, t, j]) for j in range(d))
+                     for i in range(d)]
+                gate = 1.0 / (1.0 + np.exp(-x.gate_logit[b, h, t].astype(np.float64)))
+                assert np.allclose(out[b, h, t], np.array(u) * gate, rtol=1e-13, atol=1e-15)
+
+
+def test_gate_limits():
+    x = small(2)
+    x.gate_logit[:] = np.inf
+    out_open, W = run(x)
+    x.gate_logit[:] = -np.inf
+    out_shut, W2 = run(x)
+    assert np.array_equal(W, W2)
+    assert np.all(out_shut == 0.0)
+    # gate fully open: o_t = W_t q_t; at the last token W_t is W_final
+    want = np.einsum("bhij,bhj->bhi", W, x.q[:, :, -1].astype(np.float64))
+    assert np.allclose(out_open[:, :, -1], want, rtol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# no LayerNorm: the delta rule of linear attention ("Key Innovations")
+# --------------------------------------------------------------------------
+def test_delta_rule_unrolled_product():
+    B, H, T, d = 1, 2, 6, 4
+    x = small(5, B=B, H=H, T=T, d=d)
+    out, W = run(x, ln="none")
+    for h in range(H):
+        k = x.k[0, h].astype(np.float64)
+        v = x.v[0, h].astype(np.float64)
+        q = x.q[0, h].astype(np.float64)
+        eta = 1.0 / (1.0 + np.exp(-x.eta_logit[0, h].astype(np.float64))) / d
+        A = [np.eye(d) - eta[t] * np.outer(k[t], k[t]) for t in range(T)]
+        # W_T = W0 A_1 ... A_T + sum_t eta_t v_t k_t^T A_{t+1} ... A_T
+        def prod(a, b):
+            m = np.eye(d)
+            for t in range(a, b):
+                m = m @ A[t]
+            return m
+        WT = x.W0[0, h].astype(np.float64) @ prod(0, T)
+        for t in range(T):
+            WT = WT + eta[t] * np.outer(v[t], k[t]) @ prod(t + 1, T)
+        assert np.allclose(W[0, h], WT, rtol=1e-12, atol=1e-14)
+        # outputs through the one-step form W_t = W_{t-1}(I - eta k k^T) + eta v k^T
+        Wt = x.W0[0, h].astype(np.float64)
+        for t in range(T):
+            Wt = Wt @ A[t] + eta[t] * np.outer(v[t], k[t])
+            g = 1.0 / (1.0 + np.exp(-x.gate_logit[0, h, t].astype(np.float64)))
+            assert np.allclose(out[0, h, t], (Wt @ q[t]) * g, rtol=1e-12, atol=1e-14)
+
+
+def test_overwrite_identity():
+    """eta_t ||k_t||^2 = 1 makes the no-LN step write v_t exactly at k_t."""
+    B, H, T, d = 1, 2, 7, 8
+    x = small(6, B=B, H=H, T=T, d=d)
+    k = x.k.astype(np.float64)
+    k = k / np.linalg.norm(k, axis=-1, keepdims=True) * np.sqrt(2.0 * d)   # ||k||^2 = 2d
+    x.k = k
+    x.q = k.copy()
+    x.eta_logit[:] = 0.0               # eta = 1/(2d)
+    out, _ = run(x, ln="none")
+    gate = 1.0 / (1.0 + np.exp(-x.gate_logit.astype(np.float64)))
+    assert np.allclose(out, x.v * gate, rtol=1e-11, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# inner gradients through a library autodiff
+# --------------------------------------------------------------------------
+def torch_scan(x, ln, dual=False, chunk=1, eps=oracle.EPS):
+    """The scan as gradient steps on the stated inner loss, via torch autograd."""
+    B, H, T, d = x.q.shape
+    tt = lambda a: torch.tensor(np.asarray(a, dtype=np.float64))
+    q, k, v, el, gl, W0 = map(tt, (x.q, x.k, x.v, x.eta_logit, x.gate_logit, x.W0))
+    gam, bet = tt(x.gamma), tt(x.beta)
+    out = torch.zeros(B, H, T, d, dtype=torch.float64)
+    Wfin = torch.zeros(B, H, d, d, dtype=torch.float64)
+    for b in range(B):
+        for h in range(H):
+            W = W0[b, h].clone()
+            Wc = W.clone()
+            for t in range(T):
+                if dual and t % chunk == 0:
+                    Wc = W.clone()
+                P = (Wc if dual else W).clone().requires_grad_(True)
+                z = P @ k[b, h, t]
+                if ln == "none":
+                    pred = z
+                else:
+                    lnz = F.layer_norm(z, (d,), gam[h], bet[h], eps=eps)
+                    # straight-through: forward value LN(z), derivative of the identity
+                    pred = lnz if ln == "exact" else z + (lnz - z).detach()
+                loss = 0.5 * ((pred - v[b, h, t]) ** 2).sum()
+                (grad,) = torch.autograd.grad(loss, P)
+                eta = torch.sigmoid(el[b, h, t]) / d
+                W = W - eta * grad
+                out[b, h, t] = (W @ q[b, h, t]) * torch.sigmoid(gl[b, h, t])
+            Wfin[b, h] = W
+    return out.numpy(), Wfin.numpy()
+
+
+@pytest.mark.parametrize("ln", ["st", "exact", "none"])
+def test_scan_equals_autograd_inner_steps(ln):
+    x = small(7, B=1, H=2, T=6, d=6)
+    out, W = run(x, ln=ln)
+    out_t, W_t = torch_scan(x, ln)
+    assert np.allclose(out, out_t, rtol=1e-11, atol=1e-13)
+    assert np.allclose(W, W_t, rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("ln", ["st", "exact"])
+@pytest.mark.parametrize("chunk", [2, 4, 7])
+def test_dual_equals_autograd_at_chunk_start(ln, chunk):
+    x = small(8, B=1, H=2, T=9, d=5)
+    out, W = run(x, ln=ln, dual=True, chunk=chunk)
+    out_t, W_t = torch_scan(x, ln, dual=True, chunk=chunk)
+    assert np.allclose(out, out_t, rtol=1e-11, atol=1e-13)
+    assert np.allclose(W, W_t, rtol=1e-11, atol=1e-13)
+
+
+def test_exact_gradient_finite_differences():
+    """d/dW 0.5||LN(Wk) - v||^2 = (J^T e) k^T, by central differences."""
+    rng = np.random.default_rng(9)
+    d = 6
+    W = rng.standard_normal((d, d)) * 0.3
+    k = rng.standard_normal(d)
+    v = rng.standard_normal(d)
+    g = 1 + 0.1 * rng.standard_normal(d)
+    b = 0.1 * rng.standard_normal(d)
+
+    def loss(Wm):
+        pred, _, _ = oracle.layer_norm(Wm @ k, g, b)
+        return 0.5 * np.sum((pred - v) ** 2)
+
+    delta = oracle.inner_grad_vector(W @ k, v, g, b, "exact")
+    analytic = np.outer(delta, k)
+    h = 1e-6
+    fd = np.zeros_like(W)
+    for i in range(d):
+        for j in range(d):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[i, j] += h
+            Wm[i, j] -= h
+            fd[i, j] = (loss(Wp) - loss(Wm)) / (2 * h)
+    assert np.allclose(fd, analytic, rtol=1e-7, atol=1e-8)
+
+
+def test_exact_jacobian_reduction_form():
+    """Explicit J^T e equals (d g - sum g - xhat sum(g xhat)) / (d s), g = gamma*e."""
+    rng = np.random.default_rng(10)
+    d = 64
+    z = rng.standard_normal((5, d)) * 0.2
+    v = rng.standard_normal((5, d))
+    gam = 1 + 0.1 * rng.standard_normal(d)
+    bet = 0.1 * rng.standard_normal(d)
+    delta = oracle.inner_grad_vector(z, v, gam, bet, "exact")
+    mu = z.mean(-1, keepdims=True)
+    s = np.sqrt(((z - mu) ** 2).mean(-1, keepdims=True) + oracle.EPS)
+    xh = (z - mu) / s
+    g = gam * (gam * xh + bet - v)
+    want = (d * g - g.sum(-1, keepdims=True) - xh * (g * xh).sum(-1, keepdims=True)) / (d * s)
+    assert np.allclose(delta, want, rtol=1e-12, atol=1e-14)
+
+
+def test_prediction_cancellation():
+    """At gamma=1, beta=0: J^T xhat = eps * xhat / s^3, zero when eps = 0.
+
+    Error Correction in Trained TTT Layers (abstract): the prediction-derived
+    part of the LayerNorm inner gradient cancels at this initialisation in the
+    zero-epsilon limit.  With v = 0 the whole error is that part, so exact
+    mode leaves W fixed at eps = 0 while the straight-through gradient moves it.
+    """
+    rng = np.random.default_rng(11)
+    d = 16
+    z = rng.standard_normal((4, d)) * 0.1
+    for eps in (1e-6, 1e-3, 0.0):
+        _, xhat, s = oracle.layer_norm(z, np.ones(d), np.zeros(d), eps)
+        J = oracle.ln_jacobian(xhat, s, np.ones(d))
+        got = np.einsum("nim,ni->nm", J, xhat)
+        assert np.allclose(got, eps * xhat / s ** 3, rtol=1e-10, atol=1e-14)
+    x = make_case(1, 2, 12, d, 12)
+    x.v[:] = 0.0
+    _, W_ex = run(x, ln="exact", eps=0.0)
+    _, W_st = run(x, ln="st", eps=0.0)
+    assert np.allclose(W_ex, x.W0, rtol=0, atol=1e-14)
+    assert np.max(np.abs(W_st - x.W0)) > 1e-2
+
+
+# --------------------------------------------------------------------------
+# dual form: special cases and closed forms
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("ln", ["st", "exact", "none"])
+def test_dual_chunk1_is_per_token_bitwise(ln):
+    x = small(13)
+    a = run(x, ln=ln, dual=False)
+    b = run(x, ln=ln, dual=True, chunk=1)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def _chunk_matrix_form(W0, Q, K, V, el, gl, gam, bet, ln):
+    """One chunk in matrix form: O = (Q W0^T - tril(eta-scaled Q K^T) D) * sig(G)."""
+    d = W0.shape[0]
+    Z = K @ W0.T
+    if ln == "none":
+        Dl = Z - V
+    else:
+        zt = torch.tensor(Z, requires_grad=True)
+        lnz = F.layer_norm(zt, (d,), torch.tensor(gam), torch.tensor(bet), eps=oracle.EPS)
+        if ln == "exact":
+            loss = 0.5 * ((lnz - torch.tensor(V)) ** 2).sum()
+            (Dt,) = torch.autograd.grad(loss, zt)
+            Dl = Dt.numpy()
+        else:
+            Dl = lnz.detach().numpy() - V
+    eta = 1.0 / (1.0 + np.exp(-el)) / d
+    A = np.tril((Q @ K.T) * eta[None, :])
+    O = (Q @ W0.T - A @ Dl) / (1.0 + np.exp(-gl))
+    WT = W0 - (eta[:, None] * Dl).T @ K
+    return O, WT
+
+
+@pytest.mark.parametrize("ln", ["st", "exact", "none"])
+@pytest.mark.parametrize("T,chunk", [(8, 8), (8, 32), (11, 4), (16, 4), (5, 3)])
+def test_dual_matrix_form(ln, T, chunk):
+    """Chunk by chunk (last chunk short), the matrix form equals the token loop."""
+    x = small(14, B=1, H=2, T=T, d=6)
+    out, W = run(x, ln=ln, dual=True, chunk=chunk)
+    f = lambda a: np.asarray(a, dtype=np.float64)
+    for h in range(2):
+        Wc = f(x.W0[0, h])
+        for c0 in range(0, T, chunk):
+            sl = slice(c0, min(T, c0 + chunk))
+            O, Wc = _chunk_matrix_form(Wc, f(x.q[0, h, sl]), f(x.k[0, h, sl]), f(x.v[0, h, sl]),
+                                       f(x.eta_logit[0, h, sl]), f(x.gate_logit[0, h, sl]),
+                                       f(x.gamma[h]), f(x.beta[h]), ln)
+            assert np.allclose(out[0, h, sl], O, rtol=1e-11, atol=1e-13)
+        assert np.allclose(W[0, h], Wc, rtol=1e-11, atol=1e-13)
+
+
+def test_dual_no_ln_single_chunk_closed_form():
+    """b >= T, no LN: W_T = W0 (I - sum eta k k^T) + sum eta v k^T."""
+    T, d = 7, 5
+    x = small(15, B=1, H=1, T=T, d=d)
+    _, W = run(x, ln="none", dual=True, chunk=T)
+    k, v = x.k[0, 0].astype(np.float64), x.v[0, 0].astype(np.float64)
+    eta = 1.0 / (1.0 + np.exp(-x.eta_logit[0, 0].astype(np.float64))) / d
+    S = sum(eta[t] * np.outer(k[t], k[t]) for t in range(T))
+    R = sum(eta[t] * np.outer(v[t], k[t]) for t in range(T))
+    assert np.allclose(W[0, 0], x.W0[0, 0] @ (np.eye(d) - S) + R, rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# state carry and independence
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("ln,dual,chunk,T1", [("st", False, 1, 5), ("exact", False, 1, 3),
+                                              ("st", True, 4, 8), ("none", True, 3, 6)])
+def test_resume(ln, dual, chunk, T1):
+    x = small(16, T=14)
+    out, W = run(x, ln=ln, dual=dual, chunk=chunk)
+    cut = lambda a, sl: np.ascontiguousarray(a[:, :, sl])
+    args1 = [cut(a, slice(0, T1)) for a in (x.q, x.k, x.v, x.eta_logit, x.gate_logit)]
+    args2 = [cut(a, slice(T1, None)) for a in (x.q, x.k, x.v, x.eta_logit, x.gate_logit)]
+    o1, W1 = oracle.ttt_linear_forward(*args1, x.W0, x.gamma, x.beta, ln=ln, dual=dual, chunk=chunk)
+    o2, W2 = oracle.ttt_linear_forward(*args2, W1, x.gamma, x.beta, ln=ln, dual=dual, chunk=chunk)
+    assert np.array_equal(np.concatenate([o1, o2], axis=2), out)
+    assert np.array_equal(W2, W)
+
+
+def test_scans_independent_under_permutation():
+    x = small(17, B=3, H=2)
+    out, W = run(x)
+    pairs = [(2, 1), (0, 0), (1, 1), (0, 1)]
+    s = x.subset(pairs)
+    o2, W2 = run(s)
+    for n, (b, h) in enumerate(pairs):
+        assert np.array_equal(o2[0, n], out[b, h])
+        assert np.array_equal(W2[0, n], W[b, h])
+
+
+def test_empty_sequence_returns_initial_state():
+    x = small(18, T=0)
+    out, W = run(x)
+    assert out.shape == (2, 3, 0, 5)
+    assert np.array_equal(W, x.W0)
