@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Throughput of the TTT-Linear scan on one MI355X.
+
+One step is one call of ``ttt_linear_forward`` over the whole workload (every
+(batch, head) scan over the full sequence), with the inputs already resident
+in device memory.  W warm-up steps run untimed; then exactly K steps are
+timed between two device synchronisations, and each launch is also bracketed
+by events on its stream for the per-kernel duration.  Rank 0 prints one JSON
+line.
+
+The default workload is the 256-scan per-token scan with bf16 inputs
+(B=16, H=16, T=4096, d=64, hidden 1024).  The float64 CPU oracle is timed on
+a bounded sample of the same workload (a subset of the scans at full length,
+split over worker processes) as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+from test_rnn_layer_ttt_amd.inputs import WORKLOADS, make_inputs  # noqa: E402
+
+METRIC = "TTT-Linear scan token-heads/s at d=64 + % of HBM/FP32 roofline, 1 MI355X"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # 256 CU x 2.4 GHz x 256 flop/clk (packed FMA), published
+FP32_MATRIX_PEAK_TFLOPS = 157.3  # MFMA fp32, published
+BF16_MATRIX_PEAK_TFLOPS = 2500.0  # dense MFMA bf16, published
+
+
+def algorithmic_work(x):
+    """Compulsory HBM bytes and flops of one launch (counted per token-head)."""
+    B, H, T, d = x.q.shape
+    n = B * H * T
+    s_in = 2 if x.in_bf16 else 4
+    per_tok_bytes = (4 * d + 1) * s_in + 4 * d        # q,k,v,gate,eta in; out fp32
+    nbytes = n * per_tok_bytes + B * H * 8 * d * d + H * 8 * d
+    per_tok_flops = 6 * d * d + (4 * x.chunk * d if x.dual else 0)
+    return n, nbytes, n * per_tok_flops
+
+
+def kernel_info(x):
+    """Which kernel family runs this workload and which roof bounds it."""
+    import test_rnn_layer_ttt_amd as ttt
+    d = x.q.shape[-1]
+    name = ttt.ttt_linear_kernel(d, ttt.mode_bits(x.ln, x.dual, x.in_bf16), x.chunk)
+    if name == "scan_mfma":
+        # the d^2 work runs on the matrix cores: the HBM stream is the binding roof
+        return name, "hbm"
+    # vector-ALU scan: bf16 inputs put it above the FP32-vector ridge, fp32 inputs below
+    return name, ("alu" if x.in_bf16 else "hbm")
+
+
+def roofline(x, kernel_ms, traffic):
+    n, nbytes, flops = algorithmic_work(x)
+    name, bound = kernel_info(x)
+    sec = kernel_ms / 1e3
+    if bound == "hbm":
+        achieved = nbytes / sec / 1e9
+        return name, dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+                          unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic)
+    achieved = flops / sec / 1e12
+    return name, dict(bound="alu", achieved=round(achieved, 2), peak=FP32_VECTOR_PEAK_TFLOPS,
+                      unit="TFLOP/s", frac=round(achieved / FP32_VECTOR_PEAK_TFLOPS, 4),
+                      traffic=traffic)
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the float64 oracle, unmodified, on a bounded sample
+# ---------------------------------------------------------------------------
+_CPU_SAMPLE = None
+
+
+def _oracle_worker(idx):
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    x = _CPU_SAMPLE
+    with threadpool_limits(limits=1):
+        oracle.ttt_linear_forward(
+            x.q[:, idx], x.k[:, idx], x.v[:, idx], x.eta_logit[:, idx], x.gate_logit[:, idx],
+            x.W0[:, idx], x.gamma[idx], x.beta[idx], ln=x.ln, dual=x.dual, chunk=x.chunk)
+    return len(idx)
+
+
+def cpu_baseline(x, n_scans, workers):
+    """Time the oracle on ``n_scans`` scans of ``x`` (full length) over ``workers`` processes."""
+    import multiprocessing as mp
+    global _CPU_SAMPLE
+    B, H, T, d = x.q.shape
+    n_scans = min(n_scans, B * H)
+    step = max(1, (B * H) // n_scans)
+    pairs = [(i // H, i % H) for i in range(0, B * H, step)][:n_scans]
+    _CPU_SAMPLE = x.subset(pairs)
+    groups = [list(range(w, n_scans, workers)) for w in range(workers)]
+    groups = [g for g in groups if g]
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(len(groups)) as pool:
+        done = sum(pool.map(_oracle_worker, groups))
+    sec = time.perf_counter() - t0
+    _CPU_SAMPLE = None
+    return dict(value=round(done * T / sec, 1), unit="token-heads/s", cores=len(groups),
+                kind="oracle",
+                sample=f"{done} of {B * H} scans at full length T={T} (float64 NumPy, "
+                       f"{len(groups)} processes x 1 BLAS thread, {sec:.1f} s wall)")
+
+
+def host_cores():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+# ---------------------------------------------------------------------------
+def load_traffic(kernel, workload):
+    """HBM traffic measured by rocprofv3 counters for this kernel and source, if recorded."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{kernel}|{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    from test_rnn_layer_ttt_amd.build import source_digest
+    if rec.get("source_digest") != source_digest():
+        return None        # the kernel changed since the counters were taken
+    return rec.get("traffic_bytes")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="h1024_T4096_bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-scans", type=int, default=128,
+                    help="scans of the workload the CPU oracle is timed on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only; the scans of a workload shard "
+              "over GPUs by (batch, head) with no communication, and no multi-GPU figure "
+              "is produced.", file=sys.stderr)
+        sys.exit(2)
+
+    x = make_inputs(args.workload)
+    B, H, T, d = x.q.shape
+
+    # the CPU baseline runs before any GPU use (its workers are forked)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(x, args.cpu_scans, host_cores())
+
+    import torch
+
+    import test_rnn_layer_ttt_amd as ttt
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dt = torch.bfloat16 if x.in_bf16 else torch.float32
+    f = lambda a: torch.from_numpy(a).to(dev).to(dt)
+    q, k, v, el, gl = f(x.q), f(x.k), f(x.v), f(x.eta_logit), f(x.gate_logit)
+    W0 = torch.from_numpy(x.W0).to(dev)
+    gamma = torch.from_numpy(x.gamma).to(dev)
+    beta = torch.from_numpy(x.beta).to(dev)
+    out = torch.empty((B, H, T, d), dtype=torch.float32, device=dev)
+    Wf = torch.empty_like(W0)
+    stream = torch.cuda.current_stream(dev)
+    mode = ttt.mode_bits(x.ln, x.dual, x.in_bf16)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), el.data_ptr(), gl.data_ptr(),
+            W0.data_ptr(), gamma.data_ptr(), beta.data_ptr(), out.data_ptr(), Wf.data_ptr())
+
+    def step():
+        st = ttt.ttt_linear_forward(*ptrs, B, H, T, d, mode, x.chunk, stream.cuda_stream)
+        if st != ttt.TTT_OK:
+            raise RuntimeError(f"ttt_linear_forward: {ttt.ttt_status_string(st)}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_kernel_ms = float(np.mean(kernel_ms))
+    ms_per_step = wall * 1e3 / args.steps
+    n_tok = B * H * T
+    kernel, _ = kernel_info(x)
+    kname, roof = roofline(x, avg_kernel_ms, load_traffic(kernel, args.workload))
+
+    mode_name = ("dual-form chunk %d" % x.chunk if x.dual else "per-token") + \
+        {"st": "", "exact": ", exact LN Jacobian", "none": ", no LN"}[x.ln]
+    line = {
+        "metric": METRIC,
+        "value": round(n_tok / (ms_per_step / 1e3), 1),
+        "unit": "token-heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "H": H, "T": T, "d": d,
+                   "hidden": H * d, "mode": mode_name,
+                   "inputs": "bf16" if x.in_bf16 else "fp32", "state": "fp32",
+                   "kernel": kname, "kernel_ms_avg": round(avg_kernel_ms, 4),
+                   "kernel_ms_min": round(min(kernel_ms), 4)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,122 @@
+/*
+ * ttt_linear.h -- C ABI of the TTT-Linear fast-weight scan on gfx950 (MI355X).
+ *
+ * The operation ("Edifice.Recurrent.TTT", sections "Equations (TTT-Linear)",
+ * "Architecture" and "Paper-Faithful Implementation"): for every
+ * (batch b, head h) an inner weight W (d x d, fp32) starts at W0[b,h] and, for
+ * t = 0 .. T-1,
+ *
+ *     eta_t   = sigmoid(eta_logit[b,h,t]) / d
+ *     z_t     = P k_t                        (z_i = sum_j P[i][j] k_t[j])
+ *     pred_t  = gamma[h] * (z_t - mean) / sqrt(var + 1e-6) + beta[h]
+ *                                            (biased variance over the d entries)
+ *     e_t     = pred_t - v_t
+ *     delta_t = e_t                          (default: the page's grad_W = e_t k_t^T)
+ *             | J_LN(z_t)^T e_t              (TTT_LN_EXACT: exact gradient of
+ *                                             0.5*||LN(z)-v||^2, "Error Correction in
+ *                                             Trained TTT Layers", abstract)
+ *             | z_t - v_t                    (TTT_NO_LN: LayerNorm removed; the
+ *                                             delta rule of linear attention)
+ *     W       = W - eta_t * delta_t k_t^T
+ *     out[b,h,t] = (W q_t) * sigmoid(gate_logit[b,h,t])   (updated W; elementwise gate)
+ *
+ * P is the current W (per-token mode) or, with TTT_DUAL, the weight at the
+ * start of t's chunk of `chunk` tokens (the dual-form / mini-batch update of
+ * "PonderTTT", "Technical Architecture", with the chunking of cortex_rust's
+ * forward_chunkwise: a final chunk may be shorter).  W_final receives W after
+ * the last token, so a scan can be resumed by passing it back as W0.
+ *
+ * Layout: every array is dense, row-major, C-contiguous, in device memory
+ * (hipMalloc'd or equivalent):
+ *     q, k, v, gate_logit   [B,H,T,d]  fp32, or bf16 when TTT_IN_BF16
+ *     eta_logit             [B,H,T]    same element type as q
+ *     W0, W_final           [B,H,d,d]  fp32
+ *     gamma, beta           [H,d]      fp32 (unused, may be NULL, with TTT_NO_LN)
+ *     out                   [B,H,T,d]  fp32
+ *
+ * Ownership: the caller owns every buffer.  The library allocates nothing,
+ * keeps no pointer after returning and holds no mutable global state; calls
+ * are reentrant.  Inputs are read-only and may alias one another (q == k is
+ * fine).  `out` must not overlap any other argument.  W_final may be NULL (not
+ * written), may equal W0 exactly (in-place state update), and must not
+ * overlap anything else.
+ *
+ * Errors: every argument check below runs before any HIP call, so all of them
+ * can be exercised on a host without a GPU.  The kernel is launched
+ * asynchronously on `stream` (a hipStream_t; NULL = the default stream); a
+ * device fault surfaces at the caller's next synchronisation.  No exception
+ * crosses this boundary.
+ */
+#ifndef TTT_LINEAR_H_
+#define TTT_LINEAR_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* mode bits */
+#define TTT_DUAL      1u  /* chunk-start gradients (dual form); needs chunk >= 1 */
+#define TTT_LN_EXACT  2u  /* LayerNorm Jacobian applied to the error */
+#define TTT_IN_BF16   4u  /* q, k, v, eta_logit, gate_logit are bf16 */
+#define TTT_NO_LN     8u  /* inner LayerNorm removed (delta rule); excludes TTT_LN_EXACT */
+
+/* status codes */
+#define TTT_OK               0
+#define TTT_ERR_NULL         1  /* a required pointer is NULL */
+#define TTT_ERR_SHAPE        2  /* B, H or d < 1, T < 0, or a size overflows */
+#define TTT_ERR_MODE         3  /* unknown mode bit, EXACT|NO_LN, or DUAL with chunk < 1 */
+#define TTT_ERR_UNSUPPORTED  4  /* d not in {16, 32, 64, 128}, or a misaligned pointer */
+#define TTT_ERR_ALIAS        5  /* out overlaps an argument, or W_final partially overlaps */
+#define TTT_ERR_HIP          6  /* the HIP runtime reported an error at launch */
+
+/*
+ * Run the scan over all B*H (batch, head) pairs.
+ *
+ * d must be 16, 32, 64 or 128.  Pointers to the [.,d]- and [.,d,d]-shaped
+ * arrays must be 16-byte aligned; eta_logit, gamma and beta need only their
+ * element alignment.  `chunk` is read only when TTT_DUAL is set.  The
+ * LayerNorm epsilon is fixed at 1e-6 (inside the square root).
+ * T == 0 writes nothing to `out` and copies W0 to W_final (if distinct and
+ * non-NULL); q, k, v, eta_logit, gate_logit and out may then be NULL.
+ *
+ * Returns TTT_OK or one of the TTT_ERR_* codes above.
+ */
+int32_t ttt_linear_forward(const void* q, const void* k, const void* v,
+                           const void* eta_logit, const void* gate_logit,
+                           const float* W0, const float* gamma, const float* beta,
+                           float* out, float* W_final,
+                           int64_t B, int64_t H, int64_t T, int64_t d,
+                           uint32_t mode, int64_t chunk, void* stream);
+
+/*
+ * Run only the argument checks of ttt_linear_forward (same arguments, no
+ * stream) and return the status it would return before launching.  Makes no
+ * HIP call and touches no memory behind the pointers.
+ */
+int32_t ttt_linear_validate(const void* q, const void* k, const void* v,
+                            const void* eta_logit, const void* gate_logit,
+                            const float* W0, const float* gamma, const float* beta,
+                            float* out, float* W_final,
+                            int64_t B, int64_t H, int64_t T, int64_t d,
+                            uint32_t mode, int64_t chunk);
+
+/*
+ * The kernel family a valid call with this d, mode and chunk launches:
+ * "scan_mfma" (matrix-core chunk scan) or "scan_valu" (vector-ALU scan), or
+ * "none" if the combination is not supported.  For profiling and reporting.
+ */
+const char* ttt_linear_kernel(int64_t d, uint32_t mode, int64_t chunk);
+
+/* A static, human-readable description of a status code (never NULL). */
+const char* ttt_status_string(int32_t status);
+
+/* A static version string of the library (never NULL). */
+const char* ttt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTT_LINEAR_H_ */

@@ -1,0 +1,184 @@
+// C-ABI entry points of the TTT-Linear scan library: argument validation,
+// alias checks, and dispatch to the gfx950 kernels.  Every check runs before
+// the first HIP call, so the error paths are testable on a host without a GPU.
+#include "ttt_linear.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "scan_common.h"
+
+namespace {
+
+constexpr float kLnEps = 1e-6f;  // cortex_rust ttt.rs, TTT_NORM_EPS
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range span(const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlaps(const Range& a, const Range& b) {
+  if (a.lo == 0 || b.lo == 0 || a.hi == a.lo || b.hi == b.lo) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, uintptr_t n) {
+  return (reinterpret_cast<uintptr_t>(p) % n) == 0;
+}
+
+// a * b with overflow detection for non-negative operands
+bool mul_ok(int64_t a, int64_t b, int64_t* r) {
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *r = a * b;
+  return true;
+}
+
+// Every argument check of ttt_linear_forward; fills *a on success.  Makes
+// no HIP call.
+int32_t validate(const void* q, const void* k, const void* v, const void* eta_logit,
+                 const void* gate_logit, const float* W0, const float* gamma,
+                 const float* beta, float* out, float* W_final, int64_t B, int64_t H,
+                 int64_t T, int64_t d, uint32_t mode, int64_t chunk, ttt::ScanArgs* a) {
+  // ---- mode ----
+  const uint32_t known = TTT_DUAL | TTT_LN_EXACT | TTT_IN_BF16 | TTT_NO_LN;
+  if (mode & ~known) return TTT_ERR_MODE;
+  if ((mode & TTT_LN_EXACT) && (mode & TTT_NO_LN)) return TTT_ERR_MODE;
+  const bool dual = (mode & TTT_DUAL) != 0;
+  if (dual && chunk < 1) return TTT_ERR_MODE;
+  const bool no_ln = (mode & TTT_NO_LN) != 0;
+  const bool bf16 = (mode & TTT_IN_BF16) != 0;
+
+  // ---- shapes ----
+  if (B < 1 || H < 1 || d < 1 || T < 0) return TTT_ERR_SHAPE;
+  int64_t BH, BHT, seq_elems, dd, w_elems;
+  if (!mul_ok(B, H, &BH) || BH > INT32_MAX) return TTT_ERR_SHAPE;
+  if (!mul_ok(BH, T, &BHT) || !mul_ok(BHT, d, &seq_elems)) return TTT_ERR_SHAPE;
+  if (!mul_ok(d, d, &dd) || !mul_ok(BH, dd, &w_elems)) return TTT_ERR_SHAPE;
+  if (w_elems > INT64_MAX / 4 || !mul_ok(H, d, &dd) || dd > INT64_MAX / 4) return TTT_ERR_SHAPE;
+  if (seq_elems > INT64_MAX / 4) return TTT_ERR_SHAPE;
+
+  // ---- pointers ----
+  if (W0 == nullptr) return TTT_ERR_NULL;
+  if (!no_ln && (gamma == nullptr || beta == nullptr)) return TTT_ERR_NULL;
+  if (T > 0 && (q == nullptr || k == nullptr || v == nullptr || eta_logit == nullptr ||
+                gate_logit == nullptr || out == nullptr))
+    return TTT_ERR_NULL;
+
+  // ---- supported sizes and alignment ----
+  if (d != 16 && d != 32 && d != 64 && d != 128) return TTT_ERR_UNSUPPORTED;
+  const int64_t in_size = bf16 ? 2 : 4;
+  if (!aligned(W0, 16) || (W_final && !aligned(W_final, 16))) return TTT_ERR_UNSUPPORTED;
+  if (!no_ln && (!aligned(gamma, 4) || !aligned(beta, 4))) return TTT_ERR_UNSUPPORTED;
+  if (T > 0) {
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(gate_logit, 16) ||
+        !aligned(out, 16) || !aligned(eta_logit, static_cast<uintptr_t>(in_size)))
+      return TTT_ERR_UNSUPPORTED;
+  }
+
+  // ---- aliasing ----
+  const Range r_out = span(out, T > 0 ? seq_elems * 4 : 0);
+  const Range r_w0 = span(W0, w_elems * 4);
+  const Range r_wf = span(W_final, W_final ? w_elems * 4 : 0);
+  const Range inputs[] = {span(q, T > 0 ? seq_elems * in_size : 0),
+                          span(k, T > 0 ? seq_elems * in_size : 0),
+                          span(v, T > 0 ? seq_elems * in_size : 0),
+                          span(gate_logit, T > 0 ? seq_elems * in_size : 0),
+                          span(eta_logit, T > 0 ? BHT * in_size : 0),
+                          span(gamma, no_ln ? 0 : H * d * 4),
+                          span(beta, no_ln ? 0 : H * d * 4)};
+  for (const Range& r : inputs) {
+    if (overlaps(r_out, r) || overlaps(r_wf, r)) return TTT_ERR_ALIAS;
+  }
+  if (overlaps(r_out, r_w0) || overlaps(r_out, r_wf)) return TTT_ERR_ALIAS;
+  if (W_final && W_final != W0 && overlaps(r_wf, r_w0)) return TTT_ERR_ALIAS;
+
+  *a = ttt::ScanArgs{};
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->eta_logit = eta_logit;
+  a->gate_logit = gate_logit;
+  a->W0 = W0;
+  a->gamma = no_ln ? nullptr : gamma;
+  a->beta = no_ln ? nullptr : beta;
+  a->out = out;
+  a->W_final = W_final;
+  a->B = B;
+  a->H = H;
+  a->T = T;
+  a->d = d;
+  a->ln = no_ln ? ttt::kLnNone : ((mode & TTT_LN_EXACT) ? ttt::kLnExact : ttt::kLnST);
+  a->dual = dual;
+  a->chunk = dual ? chunk : 1;
+  a->in_bf16 = bf16;
+  a->eps = kLnEps;
+  return TTT_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t ttt_linear_validate(const void* q, const void* k, const void* v,
+                                       const void* eta_logit, const void* gate_logit,
+                                       const float* W0, const float* gamma, const float* beta,
+                                       float* out, float* W_final, int64_t B, int64_t H,
+                                       int64_t T, int64_t d, uint32_t mode, int64_t chunk) {
+  ttt::ScanArgs a;
+  return validate(q, k, v, eta_logit, gate_logit, W0, gamma, beta, out, W_final, B, H, T, d,
+                  mode, chunk, &a);
+}
+
+extern "C" int32_t ttt_linear_forward(const void* q, const void* k, const void* v,
+                                      const void* eta_logit, const void* gate_logit,
+                                      const float* W0, const float* gamma, const float* beta,
+                                      float* out, float* W_final, int64_t B, int64_t H,
+                                      int64_t T, int64_t d, uint32_t mode, int64_t chunk,
+                                      void* stream) {
+  ttt::ScanArgs a;
+  const int32_t st = validate(q, k, v, eta_logit, gate_logit, W0, gamma, beta, out, W_final,
+                              B, H, T, d, mode, chunk, &a);
+  if (st != TTT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    if (W_final && W_final != W0) {
+      const size_t bytes = static_cast<size_t>(B * H * d * d) * sizeof(float);
+      if (hipMemcpyAsync(W_final, W0, bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        return TTT_ERR_HIP;
+    }
+    return TTT_OK;
+  }
+  const hipError_t err = ttt::scan_mfma_supports(a) ? ttt::launch_scan_mfma(a, s)
+                                                    : ttt::launch_scan_valu(a, s);
+  return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+extern "C" const char* ttt_linear_kernel(int64_t d, uint32_t mode, int64_t chunk) {
+  // a 16-byte aligned stand-in for every pointer: only the mode and sizes matter here
+  alignas(16) static const float dummy[4] = {0, 0, 0, 0};
+  const void* p = dummy;
+  float* o = reinterpret_cast<float*>(0x100000);  // never dereferenced
+  ttt::ScanArgs a;
+  if (validate(p, p, p, p, p, dummy, dummy, dummy, o, nullptr, 1, 1, 1, d, mode, chunk, &a) !=
+      TTT_OK)
+    return "none";
+  return ttt::scan_mfma_supports(a) ? "scan_mfma" : "scan_valu";
+}
+
+extern "C" const char* ttt_status_string(int32_t status) {
+  switch (status) {
+    case TTT_OK: return "ok";
+    case TTT_ERR_NULL: return "a required pointer is NULL";
+    case TTT_ERR_SHAPE: return "invalid shape (B, H, d must be >= 1, T >= 0, sizes must not overflow)";
+    case TTT_ERR_MODE: return "invalid mode (unknown bit, LN_EXACT with NO_LN, or DUAL with chunk < 1)";
+    case TTT_ERR_UNSUPPORTED: return "unsupported (d must be 16, 32, 64 or 128; pointers must be aligned)";
+    case TTT_ERR_ALIAS: return "out or W_final overlaps another argument";
+    case TTT_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+extern "C" const char* ttt_version(void) { return "ttt_linear 0.1.0 (gfx950)"; }
