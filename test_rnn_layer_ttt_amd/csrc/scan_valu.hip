@@ -91,6 +91,7 @@ scan_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   constexpr int VE = BF16 ? 8 : 4;        // elements per 16-byte vector
   constexpr int NVEC = kTileElems / VE;   // vectors per array per tile
   constexpr int NV = (NVEC + NT - 1) / NT;
+  constexpr int NE = (TT + NT - 1) / NT;   // eta values per thread per tile
   constexpr float kInvD = 1.0f / D;
 
   __shared__ __align__(16) float sK[kTileElems];
@@ -133,7 +134,7 @@ scan_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   }
 
   uint4 pre[4][NV];
-  float pre_eta = 0.0f;
+  float pre_eta[NE];
   auto load_tile = [&](int64_t tile) {
     const int64_t base = tile * TT * D;
 #pragma unroll
@@ -147,14 +148,18 @@ scan_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         pre[a][r] = x;
       }
     }
-    if (tid < TT) {
-      const int64_t t = tile * TT + tid;
-      if (t < T) {
+#pragma unroll
+    for (int r = 0; r < NE; ++r) {
+      const int j = tid + r * NT;
+      const int64_t t = tile * TT + j;
+      float x = 0.0f;
+      if (j < TT && t < T) {
         if constexpr (BF16)
-          pre_eta = __uint_as_float(static_cast<uint32_t>(eta[t]) << 16);
+          x = __uint_as_float(static_cast<uint32_t>(eta[t]) << 16);
         else
-          pre_eta = eta[t];
+          x = eta[t];
       }
+      pre_eta[r] = x;
     }
   };
   auto store_tile = [&]() {
@@ -178,7 +183,11 @@ scan_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         }
       }
     }
-    if (tid < TT) sEta[tid] = fast_sigmoid(pre_eta) * kInvD;
+#pragma unroll
+    for (int r = 0; r < NE; ++r) {
+      const int j = tid + r * NT;
+      if (j < TT) sEta[j] = fast_sigmoid(pre_eta[r]) * kInvD;
+    }
   };
 
   int par = 0;
