@@ -146,7 +146,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="h1024_T4096_bf16", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-scans", type=int, default=128,
+    ap.add_argument("--cpu-scans", type=int, default=256,
                     help="scans of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
