@@ -1,7 +1,486 @@
-// MFMA chunk scan (d = 64).  Not built yet: every call goes to the VALU scan.
+// Matrix-core chunk scan of the TTT-Linear recurrence for d = 64 (gfx950).
+//
+// Recurrence: "Edifice.Recurrent.TTT", "Equations (TTT-Linear)"; exact
+// LayerNorm gradient: "Error Correction in Trained TTT Layers", abstract;
+// chunk-start gradients: "PonderTTT", "Technical Architecture" (dual form).
+//
+// The sequence is cut into tiles of 16 tokens.  With W_c the weight at the
+// start of a tile, E_s = eta_s delta_s and k_s.k_t the key Gram matrix, the
+// per-token recurrence is, exactly,
+//
+//   z_t = W_c k_t - sum_{s<t in tile} eta_s (k_s.k_t) delta_s      (gradient point)
+//   o_t = W_c q_t - sum_{s<=t in tile} eta_s (k_s.q_t) delta_s     (= W_t q_t)
+//   W_{c+1} = W_c - sum_s eta_s delta_s k_s^T
+//
+// so every d x d product is a dense tile contraction (K W_c^T, Q W_c^T, K K^T,
+// K Q^T, the output correction and the rank-16 update) and runs on MFMA; the
+// only serial part left is, per token, the d-vector correction, the LayerNorm
+// statistics and delta (one wave, 64 lanes = 64 rows, DPP + permlane
+// reductions).  The dual form drops the in-tile correction of z_t (tile =
+// chunk = 16), which makes the 16 tokens of a tile independent.
+//
+// Precision: W is kept in fp32 as MFMA accumulators.  With bf16 inputs every
+// product runs as bf16 MFMA with fp32 accumulation; the fp32 operands (W,
+// delta, the eta-scaled Gram entries) are split into bf16 hi + lo parts, so
+// only the lo*lo term (~2^-17 relative) is dropped.  With fp32 inputs the
+// products run as fp32 MFMA (16x16x4).
+//
+// Work split: 4 waves; wave w owns rows 16w..16w+15 of W (as W^T tiles in the
+// 16x16 accumulator layout: lane l holds W[16w + l%16][16jt + 4(l/16) + r]).
+// Wave 0 also runs the serial part.  Per tile: (A) all waves form their
+// 16-column slices of K W^T and Q W^T; (B) the serial LayerNorm pass; (C) all
+// waves apply the output correction, gate, store, and update their W rows.
 #include "scan_common.h"
 
+#include <type_traits>
+
 namespace ttt {
-bool scan_mfma_supports(const ScanArgs&) { return false; }
-hipError_t launch_scan_mfma(const ScanArgs&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int D = 64;
+constexpr int BT = 16;      // tokens per tile
+constexpr int NT = 256;     // 4 waves
+constexpr int KPAD = 68;    // padded fp32 row (floats) of K/Q tiles in LDS
+constexpr int ZPAD = 20;    // padded row (floats) of the per-feature z / delta tiles
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float fast_sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the 64 lanes of a wave; every lane receives the same bits.
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);   // row_half_mirror
+  x += dpp<0x140>(x);   // row_mirror
+  const unsigned u = __float_as_uint(x);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);   // rows (0,0,2,2) | (1,1,3,3)
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const unsigned w = __float_as_uint(x);
+  const auto q = __builtin_amdgcn_permlane32_swap(w, w, false, false);   // halves (lo,lo) | (hi,hi)
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+__device__ __forceinline__ unsigned short bf16_bits(float x) {
+  const __bf16 b = static_cast<__bf16>(x);
+  return __builtin_bit_cast(unsigned short, b);
+}
+__device__ __forceinline__ float bf16_val(unsigned short b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// x = hi + lo with hi, lo bf16 (round to nearest even each)
+__device__ __forceinline__ void split_bf16(float x, unsigned short& hi, unsigned short& lo) {
+  hi = bf16_bits(x);
+  lo = bf16_bits(x - bf16_val(hi));
+}
+
+__device__ __forceinline__ f32x4 mfma_k32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_k16(const i16x4& a, const i16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_k4(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// LDS layout of one staged tile
+// ---------------------------------------------------------------------------
+// bf16 inputs: K and Q rows in the operand layout of the 16x16x32 MFMA
+// (lane l = t + 16G holds, in slot e, column j = 32ks + 16(e/4) + 4G + e%4 of
+// row t), and K^T in the A layout of the 16x16x16 MFMA (lane l = j%16 + 16G
+// of column tile jt holds rows s = 4G + e of column j).
+struct TileBf16 {
+  uint16_t KA[2][64][8];
+  uint16_t QA[2][64][8];
+  uint16_t KT[4][64][4];
+  float V[BT][D];
+  float SG[BT][D];
+  float ETA[BT];
+};
+// fp32 inputs: K and Q rows, padded against bank conflicts.
+struct TileF32 {
+  float K[BT][KPAD];
+  float Q[BT][KPAD];
+  float V[BT][D];
+  float SG[BT][D];
+  float ETA[BT];
+};
+
+template <bool BF16>
+struct Smem {
+  using Tile = typename std::conditional<BF16, TileBf16, TileF32>::type;
+  Tile tile[2];
+  float Zt[D][ZPAD];  // z_t (gradient points) of the tile, by feature i (padded rows)
+  float Dt[D][ZPAD];  // delta_t of the tile, by feature i (padded rows)
+  float Cc[BT][BT];   // eta_s (k_s . k_t)
+};
+
+// Registers of one prefetched tile: each thread stages 16-byte vectors.
+template <bool BF16>
+struct Prefetch {
+  static constexpr int kVecPerArr = BF16 ? 128 : 256;  // 16-byte vectors per 16x64 tile
+  static constexpr int kPerThread = 4 * kVecPerArr / NT;
+  uint4 v[kPerThread];
+  float eta;
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load_tile(Prefetch<BF16>& p, const void* const src[4],
+                                          const void* etap, int64_t bhT, int64_t t0, int64_t T,
+                                          int tid) {
+  using In = typename std::conditional<BF16, uint16_t, float>::type;
+  constexpr int VE = BF16 ? 8 : 4;
+  constexpr int NVA = Prefetch<BF16>::kVecPerArr;
+#pragma unroll
+  for (int r = 0; r < Prefetch<BF16>::kPerThread; ++r) {
+    const int idx = tid + r * NT;      // 0 .. 4*NVA-1
+    const int a = idx / NVA;           // array: q, k, v, gate
+    const int vid = idx % NVA;
+    const int t = (vid * VE) / D;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (t0 + t < T) {
+      const In* base = static_cast<const In*>(src[a]) + (bhT + t0) * D;
+      x = *reinterpret_cast<const uint4*>(base + vid * VE);
+    }
+    p.v[r] = x;
+  }
+  p.eta = 0.0f;
+  if (tid < BT && t0 + tid < T) {
+    const In* e = static_cast<const In*>(etap) + bhT + t0 + tid;
+    if constexpr (BF16)
+      p.eta = __uint_as_float(static_cast<uint32_t>(*e) << 16);
+    else
+      p.eta = *e;
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_tile(const Prefetch<BF16>& p,
+                                           typename Smem<BF16>::Tile& tl, int64_t t0,
+                                           int64_t T, int tid) {
+  constexpr int VE = BF16 ? 8 : 4;
+  constexpr int NVA = Prefetch<BF16>::kVecPerArr;
+#pragma unroll
+  for (int r = 0; r < Prefetch<BF16>::kPerThread; ++r) {
+    const int idx = tid + r * NT;
+    const int a = idx / NVA;
+    const int vid = idx % NVA;
+    const int t = (vid * VE) / D;
+    const int j0 = (vid * VE) % D;
+    const uint4 x = p.v[r];
+    if constexpr (BF16) {
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+      if (a == 0 || a == 1) {
+        // rows of q (a=0) or k (a=1) into the 16x16x32 operand layout
+        uint16_t(*dst)[64][8] = (a == 0) ? tl.QA : tl.KA;
+        const int ks = j0 / 32, hh = (j0 % 32) / 16, g = (j0 % 16) / 4;
+        *reinterpret_cast<uint2*>(&dst[ks][t + 16 * g][4 * hh]) = make_uint2(w[0], w[1]);
+        *reinterpret_cast<uint2*>(&dst[ks][t + 16 * (g + 1)][4 * hh]) = make_uint2(w[2], w[3]);
+        if (a == 1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j = j0 + e;
+            const uint16_t bits = (e & 1) ? static_cast<uint16_t>(w[e / 2] >> 16)
+                                          : static_cast<uint16_t>(w[e / 2] & 0xFFFFu);
+            tl.KT[j / 16][(j % 16) + 16 * (t / 4)][t % 4] = bits;
+          }
+        }
+      } else {
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[2 * i] = __uint_as_float(w[i] << 16);
+          f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+        float* dst = (a == 2) ? &tl.V[t][j0] : &tl.SG[t][j0];
+        if (a == 3) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) f[i] = fast_sigmoid(f[i]);
+        }
+        *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
+      }
+    } else {
+      float4 f = make_float4(__uint_as_float(x.x), __uint_as_float(x.y),
+                             __uint_as_float(x.z), __uint_as_float(x.w));
+      float* dst;
+      if (a == 0) dst = &tl.Q[t][j0];
+      else if (a == 1) dst = &tl.K[t][j0];
+      else if (a == 2) dst = &tl.V[t][j0];
+      else {
+        dst = &tl.SG[t][j0];
+        f = make_float4(fast_sigmoid(f.x), fast_sigmoid(f.y), fast_sigmoid(f.z), fast_sigmoid(f.w));
+      }
+      *reinterpret_cast<float4*>(dst) = f;
+    }
+  }
+  if (tid < BT) tl.ETA[tid] = (t0 + tid < T) ? fast_sigmoid(p.eta) * (1.0f / D) : 0.0f;
+}
+
+// delta for one token from z (lane = feature i), per inner-gradient mode
+template <int LN>
+__device__ __forceinline__ float token_delta(float z, float v, float gam, float bet, float eps) {
+  if constexpr (LN == kLnNone) {
+    return z - v;
+  } else {
+    const float s1 = wave_sum(z);
+    const float s2 = wave_sum(z * z);
+    const float mu = s1 * (1.0f / D);
+    const float var = fmaxf(s2 * (1.0f / D) - mu * mu, 0.0f);
+    const float rs = __builtin_amdgcn_rsqf(var + eps);
+    const float xh = (z - mu) * rs;
+    const float e = fmaf(gam, xh, bet - v);
+    if constexpr (LN == kLnST) {
+      return e;
+    } else {
+      const float g = gam * e;
+      const float sg = wave_sum(g);
+      const float sgx = wave_sum(g * xh);
+      return rs * (g - sg * (1.0f / D) - xh * (sgx * (1.0f / D)));
+    }
+  }
+}
+
+template <bool BF16, int LN, bool DUAL>
+__global__ void __launch_bounds__(NT)
+scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
+                 const void* __restrict__ vp, const void* __restrict__ etap,
+                 const void* __restrict__ gatep, const float* __restrict__ W0,
+                 const float* __restrict__ gamma, const float* __restrict__ beta,
+                 float* __restrict__ out, float* __restrict__ W_final, int H, int64_t T,
+                 float eps) {
+  __shared__ Smem<BF16> sm;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int G = lane >> 4;
+  const int64_t bh = blockIdx.x;
+  const int h = static_cast<int>(bh % H);
+  const int64_t bhT = bh * T;
+  const void* const src[4] = {qp, kp, vp, gatep};
+  const int irow = 16 * wave + l16;   // the W row (feature i) this lane's accumulators hold
+
+  // W^T tiles: Wt[jt][r] = W[irow][16 jt + 4G + r]
+  f32x4 Wt[4];
+  {
+    const float* w = W0 + bh * D * D + irow * D + 4 * G;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      const float4 x = *reinterpret_cast<const float4*>(w + 16 * jt);
+      Wt[jt] = f32x4{x.x, x.y, x.z, x.w};
+    }
+  }
+  float gam = 1.0f, bet = 0.0f;   // LayerNorm affine of feature `lane` (serial part)
+  if constexpr (LN != kLnNone) {
+    gam = gamma[h * D + lane];
+    bet = beta[h * D + lane];
+  }
+
+  const int64_t ntiles = (T + BT - 1) / BT;
+  Prefetch<BF16> pf;
+  if (ntiles > 0) {
+    load_tile<BF16>(pf, src, etap, bhT, 0, T, tid);
+    store_tile<BF16>(pf, sm.tile[0], 0, T, tid);
+  }
+  __syncthreads();
+
+  for (int64_t c = 0; c < ntiles; ++c) {
+    const int64_t t0 = c * BT;
+    auto& tl = sm.tile[c & 1];
+    if (c + 1 < ntiles) load_tile<BF16>(pf, src, etap, bhT, t0 + BT, T, tid);
+
+    // ---------------- (A) Z = K W^T, U = Q W^T, Gram matrices ----------------
+    f32x4 Z = {0, 0, 0, 0}, U = {0, 0, 0, 0}, KQ = {0, 0, 0, 0}, KK = {0, 0, 0, 0};
+    if constexpr (BF16) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 bh_, bl_;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          unsigned short hi, lo;
+          split_bf16(Wt[2 * ks + e / 4][e % 4], hi, lo);
+          bh_[e] = __builtin_bit_cast(__bf16, hi);
+          bl_[e] = __builtin_bit_cast(__bf16, lo);
+        }
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&tl.KA[ks][lane][0]);
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&tl.QA[ks][lane][0]);
+        Z = mfma_k32(ka, bh_, Z);
+        Z = mfma_k32(ka, bl_, Z);
+        U = mfma_k32(qa, bh_, U);
+        U = mfma_k32(qa, bl_, U);
+        KQ = mfma_k32(ka, qa, KQ);
+        if (!DUAL && wave == 0) KK = mfma_k32(ka, ka, KK);
+      }
+    } else {
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const float4 ka = *reinterpret_cast<const float4*>(&tl.K[l16][16 * jt + 4 * G]);
+        const float4 qa = *reinterpret_cast<const float4*>(&tl.Q[l16][16 * jt + 4 * G]);
+        const float kv[4] = {ka.x, ka.y, ka.z, ka.w};
+        const float qv[4] = {qa.x, qa.y, qa.z, qa.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          Z = mfma_k4(kv[r], Wt[jt][r], Z);
+          U = mfma_k4(qv[r], Wt[jt][r], U);
+          KQ = mfma_k4(kv[r], qv[r], KQ);
+          if (!DUAL && wave == 0) KK = mfma_k4(kv[r], kv[r], KK);
+        }
+      }
+    }
+    // Z[t = 4G + r][i = irow] -> Zt[i][t]
+    *reinterpret_cast<float4*>(&sm.Zt[irow][4 * G]) = make_float4(Z[0], Z[1], Z[2], Z[3]);
+    // KQ[s = 4G + r][t = l16] -> eta_s-scaled, causal (s <= t): operand M[t][s]
+    float M[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int s = 4 * G + r;
+      M[r] = (s <= l16) ? tl.ETA[s] * KQ[r] : 0.0f;
+    }
+    if (!DUAL && wave == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = 4 * G + r;
+        sm.Cc[s][l16] = tl.ETA[s] * KK[r];
+      }
+    }
+    __syncthreads();
+
+    // ---------------- (B) serial LayerNorm pass -> delta ----------------
+    if constexpr (!DUAL) {
+      if (wave == 0) {
+        float zr[BT], dr[BT];
+#pragma unroll
+        for (int q4 = 0; q4 < BT / 4; ++q4) {
+          const float4 x = *reinterpret_cast<const float4*>(&sm.Zt[lane][4 * q4]);
+          zr[4 * q4] = x.x; zr[4 * q4 + 1] = x.y; zr[4 * q4 + 2] = x.z; zr[4 * q4 + 3] = x.w;
+        }
+#pragma unroll
+        for (int s = 0; s < BT; ++s) {
+          const float dl = token_delta<LN>(zr[s], tl.V[s][lane], gam, bet, eps);
+          dr[s] = dl;
+#pragma unroll
+          for (int t = s + 1; t < BT; ++t) zr[t] = fmaf(-sm.Cc[s][t], dl, zr[t]);
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < BT / 4; ++q4)
+          *reinterpret_cast<float4*>(&sm.Dt[lane][4 * q4]) =
+              make_float4(dr[4 * q4], dr[4 * q4 + 1], dr[4 * q4 + 2], dr[4 * q4 + 3]);
+      }
+    } else {
+      // dual form: the 16 tokens are independent; wave w takes tokens 4w..4w+3
+      const float4 x = *reinterpret_cast<const float4*>(&sm.Zt[lane][4 * wave]);
+      const float zz[4] = {x.x, x.y, x.z, x.w};
+      float dd[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        dd[u] = token_delta<LN>(zz[u], tl.V[4 * wave + u][lane], gam, bet, eps);
+      *reinterpret_cast<float4*>(&sm.Dt[lane][4 * wave]) = make_float4(dd[0], dd[1], dd[2], dd[3]);
+    }
+    __syncthreads();
+
+    // ---------------- (C) outputs and the W update ----------------
+    const float4 dv4 = *reinterpret_cast<const float4*>(&sm.Dt[irow][4 * G]);
+    const float dv[4] = {dv4.x, dv4.y, dv4.z, dv4.w};   // delta[s = 4G + e][irow]
+    float ev[4];                                          // eta_s delta[s][irow]
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ev[e] = tl.ETA[4 * G + e] * dv[e];
+    if constexpr (BF16) {
+      i16x4 mh, ml, dh, dlo, eh, el;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        unsigned short a, b;
+        split_bf16(-M[e], a, b);
+        mh[e] = static_cast<short>(a);
+        ml[e] = static_cast<short>(b);
+        split_bf16(dv[e], a, b);
+        dh[e] = static_cast<short>(a);
+        dlo[e] = static_cast<short>(b);
+        split_bf16(-ev[e], a, b);
+        eh[e] = static_cast<short>(a);
+        el[e] = static_cast<short>(b);
+      }
+      U = mfma_k16(mh, dh, U);
+      U = mfma_k16(mh, dlo, U);
+      U = mfma_k16(ml, dh, U);
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const i16x4 kt = *reinterpret_cast<const i16x4*>(&tl.KT[jt][lane][0]);
+        Wt[jt] = mfma_k16(kt, eh, Wt[jt]);
+        Wt[jt] = mfma_k16(kt, el, Wt[jt]);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) U = mfma_k4(-M[q], dv[q], U);
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          Wt[jt] = mfma_k4(tl.K[4 * G + q][16 * jt + l16], -ev[q], Wt[jt]);
+      }
+    }
+    // gate and store: U[t = 4G + r][irow]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * G + r;
+      if (t0 + t < T) out[(bhT + t0 + t) * D + irow] = U[r] * tl.SG[t][irow];
+    }
+    if (c + 1 < ntiles) store_tile<BF16>(pf, sm.tile[(c + 1) & 1], t0 + BT, T, tid);
+    __syncthreads();
+  }
+
+  if (W_final != nullptr) {
+    float* w = W_final + bh * D * D + irow * D + 4 * G;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+      *reinterpret_cast<float4*>(w + 16 * jt) = make_float4(Wt[jt][0], Wt[jt][1], Wt[jt][2], Wt[jt][3]);
+  }
+}
+
+template <bool BF16, int LN, bool DUAL>
+hipError_t launch_one(const ScanArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((scan_mfma_kernel<BF16, LN, DUAL>), dim3(static_cast<unsigned>(a.B * a.H)),
+                     dim3(NT), 0, s, a.q, a.k, a.v, a.eta_logit, a.gate_logit, a.W0, a.gamma,
+                     a.beta, a.out, a.W_final, static_cast<int>(a.H), a.T, a.eps);
+  return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_ln(const ScanArgs& a, hipStream_t s) {
+  if (a.dual) {
+    switch (a.ln) {
+      case kLnST: return launch_one<BF16, kLnST, true>(a, s);
+      case kLnExact: return launch_one<BF16, kLnExact, true>(a, s);
+      default: return launch_one<BF16, kLnNone, true>(a, s);
+    }
+  }
+  switch (a.ln) {
+    case kLnST: return launch_one<BF16, kLnST, false>(a, s);
+    case kLnExact: return launch_one<BF16, kLnExact, false>(a, s);
+    default: return launch_one<BF16, kLnNone, false>(a, s);
+  }
+}
+
+}  // namespace
+
+bool scan_mfma_supports(const ScanArgs& a) {
+  return a.d == D && (!a.dual || a.chunk == BT);
+}
+
+hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t s) {
+  if (!scan_mfma_supports(a)) return hipErrorNotSupported;
+  return a.in_bf16 ? launch_ln<true>(a, s) : launch_ln<false>(a, s);
+}
+
 }  // namespace ttt
