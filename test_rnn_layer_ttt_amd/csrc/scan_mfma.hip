@@ -56,20 +56,6 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
-// Sum over the 64 lanes of a wave; every lane receives the same bits.
-__device__ __forceinline__ float wave_sum(float x) {
-  x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]
-  x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]
-  x += dpp<0x141>(x);   // row_half_mirror
-  x += dpp<0x140>(x);   // row_mirror
-  const unsigned u = __float_as_uint(x);
-  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);   // rows (0,0,2,2) | (1,1,3,3)
-  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-  const unsigned w = __float_as_uint(x);
-  const auto q = __builtin_amdgcn_permlane32_swap(w, w, false, false);   // halves (lo,lo) | (hi,hi)
-  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
-}
-
 __device__ __forceinline__ unsigned short bf16_bits(float x) {
   const __bf16 b = static_cast<__bf16>(x);
   return __builtin_bit_cast(unsigned short, b);
@@ -98,65 +84,74 @@ __device__ __forceinline__ f32x4 mfma_k4(float a, float b, const f32x4& c) {
 // ---------------------------------------------------------------------------
 // bf16 inputs: K and Q rows in the operand layout of the 16x16x32 MFMA
 // (lane l = t + 16G holds, in slot e, column j = 32ks + 16(e/4) + 4G + e%4 of
-// row t), and K^T in the A layout of the 16x16x16 MFMA (lane l = j%16 + 16G
-// of column tile jt holds rows s = 4G + e of column j).
+// row t), K^T in the A layout of the 16x16x16 MFMA (lane l = j%16 + 16G of
+// column tile jt holds rows s = 4G + e of column j), v transposed to
+// feature-major rows for the serial pass, and the raw gate logits.
 struct TileBf16 {
   uint16_t KA[2][64][8];
   uint16_t QA[2][64][8];
   uint16_t KT[4][64][4];
-  float V[BT][D];
-  float SG[BT][D];
-  float ETA[BT];
+  uint16_t Vt[D][24];      // v[t][i] at Vt[i][t] (rows padded to 48 bytes)
+  uint16_t Gl[BT][D];
+  float ETA[BT];           // sigmoid(eta_logit)/d, 0 for tokens past the end
 };
-// fp32 inputs: K and Q rows, padded against bank conflicts.
+// fp32 inputs: K and Q rows (padded against bank conflicts), v transposed.
 struct TileF32 {
   float K[BT][KPAD];
   float Q[BT][KPAD];
-  float V[BT][D];
-  float SG[BT][D];
+  float Vt[D][ZPAD];
+  float Gl[BT][D];
   float ETA[BT];
+};
+
+// Tiles per staged batch: 32 KB of input per batch for either element type,
+// so that one batch in flight per CU covers the HBM latency.
+template <bool BF16>
+struct Cfg {
+  static constexpr int kTiles = BF16 ? 4 : 2;
+  static constexpr int kTokens = kTiles * BT;
+  static constexpr int kVE = BF16 ? 8 : 4;                    // elements per 16-byte vector
+  static constexpr int kVecPerArr = kTokens * D / kVE;         // 16-byte vectors per array
+  static constexpr int kPerThread = 4 * kVecPerArr / NT;       // q, k, v, gate
 };
 
 template <bool BF16>
 struct Smem {
   using Tile = typename std::conditional<BF16, TileBf16, TileF32>::type;
-  Tile tile[2];
+  Tile tile[2][Cfg<BF16>::kTiles];
   float Zt[D][ZPAD];  // z_t (gradient points) of the tile, by feature i (padded rows)
   float Dt[D][ZPAD];  // delta_t of the tile, by feature i (padded rows)
   float Cc[BT][BT];   // eta_s (k_s . k_t)
 };
 
-// Registers of one prefetched tile: each thread stages 16-byte vectors.
 template <bool BF16>
 struct Prefetch {
-  static constexpr int kVecPerArr = BF16 ? 128 : 256;  // 16-byte vectors per 16x64 tile
-  static constexpr int kPerThread = 4 * kVecPerArr / NT;
-  uint4 v[kPerThread];
+  uint4 v[Cfg<BF16>::kPerThread];
   float eta;
 };
 
+// Issue the global loads of one batch (tokens t0 .. t0 + kTokens - 1).
 template <bool BF16>
-__device__ __forceinline__ void load_tile(Prefetch<BF16>& p, const void* const src[4],
-                                          const void* etap, int64_t bhT, int64_t t0, int64_t T,
-                                          int tid) {
+__device__ __forceinline__ void load_batch(Prefetch<BF16>& p, const void* const src[4],
+                                           const void* etap, int64_t bhT, int64_t t0, int64_t T,
+                                           int tid) {
   using In = typename std::conditional<BF16, uint16_t, float>::type;
-  constexpr int VE = BF16 ? 8 : 4;
-  constexpr int NVA = Prefetch<BF16>::kVecPerArr;
+  using C = Cfg<BF16>;
 #pragma unroll
-  for (int r = 0; r < Prefetch<BF16>::kPerThread; ++r) {
-    const int idx = tid + r * NT;      // 0 .. 4*NVA-1
-    const int a = idx / NVA;           // array: q, k, v, gate
-    const int vid = idx % NVA;
-    const int t = (vid * VE) / D;
+  for (int r = 0; r < C::kPerThread; ++r) {
+    const int idx = tid + r * NT;
+    const int a = idx / C::kVecPerArr;     // q, k, v, gate
+    const int vid = idx % C::kVecPerArr;
+    const int t = (vid * C::kVE) / D;
     uint4 x = make_uint4(0, 0, 0, 0);
     if (t0 + t < T) {
       const In* base = static_cast<const In*>(src[a]) + (bhT + t0) * D;
-      x = *reinterpret_cast<const uint4*>(base + vid * VE);
+      x = *reinterpret_cast<const uint4*>(base + vid * C::kVE);
     }
     p.v[r] = x;
   }
   p.eta = 0.0f;
-  if (tid < BT && t0 + tid < T) {
+  if (tid < C::kTokens && t0 + tid < T) {
     const In* e = static_cast<const In*>(etap) + bhT + t0 + tid;
     if constexpr (BF16)
       p.eta = __uint_as_float(static_cast<uint32_t>(*e) << 16);
@@ -165,91 +160,136 @@ __device__ __forceinline__ void load_tile(Prefetch<BF16>& p, const void* const s
   }
 }
 
+// Write a loaded batch into its LDS tiles, in the layouts above.
 template <bool BF16>
-__device__ __forceinline__ void store_tile(const Prefetch<BF16>& p,
-                                           typename Smem<BF16>::Tile& tl, int64_t t0,
-                                           int64_t T, int tid) {
-  constexpr int VE = BF16 ? 8 : 4;
-  constexpr int NVA = Prefetch<BF16>::kVecPerArr;
+__device__ __forceinline__ void store_batch(const Prefetch<BF16>& p,
+                                            typename Smem<BF16>::Tile* tiles, int64_t t0,
+                                            int64_t T, int tid) {
+  using C = Cfg<BF16>;
 #pragma unroll
-  for (int r = 0; r < Prefetch<BF16>::kPerThread; ++r) {
+  for (int r = 0; r < C::kPerThread; ++r) {
     const int idx = tid + r * NT;
-    const int a = idx / NVA;
-    const int vid = idx % NVA;
-    const int t = (vid * VE) / D;
-    const int j0 = (vid * VE) % D;
+    const int a = idx / C::kVecPerArr;
+    const int vid = idx % C::kVecPerArr;
+    const int tb = (vid * C::kVE) / D;      // token within the batch
+    const int t = tb % BT;                  // token within its tile
+    const int j0 = (vid * C::kVE) % D;
+    auto& tl = tiles[tb / BT];
     const uint4 x = p.v[r];
     if constexpr (BF16) {
       const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-      if (a == 0 || a == 1) {
+      if (a <= 1) {
         // rows of q (a=0) or k (a=1) into the 16x16x32 operand layout
         uint16_t(*dst)[64][8] = (a == 0) ? tl.QA : tl.KA;
         const int ks = j0 / 32, hh = (j0 % 32) / 16, g = (j0 % 16) / 4;
         *reinterpret_cast<uint2*>(&dst[ks][t + 16 * g][4 * hh]) = make_uint2(w[0], w[1]);
         *reinterpret_cast<uint2*>(&dst[ks][t + 16 * (g + 1)][4 * hh]) = make_uint2(w[2], w[3]);
-        if (a == 1) {
+      }
+      if (a == 1 || a == 2) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = j0 + e;
-            const uint16_t bits = (e & 1) ? static_cast<uint16_t>(w[e / 2] >> 16)
-                                          : static_cast<uint16_t>(w[e / 2] & 0xFFFFu);
+        for (int e = 0; e < 8; ++e) {
+          const int j = j0 + e;
+          const uint16_t bits = (e & 1) ? static_cast<uint16_t>(w[e / 2] >> 16)
+                                        : static_cast<uint16_t>(w[e / 2] & 0xFFFFu);
+          if (a == 1)
             tl.KT[j / 16][(j % 16) + 16 * (t / 4)][t % 4] = bits;
-          }
+          else
+            tl.Vt[j][t] = bits;
         }
-      } else {
-        float f[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f[2 * i] = __uint_as_float(w[i] << 16);
-          f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-        }
-        float* dst = (a == 2) ? &tl.V[t][j0] : &tl.SG[t][j0];
-        if (a == 3) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) f[i] = fast_sigmoid(f[i]);
-        }
-        *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
       }
+      if (a == 3) *reinterpret_cast<uint4*>(&tl.Gl[t][j0]) = x;
     } else {
-      float4 f = make_float4(__uint_as_float(x.x), __uint_as_float(x.y),
-                             __uint_as_float(x.z), __uint_as_float(x.w));
-      float* dst;
-      if (a == 0) dst = &tl.Q[t][j0];
-      else if (a == 1) dst = &tl.K[t][j0];
-      else if (a == 2) dst = &tl.V[t][j0];
-      else {
-        dst = &tl.SG[t][j0];
-        f = make_float4(fast_sigmoid(f.x), fast_sigmoid(f.y), fast_sigmoid(f.z), fast_sigmoid(f.w));
+      const float4 f = make_float4(__uint_as_float(x.x), __uint_as_float(x.y),
+                                   __uint_as_float(x.z), __uint_as_float(x.w));
+      if (a == 0) *reinterpret_cast<float4*>(&tl.Q[t][j0]) = f;
+      if (a == 1) *reinterpret_cast<float4*>(&tl.K[t][j0]) = f;
+      if (a == 2) {
+        tl.Vt[j0][t] = f.x;
+        tl.Vt[j0 + 1][t] = f.y;
+        tl.Vt[j0 + 2][t] = f.z;
+        tl.Vt[j0 + 3][t] = f.w;
       }
-      *reinterpret_cast<float4*>(dst) = f;
+      if (a == 3) *reinterpret_cast<float4*>(&tl.Gl[t][j0]) = f;
     }
   }
-  if (tid < BT) tl.ETA[tid] = (t0 + tid < T) ? fast_sigmoid(p.eta) * (1.0f / D) : 0.0f;
+  if (tid < C::kTokens)
+    tiles[tid / BT].ETA[tid % BT] = (t0 + tid < T) ? fast_sigmoid(p.eta) * (1.0f / D) : 0.0f;
 }
 
-// delta for one token from z (lane = feature i), per inner-gradient mode
+// Two independent sums over the 64 lanes of a wave, interleaved step by step;
+// every lane receives the same bits (quad, half-row, row, then 16- and
+// 32-lane swaps).
+__device__ __forceinline__ void wave_sum2(float& a, float& b) {
+  a += dpp<0xB1>(a);
+  b += dpp<0xB1>(b);
+  a += dpp<0x4E>(a);
+  b += dpp<0x4E>(b);
+  a += dpp<0x141>(a);
+  b += dpp<0x141>(b);
+  a += dpp<0x140>(a);
+  b += dpp<0x140>(b);
+  const unsigned ua = __float_as_uint(a), ub = __float_as_uint(b);
+  const auto pa = __builtin_amdgcn_permlane16_swap(ua, ua, false, false);
+  const auto pb = __builtin_amdgcn_permlane16_swap(ub, ub, false, false);
+  a = __uint_as_float(pa[0]) + __uint_as_float(pa[1]);
+  b = __uint_as_float(pb[0]) + __uint_as_float(pb[1]);
+  const unsigned va = __float_as_uint(a), vb = __float_as_uint(b);
+  const auto qa = __builtin_amdgcn_permlane32_swap(va, va, false, false);
+  const auto qb = __builtin_amdgcn_permlane32_swap(vb, vb, false, false);
+  a = __uint_as_float(qa[0]) + __uint_as_float(qa[1]);
+  b = __uint_as_float(qb[0]) + __uint_as_float(qb[1]);
+}
+
+// delta for one token from z (lane = feature i); bv = beta_i - v_t[i]
 template <int LN>
-__device__ __forceinline__ float token_delta(float z, float v, float gam, float bet, float eps) {
+__device__ __forceinline__ float token_delta(float z, float v, float bv, float gam, float eps) {
   if constexpr (LN == kLnNone) {
     return z - v;
   } else {
-    const float s1 = wave_sum(z);
-    const float s2 = wave_sum(z * z);
+    float s1 = z, s2 = z * z;
+    wave_sum2(s1, s2);
     const float mu = s1 * (1.0f / D);
-    const float var = fmaxf(s2 * (1.0f / D) - mu * mu, 0.0f);
+    const float var = fmaxf(fmaf(s2, 1.0f / D, -mu * mu), 0.0f);
     const float rs = __builtin_amdgcn_rsqf(var + eps);
     const float xh = (z - mu) * rs;
-    const float e = fmaf(gam, xh, bet - v);
+    const float e = fmaf(gam, xh, bv);
     if constexpr (LN == kLnST) {
       return e;
     } else {
       const float g = gam * e;
-      const float sg = wave_sum(g);
-      const float sgx = wave_sum(g * xh);
+      float sg = g, sgx = g * xh;
+      wave_sum2(sg, sgx);
       return rs * (g - sg * (1.0f / D) - xh * (sgx * (1.0f / D)));
     }
   }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void read_v16(const typename Smem<BF16>::Tile& tl, int lane, float* v) {
+  if constexpr (BF16) {
+    const uint4 a = *reinterpret_cast<const uint4*>(&tl.Vt[lane][0]);
+    const uint4 b = *reinterpret_cast<const uint4*>(&tl.Vt[lane][8]);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 x = *reinterpret_cast<const float4*>(&tl.Vt[lane][4 * q4]);
+      v[4 * q4] = x.x; v[4 * q4 + 1] = x.y; v[4 * q4 + 2] = x.z; v[4 * q4 + 3] = x.w;
+    }
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float gate_logit(const typename Smem<BF16>::Tile& tl, int t, int i) {
+  if constexpr (BF16)
+    return __uint_as_float(static_cast<uint32_t>(tl.Gl[t][i]) << 16);
+  else
+    return tl.Gl[t][i];
 }
 
 template <bool BF16, int LN, bool DUAL>
@@ -260,6 +300,7 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
                  const float* __restrict__ gamma, const float* __restrict__ beta,
                  float* __restrict__ out, float* __restrict__ W_final, int H, int64_t T,
                  float eps) {
+  using C = Cfg<BF16>;
   __shared__ Smem<BF16> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -289,154 +330,179 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   }
 
   const int64_t ntiles = (T + BT - 1) / BT;
+  const int64_t nbatches = (T + C::kTokens - 1) / C::kTokens;
   Prefetch<BF16> pf;
-  if (ntiles > 0) {
-    load_tile<BF16>(pf, src, etap, bhT, 0, T, tid);
-    store_tile<BF16>(pf, sm.tile[0], 0, T, tid);
+  if (nbatches > 0) {
+    load_batch<BF16>(pf, src, etap, bhT, 0, T, tid);
+    store_batch<BF16>(pf, sm.tile[0], 0, T, tid);
   }
+  // every load issued so far has landed: nothing inside the loop waits on them
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int64_t c = 0; c < ntiles; ++c) {
-    const int64_t t0 = c * BT;
-    auto& tl = sm.tile[c & 1];
-    if (c + 1 < ntiles) load_tile<BF16>(pf, src, etap, bhT, t0 + BT, T, tid);
+  for (int64_t b = 0; b < nbatches; ++b) {
+    const int64_t tb0 = b * C::kTokens;
+    if (b + 1 < nbatches) load_batch<BF16>(pf, src, etap, bhT, tb0 + C::kTokens, T, tid);
+    const int ntb = static_cast<int>(min<int64_t>(C::kTiles, ntiles - b * C::kTiles));
+    for (int ct = 0; ct < ntb; ++ct) {
+      const int64_t t0 = tb0 + ct * BT;
+      const auto& tl = sm.tile[b & 1][ct];
 
-    // ---------------- (A) Z = K W^T, U = Q W^T, Gram matrices ----------------
-    f32x4 Z = {0, 0, 0, 0}, U = {0, 0, 0, 0}, KQ = {0, 0, 0, 0}, KK = {0, 0, 0, 0};
-    if constexpr (BF16) {
+      // ---------------- (A) Z = K W^T, U = Q W^T, Gram matrices ----------------
+      f32x4 Z = {0, 0, 0, 0}, U = {0, 0, 0, 0}, KQ = {0, 0, 0, 0}, KK = {0, 0, 0, 0};
+      if constexpr (BF16) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 bh_, bl_;
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 bh_, bl_;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          unsigned short hi, lo;
-          split_bf16(Wt[2 * ks + e / 4][e % 4], hi, lo);
-          bh_[e] = __builtin_bit_cast(__bf16, hi);
-          bl_[e] = __builtin_bit_cast(__bf16, lo);
+          for (int e = 0; e < 8; ++e) {
+            unsigned short hi, lo;
+            split_bf16(Wt[2 * ks + e / 4][e % 4], hi, lo);
+            bh_[e] = __builtin_bit_cast(__bf16, hi);
+            bl_[e] = __builtin_bit_cast(__bf16, lo);
+          }
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&tl.KA[ks][lane][0]);
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&tl.QA[ks][lane][0]);
+          Z = mfma_k32(ka, bh_, Z);
+          U = mfma_k32(qa, bh_, U);
+          Z = mfma_k32(ka, bl_, Z);
+          U = mfma_k32(qa, bl_, U);
+          KQ = mfma_k32(ka, qa, KQ);
+          if (!DUAL && wave == 0) KK = mfma_k32(ka, ka, KK);
         }
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&tl.KA[ks][lane][0]);
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&tl.QA[ks][lane][0]);
-        Z = mfma_k32(ka, bh_, Z);
-        Z = mfma_k32(ka, bl_, Z);
-        U = mfma_k32(qa, bh_, U);
-        U = mfma_k32(qa, bl_, U);
-        KQ = mfma_k32(ka, qa, KQ);
-        if (!DUAL && wave == 0) KK = mfma_k32(ka, ka, KK);
-      }
-    } else {
+      } else {
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const float4 ka = *reinterpret_cast<const float4*>(&tl.K[l16][16 * jt + 4 * G]);
-        const float4 qa = *reinterpret_cast<const float4*>(&tl.Q[l16][16 * jt + 4 * G]);
-        const float kv[4] = {ka.x, ka.y, ka.z, ka.w};
-        const float qv[4] = {qa.x, qa.y, qa.z, qa.w};
+        for (int jt = 0; jt < 4; ++jt) {
+          const float4 ka = *reinterpret_cast<const float4*>(&tl.K[l16][16 * jt + 4 * G]);
+          const float4 qa = *reinterpret_cast<const float4*>(&tl.Q[l16][16 * jt + 4 * G]);
+          const float kv[4] = {ka.x, ka.y, ka.z, ka.w};
+          const float qv[4] = {qa.x, qa.y, qa.z, qa.w};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          Z = mfma_k4(kv[r], Wt[jt][r], Z);
-          U = mfma_k4(qv[r], Wt[jt][r], U);
-          KQ = mfma_k4(kv[r], qv[r], KQ);
-          if (!DUAL && wave == 0) KK = mfma_k4(kv[r], kv[r], KK);
+          for (int r = 0; r < 4; ++r) {
+            Z = mfma_k4(kv[r], Wt[jt][r], Z);
+            U = mfma_k4(qv[r], Wt[jt][r], U);
+            KQ = mfma_k4(kv[r], qv[r], KQ);
+            if (!DUAL && wave == 0) KK = mfma_k4(kv[r], kv[r], KK);
+          }
         }
       }
-    }
-    // Z[t = 4G + r][i = irow] -> Zt[i][t]
-    *reinterpret_cast<float4*>(&sm.Zt[irow][4 * G]) = make_float4(Z[0], Z[1], Z[2], Z[3]);
-    // KQ[s = 4G + r][t = l16] -> eta_s-scaled, causal (s <= t): operand M[t][s]
-    float M[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int s = 4 * G + r;
-      M[r] = (s <= l16) ? tl.ETA[s] * KQ[r] : 0.0f;
-    }
-    if (!DUAL && wave == 0) {
+      // Z[t = 4G + r][i = irow] -> Zt[i][t]
+      *reinterpret_cast<float4*>(&sm.Zt[irow][4 * G]) = make_float4(Z[0], Z[1], Z[2], Z[3]);
+      // KQ[s = 4G + r][t = l16] -> eta_s-scaled, causal (s <= t): operand M[t][s]
+      float M[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = 4 * G + r;
-        sm.Cc[s][l16] = tl.ETA[s] * KK[r];
+        M[r] = (s <= l16) ? tl.ETA[s] * KQ[r] : 0.0f;
       }
-    }
-    __syncthreads();
-
-    // ---------------- (B) serial LayerNorm pass -> delta ----------------
-    if constexpr (!DUAL) {
-      if (wave == 0) {
-        float zr[BT], dr[BT];
+      if (!DUAL && wave == 0) {
 #pragma unroll
-        for (int q4 = 0; q4 < BT / 4; ++q4) {
-          const float4 x = *reinterpret_cast<const float4*>(&sm.Zt[lane][4 * q4]);
-          zr[4 * q4] = x.x; zr[4 * q4 + 1] = x.y; zr[4 * q4 + 2] = x.z; zr[4 * q4 + 3] = x.w;
+        for (int r = 0; r < 4; ++r) {
+          const int s = 4 * G + r;
+          sm.Cc[s][l16] = tl.ETA[s] * KK[r];
         }
-#pragma unroll
-        for (int s = 0; s < BT; ++s) {
-          const float dl = token_delta<LN>(zr[s], tl.V[s][lane], gam, bet, eps);
-          dr[s] = dl;
-#pragma unroll
-          for (int t = s + 1; t < BT; ++t) zr[t] = fmaf(-sm.Cc[s][t], dl, zr[t]);
-        }
-#pragma unroll
-        for (int q4 = 0; q4 < BT / 4; ++q4)
-          *reinterpret_cast<float4*>(&sm.Dt[lane][4 * q4]) =
-              make_float4(dr[4 * q4], dr[4 * q4 + 1], dr[4 * q4 + 2], dr[4 * q4 + 3]);
       }
-    } else {
-      // dual form: the 16 tokens are independent; wave w takes tokens 4w..4w+3
-      const float4 x = *reinterpret_cast<const float4*>(&sm.Zt[lane][4 * wave]);
-      const float zz[4] = {x.x, x.y, x.z, x.w};
-      float dd[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        dd[u] = token_delta<LN>(zz[u], tl.V[4 * wave + u][lane], gam, bet, eps);
-      *reinterpret_cast<float4*>(&sm.Dt[lane][4 * wave]) = make_float4(dd[0], dd[1], dd[2], dd[3]);
-    }
-    __syncthreads();
+      __syncthreads();
 
-    // ---------------- (C) outputs and the W update ----------------
-    const float4 dv4 = *reinterpret_cast<const float4*>(&sm.Dt[irow][4 * G]);
-    const float dv[4] = {dv4.x, dv4.y, dv4.z, dv4.w};   // delta[s = 4G + e][irow]
-    float ev[4];                                          // eta_s delta[s][irow]
+      // ---------------- (B) serial LayerNorm pass -> delta ----------------
+      if constexpr (!DUAL) {
+        if (wave == 0) {
+          float zr[BT], dr[BT], vv[BT];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ev[e] = tl.ETA[4 * G + e] * dv[e];
-    if constexpr (BF16) {
-      i16x4 mh, ml, dh, dlo, eh, el;
+          for (int q4 = 0; q4 < BT / 4; ++q4) {
+            const float4 x = *reinterpret_cast<const float4*>(&sm.Zt[lane][4 * q4]);
+            zr[4 * q4] = x.x; zr[4 * q4 + 1] = x.y; zr[4 * q4 + 2] = x.z; zr[4 * q4 + 3] = x.w;
+          }
+          read_v16<BF16>(tl, lane, vv);
+          // eta_s (k_s . k_t) for t > s, broadcast from LDS into registers
+          float cc[BT][BT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        unsigned short a, b;
-        split_bf16(-M[e], a, b);
-        mh[e] = static_cast<short>(a);
-        ml[e] = static_cast<short>(b);
-        split_bf16(dv[e], a, b);
-        dh[e] = static_cast<short>(a);
-        dlo[e] = static_cast<short>(b);
-        split_bf16(-ev[e], a, b);
-        eh[e] = static_cast<short>(a);
-        el[e] = static_cast<short>(b);
+          for (int s = 0; s < BT - 1; ++s) {
+#pragma unroll
+            for (int q4 = (s + 1) / 4; q4 < BT / 4; ++q4) {
+              const float4 x = *reinterpret_cast<const float4*>(&sm.Cc[s][4 * q4]);
+              cc[s][4 * q4] = x.x; cc[s][4 * q4 + 1] = x.y;
+              cc[s][4 * q4 + 2] = x.z; cc[s][4 * q4 + 3] = x.w;
+            }
+          }
+#pragma unroll
+          for (int s = 0; s < BT; ++s) {
+            const float dl = token_delta<LN>(zr[s], vv[s], bet - vv[s], gam, eps);
+            dr[s] = dl;
+#pragma unroll
+            for (int t = s + 1; t < BT; ++t) zr[t] = fmaf(-cc[s][t], dl, zr[t]);
+          }
+#pragma unroll
+          for (int q4 = 0; q4 < BT / 4; ++q4)
+            *reinterpret_cast<float4*>(&sm.Dt[lane][4 * q4]) =
+                make_float4(dr[4 * q4], dr[4 * q4 + 1], dr[4 * q4 + 2], dr[4 * q4 + 3]);
+        }
+      } else {
+        // dual form: the 16 tokens are independent; wave w takes tokens 4w..4w+3
+        const float4 x = *reinterpret_cast<const float4*>(&sm.Zt[lane][4 * wave]);
+        float vv[BT];
+        read_v16<BF16>(tl, lane, vv);
+        const float zz[4] = {x.x, x.y, x.z, x.w};
+        float dd[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float v = vv[4 * wave + u];
+          dd[u] = token_delta<LN>(zz[u], v, bet - v, gam, eps);
+        }
+        *reinterpret_cast<float4*>(&sm.Dt[lane][4 * wave]) =
+            make_float4(dd[0], dd[1], dd[2], dd[3]);
       }
-      U = mfma_k16(mh, dh, U);
-      U = mfma_k16(mh, dlo, U);
-      U = mfma_k16(ml, dh, U);
+      __syncthreads();
+
+      // ---------------- (C) outputs and the W update ----------------
+      const float4 dv4 = *reinterpret_cast<const float4*>(&sm.Dt[irow][4 * G]);
+      const float dv[4] = {dv4.x, dv4.y, dv4.z, dv4.w};   // delta[s = 4G + e][irow]
+      float ev[4];                                          // eta_s delta[s][irow]
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const i16x4 kt = *reinterpret_cast<const i16x4*>(&tl.KT[jt][lane][0]);
-        Wt[jt] = mfma_k16(kt, eh, Wt[jt]);
-        Wt[jt] = mfma_k16(kt, el, Wt[jt]);
+      for (int e = 0; e < 4; ++e) ev[e] = tl.ETA[4 * G + e] * dv[e];
+      if constexpr (BF16) {
+        i16x4 mh, ml, dh, dlo, eh, el;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          unsigned short a, bb;
+          split_bf16(-M[e], a, bb);
+          mh[e] = static_cast<short>(a);
+          ml[e] = static_cast<short>(bb);
+          split_bf16(dv[e], a, bb);
+          dh[e] = static_cast<short>(a);
+          dlo[e] = static_cast<short>(bb);
+          split_bf16(-ev[e], a, bb);
+          eh[e] = static_cast<short>(a);
+          el[e] = static_cast<short>(bb);
+        }
+        U = mfma_k16(mh, dh, U);
+        U = mfma_k16(mh, dlo, U);
+        U = mfma_k16(ml, dh, U);
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          const i16x4 kt = *reinterpret_cast<const i16x4*>(&tl.KT[jt][lane][0]);
+          Wt[jt] = mfma_k16(kt, eh, Wt[jt]);
+          Wt[jt] = mfma_k16(kt, el, Wt[jt]);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) U = mfma_k4(-M[q], dv[q], U);
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            Wt[jt] = mfma_k4(tl.K[4 * G + q][16 * jt + l16], -ev[q], Wt[jt]);
+        }
       }
-    } else {
+      // gate and store: U[t = 4G + r][irow]
 #pragma unroll
-      for (int q = 0; q < 4; ++q) U = mfma_k4(-M[q], dv[q], U);
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          Wt[jt] = mfma_k4(tl.K[4 * G + q][16 * jt + l16], -ev[q], Wt[jt]);
+      for (int r = 0; r < 4; ++r) {
+        const int t = 4 * G + r;
+        if (t0 + t < T)
+          out[(bhT + t0 + t) * D + irow] = U[r] * fast_sigmoid(gate_logit<BF16>(tl, t, irow));
       }
     }
-    // gate and store: U[t = 4G + r][irow]
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 4 * G + r;
-      if (t0 + t < T) out[(bhT + t0 + t) * D + irow] = U[r] * tl.SG[t][irow];
-    }
-    if (c + 1 < ntiles) store_tile<BF16>(pf, sm.tile[(c + 1) & 1], t0 + BT, T, tid);
+    if (b + 1 < nbatches) store_batch<BF16>(pf, sm.tile[(b + 1) & 1], tb0 + C::kTokens, T, tid);
     __syncthreads();
   }
 
