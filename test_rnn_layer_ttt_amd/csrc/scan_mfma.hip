@@ -122,41 +122,44 @@ struct Smem {
   float Zt[D][ZPAD];  // z_t (gradient points) of the tile, by feature i (padded rows)
   float Dt[D][ZPAD];  // delta_t of the tile, by feature i (padded rows)
   float Cc[BT][BT];   // eta_s (k_s . k_t)
+  float O[Cfg<BF16>::kTokens][KPAD];   // gated outputs of the batch, written back at its end
 };
 
 template <bool BF16>
 struct Prefetch {
   uint4 v[Cfg<BF16>::kPerThread];
-  float eta;
+  uint32_t eta;   // raw bits (bf16 in the low half, or fp32)
 };
 
-// Issue the global loads of one batch (tokens t0 .. t0 + kTokens - 1).
+// Issue the global loads of one batch (tokens t0 .. t0 + kTokens - 1).  The
+// array loop is unrolled, so each load's base pointer is a kernel argument and
+// the loads issue as global loads (counted by vmcnt only, not lgkmcnt).
 template <bool BF16>
 __device__ __forceinline__ void load_batch(Prefetch<BF16>& p, const void* const src[4],
                                            const void* etap, int64_t bhT, int64_t t0, int64_t T,
                                            int tid) {
   using In = typename std::conditional<BF16, uint16_t, float>::type;
   using C = Cfg<BF16>;
+  constexpr int kPerArr = C::kPerThread / 4;
 #pragma unroll
-  for (int r = 0; r < C::kPerThread; ++r) {
-    const int idx = tid + r * NT;
-    const int a = idx / C::kVecPerArr;     // q, k, v, gate
-    const int vid = idx % C::kVecPerArr;
-    const int t = (vid * C::kVE) / D;
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (t0 + t < T) {
-      const In* base = static_cast<const In*>(src[a]) + (bhT + t0) * D;
-      x = *reinterpret_cast<const uint4*>(base + vid * C::kVE);
+  for (int a = 0; a < 4; ++a) {
+    const In* base = static_cast<const In*>(src[a]) + (bhT + t0) * D;
+#pragma unroll
+    for (int r = 0; r < kPerArr; ++r) {
+      const int vid = tid + r * NT;
+      const int t = (vid * C::kVE) / D;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (t0 + t < T) x = *reinterpret_cast<const uint4*>(base + vid * C::kVE);
+      p.v[a * kPerArr + r] = x;
     }
-    p.v[r] = x;
   }
-  p.eta = 0.0f;
+  p.eta = 0u;
   if (tid < C::kTokens && t0 + tid < T) {
     const In* e = static_cast<const In*>(etap) + bhT + t0 + tid;
     if constexpr (BF16)
-      p.eta = __uint_as_float(static_cast<uint32_t>(*e) << 16);
-    else
       p.eta = *e;
+    else
+      p.eta = __float_as_uint(*e);
   }
 }
 
@@ -166,11 +169,11 @@ __device__ __forceinline__ void store_batch(const Prefetch<BF16>& p,
                                             typename Smem<BF16>::Tile* tiles, int64_t t0,
                                             int64_t T, int tid) {
   using C = Cfg<BF16>;
+  constexpr int kPerArr = C::kPerThread / 4;
 #pragma unroll
   for (int r = 0; r < C::kPerThread; ++r) {
-    const int idx = tid + r * NT;
-    const int a = idx / C::kVecPerArr;
-    const int vid = idx % C::kVecPerArr;
+    const int a = r / kPerArr;              // q, k, v, gate
+    const int vid = tid + (r % kPerArr) * NT;
     const int tb = (vid * C::kVE) / D;      // token within the batch
     const int t = tb % BT;                  // token within its tile
     const int j0 = (vid * C::kVE) % D;
@@ -212,8 +215,10 @@ __device__ __forceinline__ void store_batch(const Prefetch<BF16>& p,
       if (a == 3) *reinterpret_cast<float4*>(&tl.Gl[t][j0]) = f;
     }
   }
-  if (tid < C::kTokens)
-    tiles[tid / BT].ETA[tid % BT] = (t0 + tid < T) ? fast_sigmoid(p.eta) * (1.0f / D) : 0.0f;
+  if (tid < C::kTokens) {
+    const float x = BF16 ? __uint_as_float(p.eta << 16) : __uint_as_float(p.eta);
+    tiles[tid / BT].ETA[tid % BT] = (t0 + tid < T) ? fast_sigmoid(x) * (1.0f / D) : 0.0f;
+  }
 }
 
 // Two independent sums over the 64 lanes of a wave, interleaved step by step;
@@ -331,18 +336,24 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
 
   const int64_t ntiles = (T + BT - 1) / BT;
   const int64_t nbatches = (T + C::kTokens - 1) / C::kTokens;
+  // Pipeline: LDS holds the current batch and (from the end of the previous
+  // batch) the next one; the registers of `pf` hold the batch after that, in
+  // flight.  All global loads are issued right after a batch boundary, next to
+  // the output stores, so the single wait per batch (before store_batch) finds
+  // them a whole batch old.
+  // W0, gamma and beta have landed before the first input load is issued, so
+  // no use of them inside the loop waits on an in-flight batch.
+  __builtin_amdgcn_s_waitcnt(0);
   Prefetch<BF16> pf;
   if (nbatches > 0) {
     load_batch<BF16>(pf, src, etap, bhT, 0, T, tid);
     store_batch<BF16>(pf, sm.tile[0], 0, T, tid);
   }
-  // every load issued so far has landed: nothing inside the loop waits on them
-  __builtin_amdgcn_s_waitcnt(0);
+  if (nbatches > 1) load_batch<BF16>(pf, src, etap, bhT, C::kTokens, T, tid);
   __syncthreads();
 
   for (int64_t b = 0; b < nbatches; ++b) {
     const int64_t tb0 = b * C::kTokens;
-    if (b + 1 < nbatches) load_batch<BF16>(pf, src, etap, bhT, tb0 + C::kTokens, T, tid);
     const int ntb = static_cast<int>(min<int64_t>(C::kTiles, ntiles - b * C::kTiles));
     for (int ct = 0; ct < ntb; ++ct) {
       const int64_t t0 = tb0 + ct * BT;
@@ -414,23 +425,28 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
             zr[4 * q4] = x.x; zr[4 * q4 + 1] = x.y; zr[4 * q4 + 2] = x.z; zr[4 * q4 + 3] = x.w;
           }
           read_v16<BF16>(tl, lane, vv);
-          // eta_s (k_s . k_t) for t > s, broadcast from LDS into registers
-          float cc[BT][BT];
+          // eta_s (k_s . k_t), row s broadcast from LDS one token ahead of its use
+          float cc[2][BT];
 #pragma unroll
-          for (int s = 0; s < BT - 1; ++s) {
-#pragma unroll
-            for (int q4 = (s + 1) / 4; q4 < BT / 4; ++q4) {
-              const float4 x = *reinterpret_cast<const float4*>(&sm.Cc[s][4 * q4]);
-              cc[s][4 * q4] = x.x; cc[s][4 * q4 + 1] = x.y;
-              cc[s][4 * q4 + 2] = x.z; cc[s][4 * q4 + 3] = x.w;
-            }
+          for (int q4 = 0; q4 < BT / 4; ++q4) {
+            const float4 x = *reinterpret_cast<const float4*>(&sm.Cc[0][4 * q4]);
+            cc[0][4 * q4] = x.x; cc[0][4 * q4 + 1] = x.y;
+            cc[0][4 * q4 + 2] = x.z; cc[0][4 * q4 + 3] = x.w;
           }
 #pragma unroll
           for (int s = 0; s < BT; ++s) {
+            if (s + 1 < BT - 1) {
+#pragma unroll
+              for (int q4 = (s + 2) / 4; q4 < BT / 4; ++q4) {
+                const float4 x = *reinterpret_cast<const float4*>(&sm.Cc[s + 1][4 * q4]);
+                float* d = &cc[(s + 1) & 1][4 * q4];
+                d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
+              }
+            }
             const float dl = token_delta<LN>(zr[s], vv[s], bet - vv[s], gam, eps);
             dr[s] = dl;
 #pragma unroll
-            for (int t = s + 1; t < BT; ++t) zr[t] = fmaf(-cc[s][t], dl, zr[t]);
+            for (int t = s + 1; t < BT; ++t) zr[t] = fmaf(-cc[s & 1][t], dl, zr[t]);
           }
 #pragma unroll
           for (int q4 = 0; q4 < BT / 4; ++q4)
@@ -494,16 +510,26 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
             Wt[jt] = mfma_k4(tl.K[4 * G + q][16 * jt + l16], -ev[q], Wt[jt]);
         }
       }
-      // gate and store: U[t = 4G + r][irow]
+      // gate and stage: U[t = 4G + r][irow]
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 4 * G + r;
-        if (t0 + t < T)
-          out[(bhT + t0 + t) * D + irow] = U[r] * fast_sigmoid(gate_logit<BF16>(tl, t, irow));
+        sm.O[ct * BT + t][irow] = U[r] * fast_sigmoid(gate_logit<BF16>(tl, t, irow));
       }
     }
     if (b + 1 < nbatches) store_batch<BF16>(pf, sm.tile[(b + 1) & 1], tb0 + C::kTokens, T, tid);
     __syncthreads();
+    if (b + 2 < nbatches) load_batch<BF16>(pf, src, etap, bhT, tb0 + 2 * C::kTokens, T, tid);
+    // write the batch's outputs back as 16-byte stores (rows past T skipped)
+    {
+      const int rows = static_cast<int>(min<int64_t>(C::kTokens, T - tb0));
+      float* dst = out + (bhT + tb0) * D;
+      for (int i = tid; i < rows * (D / 4); i += NT) {
+        const int t = i / (D / 4), c4 = i % (D / 4);
+        *reinterpret_cast<float4*>(dst + t * D + 4 * c4) =
+            *reinterpret_cast<const float4*>(&sm.O[t][4 * c4]);
+      }
+    }
   }
 
   if (W_final != nullptr) {
