@@ -221,51 +221,113 @@ __device__ __forceinline__ void store_batch(const Prefetch<BF16>& p,
   }
 }
 
-// Two independent sums over the 64 lanes of a wave, interleaved step by step;
-// every lane receives the same bits (quad, half-row, row, then 16- and
-// 32-lane swaps).
-__device__ __forceinline__ void wave_sum2(float& a, float& b) {
-  a += dpp<0xB1>(a);
-  b += dpp<0xB1>(b);
-  a += dpp<0x4E>(a);
-  b += dpp<0x4E>(b);
-  a += dpp<0x141>(a);
-  b += dpp<0x141>(b);
-  a += dpp<0x140>(a);
-  b += dpp<0x140>(b);
-  const unsigned ua = __float_as_uint(a), ub = __float_as_uint(b);
-  const auto pa = __builtin_amdgcn_permlane16_swap(ua, ua, false, false);
-  const auto pb = __builtin_amdgcn_permlane16_swap(ub, ub, false, false);
-  a = __uint_as_float(pa[0]) + __uint_as_float(pa[1]);
-  b = __uint_as_float(pb[0]) + __uint_as_float(pb[1]);
-  const unsigned va = __float_as_uint(a), vb = __float_as_uint(b);
-  const auto qa = __builtin_amdgcn_permlane32_swap(va, va, false, false);
-  const auto qb = __builtin_amdgcn_permlane32_swap(vb, vb, false, false);
-  a = __uint_as_float(qa[0]) + __uint_as_float(qa[1]);
-  b = __uint_as_float(qb[0]) + __uint_as_float(qb[1]);
+// Step K of a sum over the 64 lanes of a wave: an inclusive scan inside each
+// 16-lane row (row_shr 1, 2, 4, 8; out-of-row sources add zero), then
+// row_bcast:15 and row_bcast:31.  After the six steps lane 63 holds the total
+// (rows 1 and 3 pick up the rows below them, then rows 2 and 3 pick up lane
+// 31); the other lanes hold partial sums that are never read.
+template <int K>
+__device__ __forceinline__ float red_step(float x) {
+  constexpr int kCtrl[6] = {0x111, 0x112, 0x114, 0x118, 0x142, 0x143};
+  return x + __int_as_float(
+                 __builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl[K], 0xF, 0xF, true));
+}
+__device__ __forceinline__ float lane63(float x) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
-// delta for one token from z (lane = feature i); bv = beta_i - v_t[i]
+// Two independent wave sums, interleaved step by step; wave-uniform results.
+__device__ __forceinline__ void wave_total2(float& a, float& b) {
+  a = red_step<0>(a); b = red_step<0>(b);
+  a = red_step<1>(a); b = red_step<1>(b);
+  a = red_step<2>(a); b = red_step<2>(b);
+  a = red_step<3>(a); b = red_step<3>(b);
+  a = red_step<4>(a); b = red_step<4>(b);
+  a = red_step<5>(a); b = red_step<5>(b);
+  a = lane63(a);
+  b = lane63(b);
+}
+
+// delta for one token from z (lane = feature i) and the wave sums s1 = sum z,
+// s2 = sum z^2; bv = beta_i - v_t[i].  mu = s1/d, d*var = s2 - s1*mu.
+template <int LN>
+__device__ __forceinline__ float delta_from_sums(float z, float s1, float s2, float bv, float gam,
+                                                 float eps) {
+  const float mu = s1 * (1.0f / D);
+  const float dvar = fmaf(-s1, mu, s2);
+  const float rs = __builtin_amdgcn_rsqf(fmaxf(fmaf(dvar, 1.0f / D, eps), eps));
+  const float zc = z - mu;
+  if constexpr (LN == kLnST) {
+    return fmaf(gam * rs, zc, bv);
+  } else {
+    const float xh = zc * rs;
+    const float g = gam * fmaf(gam, xh, bv);
+    float sg = g, sgx = g * xh;
+    wave_total2(sg, sgx);
+    return rs * (g - sg * (1.0f / D) - xh * (sgx * (1.0f / D)));
+  }
+}
+
+// delta for one token from z (lane = feature i); bv = beta_i - v_t[i].
 template <int LN>
 __device__ __forceinline__ float token_delta(float z, float v, float bv, float gam, float eps) {
   if constexpr (LN == kLnNone) {
     return z - v;
   } else {
     float s1 = z, s2 = z * z;
-    wave_sum2(s1, s2);
-    const float mu = s1 * (1.0f / D);
-    const float var = fmaxf(fmaf(s2, 1.0f / D, -mu * mu), 0.0f);
-    const float rs = __builtin_amdgcn_rsqf(var + eps);
-    const float xh = (z - mu) * rs;
-    const float e = fmaf(gam, xh, bv);
-    if constexpr (LN == kLnST) {
-      return e;
-    } else {
-      const float g = gam * e;
-      float sg = g, sgx = g * xh;
-      wave_sum2(sg, sgx);
-      return rs * (g - sg * (1.0f / D) - xh * (sgx * (1.0f / D)));
+    wave_total2(s1, s2);
+    return delta_from_sums<LN>(z, s1, s2, bv, gam, eps);
+  }
+}
+
+// The serial pass over one tile (lane = feature i).  zr[t] = (W_c k_t)_i on
+// entry; cc points at eta_s (k_s . k_t) in LDS.  Token s's delta is applied to
+// row s+1 at once; its updates of rows s+2.. are spread over the reduction
+// steps of token s+1, where they fill the DPP wait states.
+template <int LN>
+__device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[BT],
+                                            const float (&vv)[BT], const float (*cc)[BT],
+                                            float gam, float eps, float (&dr)[BT]) {
+  float cprev[BT];
+  float dprev = 0.0f;
+#pragma unroll
+  for (int s = 0; s < BT; ++s) {
+    float crow[BT];
+#pragma unroll
+    for (int q4 = (s + 1) / 4; q4 < BT / 4; ++q4) {
+      const float4 x = *reinterpret_cast<const float4*>(&cc[s][4 * q4]);
+      crow[4 * q4] = x.x; crow[4 * q4 + 1] = x.y; crow[4 * q4 + 2] = x.z; crow[4 * q4 + 3] = x.w;
     }
+    const float z = zr[s];
+    // deferred rows s+1 .. BT-1 of the previous token, split into six slices
+    constexpr int kSlots = 6;
+    const int n = BT - 1 - s;
+    auto fill = [&](int k) {
+      if (s == 0) return;
+#pragma unroll
+      for (int t = s + 1 + (k * n) / kSlots; t < s + 1 + ((k + 1) * n) / kSlots; ++t)
+        zr[t] = fmaf(-cprev[t], dprev, zr[t]);
+    };
+    float dl;
+    if constexpr (LN == kLnNone) {
+#pragma unroll
+      for (int k = 0; k < kSlots; ++k) fill(k);
+      dl = z - vv[s];
+    } else {
+      float a = z, b = z * z;
+      a = red_step<0>(a); b = red_step<0>(b); fill(0);
+      a = red_step<1>(a); b = red_step<1>(b); fill(1);
+      a = red_step<2>(a); b = red_step<2>(b); fill(2);
+      a = red_step<3>(a); b = red_step<3>(b); fill(3);
+      a = red_step<4>(a); b = red_step<4>(b); fill(4);
+      a = red_step<5>(a); b = red_step<5>(b); fill(5);
+      dl = delta_from_sums<LN>(z, lane63(a), lane63(b), bv[s], gam, eps);
+    }
+    dr[s] = dl;
+    if (s + 1 < BT) zr[s + 1] = fmaf(-crow[s + 1], dl, zr[s + 1]);
+#pragma unroll
+    for (int t = s + 2; t < BT; ++t) cprev[t] = crow[t];
+    dprev = dl;
   }
 }
 
@@ -400,18 +462,14 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       // Z[t = 4G + r][i = irow] -> Zt[i][t]
       *reinterpret_cast<float4*>(&sm.Zt[irow][4 * G]) = make_float4(Z[0], Z[1], Z[2], Z[3]);
       // KQ[s = 4G + r][t = l16] -> eta_s-scaled, causal (s <= t): operand M[t][s]
+      const float4 eta4 = *reinterpret_cast<const float4*>(&tl.ETA[4 * G]);   // eta_{4G+r}
+      const float etav[4] = {eta4.x, eta4.y, eta4.z, eta4.w};
       float M[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int s = 4 * G + r;
-        M[r] = (s <= l16) ? tl.ETA[s] * KQ[r] : 0.0f;
-      }
+      for (int r = 0; r < 4; ++r) M[r] = (4 * G + r <= l16) ? etav[r] * KQ[r] : 0.0f;
       if (!DUAL && wave == 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int s = 4 * G + r;
-          sm.Cc[s][l16] = tl.ETA[s] * KK[r];
-        }
+        for (int r = 0; r < 4; ++r) sm.Cc[4 * G + r][l16] = etav[r] * KK[r];
       }
       __syncthreads();
 
@@ -425,29 +483,10 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
             zr[4 * q4] = x.x; zr[4 * q4 + 1] = x.y; zr[4 * q4 + 2] = x.z; zr[4 * q4 + 3] = x.w;
           }
           read_v16<BF16>(tl, lane, vv);
-          // eta_s (k_s . k_t), row s broadcast from LDS one token ahead of its use
-          float cc[2][BT];
+          float bv[BT];
 #pragma unroll
-          for (int q4 = 0; q4 < BT / 4; ++q4) {
-            const float4 x = *reinterpret_cast<const float4*>(&sm.Cc[0][4 * q4]);
-            cc[0][4 * q4] = x.x; cc[0][4 * q4 + 1] = x.y;
-            cc[0][4 * q4 + 2] = x.z; cc[0][4 * q4 + 3] = x.w;
-          }
-#pragma unroll
-          for (int s = 0; s < BT; ++s) {
-            if (s + 1 < BT - 1) {
-#pragma unroll
-              for (int q4 = (s + 2) / 4; q4 < BT / 4; ++q4) {
-                const float4 x = *reinterpret_cast<const float4*>(&sm.Cc[s + 1][4 * q4]);
-                float* d = &cc[(s + 1) & 1][4 * q4];
-                d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
-              }
-            }
-            const float dl = token_delta<LN>(zr[s], vv[s], bet - vv[s], gam, eps);
-            dr[s] = dl;
-#pragma unroll
-            for (int t = s + 1; t < BT; ++t) zr[t] = fmaf(-cc[s & 1][t], dl, zr[t]);
-          }
+          for (int t = 0; t < BT; ++t) bv[t] = bet - vv[t];
+          serial_tile<LN>(zr, bv, vv, sm.Cc, gam, eps, dr);
 #pragma unroll
           for (int q4 = 0; q4 < BT / 4; ++q4)
             *reinterpret_cast<float4*>(&sm.Dt[lane][4 * q4]) =
@@ -475,7 +514,7 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       const float dv[4] = {dv4.x, dv4.y, dv4.z, dv4.w};   // delta[s = 4G + e][irow]
       float ev[4];                                          // eta_s delta[s][irow]
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ev[e] = tl.ETA[4 * G + e] * dv[e];
+      for (int e = 0; e < 4; ++e) ev[e] = etav[e] * dv[e];
       if constexpr (BF16) {
         i16x4 mh, ml, dh, dlo, eh, el;
 #pragma unroll
