@@ -5,31 +5,40 @@
 // chunk-start gradients: "PonderTTT", "Technical Architecture" (dual form).
 //
 // The sequence is cut into tiles of 16 tokens.  With W_c the weight at the
-// start of a tile, E_s = eta_s delta_s and k_s.k_t the key Gram matrix, the
+// start of tile c, E_s = eta_s delta_s and k_s.k_t the key Gram matrix, the
 // per-token recurrence is, exactly,
 //
 //   z_t = W_c k_t - sum_{s<t in tile} eta_s (k_s.k_t) delta_s      (gradient point)
 //   o_t = W_c q_t - sum_{s<=t in tile} eta_s (k_s.q_t) delta_s     (= W_t q_t)
 //   W_{c+1} = W_c - sum_s eta_s delta_s k_s^T
 //
-// so every d x d product is a dense tile contraction (K W_c^T, Q W_c^T, K K^T,
-// K Q^T, the output correction and the rank-16 update) and runs on MFMA; the
-// only serial part left is, per token, the d-vector correction, the LayerNorm
-// statistics and delta (one wave, 64 lanes = 64 rows, DPP + permlane
-// reductions).  The dual form drops the in-tile correction of z_t (tile =
-// chunk = 16), which makes the 16 tokens of a tile independent.
+// and one tile ahead, K_{c+1} W_{c+1}^T = K_{c+1} W_c^T - (K_{c+1} K_c^T) E_c.
+// Every d x d product is therefore a dense tile contraction on MFMA that can
+// run while the previous tile is still in its serial part; what stays serial
+// is, per token, the d-vector correction of z_t, its LayerNorm statistics and
+// delta_t.  The dual form drops the in-tile correction of z_t (tile = chunk =
+// 16), so its 16 tokens are independent.
 //
-// Precision: W is kept in fp32 as MFMA accumulators.  With bf16 inputs every
-// product runs as bf16 MFMA with fp32 accumulation; the fp32 operands (W,
+// Precision: W stays fp32 in MFMA accumulators.  With bf16 inputs every
+// product runs as bf16 MFMA with fp32 accumulation and the fp32 operands (W,
 // delta, the eta-scaled Gram entries) are split into bf16 hi + lo parts, so
 // only the lo*lo term (~2^-17 relative) is dropped.  With fp32 inputs the
 // products run as fp32 MFMA (16x16x4).
 //
-// Work split: 4 waves; wave w owns rows 16w..16w+15 of W (as W^T tiles in the
-// 16x16 accumulator layout: lane l holds W[16w + l%16][16jt + 4(l/16) + r]).
-// Wave 0 also runs the serial part.  Per tile: (A) all waves form their
-// 16-column slices of K W^T and Q W^T; (B) the serial LayerNorm pass; (C) all
-// waves apply the output correction, gate, store, and update their W rows.
+// Wave roles (8 waves; wave w runs on SIMD w % 4):
+//   wave 0      serial LayerNorm pass, alone on its SIMD (wave 4 only joins
+//               the barriers)
+//   waves 1,2,5,6  one 16-row slice of W each, as W^T tiles in the 16x16
+//               accumulator layout (lane l holds W[16s + l%16][16jt + 4(l/16) + r]);
+//               they apply the updates, form K W^T and Q W^T, the outputs,
+//               and the one-tile-ahead correction between serial passes
+//   wave 3      input staging of even tiles (global loads two tiles ahead,
+//               LDS layouts) and output write-back
+//   wave 7      input staging of odd tiles and the Gram matrices (K K^T,
+//               K Q^T, cross-tile K K^T)
+// Per tile c there are two barriers: S_c (z_c and the coefficients are in
+// LDS; the serial pass of tile c starts) and G_c (delta_c is in LDS; the
+// slices form z_{c+1}).
 #include "scan_common.h"
 
 #include <type_traits>
@@ -39,9 +48,19 @@ namespace {
 
 constexpr int D = 64;
 constexpr int BT = 16;      // tokens per tile
-constexpr int NT = 256;     // 4 waves
-constexpr int KPAD = 68;    // padded fp32 row (floats) of K/Q tiles in LDS
+constexpr int NWAVES = 8;
+constexpr int NT = 64 * NWAVES;
+constexpr int RING = 4;     // staged input tiles held in LDS
+constexpr int KPAD = 68;    // padded fp32 row (floats) of K/Q/output tiles in LDS
 constexpr int ZPAD = 20;    // padded row (floats) of the per-feature z / delta tiles
+constexpr int kSerialWave = 0;
+constexpr int kOutWave = 3;    // stages even tiles, writes outputs back
+constexpr int kGramWave = 7;   // stages odd tiles, forms the Gram matrices
+
+// W row slice owned by a wave, or -1
+__device__ __forceinline__ int slice_of(int wave) {
+  return wave == 1 ? 0 : wave == 2 ? 1 : wave == 5 ? 2 : wave == 6 ? 3 : -1;
+}
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -49,11 +68,6 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float fast_sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
 __device__ __forceinline__ unsigned short bf16_bits(float x) {
@@ -68,6 +82,15 @@ __device__ __forceinline__ void split_bf16(float x, unsigned short& hi, unsigned
   hi = bf16_bits(x);
   lo = bf16_bits(x - bf16_val(hi));
 }
+__device__ __forceinline__ void split4(const float (&x)[4], i16x4& hi, i16x4& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    unsigned short a, b;
+    split_bf16(x[e], a, b);
+    hi[e] = static_cast<short>(a);
+    lo[e] = static_cast<short>(b);
+  }
+}
 
 __device__ __forceinline__ f32x4 mfma_k32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -78,21 +101,28 @@ __device__ __forceinline__ f32x4 mfma_k16(const i16x4& a, const i16x4& b, const 
 __device__ __forceinline__ f32x4 mfma_k4(float a, float b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+// (a_hi + a_lo)(b_hi + b_lo) without the lo*lo term, accumulated into c
+__device__ __forceinline__ f32x4 mfma_k16x3(const i16x4& ah, const i16x4& al, const i16x4& bh,
+                                            const i16x4& bl, f32x4 c) {
+  c = mfma_k16(ah, bh, c);
+  c = mfma_k16(ah, bl, c);
+  return mfma_k16(al, bh, c);
+}
 
 // ---------------------------------------------------------------------------
-// LDS layout of one staged tile
+// LDS layouts
 // ---------------------------------------------------------------------------
 // bf16 inputs: K and Q rows in the operand layout of the 16x16x32 MFMA
 // (lane l = t + 16G holds, in slot e, column j = 32ks + 16(e/4) + 4G + e%4 of
 // row t), K^T in the A layout of the 16x16x16 MFMA (lane l = j%16 + 16G of
 // column tile jt holds rows s = 4G + e of column j), v transposed to
-// feature-major rows for the serial pass, and the raw gate logits.
+// feature-major rows for the serial pass.
 struct TileBf16 {
   uint16_t KA[2][64][8];
   uint16_t QA[2][64][8];
   uint16_t KT[4][64][4];
   uint16_t Vt[D][24];      // v[t][i] at Vt[i][t] (rows padded to 48 bytes)
-  uint16_t Gl[BT][D];
+  float SG[BT][D];         // sigmoid(gate_logit)
   float ETA[BT];           // sigmoid(eta_logit)/d, 0 for tokens past the end
 };
 // fp32 inputs: K and Q rows (padded against bank conflicts), v transposed.
@@ -100,127 +130,146 @@ struct TileF32 {
   float K[BT][KPAD];
   float Q[BT][KPAD];
   float Vt[D][ZPAD];
-  float Gl[BT][D];
+  float SG[BT][D];
   float ETA[BT];
 };
 
-// Tiles per staged batch: 32 KB of input per batch for either element type,
-// so that one batch in flight per CU covers the HBM latency.
+// A operand (t = lane % 16, s = 4 (lane / 16) + e) of a 16 x 16 token matrix:
+// bf16 hi and lo parts for the 16x16x16 MFMA, or the fp32 value of k-step e.
 template <bool BF16>
-struct Cfg {
-  static constexpr int kTiles = BF16 ? 4 : 2;
-  static constexpr int kTokens = kTiles * BT;
-  static constexpr int kVE = BF16 ? 8 : 4;                    // elements per 16-byte vector
-  static constexpr int kVecPerArr = kTokens * D / kVE;         // 16-byte vectors per array
-  static constexpr int kPerThread = 4 * kVecPerArr / NT;       // q, k, v, gate
+struct TokOp;
+template <>
+struct TokOp<true> {
+  uint16_t hi[64][4];
+  uint16_t lo[64][4];
+};
+template <>
+struct TokOp<false> {
+  float v[64][4];
 };
 
 template <bool BF16>
 struct Smem {
   using Tile = typename std::conditional<BF16, TileBf16, TileF32>::type;
-  Tile tile[2][Cfg<BF16>::kTiles];
-  float Zt[D][ZPAD];  // z_t (gradient points) of the tile, by feature i (padded rows)
-  float Dt[D][ZPAD];  // delta_t of the tile, by feature i (padded rows)
-  float Cc[BT][BT];   // eta_s (k_s . k_t)
-  float O[Cfg<BF16>::kTokens][KPAD];   // gated outputs of the batch, written back at its end
+  Tile ring[RING];
+  float Zt[D][ZPAD];       // z of the next serial pass, by feature
+  float Dt[2][D][ZPAD];    // delta of a tile, by feature
+  float Cc[2][BT][BT];     // eta_s (k_s . k_t) of a tile
+  TokOp<BF16> Mop[2];      // -eta_s (k_s . q_t), s <= t: output correction
+  TokOp<BF16> Xop;         // -(k_t of the next tile) . (k_s of this tile)
+  float Ob[2][BT][KPAD];   // gated outputs awaiting write-back
 };
 
+// ---------------------------------------------------------------------------
+// input staging (one wave): global loads into registers, then LDS layouts
+// ---------------------------------------------------------------------------
 template <bool BF16>
-struct Prefetch {
-  uint4 v[Cfg<BF16>::kPerThread];
-  uint32_t eta;   // raw bits (bf16 in the low half, or fp32)
+struct Stage {
+  static constexpr int kVE = BF16 ? 8 : 4;             // elements per 16-byte vector
+  static constexpr int kPerLane = BT * D / kVE / 64;   // vectors per lane per array
+  uint4 v[4][kPerLane];                                // q, k, v, gate
+  uint32_t eta;                                        // raw bits
 };
 
-// Issue the global loads of one batch (tokens t0 .. t0 + kTokens - 1).  The
-// array loop is unrolled, so each load's base pointer is a kernel argument and
-// the loads issue as global loads (counted by vmcnt only, not lgkmcnt).
+// The array loop is unrolled, so each base pointer is a kernel argument and
+// the loads issue as global loads (counted by vmcnt only).
 template <bool BF16>
-__device__ __forceinline__ void load_batch(Prefetch<BF16>& p, const void* const src[4],
-                                           const void* etap, int64_t bhT, int64_t t0, int64_t T,
-                                           int tid) {
+__device__ __forceinline__ void load_tile(Stage<BF16>& st, const void* const src[4],
+                                          const void* etap, int64_t bhT, int64_t t0, int64_t T,
+                                          int lane) {
   using In = typename std::conditional<BF16, uint16_t, float>::type;
-  using C = Cfg<BF16>;
-  constexpr int kPerArr = C::kPerThread / 4;
+  using S = Stage<BF16>;
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     const In* base = static_cast<const In*>(src[a]) + (bhT + t0) * D;
 #pragma unroll
-    for (int r = 0; r < kPerArr; ++r) {
-      const int vid = tid + r * NT;
-      const int t = (vid * C::kVE) / D;
+    for (int r = 0; r < S::kPerLane; ++r) {
+      const int vid = lane + 64 * r;
       uint4 x = make_uint4(0, 0, 0, 0);
-      if (t0 + t < T) x = *reinterpret_cast<const uint4*>(base + vid * C::kVE);
-      p.v[a * kPerArr + r] = x;
+      if (t0 + (vid * S::kVE) / D < T) x = *reinterpret_cast<const uint4*>(base + vid * S::kVE);
+      st.v[a][r] = x;
     }
   }
-  p.eta = 0u;
-  if (tid < C::kTokens && t0 + tid < T) {
-    const In* e = static_cast<const In*>(etap) + bhT + t0 + tid;
+  st.eta = 0u;
+  if (lane < BT && t0 + lane < T) {
+    const In* e = static_cast<const In*>(etap) + bhT + t0 + lane;
     if constexpr (BF16)
-      p.eta = *e;
+      st.eta = *e;
     else
-      p.eta = __float_as_uint(*e);
+      st.eta = __float_as_uint(*e);
   }
 }
 
-// Write a loaded batch into its LDS tiles, in the layouts above.
 template <bool BF16>
-__device__ __forceinline__ void store_batch(const Prefetch<BF16>& p,
-                                            typename Smem<BF16>::Tile* tiles, int64_t t0,
-                                            int64_t T, int tid) {
-  using C = Cfg<BF16>;
-  constexpr int kPerArr = C::kPerThread / 4;
+__device__ __forceinline__ void store_tile(const Stage<BF16>& st,
+                                           typename Smem<BF16>::Tile& tl, int64_t t0, int64_t T,
+                                           int lane) {
+  using S = Stage<BF16>;
 #pragma unroll
-  for (int r = 0; r < C::kPerThread; ++r) {
-    const int a = r / kPerArr;              // q, k, v, gate
-    const int vid = tid + (r % kPerArr) * NT;
-    const int tb = (vid * C::kVE) / D;      // token within the batch
-    const int t = tb % BT;                  // token within its tile
-    const int j0 = (vid * C::kVE) % D;
-    auto& tl = tiles[tb / BT];
-    const uint4 x = p.v[r];
-    if constexpr (BF16) {
-      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-      if (a <= 1) {
-        // rows of q (a=0) or k (a=1) into the 16x16x32 operand layout
-        uint16_t(*dst)[64][8] = (a == 0) ? tl.QA : tl.KA;
-        const int ks = j0 / 32, hh = (j0 % 32) / 16, g = (j0 % 16) / 4;
-        *reinterpret_cast<uint2*>(&dst[ks][t + 16 * g][4 * hh]) = make_uint2(w[0], w[1]);
-        *reinterpret_cast<uint2*>(&dst[ks][t + 16 * (g + 1)][4 * hh]) = make_uint2(w[2], w[3]);
-      }
-      if (a == 1 || a == 2) {
+  for (int a = 0; a < 4; ++a) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = j0 + e;
-          const uint16_t bits = (e & 1) ? static_cast<uint16_t>(w[e / 2] >> 16)
-                                        : static_cast<uint16_t>(w[e / 2] & 0xFFFFu);
-          if (a == 1)
-            tl.KT[j / 16][(j % 16) + 16 * (t / 4)][t % 4] = bits;
-          else
-            tl.Vt[j][t] = bits;
+    for (int r = 0; r < S::kPerLane; ++r) {
+      const int vid = lane + 64 * r;
+      const int t = (vid * S::kVE) / D;
+      const int j0 = (vid * S::kVE) % D;
+      const uint4 x = st.v[a][r];
+      if constexpr (BF16) {
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+        if (a <= 1) {
+          uint16_t(*dst)[64][8] = (a == 0) ? tl.QA : tl.KA;
+          const int ks = j0 / 32, hh = (j0 % 32) / 16, g = (j0 % 16) / 4;
+          *reinterpret_cast<uint2*>(&dst[ks][t + 16 * g][4 * hh]) = make_uint2(w[0], w[1]);
+          *reinterpret_cast<uint2*>(&dst[ks][t + 16 * (g + 1)][4 * hh]) = make_uint2(w[2], w[3]);
         }
+        if (a == 1 || a == 2) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j = j0 + e;
+            const uint16_t bits = (e & 1) ? static_cast<uint16_t>(w[e / 2] >> 16)
+                                          : static_cast<uint16_t>(w[e / 2] & 0xFFFFu);
+            if (a == 1)
+              tl.KT[j / 16][(j % 16) + 16 * (t / 4)][t % 4] = bits;
+            else
+              tl.Vt[j][t] = bits;
+          }
+        }
+        if (a == 3) {
+          float f[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f[2 * i] = fast_sigmoid(__uint_as_float(w[i] << 16));
+            f[2 * i + 1] = fast_sigmoid(__uint_as_float(w[i] & 0xFFFF0000u));
+          }
+          *reinterpret_cast<float4*>(&tl.SG[t][j0]) = make_float4(f[0], f[1], f[2], f[3]);
+          *reinterpret_cast<float4*>(&tl.SG[t][j0 + 4]) = make_float4(f[4], f[5], f[6], f[7]);
+        }
+      } else {
+        const float4 f = make_float4(__uint_as_float(x.x), __uint_as_float(x.y),
+                                     __uint_as_float(x.z), __uint_as_float(x.w));
+        if (a == 0) *reinterpret_cast<float4*>(&tl.Q[t][j0]) = f;
+        if (a == 1) *reinterpret_cast<float4*>(&tl.K[t][j0]) = f;
+        if (a == 2) {
+          tl.Vt[j0][t] = f.x;
+          tl.Vt[j0 + 1][t] = f.y;
+          tl.Vt[j0 + 2][t] = f.z;
+          tl.Vt[j0 + 3][t] = f.w;
+        }
+        if (a == 3)
+          *reinterpret_cast<float4*>(&tl.SG[t][j0]) =
+              make_float4(fast_sigmoid(f.x), fast_sigmoid(f.y), fast_sigmoid(f.z),
+                          fast_sigmoid(f.w));
       }
-      if (a == 3) *reinterpret_cast<uint4*>(&tl.Gl[t][j0]) = x;
-    } else {
-      const float4 f = make_float4(__uint_as_float(x.x), __uint_as_float(x.y),
-                                   __uint_as_float(x.z), __uint_as_float(x.w));
-      if (a == 0) *reinterpret_cast<float4*>(&tl.Q[t][j0]) = f;
-      if (a == 1) *reinterpret_cast<float4*>(&tl.K[t][j0]) = f;
-      if (a == 2) {
-        tl.Vt[j0][t] = f.x;
-        tl.Vt[j0 + 1][t] = f.y;
-        tl.Vt[j0 + 2][t] = f.z;
-        tl.Vt[j0 + 3][t] = f.w;
-      }
-      if (a == 3) *reinterpret_cast<float4*>(&tl.Gl[t][j0]) = f;
     }
   }
-  if (tid < C::kTokens) {
-    const float x = BF16 ? __uint_as_float(p.eta << 16) : __uint_as_float(p.eta);
-    tiles[tid / BT].ETA[tid % BT] = (t0 + tid < T) ? fast_sigmoid(x) * (1.0f / D) : 0.0f;
+  if (lane < BT) {
+    const float x = BF16 ? __uint_as_float(st.eta << 16) : __uint_as_float(st.eta);
+    tl.ETA[lane] = (t0 + lane < T) ? fast_sigmoid(x) * (1.0f / D) : 0.0f;
   }
 }
 
+// ---------------------------------------------------------------------------
+// the serial LayerNorm pass (one wave, lane = feature i)
+// ---------------------------------------------------------------------------
 // Step K of a sum over the 64 lanes of a wave: an inclusive scan inside each
 // 16-lane row (row_shr 1, 2, 4, 8; out-of-row sources add zero), then
 // row_bcast:15 and row_bcast:31.  After the six steps lane 63 holds the total
@@ -280,10 +329,10 @@ __device__ __forceinline__ float token_delta(float z, float v, float bv, float g
   }
 }
 
-// The serial pass over one tile (lane = feature i).  zr[t] = (W_c k_t)_i on
-// entry; cc points at eta_s (k_s . k_t) in LDS.  Token s's delta is applied to
-// row s+1 at once; its updates of rows s+2.. are spread over the reduction
-// steps of token s+1, where they fill the DPP wait states.
+// The serial pass over one tile.  zr[t] = (W_c k_t)_i on entry; cc points at
+// eta_s (k_s . k_t) in LDS.  Token s's delta is applied to row s+1 at once;
+// its updates of rows s+2.. are spread over the reduction steps of token s+1,
+// where they fill the DPP wait states.
 template <int LN>
 __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[BT],
                                             const float (&vv)[BT], const float (*cc)[BT],
@@ -351,14 +400,177 @@ __device__ __forceinline__ void read_v16(const typename Smem<BF16>::Tile& tl, in
   }
 }
 
-template <bool BF16>
-__device__ __forceinline__ float gate_logit(const typename Smem<BF16>::Tile& tl, int t, int i) {
-  if constexpr (BF16)
-    return __uint_as_float(static_cast<uint32_t>(tl.Gl[t][i]) << 16);
-  else
-    return tl.Gl[t][i];
+// One serial (or, in the dual form, parallel) LayerNorm pass: z from Zt,
+// delta into dt.
+template <bool BF16, int LN, bool DUAL>
+__device__ __forceinline__ void ln_pass(Smem<BF16>& sm, const typename Smem<BF16>::Tile& tl,
+                                        const float (*cc)[BT], float (*dt)[ZPAD], int lane,
+                                        float gam, float bet, float eps) {
+  float zr[BT], dr[BT], vv[BT], bv[BT];
+#pragma unroll
+  for (int q4 = 0; q4 < BT / 4; ++q4) {
+    const float4 x = *reinterpret_cast<const float4*>(&sm.Zt[lane][4 * q4]);
+    zr[4 * q4] = x.x; zr[4 * q4 + 1] = x.y; zr[4 * q4 + 2] = x.z; zr[4 * q4 + 3] = x.w;
+  }
+  read_v16<BF16>(tl, lane, vv);
+#pragma unroll
+  for (int t = 0; t < BT; ++t) bv[t] = bet - vv[t];
+  if constexpr (DUAL) {
+#pragma unroll
+    for (int t = 0; t < BT; ++t) dr[t] = token_delta<LN>(zr[t], vv[t], bv[t], gam, eps);
+  } else {
+    serial_tile<LN>(zr, bv, vv, cc, gam, eps, dr);
+  }
+#pragma unroll
+  for (int q4 = 0; q4 < BT / 4; ++q4)
+    *reinterpret_cast<float4*>(&dt[lane][4 * q4]) =
+        make_float4(dr[4 * q4], dr[4 * q4 + 1], dr[4 * q4 + 2], dr[4 * q4 + 3]);
 }
 
+// ---------------------------------------------------------------------------
+// products of a W slice
+// ---------------------------------------------------------------------------
+// bf16 hi/lo B operands of W^T for the two 32-deep k-steps
+struct WOps {
+  bf16x8 hi[2], lo[2];
+};
+__device__ __forceinline__ WOps split_w(const f32x4 (&Wt)[4]) {
+  WOps w;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      unsigned short hi, lo;
+      split_bf16(Wt[2 * ks + e / 4][e % 4], hi, lo);
+      w.hi[ks][e] = __builtin_bit_cast(__bf16, hi);
+      w.lo[ks][e] = __builtin_bit_cast(__bf16, lo);
+    }
+  }
+  return w;
+}
+
+// rows (k or q) of a tile times W^T -> [token][feature slice] accumulator
+__device__ __forceinline__ f32x4 rows_times_wt(const uint16_t (*A)[64][8], const WOps& w,
+                                               int lane) {
+  f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(&A[ks][lane][0]);
+    acc = mfma_k32(a, w.hi[ks], acc);
+    acc = mfma_k32(a, w.lo[ks], acc);
+  }
+  return acc;
+}
+__device__ __forceinline__ f32x4 rows_times_wt(const float (*A)[KPAD], const f32x4 (&Wt)[4],
+                                               int l16, int G) {
+  f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    const float4 a = *reinterpret_cast<const float4*>(&A[l16][16 * jt + 4 * G]);
+    acc = mfma_k4(a.x, Wt[jt][0], acc);
+    acc = mfma_k4(a.y, Wt[jt][1], acc);
+    acc = mfma_k4(a.z, Wt[jt][2], acc);
+    acc = mfma_k4(a.w, Wt[jt][3], acc);
+  }
+  return acc;
+}
+
+// acc += A (16 x 16, A operand TokOp) times B[s][slice feature], B = b[e] for s = 4G + e
+__device__ __forceinline__ f32x4 tok_times(const TokOp<true>& op, const float (&b)[4], int lane,
+                                           f32x4 acc) {
+  i16x4 bh, bl;
+  split4(b, bh, bl);
+  const i16x4 ah = *reinterpret_cast<const i16x4*>(&op.hi[lane][0]);
+  const i16x4 al = *reinterpret_cast<const i16x4*>(&op.lo[lane][0]);
+  return mfma_k16x3(ah, al, bh, bl, acc);
+}
+__device__ __forceinline__ f32x4 tok_times(const TokOp<false>& op, const float (&b)[4], int lane,
+                                           f32x4 acc) {
+  const float4 a = *reinterpret_cast<const float4*>(&op.v[lane][0]);
+  acc = mfma_k4(a.x, b[0], acc);
+  acc = mfma_k4(a.y, b[1], acc);
+  acc = mfma_k4(a.z, b[2], acc);
+  return mfma_k4(a.w, b[3], acc);
+}
+
+// Wt[jt] -= sum_s K[s][16jt + i] e[s][slice feature], with ne[e] = -e[s = 4G + e]
+__device__ __forceinline__ void update_w(f32x4 (&Wt)[4], const TileBf16& tl, const float (&ne)[4],
+                                         int lane, int, int) {
+  i16x4 eh, el;
+  split4(ne, eh, el);
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    const i16x4 kt = *reinterpret_cast<const i16x4*>(&tl.KT[jt][lane][0]);
+    Wt[jt] = mfma_k16(kt, eh, Wt[jt]);
+    Wt[jt] = mfma_k16(kt, el, Wt[jt]);
+  }
+}
+__device__ __forceinline__ void update_w(f32x4 (&Wt)[4], const TileF32& tl, const float (&ne)[4],
+                                         int, int l16, int G) {
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Wt[jt] = mfma_k4(tl.K[4 * G + q][16 * jt + l16], ne[q], Wt[jt]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gram matrices of two staged tiles: D[s][t] = a_s . b_t, at lane
+// (s = 4G + r, t = l16), r = 0..3 -- the A layout of the 16 x 16 matrix D^T
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 gram(const uint16_t (*A)[64][8], const uint16_t (*B)[64][8],
+                                      int lane, int, int) {
+  f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    acc = mfma_k32(*reinterpret_cast<const bf16x8*>(&A[ks][lane][0]),
+                   *reinterpret_cast<const bf16x8*>(&B[ks][lane][0]), acc);
+  return acc;
+}
+__device__ __forceinline__ f32x4 gram(const float (*A)[KPAD], const float (*B)[KPAD], int,
+                                      int l16, int G) {
+  f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    const float4 a = *reinterpret_cast<const float4*>(&A[l16][16 * jt + 4 * G]);
+    const float4 b = *reinterpret_cast<const float4*>(&B[l16][16 * jt + 4 * G]);
+    acc = mfma_k4(a.x, b.x, acc);
+    acc = mfma_k4(a.y, b.y, acc);
+    acc = mfma_k4(a.z, b.z, acc);
+    acc = mfma_k4(a.w, b.w, acc);
+  }
+  return acc;
+}
+__device__ __forceinline__ void put_tok(TokOp<true>& op, const float (&x)[4], int lane) {
+  i16x4 hi, lo;
+  split4(x, hi, lo);
+  *reinterpret_cast<i16x4*>(&op.hi[lane][0]) = hi;
+  *reinterpret_cast<i16x4*>(&op.lo[lane][0]) = lo;
+}
+__device__ __forceinline__ void put_tok(TokOp<false>& op, const float (&x)[4], int lane) {
+  *reinterpret_cast<float4*>(&op.v[lane][0]) = make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ const uint16_t (*krows(const TileBf16& t))[64][8] { return t.KA; }
+__device__ __forceinline__ const uint16_t (*qrows(const TileBf16& t))[64][8] { return t.QA; }
+__device__ __forceinline__ const float (*krows(const TileF32& t))[KPAD] { return t.K; }
+__device__ __forceinline__ const float (*qrows(const TileF32& t))[KPAD] { return t.Q; }
+
+// write back the gated outputs of one tile (one wave, 16-byte stores)
+__device__ __forceinline__ void write_tile_out(const float (*ob)[KPAD], float* out, int64_t bhT,
+                                               int64_t t0, int64_t T, int lane) {
+  const int rows = static_cast<int>(min<int64_t>(BT, T - t0));
+  float* dst = out + (bhT + t0) * D;
+#pragma unroll
+  for (int k = 0; k < BT * D / 4 / 64; ++k) {
+    const int i = lane + 64 * k;
+    const int t = i / (D / 4), c4 = i % (D / 4);
+    if (t < rows)
+      *reinterpret_cast<float4*>(dst + t * D + 4 * c4) =
+          *reinterpret_cast<const float4*>(&ob[t][4 * c4]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 template <bool BF16, int LN, bool DUAL>
 __global__ void __launch_bounds__(NT)
 scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
@@ -367,7 +579,6 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
                  const float* __restrict__ gamma, const float* __restrict__ beta,
                  float* __restrict__ out, float* __restrict__ W_final, int H, int64_t T,
                  float eps) {
-  using C = Cfg<BF16>;
   __shared__ Smem<BF16> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -378,11 +589,18 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   const int h = static_cast<int>(bh % H);
   const int64_t bhT = bh * T;
   const void* const src[4] = {qp, kp, vp, gatep};
-  const int irow = 16 * wave + l16;   // the W row (feature i) this lane's accumulators hold
+  const int64_t ntiles = (T + BT - 1) / BT;
+  const int slice = slice_of(wave);
+  const int irow = 16 * slice + l16;   // W row (feature i) held by this lane, slice waves
 
-  // W^T tiles: Wt[jt][r] = W[irow][16 jt + 4G + r]
-  f32x4 Wt[4];
-  {
+  // slice waves: W^T tiles, Wt[jt][r] = W[irow][16 jt + 4G + r]; P, U accumulators
+  f32x4 Wt[4] = {};
+  f32x4 P = {0, 0, 0, 0}, U = {0, 0, 0, 0};
+  // serial wave: LayerNorm affine of feature `lane`
+  float gam = 1.0f, bet = 0.0f;
+  Stage<BF16> st;   // staging waves: the tile in flight
+
+  if (slice >= 0) {
     const float* w = W0 + bh * D * D + irow * D + 4 * G;
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
@@ -390,192 +608,130 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       Wt[jt] = f32x4{x.x, x.y, x.z, x.w};
     }
   }
-  float gam = 1.0f, bet = 0.0f;   // LayerNorm affine of feature `lane` (serial part)
-  if constexpr (LN != kLnNone) {
+  if (wave == kSerialWave && LN != kLnNone) {
     gam = gamma[h * D + lane];
     bet = beta[h * D + lane];
   }
-
-  const int64_t ntiles = (T + BT - 1) / BT;
-  const int64_t nbatches = (T + C::kTokens - 1) / C::kTokens;
-  // Pipeline: LDS holds the current batch and (from the end of the previous
-  // batch) the next one; the registers of `pf` hold the batch after that, in
-  // flight.  All global loads are issued right after a batch boundary, next to
-  // the output stores, so the single wait per batch (before store_batch) finds
-  // them a whole batch old.
-  // W0, gamma and beta have landed before the first input load is issued, so
-  // no use of them inside the loop waits on an in-flight batch.
   __builtin_amdgcn_s_waitcnt(0);
-  Prefetch<BF16> pf;
-  if (nbatches > 0) {
-    load_batch<BF16>(pf, src, etap, bhT, 0, T, tid);
-    store_batch<BF16>(pf, sm.tile[0], 0, T, tid);
+  // staging prologue: tiles 0 and 1 into LDS, tiles 2 and 3 in flight
+  const int stage_parity = wave == kOutWave ? 0 : wave == kGramWave ? 1 : -1;
+  if (stage_parity >= 0) {
+    const int u = stage_parity;
+    if (u < ntiles) {
+      load_tile<BF16>(st, src, etap, bhT, u * BT, T, lane);
+      store_tile<BF16>(st, sm.ring[u], u * BT, T, lane);
+    }
+    if (u + 2 < ntiles) load_tile<BF16>(st, src, etap, bhT, (u + 2) * BT, T, lane);
   }
-  if (nbatches > 1) load_batch<BF16>(pf, src, etap, bhT, C::kTokens, T, tid);
   __syncthreads();
-
-  for (int64_t b = 0; b < nbatches; ++b) {
-    const int64_t tb0 = b * C::kTokens;
-    const int ntb = static_cast<int>(min<int64_t>(C::kTiles, ntiles - b * C::kTiles));
-    for (int ct = 0; ct < ntb; ++ct) {
-      const int64_t t0 = tb0 + ct * BT;
-      const auto& tl = sm.tile[b & 1][ct];
-
-      // ---------------- (A) Z = K W^T, U = Q W^T, Gram matrices ----------------
-      f32x4 Z = {0, 0, 0, 0}, U = {0, 0, 0, 0}, KQ = {0, 0, 0, 0}, KK = {0, 0, 0, 0};
-      if constexpr (BF16) {
+  // z of tile 0 and its coefficients
+  if (slice >= 0 && ntiles > 0) {
+    f32x4 Z;
+    if constexpr (BF16)
+      Z = rows_times_wt(krows(sm.ring[0]), split_w(Wt), lane);
+    else
+      Z = rows_times_wt(krows(sm.ring[0]), Wt, l16, G);
+    *reinterpret_cast<float4*>(&sm.Zt[irow][4 * G]) = make_float4(Z[0], Z[1], Z[2], Z[3]);
+  }
+  if (!DUAL && wave == kGramWave && ntiles > 0) {
+    const auto& t0 = sm.ring[0];
+    const f32x4 g = gram(krows(t0), krows(t0), lane, l16, G);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          bf16x8 bh_, bl_;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            unsigned short hi, lo;
-            split_bf16(Wt[2 * ks + e / 4][e % 4], hi, lo);
-            bh_[e] = __builtin_bit_cast(__bf16, hi);
-            bl_[e] = __builtin_bit_cast(__bf16, lo);
-          }
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&tl.KA[ks][lane][0]);
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&tl.QA[ks][lane][0]);
-          Z = mfma_k32(ka, bh_, Z);
-          U = mfma_k32(qa, bh_, U);
-          Z = mfma_k32(ka, bl_, Z);
-          U = mfma_k32(qa, bl_, U);
-          KQ = mfma_k32(ka, qa, KQ);
-          if (!DUAL && wave == 0) KK = mfma_k32(ka, ka, KK);
-        }
-      } else {
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-          const float4 ka = *reinterpret_cast<const float4*>(&tl.K[l16][16 * jt + 4 * G]);
-          const float4 qa = *reinterpret_cast<const float4*>(&tl.Q[l16][16 * jt + 4 * G]);
-          const float kv[4] = {ka.x, ka.y, ka.z, ka.w};
-          const float qv[4] = {qa.x, qa.y, qa.z, qa.w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            Z = mfma_k4(kv[r], Wt[jt][r], Z);
-            U = mfma_k4(qv[r], Wt[jt][r], U);
-            KQ = mfma_k4(kv[r], qv[r], KQ);
-            if (!DUAL && wave == 0) KK = mfma_k4(kv[r], kv[r], KK);
-          }
-        }
-      }
-      // Z[t = 4G + r][i = irow] -> Zt[i][t]
-      *reinterpret_cast<float4*>(&sm.Zt[irow][4 * G]) = make_float4(Z[0], Z[1], Z[2], Z[3]);
-      // KQ[s = 4G + r][t = l16] -> eta_s-scaled, causal (s <= t): operand M[t][s]
-      const float4 eta4 = *reinterpret_cast<const float4*>(&tl.ETA[4 * G]);   // eta_{4G+r}
-      const float etav[4] = {eta4.x, eta4.y, eta4.z, eta4.w};
-      float M[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) M[r] = (4 * G + r <= l16) ? etav[r] * KQ[r] : 0.0f;
-      if (!DUAL && wave == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.Cc[4 * G + r][l16] = etav[r] * KK[r];
-      }
-      __syncthreads();
-
-      // ---------------- (B) serial LayerNorm pass -> delta ----------------
-      if constexpr (!DUAL) {
-        if (wave == 0) {
-          float zr[BT], dr[BT], vv[BT];
-#pragma unroll
-          for (int q4 = 0; q4 < BT / 4; ++q4) {
-            const float4 x = *reinterpret_cast<const float4*>(&sm.Zt[lane][4 * q4]);
-            zr[4 * q4] = x.x; zr[4 * q4 + 1] = x.y; zr[4 * q4 + 2] = x.z; zr[4 * q4 + 3] = x.w;
-          }
-          read_v16<BF16>(tl, lane, vv);
-          float bv[BT];
-#pragma unroll
-          for (int t = 0; t < BT; ++t) bv[t] = bet - vv[t];
-          serial_tile<LN>(zr, bv, vv, sm.Cc, gam, eps, dr);
-#pragma unroll
-          for (int q4 = 0; q4 < BT / 4; ++q4)
-            *reinterpret_cast<float4*>(&sm.Dt[lane][4 * q4]) =
-                make_float4(dr[4 * q4], dr[4 * q4 + 1], dr[4 * q4 + 2], dr[4 * q4 + 3]);
-        }
-      } else {
-        // dual form: the 16 tokens are independent; wave w takes tokens 4w..4w+3
-        const float4 x = *reinterpret_cast<const float4*>(&sm.Zt[lane][4 * wave]);
-        float vv[BT];
-        read_v16<BF16>(tl, lane, vv);
-        const float zz[4] = {x.x, x.y, x.z, x.w};
-        float dd[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float v = vv[4 * wave + u];
-          dd[u] = token_delta<LN>(zz[u], v, bet - v, gam, eps);
-        }
-        *reinterpret_cast<float4*>(&sm.Dt[lane][4 * wave]) =
-            make_float4(dd[0], dd[1], dd[2], dd[3]);
-      }
-      __syncthreads();
-
-      // ---------------- (C) outputs and the W update ----------------
-      const float4 dv4 = *reinterpret_cast<const float4*>(&sm.Dt[irow][4 * G]);
-      const float dv[4] = {dv4.x, dv4.y, dv4.z, dv4.w};   // delta[s = 4G + e][irow]
-      float ev[4];                                          // eta_s delta[s][irow]
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ev[e] = etav[e] * dv[e];
-      if constexpr (BF16) {
-        i16x4 mh, ml, dh, dlo, eh, el;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          unsigned short a, bb;
-          split_bf16(-M[e], a, bb);
-          mh[e] = static_cast<short>(a);
-          ml[e] = static_cast<short>(bb);
-          split_bf16(dv[e], a, bb);
-          dh[e] = static_cast<short>(a);
-          dlo[e] = static_cast<short>(bb);
-          split_bf16(-ev[e], a, bb);
-          eh[e] = static_cast<short>(a);
-          el[e] = static_cast<short>(bb);
-        }
-        U = mfma_k16(mh, dh, U);
-        U = mfma_k16(mh, dlo, U);
-        U = mfma_k16(ml, dh, U);
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-          const i16x4 kt = *reinterpret_cast<const i16x4*>(&tl.KT[jt][lane][0]);
-          Wt[jt] = mfma_k16(kt, eh, Wt[jt]);
-          Wt[jt] = mfma_k16(kt, el, Wt[jt]);
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) U = mfma_k4(-M[q], dv[q], U);
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            Wt[jt] = mfma_k4(tl.K[4 * G + q][16 * jt + l16], -ev[q], Wt[jt]);
-        }
-      }
-      // gate and stage: U[t = 4G + r][irow]
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 4 * G + r;
-        sm.O[ct * BT + t][irow] = U[r] * fast_sigmoid(gate_logit<BF16>(tl, t, irow));
-      }
-    }
-    if (b + 1 < nbatches) store_batch<BF16>(pf, sm.tile[(b + 1) & 1], tb0 + C::kTokens, T, tid);
-    __syncthreads();
-    if (b + 2 < nbatches) load_batch<BF16>(pf, src, etap, bhT, tb0 + 2 * C::kTokens, T, tid);
-    // write the batch's outputs back as 16-byte stores (rows past T skipped)
-    {
-      const int rows = static_cast<int>(min<int64_t>(C::kTokens, T - tb0));
-      float* dst = out + (bhT + tb0) * D;
-      for (int i = tid; i < rows * (D / 4); i += NT) {
-        const int t = i / (D / 4), c4 = i % (D / 4);
-        *reinterpret_cast<float4*>(dst + t * D + 4 * c4) =
-            *reinterpret_cast<const float4*>(&sm.O[t][4 * c4]);
-      }
-    }
+    for (int r = 0; r < 4; ++r) sm.Cc[0][4 * G + r][l16] = t0.ETA[4 * G + r] * g[r];
   }
 
-  if (W_final != nullptr) {
+  for (int64_t c = 0; c <= ntiles; ++c) {
+    __syncthreads();   // S_c
+    const bool live = c < ntiles;
+    if (wave == kSerialWave) {
+      if (live)
+        ln_pass<BF16, LN, DUAL>(sm, sm.ring[c % RING], sm.Cc[c & 1], sm.Dt[c & 1], lane, gam,
+                                bet, eps);
+    } else if (slice >= 0) {
+      if (c >= 1) {
+        // outputs of tile c-1 and the update W_c = W_{c-1} - E_{c-1}^T K_{c-1}
+        const auto& tp = sm.ring[(c - 1) % RING];
+        const float4 d4 = *reinterpret_cast<const float4*>(&sm.Dt[(c - 1) & 1][irow][4 * G]);
+        const float4 e4 = *reinterpret_cast<const float4*>(&tp.ETA[4 * G]);
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+        const float ne[4] = {-e4.x * d4.x, -e4.y * d4.y, -e4.z * d4.z, -e4.w * d4.w};
+        U = tok_times(sm.Mop[(c - 1) & 1], dv, lane, U);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 4 * G + r;
+          sm.Ob[(c - 1) & 1][t][irow] = U[r] * tp.SG[t][irow];
+        }
+        update_w(Wt, tp, ne, lane, l16, G);
+      }
+      if (live) {
+        // K_{c+1} W_c^T (for z of the next tile) and Q_c W_c^T
+        const auto& tc = sm.ring[c % RING];
+        const auto& tn = sm.ring[(c + 1) % RING];
+        if constexpr (BF16) {
+          const WOps w = split_w(Wt);
+          if (c + 1 < ntiles) P = rows_times_wt(krows(tn), w, lane);
+          U = rows_times_wt(qrows(tc), w, lane);
+        } else {
+          if (c + 1 < ntiles) P = rows_times_wt(krows(tn), Wt, l16, G);
+          U = rows_times_wt(qrows(tc), Wt, l16, G);
+        }
+      }
+    } else if (stage_parity >= 0) {
+      // tile c+2 into LDS (loaded two tiles ago), then the loads of tile c+4
+      if ((c & 1) == stage_parity) {
+        const int64_t u = c + 2;
+        if (u < ntiles) store_tile<BF16>(st, sm.ring[u % RING], u * BT, T, lane);
+        if (u + 2 < ntiles) load_tile<BF16>(st, src, etap, bhT, (u + 2) * BT, T, lane);
+      }
+      if (wave == kOutWave) {
+        if (c >= 2) write_tile_out(sm.Ob[(c - 2) & 1], out, bhT, (c - 2) * BT, T, lane);
+      } else if (live) {
+        const auto& tc = sm.ring[c % RING];
+        const float4 e4 = *reinterpret_cast<const float4*>(&tc.ETA[4 * G]);
+        const float eta[4] = {e4.x, e4.y, e4.z, e4.w};
+        // -eta_s (k_s . q_t) for s <= t
+        const f32x4 kq = gram(krows(tc), qrows(tc), lane, l16, G);
+        float m[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m[r] = (4 * G + r <= l16) ? -eta[r] * kq[r] : 0.0f;
+        put_tok(sm.Mop[c & 1], m, lane);
+        if (c + 1 < ntiles) {
+          const auto& tn = sm.ring[(c + 1) % RING];
+          // -(k_t of tile c+1) . (k_s of tile c)
+          const f32x4 x = gram(krows(tc), krows(tn), lane, l16, G);
+          const float nx[4] = {-x[0], -x[1], -x[2], -x[3]};
+          put_tok(sm.Xop, nx, lane);
+          if (!DUAL) {
+            const float4 f4 = *reinterpret_cast<const float4*>(&tn.ETA[4 * G]);
+            const float fe[4] = {f4.x, f4.y, f4.z, f4.w};
+            const f32x4 g = gram(krows(tn), krows(tn), lane, l16, G);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.Cc[(c + 1) & 1][4 * G + r][l16] = fe[r] * g[r];
+          }
+        }
+      }
+    }
+    __syncthreads();   // G_c
+    // z of tile c+1: K_{c+1} W_c^T - (K_{c+1} K_c^T) E_c
+    if (slice >= 0 && c + 1 < ntiles) {
+      const auto& tc = sm.ring[c % RING];
+      const float4 d4 = *reinterpret_cast<const float4*>(&sm.Dt[c & 1][irow][4 * G]);
+      const float4 e4 = *reinterpret_cast<const float4*>(&tc.ETA[4 * G]);
+      const float ev[4] = {e4.x * d4.x, e4.y * d4.y, e4.z * d4.z, e4.w * d4.w};
+      const f32x4 Z = tok_times(sm.Xop, ev, lane, P);
+      *reinterpret_cast<float4*>(&sm.Zt[irow][4 * G]) = make_float4(Z[0], Z[1], Z[2], Z[3]);
+    }
+  }
+  __syncthreads();
+  // outputs of the last tile (staged in the final period)
+  if (wave == kOutWave && ntiles > 0)
+    write_tile_out(sm.Ob[(ntiles - 1) & 1], out, bhT, (ntiles - 1) * BT, T, lane);
+  if (slice >= 0 && W_final != nullptr) {
     float* w = W_final + bh * D * D + irow * D + 4 * G;
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt)
-      *reinterpret_cast<float4*>(w + 16 * jt) = make_float4(Wt[jt][0], Wt[jt][1], Wt[jt][2], Wt[jt][3]);
+      *reinterpret_cast<float4*>(w + 16 * jt) =
+          make_float4(Wt[jt][0], Wt[jt][1], Wt[jt][2], Wt[jt][3]);
   }
 }
 
