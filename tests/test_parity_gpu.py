@@ -167,12 +167,21 @@ def test_state_in_place_and_not_written():
     assert_close(out.cpu().numpy(), ro, 1e-4, "out (no W_final)")
 
 
-@pytest.mark.parametrize("ln,dual,chunk", [("st", False, 1), ("exact", False, 1),
-                                           ("st", True, 16)])
-def test_resume_equals_one_call(ln, dual, chunk):
-    say(f"case resume ln={ln} dual={dual}")
-    T1, T = 64, 150
-    x = make_case(2, 2, T, 64, seed=12, ln=ln, dual=dual, chunk=chunk, random_affine=True,
+@pytest.mark.parametrize("d,ln,dual,chunk", [(64, "st", False, 1), (64, "exact", False, 1),
+                                             (64, "st", True, 16), (32, "st", False, 1),
+                                             (32, "exact", True, 5)])
+def test_resume_equals_one_call(d, ln, dual, chunk):
+    """Two calls chained through W_final equal one call over the whole sequence.
+
+    The vector-ALU scan takes every token the same way in both, so the match
+    is bitwise.  The matrix-core scan forms z of the first tile of a call from
+    W directly and of later tiles through the one-tile-ahead correction: the
+    same value in exact arithmetic, rounded differently, so it must match to
+    the fp32 tolerance.
+    """
+    say(f"case resume d={d} ln={ln} dual={dual}")
+    T1, T = 80, 150
+    x = make_case(2, 2, T, d, seed=12, ln=ln, dual=dual, chunk=chunk, random_affine=True,
                   in_bf16=True)
     t = dev(x)
     full_o, full_W = ttt.forward(t["q"], t["k"], t["v"], t["eta_logit"], t["gate_logit"],
@@ -183,8 +192,16 @@ def test_resume_equals_one_call(ln, dual, chunk):
     o1, W1 = ttt.forward(*first, t["W0"], t["gamma"], t["beta"], ln=ln, dual=dual, chunk=chunk)
     o2, W2 = ttt.forward(*second, W1, t["gamma"], t["beta"], ln=ln, dual=dual, chunk=chunk)
     torch.cuda.synchronize()
-    assert torch.equal(torch.cat([o1, o2], dim=2), full_o)
-    assert torch.equal(W2, full_W)
+    o12 = torch.cat([o1, o2], dim=2)
+    kernel = ttt.ttt_linear_kernel(d, ttt.mode_bits(ln, dual, True), chunk)
+    if kernel == "scan_valu":
+        assert torch.equal(o12, full_o)
+        assert torch.equal(W2, full_W)
+    else:
+        assert_close(o12.cpu().numpy(), full_o.cpu().numpy(), 1e-5, "out (resumed vs one call)")
+        assert_close(W2.cpu().numpy(), full_W.cpu().numpy(), 1e-5, "W_final (resumed vs one call)")
+    ro, rW = ref_run(x)
+    assert_close(o12.cpu().numpy(), ro, 2e-2, "out vs oracle")
 
 
 def test_deterministic_and_batch_split_invariant():
