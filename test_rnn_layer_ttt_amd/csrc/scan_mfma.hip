@@ -30,12 +30,13 @@
 //               the barriers)
 //   waves 1,2,5,6  one 16-row slice of W each, as W^T tiles in the 16x16
 //               accumulator layout (lane l holds W[16s + l%16][16jt + 4(l/16) + r]);
-//               they apply the updates, form K W^T and Q W^T, the outputs,
-//               and the one-tile-ahead correction between serial passes
+//               they apply the updates, form K W^T, Q W^T, the token Gram
+//               matrices K Q^T and K_{c+1} K_c^T, the outputs, and the
+//               one-tile-ahead correction between serial passes
 //   wave 3      input staging of even tiles (global loads two tiles ahead,
 //               LDS layouts) and output write-back
-//   wave 7      input staging of odd tiles and the Gram matrices (K K^T,
-//               K Q^T, cross-tile K K^T)
+//   wave 7      input staging of odd tiles and the coefficients eta (K K^T)
+//               of the serial pass
 // Per tile c there are two barriers: S_c (z_c and the coefficients are in
 // LDS; the serial pass of tile c starts) and G_c (delta_c is in LDS; the
 // slices form z_{c+1}).
@@ -55,7 +56,7 @@ constexpr int KPAD = 68;    // padded fp32 row (floats) of K/Q/output tiles in L
 constexpr int ZPAD = 20;    // padded row (floats) of the per-feature z / delta tiles
 constexpr int kSerialWave = 0;
 constexpr int kOutWave = 3;    // stages even tiles, writes outputs back
-constexpr int kGramWave = 7;   // stages odd tiles, forms the Gram matrices
+constexpr int kGramWave = 7;   // stages odd tiles, forms the serial coefficients
 
 // W row slice owned by a wave, or -1
 __device__ __forceinline__ int slice_of(int wave) {
@@ -134,18 +135,18 @@ struct TileF32 {
   float ETA[BT];
 };
 
-// A operand (t = lane % 16, s = 4 (lane / 16) + e) of a 16 x 16 token matrix:
-// bf16 hi and lo parts for the 16x16x16 MFMA, or the fp32 value of k-step e.
+// A operand (t = lane % 16, s = 4 (lane / 16) + e) of a 16 x 16 token matrix,
+// held in registers: bf16 hi and lo parts for the 16x16x16 MFMA, or the fp32
+// value of k-step e for the 16x16x4 MFMA.
 template <bool BF16>
-struct TokOp;
+struct TokReg;
 template <>
-struct TokOp<true> {
-  uint16_t hi[64][4];
-  uint16_t lo[64][4];
+struct TokReg<true> {
+  i16x4 hi, lo;
 };
 template <>
-struct TokOp<false> {
-  float v[64][4];
+struct TokReg<false> {
+  float v[4];
 };
 
 template <bool BF16>
@@ -155,8 +156,6 @@ struct Smem {
   float Zt[D][ZPAD];       // z of the next serial pass, by feature
   float Dt[2][D][ZPAD];    // delta of a tile, by feature
   float Cc[2][BT][BT];     // eta_s (k_s . k_t) of a tile
-  TokOp<BF16> Mop[2];      // -eta_s (k_s . q_t), s <= t: output correction
-  TokOp<BF16> Xop;         // -(k_t of the next tile) . (k_s of this tile)
   float Ob[2][BT][KPAD];   // gated outputs awaiting write-back
 };
 
@@ -298,18 +297,19 @@ __device__ __forceinline__ void wave_total2(float& a, float& b) {
 }
 
 // delta for one token from z (lane = feature i) and the wave sums s1 = sum z,
-// s2 = sum z^2; bv = beta_i - v_t[i].  mu = s1/d, d*var = s2 - s1*mu.
+// s2 = sum z^2; gz = gamma_i z, bv = beta_i - v_t[i].  With a = s1/d (the
+// mean) and b = s2/d + eps, var + eps = b - a^2; the terms that do not depend
+// on the sums (gz, b) are formed off the critical path.
 template <int LN>
-__device__ __forceinline__ float delta_from_sums(float z, float s1, float s2, float bv, float gam,
-                                                 float eps) {
-  const float mu = s1 * (1.0f / D);
-  const float dvar = fmaf(-s1, mu, s2);
-  const float rs = __builtin_amdgcn_rsqf(fmaxf(fmaf(dvar, 1.0f / D, eps), eps));
-  const float zc = z - mu;
+__device__ __forceinline__ float delta_from_sums(float z, float gz, float s1, float s2, float bv,
+                                                 float gam, float eps) {
+  const float a = s1 * (1.0f / D);
+  const float b = fmaf(s2, 1.0f / D, eps);
+  const float rs = __builtin_amdgcn_rsqf(fmaxf(fmaf(-a, a, b), eps));
   if constexpr (LN == kLnST) {
-    return fmaf(gam * rs, zc, bv);
+    return fmaf(rs, fmaf(-gam, a, gz), bv);
   } else {
-    const float xh = zc * rs;
+    const float xh = (z - a) * rs;
     const float g = gam * fmaf(gam, xh, bv);
     float sg = g, sgx = g * xh;
     wave_total2(sg, sgx);
@@ -325,27 +325,37 @@ __device__ __forceinline__ float token_delta(float z, float v, float bv, float g
   } else {
     float s1 = z, s2 = z * z;
     wave_total2(s1, s2);
-    return delta_from_sums<LN>(z, s1, s2, bv, gam, eps);
+    return delta_from_sums<LN>(z, gam * z, s1, s2, bv, gam, eps);
   }
 }
 
 // The serial pass over one tile.  zr[t] = (W_c k_t)_i on entry; cc points at
-// eta_s (k_s . k_t) in LDS.  Token s's delta is applied to row s+1 at once;
-// its updates of rows s+2.. are spread over the reduction steps of token s+1,
-// where they fill the DPP wait states.
+// eta_s (k_s . k_t) in LDS.  Token s's delta is applied to row s+1 at once,
+// with the superdiagonal coefficient held in a register since the start of
+// the tile; its updates of rows s+2.. are spread over the reduction steps of
+// token s+1, where they fill the DPP wait states, with their coefficients
+// read one token ahead.
 template <int LN>
 __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[BT],
                                             const float (&vv)[BT], const float (*cc)[BT],
                                             float gam, float eps, float (&dr)[BT]) {
-  float cprev[BT];
+  float cd[BT];
+#pragma unroll
+  for (int s = 0; s + 1 < BT; ++s) cd[s] = cc[s][s + 1];
+  float cprev[BT], crow[BT];   // row s-1 (in use) and row s (in flight) of eta (k.k)
   float dprev = 0.0f;
 #pragma unroll
   for (int s = 0; s < BT; ++s) {
-    float crow[BT];
+    if (s >= 1) {
 #pragma unroll
-    for (int q4 = (s + 1) / 4; q4 < BT / 4; ++q4) {
-      const float4 x = *reinterpret_cast<const float4*>(&cc[s][4 * q4]);
-      crow[4 * q4] = x.x; crow[4 * q4 + 1] = x.y; crow[4 * q4 + 2] = x.z; crow[4 * q4 + 3] = x.w;
+      for (int t = s + 1; t < BT; ++t) cprev[t] = crow[t];
+    }
+    if (s + 2 < BT) {
+#pragma unroll
+      for (int q4 = (s + 2) / 4; q4 < BT / 4; ++q4) {
+        const float4 x = *reinterpret_cast<const float4*>(&cc[s][4 * q4]);
+        crow[4 * q4] = x.x; crow[4 * q4 + 1] = x.y; crow[4 * q4 + 2] = x.z; crow[4 * q4 + 3] = x.w;
+      }
     }
     const float z = zr[s];
     // deferred rows s+1 .. BT-1 of the previous token, split into six slices
@@ -364,18 +374,17 @@ __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[B
       dl = z - vv[s];
     } else {
       float a = z, b = z * z;
+      const float gz = gam * z;
       a = red_step<0>(a); b = red_step<0>(b); fill(0);
       a = red_step<1>(a); b = red_step<1>(b); fill(1);
       a = red_step<2>(a); b = red_step<2>(b); fill(2);
       a = red_step<3>(a); b = red_step<3>(b); fill(3);
       a = red_step<4>(a); b = red_step<4>(b); fill(4);
       a = red_step<5>(a); b = red_step<5>(b); fill(5);
-      dl = delta_from_sums<LN>(z, lane63(a), lane63(b), bv[s], gam, eps);
+      dl = delta_from_sums<LN>(z, gz, lane63(a), lane63(b), bv[s], gam, eps);
     }
     dr[s] = dl;
-    if (s + 1 < BT) zr[s + 1] = fmaf(-crow[s + 1], dl, zr[s + 1]);
-#pragma unroll
-    for (int t = s + 2; t < BT; ++t) cprev[t] = crow[t];
+    if (s + 1 < BT) zr[s + 1] = fmaf(-cd[s], dl, zr[s + 1]);
     dprev = dl;
   }
 }
@@ -475,22 +484,24 @@ __device__ __forceinline__ f32x4 rows_times_wt(const float (*A)[KPAD], const f32
   return acc;
 }
 
-// acc += A (16 x 16, A operand TokOp) times B[s][slice feature], B = b[e] for s = 4G + e
-__device__ __forceinline__ f32x4 tok_times(const TokOp<true>& op, const float (&b)[4], int lane,
-                                           f32x4 acc) {
+// acc += A (16 x 16 token matrix) times B[s][slice feature], B = b[e] for s = 4G + e
+__device__ __forceinline__ f32x4 tok_mul(const TokReg<true>& a, const float (&b)[4], f32x4 acc) {
   i16x4 bh, bl;
   split4(b, bh, bl);
-  const i16x4 ah = *reinterpret_cast<const i16x4*>(&op.hi[lane][0]);
-  const i16x4 al = *reinterpret_cast<const i16x4*>(&op.lo[lane][0]);
-  return mfma_k16x3(ah, al, bh, bl, acc);
+  return mfma_k16x3(a.hi, a.lo, bh, bl, acc);
 }
-__device__ __forceinline__ f32x4 tok_times(const TokOp<false>& op, const float (&b)[4], int lane,
-                                           f32x4 acc) {
-  const float4 a = *reinterpret_cast<const float4*>(&op.v[lane][0]);
-  acc = mfma_k4(a.x, b[0], acc);
-  acc = mfma_k4(a.y, b[1], acc);
-  acc = mfma_k4(a.z, b[2], acc);
-  return mfma_k4(a.w, b[3], acc);
+__device__ __forceinline__ f32x4 tok_mul(const TokReg<false>& a, const float (&b)[4], f32x4 acc) {
+  acc = mfma_k4(a.v[0], b[0], acc);
+  acc = mfma_k4(a.v[1], b[1], acc);
+  acc = mfma_k4(a.v[2], b[2], acc);
+  return mfma_k4(a.v[3], b[3], acc);
+}
+__device__ __forceinline__ void make_tok(TokReg<true>& a, const float (&x)[4]) {
+  split4(x, a.hi, a.lo);
+}
+__device__ __forceinline__ void make_tok(TokReg<false>& a, const float (&x)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) a.v[e] = x[e];
 }
 
 // Wt[jt] -= sum_s K[s][16jt + i] e[s][slice feature], with ne[e] = -e[s = 4G + e]
@@ -541,15 +552,6 @@ __device__ __forceinline__ f32x4 gram(const float (*A)[KPAD], const float (*B)[K
   }
   return acc;
 }
-__device__ __forceinline__ void put_tok(TokOp<true>& op, const float (&x)[4], int lane) {
-  i16x4 hi, lo;
-  split4(x, hi, lo);
-  *reinterpret_cast<i16x4*>(&op.hi[lane][0]) = hi;
-  *reinterpret_cast<i16x4*>(&op.lo[lane][0]) = lo;
-}
-__device__ __forceinline__ void put_tok(TokOp<false>& op, const float (&x)[4], int lane) {
-  *reinterpret_cast<float4*>(&op.v[lane][0]) = make_float4(x[0], x[1], x[2], x[3]);
-}
 __device__ __forceinline__ const uint16_t (*krows(const TileBf16& t))[64][8] { return t.KA; }
 __device__ __forceinline__ const uint16_t (*qrows(const TileBf16& t))[64][8] { return t.QA; }
 __device__ __forceinline__ const float (*krows(const TileF32& t))[KPAD] { return t.K; }
@@ -596,6 +598,7 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   // slice waves: W^T tiles, Wt[jt][r] = W[irow][16 jt + 4G + r]; P, U accumulators
   f32x4 Wt[4] = {};
   f32x4 P = {0, 0, 0, 0}, U = {0, 0, 0, 0};
+  TokReg<BF16> Mreg{}, Xreg{};   // -eta (k.q) causal of the last tile; -(k_next . k)
   // serial wave: LayerNorm affine of feature `lane`
   float gam = 1.0f, bet = 0.0f;
   Stage<BF16> st;   // staging waves: the tile in flight
@@ -655,7 +658,7 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         const float4 e4 = *reinterpret_cast<const float4*>(&tp.ETA[4 * G]);
         const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
         const float ne[4] = {-e4.x * d4.x, -e4.y * d4.y, -e4.z * d4.z, -e4.w * d4.w};
-        U = tok_times(sm.Mop[(c - 1) & 1], dv, lane, U);
+        U = tok_mul(Mreg, dv, U);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 4 * G + r;
@@ -675,6 +678,19 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
           if (c + 1 < ntiles) P = rows_times_wt(krows(tn), Wt, l16, G);
           U = rows_times_wt(qrows(tc), Wt, l16, G);
         }
+        // -eta_s (k_s . q_t) for s <= t (outputs of tile c) and -(k_t(c+1) . k_s(c))
+        const float4 e4 = *reinterpret_cast<const float4*>(&tc.ETA[4 * G]);
+        const float eta[4] = {e4.x, e4.y, e4.z, e4.w};
+        const f32x4 kq = gram(krows(tc), qrows(tc), lane, l16, G);
+        float m[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m[r] = (4 * G + r <= l16) ? -eta[r] * kq[r] : 0.0f;
+        make_tok(Mreg, m);
+        if (c + 1 < ntiles) {
+          const f32x4 x = gram(krows(tc), krows(tn), lane, l16, G);
+          const float nx[4] = {-x[0], -x[1], -x[2], -x[3]};
+          make_tok(Xreg, nx);
+        }
       }
     } else if (stage_parity >= 0) {
       // tile c+2 into LDS (loaded two tiles ago), then the loads of tile c+4
@@ -685,30 +701,14 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       }
       if (wave == kOutWave) {
         if (c >= 2) write_tile_out(sm.Ob[(c - 2) & 1], out, bhT, (c - 2) * BT, T, lane);
-      } else if (live) {
-        const auto& tc = sm.ring[c % RING];
-        const float4 e4 = *reinterpret_cast<const float4*>(&tc.ETA[4 * G]);
-        const float eta[4] = {e4.x, e4.y, e4.z, e4.w};
-        // -eta_s (k_s . q_t) for s <= t
-        const f32x4 kq = gram(krows(tc), qrows(tc), lane, l16, G);
-        float m[4];
+      } else if (!DUAL && c + 1 < ntiles) {
+        // eta_s (k_s . k_t) of tile c+1 for its serial pass
+        const auto& tn = sm.ring[(c + 1) % RING];
+        const float4 f4 = *reinterpret_cast<const float4*>(&tn.ETA[4 * G]);
+        const float fe[4] = {f4.x, f4.y, f4.z, f4.w};
+        const f32x4 g = gram(krows(tn), krows(tn), lane, l16, G);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) m[r] = (4 * G + r <= l16) ? -eta[r] * kq[r] : 0.0f;
-        put_tok(sm.Mop[c & 1], m, lane);
-        if (c + 1 < ntiles) {
-          const auto& tn = sm.ring[(c + 1) % RING];
-          // -(k_t of tile c+1) . (k_s of tile c)
-          const f32x4 x = gram(krows(tc), krows(tn), lane, l16, G);
-          const float nx[4] = {-x[0], -x[1], -x[2], -x[3]};
-          put_tok(sm.Xop, nx, lane);
-          if (!DUAL) {
-            const float4 f4 = *reinterpret_cast<const float4*>(&tn.ETA[4 * G]);
-            const float fe[4] = {f4.x, f4.y, f4.z, f4.w};
-            const f32x4 g = gram(krows(tn), krows(tn), lane, l16, G);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sm.Cc[(c + 1) & 1][4 * G + r][l16] = fe[r] * g[r];
-          }
-        }
+        for (int r = 0; r < 4; ++r) sm.Cc[(c + 1) & 1][4 * G + r][l16] = fe[r] * g[r];
       }
     }
     __syncthreads();   // G_c
@@ -718,7 +718,7 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       const float4 d4 = *reinterpret_cast<const float4*>(&sm.Dt[c & 1][irow][4 * G]);
       const float4 e4 = *reinterpret_cast<const float4*>(&tc.ETA[4 * G]);
       const float ev[4] = {e4.x * d4.x, e4.y * d4.y, e4.z * d4.z, e4.w * d4.w};
-      const f32x4 Z = tok_times(sm.Xop, ev, lane, P);
+      const f32x4 Z = tok_mul(Xreg, ev, P);
       *reinterpret_cast<float4*>(&sm.Zt[irow][4 * G]) = make_float4(Z[0], Z[1], Z[2], Z[3]);
     }
   }
