@@ -330,33 +330,31 @@ __device__ __forceinline__ float token_delta(float z, float v, float bv, float g
 }
 
 // The serial pass over one tile.  zr[t] = (W_c k_t)_i on entry; cc points at
-// eta_s (k_s . k_t) in LDS.  Token s's delta is applied to row s+1 at once,
-// with the superdiagonal coefficient held in a register since the start of
-// the tile; its updates of rows s+2.. are spread over the reduction steps of
-// token s+1, where they fill the DPP wait states, with their coefficients
-// read one token ahead.
+// eta_s (k_s . k_t) (t > s) in LDS and cd[s] holds its superdiagonal
+// eta_s (k_s . k_{s+1}) in registers.  Token s's delta is applied to row s+1 at
+// once; its updates of rows s+2.. are spread over the reduction steps of token
+// s+1, where they fill the DPP wait states, with coefficient rows read two
+// tokens ahead of their use.
 template <int LN>
 __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[BT],
                                             const float (&vv)[BT], const float (*cc)[BT],
-                                            float gam, float eps, float (&dr)[BT]) {
-  float cd[BT];
+                                            const float (&cd)[BT], float gam, float eps,
+                                            float (&dr)[BT]) {
+  float crow[4][BT];   // rows s-1 (in use), s, s+1, s+2 (in flight); ring by row % 4
+  auto load_row = [&](int r) {
 #pragma unroll
-  for (int s = 0; s + 1 < BT; ++s) cd[s] = cc[s][s + 1];
-  float cprev[BT], crow[BT];   // row s-1 (in use) and row s (in flight) of eta (k.k)
+    for (int q4 = (r + 2) / 4; q4 < BT / 4; ++q4) {
+      const float4 x = *reinterpret_cast<const float4*>(&cc[r][4 * q4]);
+      float* d = crow[r % 4];
+      d[4 * q4] = x.x; d[4 * q4 + 1] = x.y; d[4 * q4 + 2] = x.z; d[4 * q4 + 3] = x.w;
+    }
+  };
+  load_row(0);
+  load_row(1);
   float dprev = 0.0f;
 #pragma unroll
   for (int s = 0; s < BT; ++s) {
-    if (s >= 1) {
-#pragma unroll
-      for (int t = s + 1; t < BT; ++t) cprev[t] = crow[t];
-    }
-    if (s + 2 < BT) {
-#pragma unroll
-      for (int q4 = (s + 2) / 4; q4 < BT / 4; ++q4) {
-        const float4 x = *reinterpret_cast<const float4*>(&cc[s][4 * q4]);
-        crow[4 * q4] = x.x; crow[4 * q4 + 1] = x.y; crow[4 * q4 + 2] = x.z; crow[4 * q4 + 3] = x.w;
-      }
-    }
+    if (s + 2 < BT - 2) load_row(s + 2);
     const float z = zr[s];
     // deferred rows s+1 .. BT-1 of the previous token, split into six slices
     constexpr int kSlots = 6;
@@ -365,7 +363,7 @@ __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[B
       if (s == 0) return;
 #pragma unroll
       for (int t = s + 1 + (k * n) / kSlots; t < s + 1 + ((k + 1) * n) / kSlots; ++t)
-        zr[t] = fmaf(-cprev[t], dprev, zr[t]);
+        zr[t] = fmaf(-crow[(s - 1) % 4][t], dprev, zr[t]);
     };
     float dl;
     if constexpr (LN == kLnNone) {
@@ -409,26 +407,42 @@ __device__ __forceinline__ void read_v16(const typename Smem<BF16>::Tile& tl, in
   }
 }
 
+// What the serial wave holds for a tile before its pass: v, beta - v and the
+// coefficients eta_s (k_s . k_t), loaded while the W slices form z.
+struct SerialIn {
+  float cd[BT];   // eta_s (k_s . k_{s+1})
+  float vv[BT];
+  float bv[BT];
+};
+
+template <bool BF16, bool DUAL>
+__device__ __forceinline__ void serial_prefetch(SerialIn& in, const typename Smem<BF16>::Tile& tl,
+                                                const float (*cc)[BT], int lane, float bet) {
+  read_v16<BF16>(tl, lane, in.vv);
+#pragma unroll
+  for (int t = 0; t < BT; ++t) in.bv[t] = bet - in.vv[t];
+  if constexpr (!DUAL) {
+#pragma unroll
+    for (int s = 0; s < BT - 1; ++s) in.cd[s] = cc[s][s + 1];
+  }
+}
+
 // One serial (or, in the dual form, parallel) LayerNorm pass: z from Zt,
 // delta into dt.
 template <bool BF16, int LN, bool DUAL>
-__device__ __forceinline__ void ln_pass(Smem<BF16>& sm, const typename Smem<BF16>::Tile& tl,
-                                        const float (*cc)[BT], float (*dt)[ZPAD], int lane,
-                                        float gam, float bet, float eps) {
-  float zr[BT], dr[BT], vv[BT], bv[BT];
+__device__ __forceinline__ void ln_pass(Smem<BF16>& sm, const SerialIn& in, const float (*cc)[BT],
+                                        float (*dt)[ZPAD], int lane, float gam, float eps) {
+  float zr[BT], dr[BT];
 #pragma unroll
   for (int q4 = 0; q4 < BT / 4; ++q4) {
     const float4 x = *reinterpret_cast<const float4*>(&sm.Zt[lane][4 * q4]);
     zr[4 * q4] = x.x; zr[4 * q4 + 1] = x.y; zr[4 * q4 + 2] = x.z; zr[4 * q4 + 3] = x.w;
   }
-  read_v16<BF16>(tl, lane, vv);
-#pragma unroll
-  for (int t = 0; t < BT; ++t) bv[t] = bet - vv[t];
   if constexpr (DUAL) {
 #pragma unroll
-    for (int t = 0; t < BT; ++t) dr[t] = token_delta<LN>(zr[t], vv[t], bv[t], gam, eps);
+    for (int t = 0; t < BT; ++t) dr[t] = token_delta<LN>(zr[t], in.vv[t], in.bv[t], gam, eps);
   } else {
-    serial_tile<LN>(zr, bv, vv, cc, gam, eps, dr);
+    serial_tile<LN>(zr, in.bv, in.vv, cc, in.cd, gam, eps, dr);
   }
 #pragma unroll
   for (int q4 = 0; q4 < BT / 4; ++q4)
@@ -599,8 +613,9 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   f32x4 Wt[4] = {};
   f32x4 P = {0, 0, 0, 0}, U = {0, 0, 0, 0};
   TokReg<BF16> Mreg{}, Xreg{};   // -eta (k.q) causal of the last tile; -(k_next . k)
-  // serial wave: LayerNorm affine of feature `lane`
+  // serial wave: LayerNorm affine of feature `lane`, and its inputs of the next tile
   float gam = 1.0f, bet = 0.0f;
+  SerialIn sin;
   Stage<BF16> st;   // staging waves: the tile in flight
 
   if (slice >= 0) {
@@ -647,9 +662,10 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
     __syncthreads();   // S_c
     const bool live = c < ntiles;
     if (wave == kSerialWave) {
-      if (live)
-        ln_pass<BF16, LN, DUAL>(sm, sm.ring[c % RING], sm.Cc[c & 1], sm.Dt[c & 1], lane, gam,
-                                bet, eps);
+      if (live) {
+        if (c == 0) serial_prefetch<BF16, DUAL>(sin, sm.ring[0], sm.Cc[0], lane, bet);
+        ln_pass<BF16, LN, DUAL>(sm, sin, sm.Cc[c & 1], sm.Dt[c & 1], lane, gam, eps);
+      }
     } else if (slice >= 0) {
       if (c >= 1) {
         // outputs of tile c-1 and the update W_c = W_{c-1} - E_{c-1}^T K_{c-1}
@@ -712,6 +728,9 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       }
     }
     __syncthreads();   // G_c
+    // the serial wave loads its inputs of tile c+1 while the slices form z
+    if (wave == kSerialWave && c + 1 < ntiles)
+      serial_prefetch<BF16, DUAL>(sin, sm.ring[(c + 1) % RING], sm.Cc[(c + 1) & 1], lane, bet);
     // z of tile c+1: K_{c+1} W_c^T - (K_{c+1} K_c^T) E_c
     if (slice >= 0 && c + 1 < ntiles) {
       const auto& tc = sm.ring[c % RING];
