@@ -149,6 +149,9 @@ def main():
     ap.add_argument("--cpu-scans", type=int, default=256,
                     help="scans of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed region, run one device-to-device copy of this many "
+                         "MiB: a kernel of known traffic that scales the HBM byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -234,6 +237,16 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 18          # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n}),
+              flush=True)
 
 
 if __name__ == "__main__":
