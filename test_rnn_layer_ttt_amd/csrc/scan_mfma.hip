@@ -25,18 +25,18 @@
 // only the lo*lo term (~2^-17 relative) is dropped.  With fp32 inputs the
 // products run as fp32 MFMA (16x16x4).
 //
-// Wave roles (8 waves; wave w runs on SIMD w % 4):
+// Wave roles (8 waves; wave w runs on SIMD w % 4; see Roles below):
 //   wave 0      serial LayerNorm pass, alone on its SIMD (wave 4 only joins
 //               the barriers)
 //   waves 1,2,5,6  one 16-row slice of W each, as W^T tiles in the 16x16
 //               accumulator layout (lane l holds W[16s + l%16][16jt + 4(l/16) + r]);
-//               they apply the updates, form K W^T, Q W^T, the token Gram
-//               matrices K Q^T and K_{c+1} K_c^T, the outputs, and the
-//               one-tile-ahead correction between serial passes
-//   wave 3      input staging of even tiles (global loads two tiles ahead,
-//               LDS layouts) and output write-back
-//   wave 7      input staging of odd tiles and the coefficients eta (K K^T)
-//               of the serial pass
+//               they apply the updates, form K W^T, Q W^T, the outputs and
+//               the one-tile-ahead correction between serial passes
+//   waves 3,7   input staging of even / odd tiles (global loads two tiles
+//               ahead, LDS layouts); wave 3 also writes outputs back, wave 7
+//               forms the coefficients eta (K K^T) of the serial pass
+// The token Gram matrices K Q^T and K_{c+1} K_c^T are formed by the slices
+// (bf16 inputs) or by the staging waves (fp32 inputs).
 // Per tile c there are two barriers: S_c (z_c and the coefficients are in
 // LDS; the serial pass of tile c starts) and G_c (delta_c is in LDS; the
 // slices form z_{c+1}).
@@ -55,13 +55,25 @@ constexpr int RING = 4;     // staged input tiles held in LDS
 constexpr int KPAD = 68;    // padded fp32 row (floats) of K/Q/output tiles in LDS
 constexpr int ZPAD = 20;    // padded row (floats) of the per-feature z / delta tiles
 constexpr int kSerialWave = 0;
-constexpr int kOutWave = 3;    // stages even tiles, writes outputs back
-constexpr int kGramWave = 7;   // stages odd tiles, forms the serial coefficients
 
-// W row slice owned by a wave, or -1
-__device__ __forceinline__ int slice_of(int wave) {
-  return wave == 1 ? 0 : wave == 2 ? 1 : wave == 5 ? 2 : wave == 6 ? 3 : -1;
-}
+// Wave roles.  Wave w runs on SIMD w % 4.  The serial wave keeps SIMD 0 to
+// itself (wave 4 only joins the barriers): a wave issuing MFMAs on the same
+// SIMD stretches its dependency chain by half, whatever the wave priorities.
+// The W slices pair up on SIMDs 1 and 2, the staging waves on SIMD 3.  With
+// bf16 inputs the slices form their token Gram matrices themselves; with fp32
+// inputs, where a 16x16x4 MFMA costs four times the bf16 rate per flop and the
+// slices' SIMDs are the busiest, the staging waves form them.
+template <bool BF16>
+struct Roles {
+  static constexpr int kStageEven = 3;          // stages even tiles, writes outputs back
+  static constexpr int kStageOdd = 7;           // stages odd tiles
+  static constexpr int kCoefWave = 7;           // eta (k.k) of the serial pass
+  static constexpr bool kTokInSlices = BF16;    // else: kStageEven forms M, kStageOdd X
+  // W row slice owned by a wave, or -1
+  __device__ static int slice_of(int wave) {
+    return wave == 1 ? 0 : wave == 2 ? 1 : wave == 5 ? 2 : wave == 6 ? 3 : -1;
+  }
+};
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -156,6 +168,8 @@ struct Smem {
   float Zt[D][ZPAD];       // z of the next serial pass, by feature
   float Dt[2][D][ZPAD];    // delta of a tile, by feature
   float Cc[2][BT][BT];     // eta_s (k_s . k_t) of a tile
+  float Mg[2][BT][ZPAD];   // -eta_s (k_s . q_t), s <= t, of a tile, at [t][s]
+  float Xg[BT][ZPAD];      // -(k_s . k'_t) of a tile and the next one, at [t][s]
   float Ob[2][BT][KPAD];   // gated outputs awaiting write-back
 };
 
@@ -606,13 +620,14 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   const int64_t bhT = bh * T;
   const void* const src[4] = {qp, kp, vp, gatep};
   const int64_t ntiles = (T + BT - 1) / BT;
-  const int slice = slice_of(wave);
+  using R = Roles<BF16>;
+  const int slice = R::slice_of(wave);
   const int irow = 16 * slice + l16;   // W row (feature i) held by this lane, slice waves
 
   // slice waves: W^T tiles, Wt[jt][r] = W[irow][16 jt + 4G + r]; P, U accumulators
   f32x4 Wt[4] = {};
   f32x4 P = {0, 0, 0, 0}, U = {0, 0, 0, 0};
-  TokReg<BF16> Mreg{}, Xreg{};   // -eta (k.q) causal of the last tile; -(k_next . k)
+  TokReg<BF16> Mreg{}, Xreg{};   // slices forming their own token matrices: M and X below
   // serial wave: LayerNorm affine of feature `lane`, and its inputs of the next tile
   float gam = 1.0f, bet = 0.0f;
   SerialIn sin;
@@ -626,13 +641,14 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       Wt[jt] = f32x4{x.x, x.y, x.z, x.w};
     }
   }
+  if (wave == kSerialWave) __builtin_amdgcn_s_setprio(3);
   if (wave == kSerialWave && LN != kLnNone) {
     gam = gamma[h * D + lane];
     bet = beta[h * D + lane];
   }
   __builtin_amdgcn_s_waitcnt(0);
   // staging prologue: tiles 0 and 1 into LDS, tiles 2 and 3 in flight
-  const int stage_parity = wave == kOutWave ? 0 : wave == kGramWave ? 1 : -1;
+  const int stage_parity = wave == R::kStageEven ? 0 : wave == R::kStageOdd ? 1 : -1;
   if (stage_parity >= 0) {
     const int u = stage_parity;
     if (u < ntiles) {
@@ -651,12 +667,28 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       Z = rows_times_wt(krows(sm.ring[0]), Wt, l16, G);
     *reinterpret_cast<float4*>(&sm.Zt[irow][4 * G]) = make_float4(Z[0], Z[1], Z[2], Z[3]);
   }
-  if (!DUAL && wave == kGramWave && ntiles > 0) {
+  if (!DUAL && wave == R::kCoefWave && ntiles > 0) {
     const auto& t0 = sm.ring[0];
     const f32x4 g = gram(krows(t0), krows(t0), lane, l16, G);
 #pragma unroll
     for (int r = 0; r < 4; ++r) sm.Cc[0][4 * G + r][l16] = t0.ETA[4 * G + r] * g[r];
   }
+
+  // M = -eta_s (k_s . q_t), s <= t: the in-tile part of the outputs of tile c
+  auto tok_m = [&](const typename Smem<BF16>::Tile& tc, float (&m)[4]) {
+    const float4 e4 = *reinterpret_cast<const float4*>(&tc.ETA[4 * G]);
+    const float eta[4] = {e4.x, e4.y, e4.z, e4.w};
+    const f32x4 kq = gram(krows(tc), qrows(tc), lane, l16, G);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m[r] = (4 * G + r <= l16) ? -eta[r] * kq[r] : 0.0f;
+  };
+  // X = -(k_t(c+1) . k_s(c)): carries delta of tile c into z of tile c+1
+  auto tok_x = [&](const typename Smem<BF16>::Tile& tc, const typename Smem<BF16>::Tile& tn,
+                   float (&x)[4]) {
+    const f32x4 g = gram(krows(tc), krows(tn), lane, l16, G);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = -g[r];
+  };
 
   for (int64_t c = 0; c <= ntiles; ++c) {
     __syncthreads();   // S_c
@@ -674,6 +706,11 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         const float4 e4 = *reinterpret_cast<const float4*>(&tp.ETA[4 * G]);
         const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
         const float ne[4] = {-e4.x * d4.x, -e4.y * d4.y, -e4.z * d4.z, -e4.w * d4.w};
+        if constexpr (!R::kTokInSlices) {
+          const float4 m4 = *reinterpret_cast<const float4*>(&sm.Mg[(c - 1) & 1][l16][4 * G]);
+          const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
+          make_tok(Mreg, mv);
+        }
         U = tok_mul(Mreg, dv, U);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -694,30 +731,40 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
           if (c + 1 < ntiles) P = rows_times_wt(krows(tn), Wt, l16, G);
           U = rows_times_wt(qrows(tc), Wt, l16, G);
         }
-        // -eta_s (k_s . q_t) for s <= t (outputs of tile c) and -(k_t(c+1) . k_s(c))
-        const float4 e4 = *reinterpret_cast<const float4*>(&tc.ETA[4 * G]);
-        const float eta[4] = {e4.x, e4.y, e4.z, e4.w};
-        const f32x4 kq = gram(krows(tc), qrows(tc), lane, l16, G);
-        float m[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) m[r] = (4 * G + r <= l16) ? -eta[r] * kq[r] : 0.0f;
-        make_tok(Mreg, m);
-        if (c + 1 < ntiles) {
-          const f32x4 x = gram(krows(tc), krows(tn), lane, l16, G);
-          const float nx[4] = {-x[0], -x[1], -x[2], -x[3]};
-          make_tok(Xreg, nx);
+        if constexpr (R::kTokInSlices) {
+          float m[4];
+          tok_m(tc, m);
+          make_tok(Mreg, m);
+          if (c + 1 < ntiles) {
+            float x[4];
+            tok_x(tc, tn, x);
+            make_tok(Xreg, x);
+          }
         }
       }
-    } else if (stage_parity >= 0) {
-      // tile c+2 into LDS (loaded two tiles ago), then the loads of tile c+4
-      if ((c & 1) == stage_parity) {
+    } else {
+      if (stage_parity >= 0 && (c & 1) == stage_parity) {
+        // tile c+2 into LDS (loaded two tiles ago), then the loads of tile c+4
         const int64_t u = c + 2;
         if (u < ntiles) store_tile<BF16>(st, sm.ring[u % RING], u * BT, T, lane);
         if (u + 2 < ntiles) load_tile<BF16>(st, src, etap, bhT, (u + 2) * BT, T, lane);
       }
-      if (wave == kOutWave) {
-        if (c >= 2) write_tile_out(sm.Ob[(c - 2) & 1], out, bhT, (c - 2) * BT, T, lane);
-      } else if (!DUAL && c + 1 < ntiles) {
+      if (wave == R::kStageEven && c >= 2)
+        write_tile_out(sm.Ob[(c - 2) & 1], out, bhT, (c - 2) * BT, T, lane);
+      if constexpr (!R::kTokInSlices) {
+        if (wave == R::kStageEven && live) {
+          float m[4];
+          tok_m(sm.ring[c % RING], m);
+          *reinterpret_cast<float4*>(&sm.Mg[c & 1][l16][4 * G]) =
+              make_float4(m[0], m[1], m[2], m[3]);
+        }
+        if (wave == R::kStageOdd && c + 1 < ntiles) {
+          float x[4];
+          tok_x(sm.ring[c % RING], sm.ring[(c + 1) % RING], x);
+          *reinterpret_cast<float4*>(&sm.Xg[l16][4 * G]) = make_float4(x[0], x[1], x[2], x[3]);
+        }
+      }
+      if (!DUAL && wave == R::kCoefWave && c + 1 < ntiles) {
         // eta_s (k_s . k_t) of tile c+1 for its serial pass
         const auto& tn = sm.ring[(c + 1) % RING];
         const float4 f4 = *reinterpret_cast<const float4*>(&tn.ETA[4 * G]);
@@ -737,13 +784,18 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       const float4 d4 = *reinterpret_cast<const float4*>(&sm.Dt[c & 1][irow][4 * G]);
       const float4 e4 = *reinterpret_cast<const float4*>(&tc.ETA[4 * G]);
       const float ev[4] = {e4.x * d4.x, e4.y * d4.y, e4.z * d4.z, e4.w * d4.w};
+      if constexpr (!R::kTokInSlices) {
+        const float4 x4 = *reinterpret_cast<const float4*>(&sm.Xg[l16][4 * G]);
+        const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
+        make_tok(Xreg, xv);
+      }
       const f32x4 Z = tok_mul(Xreg, ev, P);
       *reinterpret_cast<float4*>(&sm.Zt[irow][4 * G]) = make_float4(Z[0], Z[1], Z[2], Z[3]);
     }
   }
   __syncthreads();
   // outputs of the last tile (staged in the final period)
-  if (wave == kOutWave && ntiles > 0)
+  if (wave == R::kStageEven && ntiles > 0)
     write_tile_out(sm.Ob[(ntiles - 1) & 1], out, bhT, (ntiles - 1) * BT, T, lane);
   if (slice >= 0 && W_final != nullptr) {
     float* w = W_final + bh * D * D + irow * D + 4 * G;
