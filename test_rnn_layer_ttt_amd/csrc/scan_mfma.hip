@@ -26,15 +26,18 @@
 // products run as fp32 MFMA (16x16x4).
 //
 // Wave roles (8 waves; wave w runs on SIMD w % 4; see Roles below):
-//   wave 0      serial LayerNorm pass, alone on its SIMD (wave 4 only joins
-//               the barriers)
+//   wave 0      serial LayerNorm pass, alone on its SIMD but for wave 4,
+//               which only writes outputs back
 //   waves 1,2,5,6  one 16-row slice of W each, as W^T tiles in the 16x16
 //               accumulator layout (lane l holds W[16s + l%16][16jt + 4(l/16) + r]);
 //               they apply the updates, form K W^T, Q W^T, the outputs and
 //               the one-tile-ahead correction between serial passes
 //   waves 3,7   input staging of even / odd tiles (global loads two tiles
-//               ahead, LDS layouts); wave 3 also writes outputs back, wave 7
-//               forms the coefficients eta (K K^T) of the serial pass
+//               ahead, LDS layouts); wave 7 also forms the coefficients
+//               eta (K K^T) of the serial pass
+//   dual form:  the LayerNorm of a tile's independent tokens splits over
+//               waves 0 and 7, wave 4 stages the odd tiles and wave 7 writes
+//               the outputs back
 // The token Gram matrices K Q^T and K_{c+1} K_c^T are formed by the slices
 // (bf16 inputs) or by the staging waves (fp32 inputs).
 // Per tile c there are two barriers: S_c (z_c and the coefficients are in
@@ -56,17 +59,26 @@ constexpr int KPAD = 68;    // padded fp32 row (floats) of K/Q/output tiles in L
 constexpr int ZPAD = 20;    // padded row (floats) of the per-feature z / delta tiles
 constexpr int kSerialWave = 0;
 
-// Wave roles.  Wave w runs on SIMD w % 4.  The serial wave keeps SIMD 0 to
-// itself (wave 4 only joins the barriers): a wave issuing MFMAs on the same
-// SIMD stretches its dependency chain by half, whatever the wave priorities.
+// Wave roles.  Wave w runs on SIMD w % 4.  The serial wave shares SIMD 0 only
+// with wave 4, which writes outputs back and issues no MFMAs: a wave issuing
+// MFMAs on the same SIMD stretches its dependency chain by half, whatever the
+// wave priorities.
 // The W slices pair up on SIMDs 1 and 2, the staging waves on SIMD 3.  With
 // bf16 inputs the slices form their token Gram matrices themselves; with fp32
 // inputs, where a 16x16x4 MFMA costs four times the bf16 rate per flop and the
 // slices' SIMDs are the busiest, the staging waves form them.
-template <bool BF16>
+// In the dual form the LayerNorm of a tile splits over waves 0 and 7 (one on
+// SIMD 0, one on SIMD 3) and the odd tiles are staged by wave 4 instead.
+//
+// Output write-back runs on a wave that issues no loads: the staging waves
+// wait for their loads of two tiles back with vmcnt, which also counts their
+// own stores still in flight.
+template <bool BF16, bool DUAL>
 struct Roles {
-  static constexpr int kStageEven = 3;          // stages even tiles, writes outputs back
-  static constexpr int kStageOdd = 7;           // stages odd tiles
+  static constexpr int kStageEven = 3;          // stages even tiles
+  static constexpr int kStageOdd = DUAL ? 4 : 7;  // stages odd tiles
+  static constexpr int kOutWave = DUAL ? 7 : 4;   // writes outputs back
+  static constexpr int kLnHalf = 7;             // dual form: LayerNorm of tokens 8..15
   static constexpr int kCoefWave = 7;           // eta (k.k) of the serial pass
   static constexpr bool kTokInSlices = BF16;    // else: kStageEven forms M, kStageOdd X
   // W row slice owned by a wave, or -1
@@ -133,8 +145,8 @@ __device__ __forceinline__ f32x4 mfma_k16x3(const i16x4& ah, const i16x4& al, co
 struct TileBf16 {
   uint16_t KA[2][64][8];
   uint16_t QA[2][64][8];
-  uint16_t KT[4][64][4];
-  uint16_t Vt[D][24];      // v[t][i] at Vt[i][t] (rows padded to 48 bytes)
+  uint16_t KT[4][64][4];   // -K^T in the A layout of the 16x16x16 MFMA
+  float VB[D][ZPAD];       // beta_i - v_t[i] (v_t[i] without LayerNorm) at VB[i][t]
   float SG[BT][D];         // sigmoid(gate_logit)
   float ETA[BT];           // sigmoid(eta_logit)/d, 0 for tokens past the end
 };
@@ -142,7 +154,7 @@ struct TileBf16 {
 struct TileF32 {
   float K[BT][KPAD];
   float Q[BT][KPAD];
-  float Vt[D][ZPAD];
+  float VB[D][ZPAD];
   float SG[BT][D];
   float ETA[BT];
 };
@@ -168,7 +180,8 @@ struct Smem {
   float Zt[D][ZPAD];       // z of the next serial pass, by feature
   float Dt[2][D][ZPAD];    // delta of a tile, by feature
   float Cc[2][BT][BT];     // eta_s (k_s . k_t) of a tile
-  float Mg[2][BT][ZPAD];   // -eta_s (k_s . q_t), s <= t, of a tile, at [t][s]
+  float Cd[2][BT];         // its superdiagonal eta_s (k_s . k_{s+1})
+  float Mg[2][BT][ZPAD];   // -(k_s . q_t), s <= t, of a tile, at [t][s]
   float Xg[BT][ZPAD];      // -(k_s . k'_t) of a tile and the next one, at [t][s]
   float Ob[2][BT][KPAD];   // gated outputs awaiting write-back
 };
@@ -213,11 +226,14 @@ __device__ __forceinline__ void load_tile(Stage<BF16>& st, const void* const src
   }
 }
 
-template <bool BF16>
+// sb[e]: beta of feature j0 + e (the same features for every vector of a
+// lane), or 0 without LayerNorm, where VB holds v itself.
+template <bool BF16, int LN>
 __device__ __forceinline__ void store_tile(const Stage<BF16>& st,
                                            typename Smem<BF16>::Tile& tl, int64_t t0, int64_t T,
-                                           int lane) {
+                                           int lane, const float (&sb)[Stage<BF16>::kVE]) {
   using S = Stage<BF16>;
+  auto vb = [&](float v, int e) { return LN == kLnNone ? v : sb[e] - v; };
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
 #pragma unroll
@@ -241,9 +257,9 @@ __device__ __forceinline__ void store_tile(const Stage<BF16>& st,
             const uint16_t bits = (e & 1) ? static_cast<uint16_t>(w[e / 2] >> 16)
                                           : static_cast<uint16_t>(w[e / 2] & 0xFFFFu);
             if (a == 1)
-              tl.KT[j / 16][(j % 16) + 16 * (t / 4)][t % 4] = bits;
+              tl.KT[j / 16][(j % 16) + 16 * (t / 4)][t % 4] = bits ^ 0x8000u;   // -k
             else
-              tl.Vt[j][t] = bits;
+              tl.VB[j][t] = vb(__uint_as_float(static_cast<uint32_t>(bits) << 16), e);
           }
         }
         if (a == 3) {
@@ -262,10 +278,10 @@ __device__ __forceinline__ void store_tile(const Stage<BF16>& st,
         if (a == 0) *reinterpret_cast<float4*>(&tl.Q[t][j0]) = f;
         if (a == 1) *reinterpret_cast<float4*>(&tl.K[t][j0]) = f;
         if (a == 2) {
-          tl.Vt[j0][t] = f.x;
-          tl.Vt[j0 + 1][t] = f.y;
-          tl.Vt[j0 + 2][t] = f.z;
-          tl.Vt[j0 + 3][t] = f.w;
+          tl.VB[j0][t] = vb(f.x, 0);
+          tl.VB[j0 + 1][t] = vb(f.y, 1);
+          tl.VB[j0 + 2][t] = vb(f.z, 2);
+          tl.VB[j0 + 3][t] = vb(f.w, 3);
         }
         if (a == 3)
           *reinterpret_cast<float4*>(&tl.SG[t][j0]) =
@@ -290,6 +306,9 @@ __device__ __forceinline__ void store_tile(const Stage<BF16>& st,
 // 31); the other lanes hold partial sums that are never read.
 template <int K>
 __device__ __forceinline__ float red_step(float x) {
+  // not contracted into the producer of x (z*z + dpp(z*z) would become a
+  // dpp move plus an fma, one more step on the chain)
+#pragma clang fp contract(off)
   constexpr int kCtrl[6] = {0x111, 0x112, 0x114, 0x118, 0x142, 0x143};
   return x + __int_as_float(
                  __builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl[K], 0xF, 0xF, true));
@@ -331,11 +350,12 @@ __device__ __forceinline__ float delta_from_sums(float z, float gz, float s1, fl
   }
 }
 
-// delta for one token from z (lane = feature i); bv = beta_i - v_t[i].
+// delta for one token from z (lane = feature i); bv = beta_i - v_t[i] (v_t[i]
+// without LayerNorm).
 template <int LN>
-__device__ __forceinline__ float token_delta(float z, float v, float bv, float gam, float eps) {
+__device__ __forceinline__ float token_delta(float z, float bv, float gam, float eps) {
   if constexpr (LN == kLnNone) {
-    return z - v;
+    return z - bv;
   } else {
     float s1 = z, s2 = z * z;
     wave_total2(s1, s2);
@@ -351,7 +371,7 @@ __device__ __forceinline__ float token_delta(float z, float v, float bv, float g
 // tokens ahead of their use.
 template <int LN>
 __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[BT],
-                                            const float (&vv)[BT], const float (*cc)[BT],
+                                            const float (*cc)[BT],
                                             const float (&cd)[BT], float gam, float eps,
                                             float (&dr)[BT]) {
   float crow[4][BT];   // rows s-1 (in use), s, s+1, s+2 (in flight); ring by row % 4
@@ -368,7 +388,11 @@ __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[B
   float dprev = 0.0f;
 #pragma unroll
   for (int s = 0; s < BT; ++s) {
+    // the row loads stay at the top of their token: left to itself the
+    // scheduler sinks them next to their use and the wait lands on the chain
+    __builtin_amdgcn_sched_barrier(0);
     if (s + 2 < BT - 2) load_row(s + 2);
+    __builtin_amdgcn_sched_barrier(0);
     const float z = zr[s];
     // deferred rows s+1 .. BT-1 of the previous token, split into six slices
     constexpr int kSlots = 6;
@@ -383,7 +407,7 @@ __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[B
     if constexpr (LN == kLnNone) {
 #pragma unroll
       for (int k = 0; k < kSlots; ++k) fill(k);
-      dl = z - vv[s];
+      dl = z - bv[s];
     } else {
       float a = z, b = z * z;
       const float gz = gam * z;
@@ -401,43 +425,23 @@ __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[B
   }
 }
 
-template <bool BF16>
-__device__ __forceinline__ void read_v16(const typename Smem<BF16>::Tile& tl, int lane, float* v) {
-  if constexpr (BF16) {
-    const uint4 a = *reinterpret_cast<const uint4*>(&tl.Vt[lane][0]);
-    const uint4 b = *reinterpret_cast<const uint4*>(&tl.Vt[lane][8]);
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  } else {
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 x = *reinterpret_cast<const float4*>(&tl.Vt[lane][4 * q4]);
-      v[4 * q4] = x.x; v[4 * q4 + 1] = x.y; v[4 * q4 + 2] = x.z; v[4 * q4 + 3] = x.w;
-    }
-  }
-}
-
-// What the serial wave holds for a tile before its pass: v, beta - v and the
-// coefficients eta_s (k_s . k_t), loaded while the W slices form z.
+// What the serial wave holds for a tile before its pass: beta - v (v without
+// LayerNorm) and the superdiagonal coefficients eta_s (k_s . k_{s+1}), read
+// while the W slices form z.
 struct SerialIn {
-  float cd[BT];   // eta_s (k_s . k_{s+1})
-  float vv[BT];
+  float cd[BT];
   float bv[BT];
 };
 
-template <bool BF16, bool DUAL>
+template <bool BF16>
 __device__ __forceinline__ void serial_prefetch(SerialIn& in, const typename Smem<BF16>::Tile& tl,
-                                                const float (*cc)[BT], int lane, float bet) {
-  read_v16<BF16>(tl, lane, in.vv);
+                                                const float* cd, int lane) {
 #pragma unroll
-  for (int t = 0; t < BT; ++t) in.bv[t] = bet - in.vv[t];
-  if constexpr (!DUAL) {
-#pragma unroll
-    for (int s = 0; s < BT - 1; ++s) in.cd[s] = cc[s][s + 1];
+  for (int q4 = 0; q4 < BT / 4; ++q4) {
+    const float4 x = *reinterpret_cast<const float4*>(&tl.VB[lane][4 * q4]);
+    in.bv[4 * q4] = x.x; in.bv[4 * q4 + 1] = x.y; in.bv[4 * q4 + 2] = x.z; in.bv[4 * q4 + 3] = x.w;
+    const float4 y = *reinterpret_cast<const float4*>(&cd[4 * q4]);
+    in.cd[4 * q4] = y.x; in.cd[4 * q4 + 1] = y.y; in.cd[4 * q4 + 2] = y.z; in.cd[4 * q4 + 3] = y.w;
   }
 }
 
@@ -452,15 +456,44 @@ __device__ __forceinline__ void ln_pass(Smem<BF16>& sm, const SerialIn& in, cons
     const float4 x = *reinterpret_cast<const float4*>(&sm.Zt[lane][4 * q4]);
     zr[4 * q4] = x.x; zr[4 * q4 + 1] = x.y; zr[4 * q4 + 2] = x.z; zr[4 * q4 + 3] = x.w;
   }
-  if constexpr (DUAL) {
-#pragma unroll
-    for (int t = 0; t < BT; ++t) dr[t] = token_delta<LN>(zr[t], in.vv[t], in.bv[t], gam, eps);
-  } else {
-    serial_tile<LN>(zr, in.bv, in.vv, cc, in.cd, gam, eps, dr);
-  }
+  static_assert(!DUAL, "the dual form runs dual_ln_pass");
+  serial_tile<LN>(zr, in.bv, cc, in.cd, gam, eps, dr);
 #pragma unroll
   for (int q4 = 0; q4 < BT / 4; ++q4)
     *reinterpret_cast<float4*>(&dt[lane][4 * q4]) =
+        make_float4(dr[4 * q4], dr[4 * q4 + 1], dr[4 * q4 + 2], dr[4 * q4 + 3]);
+}
+
+// The dual form's tokens are independent: two waves on different SIMDs each
+// take half a tile (tokens t0 .. t0+7).
+struct DualIn {
+  float bv[BT / 2];
+};
+
+template <bool BF16>
+__device__ __forceinline__ void dual_prefetch(DualIn& in, const typename Smem<BF16>::Tile& tl,
+                                              int lane, int t0) {
+#pragma unroll
+  for (int q4 = 0; q4 < 2; ++q4) {
+    const float4 x = *reinterpret_cast<const float4*>(&tl.VB[lane][t0 + 4 * q4]);
+    in.bv[4 * q4] = x.x; in.bv[4 * q4 + 1] = x.y; in.bv[4 * q4 + 2] = x.z; in.bv[4 * q4 + 3] = x.w;
+  }
+}
+
+template <bool BF16, int LN>
+__device__ __forceinline__ void dual_ln_pass(Smem<BF16>& sm, const DualIn& in, float (*dt)[ZPAD],
+                                             int lane, int t0, float gam, float eps) {
+  float zr[BT / 2], dr[BT / 2];
+#pragma unroll
+  for (int q4 = 0; q4 < 2; ++q4) {
+    const float4 x = *reinterpret_cast<const float4*>(&sm.Zt[lane][t0 + 4 * q4]);
+    zr[4 * q4] = x.x; zr[4 * q4 + 1] = x.y; zr[4 * q4 + 2] = x.z; zr[4 * q4 + 3] = x.w;
+  }
+#pragma unroll
+  for (int t = 0; t < BT / 2; ++t) dr[t] = token_delta<LN>(zr[t], in.bv[t], gam, eps);
+#pragma unroll
+  for (int q4 = 0; q4 < 2; ++q4)
+    *reinterpret_cast<float4*>(&dt[lane][t0 + 4 * q4]) =
         make_float4(dr[4 * q4], dr[4 * q4 + 1], dr[4 * q4 + 2], dr[4 * q4 + 3]);
 }
 
@@ -513,16 +546,15 @@ __device__ __forceinline__ f32x4 rows_times_wt(const float (*A)[KPAD], const f32
 }
 
 // acc += A (16 x 16 token matrix) times B[s][slice feature], B = b[e] for s = 4G + e
-__device__ __forceinline__ f32x4 tok_mul(const TokReg<true>& a, const float (&b)[4], f32x4 acc) {
-  i16x4 bh, bl;
-  split4(b, bh, bl);
-  return mfma_k16x3(a.hi, a.lo, bh, bl, acc);
+__device__ __forceinline__ f32x4 tok_mul(const TokReg<true>& a, const TokReg<true>& b, f32x4 acc) {
+  return mfma_k16x3(a.hi, a.lo, b.hi, b.lo, acc);
 }
-__device__ __forceinline__ f32x4 tok_mul(const TokReg<false>& a, const float (&b)[4], f32x4 acc) {
-  acc = mfma_k4(a.v[0], b[0], acc);
-  acc = mfma_k4(a.v[1], b[1], acc);
-  acc = mfma_k4(a.v[2], b[2], acc);
-  return mfma_k4(a.v[3], b[3], acc);
+__device__ __forceinline__ f32x4 tok_mul(const TokReg<false>& a, const TokReg<false>& b,
+                                         f32x4 acc) {
+  acc = mfma_k4(a.v[0], b.v[0], acc);
+  acc = mfma_k4(a.v[1], b.v[1], acc);
+  acc = mfma_k4(a.v[2], b.v[2], acc);
+  return mfma_k4(a.v[3], b.v[3], acc);
 }
 __device__ __forceinline__ void make_tok(TokReg<true>& a, const float (&x)[4]) {
   split4(x, a.hi, a.lo);
@@ -532,24 +564,23 @@ __device__ __forceinline__ void make_tok(TokReg<false>& a, const float (&x)[4]) 
   for (int e = 0; e < 4; ++e) a.v[e] = x[e];
 }
 
-// Wt[jt] -= sum_s K[s][16jt + i] e[s][slice feature], with ne[e] = -e[s = 4G + e]
-__device__ __forceinline__ void update_w(f32x4 (&Wt)[4], const TileBf16& tl, const float (&ne)[4],
+// Wt[jt] -= sum_s K[s][16jt + i] E[s][slice feature], E = eta * delta as the
+// B operand of tok_mul (the bf16 tile holds K^T negated)
+__device__ __forceinline__ void update_w(f32x4 (&Wt)[4], const TileBf16& tl, const TokReg<true>& e,
                                          int lane, int, int) {
-  i16x4 eh, el;
-  split4(ne, eh, el);
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt) {
-    const i16x4 kt = *reinterpret_cast<const i16x4*>(&tl.KT[jt][lane][0]);
-    Wt[jt] = mfma_k16(kt, eh, Wt[jt]);
-    Wt[jt] = mfma_k16(kt, el, Wt[jt]);
+    const i16x4 nkt = *reinterpret_cast<const i16x4*>(&tl.KT[jt][lane][0]);
+    Wt[jt] = mfma_k16(nkt, e.hi, Wt[jt]);
+    Wt[jt] = mfma_k16(nkt, e.lo, Wt[jt]);
   }
 }
-__device__ __forceinline__ void update_w(f32x4 (&Wt)[4], const TileF32& tl, const float (&ne)[4],
-                                         int, int l16, int G) {
+__device__ __forceinline__ void update_w(f32x4 (&Wt)[4], const TileF32& tl,
+                                         const TokReg<false>& e, int, int l16, int G) {
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) Wt[jt] = mfma_k4(tl.K[4 * G + q][16 * jt + l16], ne[q], Wt[jt]);
+    for (int q = 0; q < 4; ++q) Wt[jt] = mfma_k4(tl.K[4 * G + q][16 * jt + l16], -e.v[q], Wt[jt]);
   }
 }
 
@@ -620,7 +651,7 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   const int64_t bhT = bh * T;
   const void* const src[4] = {qp, kp, vp, gatep};
   const int64_t ntiles = (T + BT - 1) / BT;
-  using R = Roles<BF16>;
+  using R = Roles<BF16, DUAL>;
   const int slice = R::slice_of(wave);
   const int irow = 16 * slice + l16;   // W row (feature i) held by this lane, slice waves
 
@@ -628,9 +659,14 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   f32x4 Wt[4] = {};
   f32x4 P = {0, 0, 0, 0}, U = {0, 0, 0, 0};
   TokReg<BF16> Mreg{}, Xreg{};   // slices forming their own token matrices: M and X below
-  // serial wave: LayerNorm affine of feature `lane`, and its inputs of the next tile
-  float gam = 1.0f, bet = 0.0f;
+  // LayerNorm waves: the serial wave (the dual form: it and the odd staging
+  // wave, half a tile each); LayerNorm affine of feature `lane`, and the
+  // inputs of the next tile
+  const int ln_half = wave == kSerialWave ? 0 : (DUAL && wave == R::kLnHalf) ? 1 : -1;
+  const int ln_t0 = (BT / 2) * ln_half;
+  float gam = 1.0f;
   SerialIn sin;
+  DualIn din;
   Stage<BF16> st;   // staging waves: the tile in flight
 
   if (slice >= 0) {
@@ -641,19 +677,22 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       Wt[jt] = f32x4{x.x, x.y, x.z, x.w};
     }
   }
-  if (wave == kSerialWave) __builtin_amdgcn_s_setprio(3);
-  if (wave == kSerialWave && LN != kLnNone) {
-    gam = gamma[h * D + lane];
-    bet = beta[h * D + lane];
-  }
+  if (ln_half >= 0 && LN != kLnNone) gam = gamma[h * D + lane];
   __builtin_amdgcn_s_waitcnt(0);
   // staging prologue: tiles 0 and 1 into LDS, tiles 2 and 3 in flight
   const int stage_parity = wave == R::kStageEven ? 0 : wave == R::kStageOdd ? 1 : -1;
+  // staging lanes: beta of the features their vectors of v cover
+  float sb[Stage<BF16>::kVE] = {};
+  if (stage_parity >= 0 && LN != kLnNone) {
+    constexpr int kVE = Stage<BF16>::kVE;
+#pragma unroll
+    for (int e = 0; e < kVE; ++e) sb[e] = beta[h * D + (lane * kVE) % D + e];
+  }
   if (stage_parity >= 0) {
     const int u = stage_parity;
     if (u < ntiles) {
       load_tile<BF16>(st, src, etap, bhT, u * BT, T, lane);
-      store_tile<BF16>(st, sm.ring[u], u * BT, T, lane);
+      store_tile<BF16, LN>(st, sm.ring[u], u * BT, T, lane, sb);
     }
     if (u + 2 < ntiles) load_tile<BF16>(st, src, etap, bhT, (u + 2) * BT, T, lane);
   }
@@ -671,17 +710,31 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
     const auto& t0 = sm.ring[0];
     const f32x4 g = gram(krows(t0), krows(t0), lane, l16, G);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.Cc[0][4 * G + r][l16] = t0.ETA[4 * G + r] * g[r];
+    for (int r = 0; r < 4; ++r) {
+      const float cv = t0.ETA[4 * G + r] * g[r];
+      sm.Cc[0][4 * G + r][l16] = cv;
+      if (4 * G + r + 1 == l16) sm.Cd[0][4 * G + r] = cv;
+    }
   }
 
-  // M = -eta_s (k_s . q_t), s <= t: the in-tile part of the outputs of tile c
+  // M = -(k_s . q_t), s <= t: with E = eta * delta, the in-tile part of the
+  // outputs of tile c is M E
   auto tok_m = [&](const typename Smem<BF16>::Tile& tc, float (&m)[4]) {
-    const float4 e4 = *reinterpret_cast<const float4*>(&tc.ETA[4 * G]);
-    const float eta[4] = {e4.x, e4.y, e4.z, e4.w};
     const f32x4 kq = gram(krows(tc), qrows(tc), lane, l16, G);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) m[r] = (4 * G + r <= l16) ? -eta[r] * kq[r] : 0.0f;
+    for (int r = 0; r < 4; ++r) m[r] = (4 * G + r <= l16) ? -kq[r] : 0.0f;
   };
+  // E = eta_s delta_s[i] of a tile for the slice's features, as a B operand
+  auto tok_e = [&](int64_t c) {
+    const auto& tc = sm.ring[c % RING];
+    const float4 d4 = *reinterpret_cast<const float4*>(&sm.Dt[c & 1][irow][4 * G]);
+    const float4 e4 = *reinterpret_cast<const float4*>(&tc.ETA[4 * G]);
+    const float ev[4] = {e4.x * d4.x, e4.y * d4.y, e4.z * d4.z, e4.w * d4.w};
+    TokReg<BF16> e;
+    make_tok(e, ev);
+    return e;
+  };
+  TokReg<BF16> Ereg{};   // E of the last tile, formed after its serial pass
   // X = -(k_t(c+1) . k_s(c)): carries delta of tile c into z of tile c+1
   auto tok_x = [&](const typename Smem<BF16>::Tile& tc, const typename Smem<BF16>::Tile& tn,
                    float (&x)[4]) {
@@ -693,31 +746,34 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   for (int64_t c = 0; c <= ntiles; ++c) {
     __syncthreads();   // S_c
     const bool live = c < ntiles;
+    if (DUAL && ln_half >= 0 && live) {
+      if (c == 0) dual_prefetch<BF16>(din, sm.ring[0], lane, ln_t0);
+      dual_ln_pass<BF16, LN>(sm, din, sm.Dt[c & 1], lane, ln_t0, gam, eps);
+    }
     if (wave == kSerialWave) {
-      if (live) {
-        if (c == 0) serial_prefetch<BF16, DUAL>(sin, sm.ring[0], sm.Cc[0], lane, bet);
-        ln_pass<BF16, LN, DUAL>(sm, sin, sm.Cc[c & 1], sm.Dt[c & 1], lane, gam, eps);
+      if constexpr (!DUAL) {
+        if (live) {
+          if (c == 0) serial_prefetch<BF16>(sin, sm.ring[0], sm.Cd[0], lane);
+          ln_pass<BF16, LN, DUAL>(sm, sin, sm.Cc[c & 1], sm.Dt[c & 1], lane, gam, eps);
+        }
       }
     } else if (slice >= 0) {
       if (c >= 1) {
         // outputs of tile c-1 and the update W_c = W_{c-1} - E_{c-1}^T K_{c-1}
         const auto& tp = sm.ring[(c - 1) % RING];
-        const float4 d4 = *reinterpret_cast<const float4*>(&sm.Dt[(c - 1) & 1][irow][4 * G]);
-        const float4 e4 = *reinterpret_cast<const float4*>(&tp.ETA[4 * G]);
-        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-        const float ne[4] = {-e4.x * d4.x, -e4.y * d4.y, -e4.z * d4.z, -e4.w * d4.w};
+        if (c == ntiles) Ereg = tok_e(c - 1);   // no z of a next tile was formed
         if constexpr (!R::kTokInSlices) {
           const float4 m4 = *reinterpret_cast<const float4*>(&sm.Mg[(c - 1) & 1][l16][4 * G]);
           const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
           make_tok(Mreg, mv);
         }
-        U = tok_mul(Mreg, dv, U);
+        U = tok_mul(Mreg, Ereg, U);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 4 * G + r;
           sm.Ob[(c - 1) & 1][t][irow] = U[r] * tp.SG[t][irow];
         }
-        update_w(Wt, tp, ne, lane, l16, G);
+        update_w(Wt, tp, Ereg, lane, l16, G);
       }
       if (live) {
         // K_{c+1} W_c^T (for z of the next tile) and Q_c W_c^T
@@ -746,10 +802,10 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       if (stage_parity >= 0 && (c & 1) == stage_parity) {
         // tile c+2 into LDS (loaded two tiles ago), then the loads of tile c+4
         const int64_t u = c + 2;
-        if (u < ntiles) store_tile<BF16>(st, sm.ring[u % RING], u * BT, T, lane);
+        if (u < ntiles) store_tile<BF16, LN>(st, sm.ring[u % RING], u * BT, T, lane, sb);
         if (u + 2 < ntiles) load_tile<BF16>(st, src, etap, bhT, (u + 2) * BT, T, lane);
       }
-      if (wave == R::kStageEven && c >= 2)
+      if (wave == R::kOutWave && c >= 2)
         write_tile_out(sm.Ob[(c - 2) & 1], out, bhT, (c - 2) * BT, T, lane);
       if constexpr (!R::kTokInSlices) {
         if (wave == R::kStageEven && live) {
@@ -771,31 +827,36 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         const float fe[4] = {f4.x, f4.y, f4.z, f4.w};
         const f32x4 g = gram(krows(tn), krows(tn), lane, l16, G);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sm.Cc[(c + 1) & 1][4 * G + r][l16] = fe[r] * g[r];
+        for (int r = 0; r < 4; ++r) {
+          const float cv = fe[r] * g[r];
+          sm.Cc[(c + 1) & 1][4 * G + r][l16] = cv;
+          if (4 * G + r + 1 == l16) sm.Cd[(c + 1) & 1][4 * G + r] = cv;
+        }
       }
     }
     __syncthreads();   // G_c
-    // the serial wave loads its inputs of tile c+1 while the slices form z
-    if (wave == kSerialWave && c + 1 < ntiles)
-      serial_prefetch<BF16, DUAL>(sin, sm.ring[(c + 1) % RING], sm.Cc[(c + 1) & 1], lane, bet);
+    // the LayerNorm waves load their inputs of tile c+1 while the slices form z
+    if (ln_half >= 0 && c + 1 < ntiles) {
+      if constexpr (DUAL)
+        dual_prefetch<BF16>(din, sm.ring[(c + 1) % RING], lane, ln_t0);
+      else
+        serial_prefetch<BF16>(sin, sm.ring[(c + 1) % RING], sm.Cd[(c + 1) & 1], lane);
+    }
     // z of tile c+1: K_{c+1} W_c^T - (K_{c+1} K_c^T) E_c
     if (slice >= 0 && c + 1 < ntiles) {
-      const auto& tc = sm.ring[c % RING];
-      const float4 d4 = *reinterpret_cast<const float4*>(&sm.Dt[c & 1][irow][4 * G]);
-      const float4 e4 = *reinterpret_cast<const float4*>(&tc.ETA[4 * G]);
-      const float ev[4] = {e4.x * d4.x, e4.y * d4.y, e4.z * d4.z, e4.w * d4.w};
+      Ereg = tok_e(c);
       if constexpr (!R::kTokInSlices) {
         const float4 x4 = *reinterpret_cast<const float4*>(&sm.Xg[l16][4 * G]);
         const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
         make_tok(Xreg, xv);
       }
-      const f32x4 Z = tok_mul(Xreg, ev, P);
+      const f32x4 Z = tok_mul(Xreg, Ereg, P);
       *reinterpret_cast<float4*>(&sm.Zt[irow][4 * G]) = make_float4(Z[0], Z[1], Z[2], Z[3]);
     }
   }
   __syncthreads();
   // outputs of the last tile (staged in the final period)
-  if (wave == R::kStageEven && ntiles > 0)
+  if (wave == R::kOutWave && ntiles > 0)
     write_tile_out(sm.Ob[(ntiles - 1) & 1], out, bhT, (ntiles - 1) * BT, T, lane);
   if (slice >= 0 && W_final != nullptr) {
     float* w = W_final + bh * D * D + irow * D + 4 * G;
