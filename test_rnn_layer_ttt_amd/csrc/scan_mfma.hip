@@ -142,7 +142,7 @@ __device__ __forceinline__ f32x4 mfma_k16x3(const i16x4& ah, const i16x4& al, co
 // row t), K^T in the A layout of the 16x16x16 MFMA (lane l = j%16 + 16G of
 // column tile jt holds rows s = 4G + e of column j), v transposed to
 // feature-major rows for the serial pass.
-struct TileBf16 {
+struct alignas(16) TileBf16 {
   uint16_t KA[2][64][8];
   uint16_t QA[2][64][8];
   uint16_t KT[4][64][4];   // -K^T in the A layout of the 16x16x16 MFMA
@@ -151,7 +151,7 @@ struct TileBf16 {
   float ETA[BT];           // sigmoid(eta_logit)/d, 0 for tokens past the end
 };
 // fp32 inputs: K and Q rows (padded against bank conflicts), v transposed.
-struct TileF32 {
+struct alignas(16) TileF32 {
   float K[BT][KPAD];
   float Q[BT][KPAD];
   float VB[D][ZPAD];
@@ -173,8 +173,10 @@ struct TokReg<false> {
   float v[4];
 };
 
+// Every member is a multiple of 16 bytes, so the 16-byte alignment of the
+// whole lets every float4 access be one 128-bit LDS operation.
 template <bool BF16>
-struct Smem {
+struct alignas(16) Smem {
   using Tile = typename std::conditional<BF16, TileBf16, TileF32>::type;
   Tile ring[RING];
   float Zt[D][ZPAD];       // z of the next serial pass, by feature
