@@ -801,11 +801,17 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         }
       }
     } else {
-      if (stage_parity >= 0 && (c & 1) == stage_parity) {
-        // tile c+2 into LDS (loaded two tiles ago), then the loads of tile c+4
-        const int64_t u = c + 2;
-        if (u < ntiles) store_tile<BF16, LN>(st, sm.ring[u % RING], u * BT, T, lane, sb);
-        if (u + 2 < ntiles) load_tile<BF16>(st, src, etap, bhT, (u + 2) * BT, T, lane);
+      if (stage_parity >= 0) {
+        // a staging wave alternates: tile c+2 into LDS, then (next period)
+        // the loads of tile c+3 into the freed registers.  A period that both
+        // stores a tile and issues loads holds the next barrier up well past
+        // the last wave's arrival.
+        if ((c & 1) == stage_parity) {
+          if (c + 2 < ntiles)
+            store_tile<BF16, LN>(st, sm.ring[(c + 2) % RING], (c + 2) * BT, T, lane, sb);
+        } else if (c + 3 < ntiles) {
+          load_tile<BF16>(st, src, etap, bhT, (c + 3) * BT, T, lane);
+        }
       }
       if (wave == R::kOutWave && c >= 2)
         write_tile_out(sm.Ob[(c - 2) & 1], out, bhT, (c - 2) * BT, T, lane);
