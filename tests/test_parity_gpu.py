@@ -251,6 +251,34 @@ def test_binding_rejects_bad_arguments():
 
 
 # ---------------------------------------------------------------------------
+# more scans than compute units (several workgroups per CU), and a long sequence
+# (thousands of tiles, a ragged last one)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("bf16,ln,dual", [(True, "st", False), (False, "exact", False),
+                                          (True, "st", True), (False, "none", True)])
+def test_more_scans_than_compute_units(bf16, ln, dual):
+    say(f"case 600 scans bf16={bf16} ln={ln} dual={dual}")
+    x = make_case(B=20, H=30, T=37, d=64, seed=11, ln=ln, dual=dual, chunk=16, in_bf16=bf16,
+                  random_affine=True)
+    out, W = gpu_run(x)
+    pairs = [(0, 0), (19, 29), (7, 13), (13, 2)]
+    ro, rW = ref_run(x.subset(pairs))
+    for n, (b, h) in enumerate(pairs):
+        assert_close(out[b, h], ro[0, n], TOL[bf16], f"out[{b},{h}]")
+        assert_close(W[b, h], rW[0, n], TOL[bf16], f"W_final[{b},{h}]")
+
+
+@pytest.mark.parametrize("bf16,ln", [(True, "st"), (False, "exact")])
+def test_long_sequence(bf16, ln):
+    say(f"case T=20011 bf16={bf16} ln={ln}")
+    x = make_case(B=1, H=2, T=20011, d=64, seed=12, ln=ln, in_bf16=bf16, random_affine=True)
+    out, W = gpu_run(x)
+    ro, rW = ref_run(x)
+    assert_close(out, ro, TOL[bf16], "out")
+    assert_close(W, rW, TOL[bf16], "W_final")
+
+
+# ---------------------------------------------------------------------------
 # the named full-size workloads, launched as the benchmark launches them
 # ---------------------------------------------------------------------------
 SAMPLES = {"tiny_d16_fp32": None}
