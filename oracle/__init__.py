@@ -4,9 +4,10 @@ Only the tests, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  It shares no code with the GPU path.
 """
 from .ttt_oracle import (EPS, LN_EXACT, LN_NONE, LN_ST, inner_grad_vector,
-                         layer_norm, ln_jacobian, rel_max_err, sigmoid,
-                         ttt_linear_forward)
+                         inner_grad_vector_vjp, layer_norm, ln_jacobian,
+                         ln_jacobian_derivative, rel_max_err, sigmoid,
+                         ttt_linear_backward, ttt_linear_forward)
 
 __all__ = ["EPS", "LN_EXACT", "LN_NONE", "LN_ST", "inner_grad_vector",
-           "layer_norm", "ln_jacobian", "rel_max_err", "sigmoid",
-           "ttt_linear_forward"]
+           "inner_grad_vector_vjp", "layer_norm", "ln_jacobian", "ln_jacobian_derivative",
+           "rel_max_err", "sigmoid", "ttt_linear_backward", "ttt_linear_forward"]

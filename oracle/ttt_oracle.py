@@ -34,8 +34,9 @@ biased (1/d) one, gamma/beta are per head, eta is one scalar per
 weight, the loss is 0.5*||.||^2, the dual-mode causal sum is inclusive, and
 a final short chunk uses the same rule.
 
-Parity status of each public function is stated in its docstring; every
-function here is pinned by ``tests/test_oracle.py``.
+Parity status of each public function is stated in its docstring; the
+forward functions are pinned by ``tests/test_oracle.py`` and the backward
+(``ttt_linear_backward`` and its helpers) by ``tests/test_oracle_backward.py``.
 """
 from __future__ import annotations
 
@@ -165,6 +166,168 @@ def ttt_linear_forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None
         W = W - eta * (delta[..., :, None] * kt[..., None, :])
         out[:, :, t, :] = np.matmul(W, q[:, :, t, :][..., None])[..., 0] * gate_all[:, :, t, :]
     return out, W
+
+
+def ln_jacobian_derivative(xhat: np.ndarray, s: np.ndarray, gamma: np.ndarray) -> np.ndarray:
+    """Derivative of the LayerNorm Jacobian: D[..., i, m, p] = d J[i, m] / d z_p.
+
+    With N[i, m] = (delta_im - 1/d - xhat_i xhat_m / d) / s (so J = gamma_i N),
+    d s / d z_p = xhat_p / d and d xhat_i / d z_p = N[i, p]:
+
+      D[i, m, p] = gamma_i * ( -(xhat_p / (d s)) N[i, m]
+                               - (N[i, p] xhat_m + xhat_i N[m, p]) / (d s) )
+
+    The backward of the exact inner gradient needs it (delta = J^T e with both
+    J and e functions of z).  Pinned by finite differences of ``ln_jacobian``.
+    """
+    d = xhat.shape[-1]
+    eye = np.eye(d, dtype=xhat.dtype)
+    N = (eye - 1.0 / d - xhat[..., :, None] * xhat[..., None, :] / d) / s[..., None]
+    ds = s[..., None, None] * d
+    term1 = -(xhat[..., None, None, :] / ds) * N[..., :, :, None]
+    term2 = -(N[..., :, None, :] * xhat[..., None, :, None]
+              + xhat[..., :, None, None] * N[..., None, :, :]) / ds
+    return gamma[..., :, None, None] * (term1 + term2)
+
+
+def inner_grad_vector_vjp(dd, z, v, gamma, beta, ln: str, eps: float = EPS):
+    """Vector-Jacobian product of ``inner_grad_vector``.
+
+    Given dd = dL/d delta, returns ``(dz, dv, dgamma, dbeta)`` (dgamma and dbeta
+    per (batch, head) row, before summing over batch and tokens; None without
+    LayerNorm), from the explicit Jacobians of each step:
+
+    * ``none``:  delta = z - v
+    * ``st``:    delta = gamma xhat + beta - v, d delta / d z = J
+    * ``exact``: delta = J^T e with e = gamma xhat + beta - v;
+                 d delta_m / d z_p = sum_i D[i, m, p] e_i + (J^T J)[m, p],
+                 d delta_m / d gamma_i = N[i, m] (e_i + gamma_i xhat_i),
+                 d delta / d beta = J^T, d delta / d v = -J^T.
+    """
+    if ln == LN_NONE:
+        return dd, -dd, None, None
+    pred, xhat, s = layer_norm(z, gamma, beta, eps)
+    jac = ln_jacobian(xhat, s, gamma)                      # [.., i, m]
+    mv = lambda M, x: np.matmul(M, x[..., None])[..., 0]
+    if ln == LN_ST:
+        dz = mv(np.swapaxes(jac, -1, -2), dd)              # J^T dd
+        return dz, -dd, dd * xhat, dd
+    if ln == LN_EXACT:
+        e = pred - v
+        dJ = ln_jacobian_derivative(xhat, s, gamma)         # [.., i, m, p]
+        d_delta_dz = (np.einsum("...imp,...i->...mp", dJ, e)
+                      + np.matmul(np.swapaxes(jac, -1, -2), jac))
+        dz = mv(np.swapaxes(d_delta_dz, -1, -2), dd)       # sum_m dd_m d delta_m / d z_p
+        de = mv(jac, dd)                                    # J dd
+        d = z.shape[-1]
+        N = (np.eye(d, dtype=z.dtype) - 1.0 / d
+             - xhat[..., :, None] * xhat[..., None, :] / d) / s[..., None]
+        dgamma = mv(N, dd) * (e + gamma * xhat)
+        return dz, -de, dgamma, de
+    raise ValueError(f"unknown ln mode {ln!r}")
+
+
+def ttt_linear_backward(q, k, v, eta_logit, gate_logit, W0, gamma, beta, dout, dW_final=None,
+                        *, ln: str = LN_ST, dual: bool = False, chunk: int = 16,
+                        eps: float = EPS, dtype=np.float64):
+    """Gradients of the scan: reverse-mode through ``ttt_linear_forward``.
+
+    For a loss L with dL/d out = ``dout`` [B,H,T,d] and dL/d W_final =
+    ``dW_final`` [B,H,d,d] (None: zero), returns a dict with dq, dk, dv,
+    dgate_logit [B,H,T,d], deta_logit [B,H,T], dW0 [B,H,d,d] and dgamma,
+    dbeta [H,d] (summed over batch and tokens; None without LayerNorm).
+
+    The forward is replayed once, keeping every W_t; the tokens are then
+    walked backwards undoing the forward's steps in reverse order:
+
+      o_t = y_t * sigmoid(g_t), y_t = W_t q_t
+        -> d y_t = dout_t * sigmoid(g_t),
+           d g_t = dout_t * y_t * sigmoid'(g_t),
+           dW_t += d y_t q_t^T,   dq_t = W_t^T d y_t
+      W_t = W_{t-1} - eta_t delta_t k_t^T
+        -> d eta_t = -delta_t^T dW_t k_t,  d delta_t = -eta_t dW_t k_t,
+           dk_t += -eta_t dW_t^T delta_t,  dW_{t-1} += dW_t,
+           d eta_logit_t = d eta_t sigmoid'(eta_logit_t) / d
+      delta_t = inner_grad_vector(z_t, v_t)  -> inner_grad_vector_vjp
+      z_t = P k_t (P = W_{t-1}, or the chunk-start W_c in the dual form)
+        -> dP += dz_t k_t^T,  dk_t += P^T dz_t
+
+    In the dual form dP accumulates over the chunk and joins dW at the
+    chunk's first token.  Parity: pinned by central finite differences of
+    the forward and by autograd (``tests/test_oracle_backward.py``).
+    """
+    f = lambda a: None if a is None else np.asarray(a, dtype=dtype)
+    q, k, v, eta_logit, gate_logit, W0, dout = map(f, (q, k, v, eta_logit, gate_logit, W0, dout))
+    B, H, T, d = q.shape
+    has_ln = ln != LN_NONE
+    if has_ln:
+        gam = f(gamma)[None, :, :]
+        bet = f(beta)[None, :, :]
+    else:
+        gam = bet = None
+    mv = lambda M, x: np.matmul(M, x[..., None])[..., 0]
+    outer = lambda a, b: a[..., :, None] * b[..., None, :]
+
+    # replay the forward, keeping W after every token
+    eta_all = sigmoid(eta_logit) / dtype(d)
+    gate_all = sigmoid(gate_logit)
+    Ws = np.empty((T + 1, B, H, d, d), dtype=dtype)
+    Ws[0] = W0
+    start = np.zeros(T, dtype=np.int64)          # index into Ws of the gradient point
+    for t in range(T):
+        start[t] = (t - t % chunk) if dual else t
+        P = Ws[start[t]]
+        z = mv(P, k[:, :, t, :])
+        delta = inner_grad_vector(z, v[:, :, t, :], gam, bet, ln, eps)
+        Ws[t + 1] = Ws[t] - eta_all[:, :, t][..., None, None] * outer(delta, k[:, :, t, :])
+
+    g = {n: np.zeros_like(q) for n in ("dq", "dk", "dv", "dgate_logit")}
+    g["deta_logit"] = np.zeros_like(eta_logit)
+    dgamma = np.zeros((B, H, d), dtype=dtype) if has_ln else None
+    dbeta = np.zeros((B, H, d), dtype=dtype) if has_ln else None
+    dW = np.zeros((B, H, d, d), dtype=dtype) if dW_final is None else f(dW_final).copy()
+    dP = np.zeros_like(dW)                        # dual form: gradient at the chunk-start W
+    for t in range(T - 1, -1, -1):
+        kt, qt, vt = k[:, :, t, :], q[:, :, t, :], v[:, :, t, :]
+        eta = eta_all[:, :, t]
+        sg = gate_all[:, :, t, :]
+        Wt = Ws[t + 1]
+        P = Ws[start[t]]
+        z = mv(P, kt)
+        delta = inner_grad_vector(z, vt, gam, bet, ln, eps)
+        # output
+        y = mv(Wt, qt)
+        dy = dout[:, :, t, :] * sg
+        g["dgate_logit"][:, :, t, :] = dout[:, :, t, :] * y * sg * (1.0 - sg)
+        dW = dW + outer(dy, qt)
+        g["dq"][:, :, t, :] = mv(np.swapaxes(Wt, -1, -2), dy)
+        # update
+        dWk = mv(dW, kt)
+        deta = -(delta * dWk).sum(axis=-1)
+        ddelta = -eta[..., None] * dWk
+        dk = -eta[..., None] * mv(np.swapaxes(dW, -1, -2), delta)
+        sl = sigmoid(eta_logit[:, :, t])
+        g["deta_logit"][:, :, t] = deta * sl * (1.0 - sl) / dtype(d)
+        # inner gradient
+        dz, dv, dga, dbe = inner_grad_vector_vjp(ddelta, z, vt, gam, bet, ln, eps)
+        g["dv"][:, :, t, :] = dv
+        if has_ln:
+            dgamma += dga
+            dbeta += dbe
+        # z = P k
+        dk = dk + mv(np.swapaxes(P, -1, -2), dz)
+        g["dk"][:, :, t, :] = dk
+        if dual:
+            dP = dP + outer(dz, kt)
+            if start[t] == t:                      # first token of its chunk
+                dW = dW + dP
+                dP = np.zeros_like(dP)
+        else:
+            dW = dW + outer(dz, kt)
+    g["dW0"] = dW
+    g["dgamma"] = dgamma.sum(axis=0) if has_ln else None
+    g["dbeta"] = dbeta.sum(axis=0) if has_ln else None
+    return g
 
 
 def rel_max_err(got, ref) -> float:
