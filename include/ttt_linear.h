@@ -70,6 +70,7 @@ extern "C" {
 #define TTT_ERR_UNSUPPORTED  4  /* d not in {16, 32, 64, 128}, or a misaligned pointer */
 #define TTT_ERR_ALIAS        5  /* out overlaps an argument, or W_final partially overlaps */
 #define TTT_ERR_HIP          6  /* the HIP runtime reported an error at launch */
+#define TTT_ERR_WORKSPACE    7  /* record_bytes is below what ttt_linear_record_bytes gives */
 
 /*
  * Run the scan over all B*H (batch, head) pairs.
@@ -108,6 +109,77 @@ int32_t ttt_linear_validate(const void* q, const void* k, const void* v,
  * "none" if the combination is not supported.  For profiling and reporting.
  */
 const char* ttt_linear_kernel(int64_t d, uint32_t mode, int64_t chunk);
+
+/*
+ * ---- Training: a recording forward and the backward pass ----
+ *
+ * The backward gives the gradients of a scalar loss L with respect to every
+ * input of the scan, from dL/dout and dL/dW_final: reverse-mode
+ * differentiation through each step of the recurrence above (the models of
+ * "Edifice.Recurrent.TTT" and "PonderTTT" train the layer end to end).  It
+ * walks the sequence backwards in tiles of 16 tokens, from a record that the
+ * forward leaves behind: delta_t for every token and W at the start of every
+ * tile (16 KiB per tile and (b,h) at d = 64).
+ *
+ * Supported: d = 64, the per-token modes (straight-through, TTT_LN_EXACT,
+ * TTT_NO_LN), fp32 or bf16 inputs.  TTT_DUAL gives TTT_ERR_UNSUPPORTED.
+ *
+ * The record is one caller-owned device buffer of ttt_linear_record_bytes()
+ * bytes, 16-byte aligned; its contents are private to the library.  The
+ * backward also uses a small tail of it as scratch (the per-(b,h) LayerNorm
+ * parameter gradients before their sum over the batch), so two backward calls
+ * on one record must not run at the same time; the recorded part is only read
+ * and may be used by any number of backward calls in sequence.
+ */
+
+/*
+ * The record size for these sizes and mode, in *bytes:
+ * 4 * B*H * (T*d + ceil(T/16)*d*d + 2*d).  Checks the shapes and mode as
+ * ttt_linear_forward_record does.  Makes no HIP call.
+ */
+int32_t ttt_linear_record_bytes(int64_t B, int64_t H, int64_t T, int64_t d, uint32_t mode,
+                                int64_t* bytes);
+
+/*
+ * ttt_linear_forward (same arguments, same results: out and W_final are
+ * identical to its) that also fills `record` for ttt_linear_backward.
+ * `record` is written, so it must not overlap any other argument.  T == 0
+ * writes no record and copies W0 to W_final as the forward does.
+ */
+int32_t ttt_linear_forward_record(const void* q, const void* k, const void* v,
+                                  const void* eta_logit, const void* gate_logit,
+                                  const float* W0, const float* gamma, const float* beta,
+                                  float* out, float* W_final, void* record, int64_t record_bytes,
+                                  int64_t B, int64_t H, int64_t T, int64_t d,
+                                  uint32_t mode, int64_t chunk, void* stream);
+
+/*
+ * Gradients of L from dout = dL/dout [B,H,T,d] fp32 and dW_final = dL/dW_final
+ * [B,H,d,d] fp32 (NULL: zero).  q, k, v, eta_logit, gate_logit, gamma, beta and
+ * mode must be those of the recording forward, and `record` what it wrote.
+ * Outputs, all fp32 whatever the input type:
+ *     dq, dk, dv, dgate_logit   [B,H,T,d]
+ *     deta_logit                [B,H,T]
+ *     dW0                       [B,H,d,d]   may equal dW_final exactly (in place)
+ *     dgamma, dbeta             [H,d]       summed over the batch and the tokens;
+ *                                           unused, may be NULL, with TTT_NO_LN
+ * Every output is overwritten, not accumulated into.  Outputs must not overlap
+ * one another, the inputs or the record (except dW0 == dW_final).  Pointer
+ * alignment as in ttt_linear_forward; deta_logit, dgamma and dbeta need 4
+ * bytes.  With T == 0 only dW0 (= dW_final, or zero), dgamma and dbeta (zero)
+ * are written, and the per-token pointers may be NULL.  Runs asynchronously on
+ * `stream`; dgamma and dbeta are reduced over the batch by a second kernel on
+ * the same stream, in a fixed order, so repeated calls give identical bits.
+ */
+int32_t ttt_linear_backward(const void* q, const void* k, const void* v,
+                            const void* eta_logit, const void* gate_logit,
+                            const float* gamma, const float* beta,
+                            void* record, int64_t record_bytes,
+                            const float* dout, const float* dW_final,
+                            float* dq, float* dk, float* dv, float* deta_logit,
+                            float* dgate_logit, float* dW0, float* dgamma, float* dbeta,
+                            int64_t B, int64_t H, int64_t T, int64_t d,
+                            uint32_t mode, int64_t chunk, void* stream);
 
 /* A static, human-readable description of a status code (never NULL). */
 const char* ttt_status_string(int32_t status);

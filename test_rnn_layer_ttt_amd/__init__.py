@@ -7,13 +7,17 @@ synthetic input generator.  Importing the package loads nothing; the library
 is opened on first use and its absence is an error.
 """
 from .binding import (TTT_DUAL, TTT_ERR_ALIAS, TTT_ERR_HIP, TTT_ERR_MODE, TTT_ERR_NULL,
-                      TTT_ERR_SHAPE, TTT_ERR_UNSUPPORTED, TTT_IN_BF16, TTT_LN_EXACT, TTT_NO_LN,
-                      TTT_OK, TTTArgumentError, TTTError, check, forward, load_library,
-                      mode_bits, ttt_linear_forward, ttt_linear_kernel, ttt_linear_validate, ttt_status_string,
-                      ttt_version)
+                      TTT_ERR_SHAPE, TTT_ERR_UNSUPPORTED, TTT_ERR_WORKSPACE, TTT_IN_BF16,
+                      TTT_LN_EXACT, TTT_NO_LN, TTT_OK, TTTArgumentError, TTTError, backward,
+                      check, forward, forward_record, load_library, mode_bits, ttt_linear,
+                      ttt_linear_backward, ttt_linear_forward, ttt_linear_forward_record,
+                      ttt_linear_kernel, ttt_linear_record_bytes, ttt_linear_validate,
+                      ttt_status_string, ttt_version)
 
 __all__ = ["TTT_DUAL", "TTT_ERR_ALIAS", "TTT_ERR_HIP", "TTT_ERR_MODE", "TTT_ERR_NULL",
-           "TTT_ERR_SHAPE", "TTT_ERR_UNSUPPORTED", "TTT_IN_BF16", "TTT_LN_EXACT", "TTT_NO_LN",
-           "TTT_OK", "TTTArgumentError", "TTTError", "check", "forward", "load_library",
-           "mode_bits", "ttt_linear_forward", "ttt_linear_kernel", "ttt_linear_validate", "ttt_status_string",
-           "ttt_version"]
+           "TTT_ERR_SHAPE", "TTT_ERR_UNSUPPORTED", "TTT_ERR_WORKSPACE", "TTT_IN_BF16",
+           "TTT_LN_EXACT", "TTT_NO_LN", "TTT_OK", "TTTArgumentError", "TTTError", "backward",
+           "check", "forward", "forward_record", "load_library", "mode_bits", "ttt_linear",
+           "ttt_linear_backward", "ttt_linear_forward", "ttt_linear_forward_record",
+           "ttt_linear_kernel", "ttt_linear_record_bytes", "ttt_linear_validate",
+           "ttt_status_string", "ttt_version"]

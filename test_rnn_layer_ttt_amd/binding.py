@@ -28,9 +28,11 @@ TTT_ERR_MODE = 3
 TTT_ERR_UNSUPPORTED = 4
 TTT_ERR_ALIAS = 5
 TTT_ERR_HIP = 6
+TTT_ERR_WORKSPACE = 7
 
 #: every symbol the header declares
-EXPORTED = ("ttt_linear_forward", "ttt_linear_kernel", "ttt_linear_validate",
+EXPORTED = ("ttt_linear_backward", "ttt_linear_forward", "ttt_linear_forward_record",
+            "ttt_linear_kernel", "ttt_linear_record_bytes", "ttt_linear_validate",
             "ttt_status_string", "ttt_version")
 
 _lib = None
@@ -38,7 +40,7 @@ _lib = None
 
 class TTTError(RuntimeError):
     def __init__(self, status: int, message: str):
-        super().__init__(f"ttt_linear_forward failed with status {status}: {message}")
+        super().__init__(f"ttt_linear call failed with status {status}: {message}")
         self.status = status
 
 
@@ -68,6 +70,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ttt_status_string.argtypes = [ctypes.c_int32]
     lib.ttt_version.restype = ctypes.c_char_p
     lib.ttt_version.argtypes = []
+    lib.ttt_linear_record_bytes.restype = ctypes.c_int32
+    lib.ttt_linear_record_bytes.argtypes = [ctypes.c_int64] * 4 + [
+        ctypes.c_uint32, ctypes.POINTER(ctypes.c_int64)]
+    lib.ttt_linear_forward_record.restype = ctypes.c_int32
+    lib.ttt_linear_forward_record.argtypes = [ctypes.c_void_p] * 11 + [ctypes.c_int64] * 5 + [
+        ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p]
+    lib.ttt_linear_backward.restype = ctypes.c_int32
+    lib.ttt_linear_backward.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.c_int64] +
+                                        [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 4 +
+                                        [ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p])
     _lib = lib
     return lib
 
@@ -109,6 +121,38 @@ def ttt_linear_validate(q, k, v, eta_logit, gate_logit, W0, gamma, beta, out, W_
         p(W_final), int(B), int(H), int(T), int(d), ctypes.c_uint32(int(mode)), int(chunk)))
 
 
+def ttt_linear_record_bytes(B, H, T, d, mode):
+    """Returns ``(status, bytes)`` of the record a recording forward needs."""
+    n = ctypes.c_int64(0)
+    st = int(load_library().ttt_linear_record_bytes(int(B), int(H), int(T), int(d),
+                                                    ctypes.c_uint32(int(mode)), ctypes.byref(n)))
+    return st, int(n.value)
+
+
+def ttt_linear_forward_record(q, k, v, eta_logit, gate_logit, W0, gamma, beta, out, W_final,
+                              record, record_bytes, B, H, T, d, mode, chunk, stream) -> int:
+    """The recording forward with raw pointers; returns the status code."""
+    lib = load_library()
+    p = lambda x: None if x is None else ctypes.c_void_p(int(x))
+    return int(lib.ttt_linear_forward_record(
+        p(q), p(k), p(v), p(eta_logit), p(gate_logit), p(W0), p(gamma), p(beta), p(out),
+        p(W_final), p(record), int(record_bytes), int(B), int(H), int(T), int(d),
+        ctypes.c_uint32(int(mode)), int(chunk), p(stream)))
+
+
+def ttt_linear_backward(q, k, v, eta_logit, gate_logit, gamma, beta, record, record_bytes,
+                        dout, dW_final, dq, dk, dv, deta_logit, dgate_logit, dW0, dgamma, dbeta,
+                        B, H, T, d, mode, chunk, stream) -> int:
+    """The backward with raw pointers; returns the status code."""
+    lib = load_library()
+    p = lambda x: None if x is None else ctypes.c_void_p(int(x))
+    return int(lib.ttt_linear_backward(
+        p(q), p(k), p(v), p(eta_logit), p(gate_logit), p(gamma), p(beta), p(record),
+        int(record_bytes), p(dout), p(dW_final), p(dq), p(dk), p(dv), p(deta_logit),
+        p(dgate_logit), p(dW0), p(dgamma), p(dbeta), int(B), int(H), int(T), int(d),
+        ctypes.c_uint32(int(mode)), int(chunk), p(stream)))
+
+
 def check(status: int) -> None:
     """Raise for a non-OK status: ValueError-derived for argument errors."""
     if status == TTT_OK:
@@ -146,6 +190,31 @@ def forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln: st
     """
     import torch
 
+    B, H, T, d = _check_inputs(q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln)
+    if out is None:
+        out = torch.empty((B, H, T, d), dtype=torch.float32, device=q.device)
+    if W_final is None:
+        W_final = torch.empty_like(W0)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    status = ttt_linear_forward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(eta_logit), _ptr(gate_logit), W0.data_ptr(),
+        _ptr(gamma) if ln != "none" else None, _ptr(beta) if ln != "none" else None,
+        _ptr(out), W_final.data_ptr(), B, H, T, d,
+        mode_bits(ln, dual, q.dtype == torch.bfloat16), chunk if dual else 1,
+        stream.cuda_stream)
+    check(status)
+    return out, W_final
+
+
+def _ptr(t):
+    return None if t is None or t.numel() == 0 else t.data_ptr()
+
+
+def _check_inputs(q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln):
+    """Shape, dtype and placement checks shared by the tensor-level calls."""
+    import torch
+
     B, H, T, d = q.shape
     in_dtype = q.dtype
     if in_dtype not in (torch.float32, torch.bfloat16):
@@ -157,28 +226,117 @@ def forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln: st
             raise TypeError(f"{name} has dtype {t.dtype}, expected {in_dtype}")
         if tuple(t.shape) != shape:
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
-    if tuple(W0.shape) != (B, H, d, d) or W0.dtype != torch.float32:
+    if W0 is not None and (tuple(W0.shape) != (B, H, d, d) or W0.dtype != torch.float32):
         raise ValueError("W0 must be float32 [B,H,d,d]")
     if ln != "none":
         for name, t in (("gamma", gamma), ("beta", beta)):
             if t is None or tuple(t.shape) != (H, d) or t.dtype != torch.float32:
                 raise ValueError(f"{name} must be float32 [H,d]")
-    tensors = [q, k, v, eta_logit, gate_logit, W0] + ([gamma, beta] if ln != "none" else [])
+    tensors = [q, k, v, eta_logit, gate_logit] + ([] if W0 is None else [W0]) + (
+        [gamma, beta] if ln != "none" else [])
     for t in tensors:
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("every tensor must be a contiguous device tensor")
+    return B, H, T, d
+
+
+def forward_record(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *,
+                   ln: str = "st", out=None, W_final=None, record=None, stream=None):
+    """:func:`forward` (per-token modes, d = 64) that also returns the record the
+    backward reads: ``(out, W_final, record)``, the record a uint8 device tensor."""
+    import torch
+
+    B, H, T, d = _check_inputs(q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln)
+    mode = mode_bits(ln, False, q.dtype == torch.bfloat16)
+    st, nbytes = ttt_linear_record_bytes(B, H, T, d, mode)
+    check(st)
     if out is None:
         out = torch.empty((B, H, T, d), dtype=torch.float32, device=q.device)
     if W_final is None:
         W_final = torch.empty_like(W0)
+    if record is None:
+        record = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    ptr = lambda t: None if t is None or t.numel() == 0 else t.data_ptr()
-    status = ttt_linear_forward(
-        ptr(q), ptr(k), ptr(v), ptr(eta_logit), ptr(gate_logit), W0.data_ptr(),
-        ptr(gamma) if ln != "none" else None, ptr(beta) if ln != "none" else None,
-        ptr(out), W_final.data_ptr(), B, H, T, d,
-        mode_bits(ln, dual, in_dtype == torch.bfloat16), chunk if dual else 1,
-        stream.cuda_stream)
-    check(status)
-    return out, W_final
+    check(ttt_linear_forward_record(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(eta_logit), _ptr(gate_logit), W0.data_ptr(),
+        _ptr(gamma) if ln != "none" else None, _ptr(beta) if ln != "none" else None,
+        _ptr(out), W_final.data_ptr(), record.data_ptr(), record.numel() * record.element_size(),
+        B, H, T, d, mode, 1, stream.cuda_stream))
+    return out, W_final, record
+
+
+def backward(q, k, v, eta_logit, gate_logit, gamma, beta, record, dout, dW_final=None, *,
+             ln: str = "st", stream=None):
+    """Gradients from a record of :func:`forward_record` and dL/dout (float32
+    [B,H,T,d]), dL/dW_final (float32 [B,H,d,d] or None).  Returns a dict with
+    dq, dk, dv, dgate_logit, deta_logit, dW0, dgamma, dbeta (float32; the last
+    two None with ``ln="none"``)."""
+    import torch
+
+    B, H, T, d = _check_inputs(q, k, v, eta_logit, gate_logit, None, gamma, beta, ln)
+    if dout.dtype != torch.float32 or tuple(dout.shape) != (B, H, T, d) or not dout.is_contiguous():
+        raise ValueError("dout must be a contiguous float32 [B,H,T,d] tensor")
+    if dW_final is not None and (dW_final.dtype != torch.float32 or not dW_final.is_contiguous()
+                                 or tuple(dW_final.shape) != (B, H, d, d)):
+        raise ValueError("dW_final must be a contiguous float32 [B,H,d,d] tensor")
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(dq=torch.empty((B, H, T, d), **f32), dk=torch.empty((B, H, T, d), **f32),
+             dv=torch.empty((B, H, T, d), **f32), dgate_logit=torch.empty((B, H, T, d), **f32),
+             deta_logit=torch.empty((B, H, T), **f32), dW0=torch.empty((B, H, d, d), **f32),
+             dgamma=None if ln == "none" else torch.empty((H, d), **f32),
+             dbeta=None if ln == "none" else torch.empty((H, d), **f32))
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    check(ttt_linear_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(eta_logit), _ptr(gate_logit),
+        _ptr(gamma) if ln != "none" else None, _ptr(beta) if ln != "none" else None,
+        record.data_ptr(), record.numel() * record.element_size(), _ptr(dout),
+        None if dW_final is None else dW_final.data_ptr(), _ptr(g["dq"]), _ptr(g["dk"]),
+        _ptr(g["dv"]), _ptr(g["deta_logit"]), _ptr(g["dgate_logit"]), g["dW0"].data_ptr(),
+        _ptr(g["dgamma"]), _ptr(g["dbeta"]), B, H, T, d,
+        mode_bits(ln, False, q.dtype == torch.bfloat16), 1, stream.cuda_stream))
+    return g
+
+
+_autograd_fn = None
+
+
+def ttt_linear(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln: str = "st"):
+    """Differentiable scan for torch autograd: ``(out, W_final)``.
+
+    The forward is :func:`forward_record`; the backward is :func:`backward`
+    on the saved record.  Per-token modes at d = 64.  Gradients come back in
+    float32 (autograd casts them to a bf16 input's dtype).
+    """
+    global _autograd_fn
+    if _autograd_fn is None:
+        import torch
+
+        class TTTLinearFunction(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln):
+                out, W_final, record = forward_record(q, k, v, eta_logit, gate_logit, W0, gamma,
+                                                      beta, ln=ln)
+                ctx.ln = ln
+                ctx.save_for_backward(q, k, v, eta_logit, gate_logit, gamma, beta, record)
+                return out, W_final
+
+            @staticmethod
+            def backward(ctx, dout, dW_final):
+                q, k, v, eta_logit, gate_logit, gamma, beta, record = ctx.saved_tensors
+                B, H, T, d = q.shape
+                if dout is None:
+                    dout = torch.zeros((B, H, T, d), dtype=torch.float32, device=q.device)
+                g = backward(q, k, v, eta_logit, gate_logit, gamma, beta, record,
+                             dout.contiguous().float(),
+                             None if dW_final is None else dW_final.contiguous().float(),
+                             ln=ctx.ln)
+                return (g["dq"], g["dk"], g["dv"], g["deta_logit"], g["dgate_logit"], g["dW0"],
+                        g["dgamma"], g["dbeta"], None)
+
+        _autograd_fn = TTTLinearFunction
+    if ln == "none":
+        gamma = beta = None
+    return _autograd_fn.apply(q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln)

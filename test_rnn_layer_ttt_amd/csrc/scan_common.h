@@ -26,7 +26,44 @@ struct ScanArgs {
   int64_t chunk;       // tokens per chunk when dual
   bool in_bf16;
   float eps;
+  // record of a forward pass for the backward (per-token modes, d = 64):
+  // delta_t [B,H,T,d] and W at the start of every tile [B,H,ntiles,d,d];
+  // nullptr: not recorded
+  float* rec_delta = nullptr;
+  float* rec_W = nullptr;
 };
+
+// One validated backward call (d = 64, per-token modes).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* eta_logit;
+  const void* gate_logit;
+  const float* gamma;  // nullptr with kLnNone
+  const float* beta;
+  const float* dout;
+  const float* dW_final;     // nullptr: zero
+  const float* rec_delta;    // [B,H,T,d]
+  const float* rec_W;        // [B,H,ntiles,d,d]
+  float* gb_part;            // [B,H,2,d] scratch: per-scan dgamma, dbeta
+  float* dq;
+  float* dk;
+  float* dv;
+  float* deta_logit;
+  float* dgate_logit;
+  float* dW0;
+  float* dgamma;       // nullptr with kLnNone
+  float* dbeta;
+  int64_t B, H, T, d;
+  int ln;
+  bool dual;
+  bool in_bf16;
+  float eps;
+};
+
+// Tokens per tile of the recorded W (and of the backward's reverse walk).
+constexpr int64_t kRecTile = 16;
 
 // Per-token VALU scan: one workgroup per (b,h), W in VGPRs, 4 lanes per row.
 // Handles every mode (including dual) for d in {16, 32, 64, 128}.
@@ -37,5 +74,9 @@ hipError_t launch_scan_valu(const ScanArgs& a, hipStream_t stream);
 // for an argument combination it does not cover.
 hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t stream);
 bool scan_mfma_supports(const ScanArgs& a);
+
+// Backward of the per-token scan for d = 64 from a record; hipErrorNotSupported
+// for anything else.
+hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace ttt

@@ -634,14 +634,16 @@ __device__ __forceinline__ void write_tile_out(const float (*ob)[KPAD], float* o
 }
 
 // ---------------------------------------------------------------------------
-template <bool BF16, int LN, bool DUAL>
+// REC: also record delta_t and W at the start of every tile (for the backward)
+template <bool BF16, int LN, bool DUAL, bool REC>
 __global__ void __launch_bounds__(NT)
 scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
                  const void* __restrict__ vp, const void* __restrict__ etap,
                  const void* __restrict__ gatep, const float* __restrict__ W0,
                  const float* __restrict__ gamma, const float* __restrict__ beta,
                  float* __restrict__ out, float* __restrict__ W_final, int H, int64_t T,
-                 float eps) {
+                 float eps, float* __restrict__ rec_delta, float* __restrict__ rec_W) {
+  static_assert(!(REC && DUAL), "the record is kept for the per-token modes");
   __shared__ Smem<BF16> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -777,6 +779,13 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         }
         update_w(Wt, tp, Ereg, lane, l16, G);
       }
+      if (REC && live) {
+        float* w = rec_W + ((bh * ntiles + c) * D + irow) * D + 4 * G;
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+          *reinterpret_cast<float4*>(w + 16 * jt) =
+              make_float4(Wt[jt][0], Wt[jt][1], Wt[jt][2], Wt[jt][3]);
+      }
       if (live) {
         // K_{c+1} W_c^T (for z of the next tile) and Q_c W_c^T
         const auto& tc = sm.ring[c % RING];
@@ -815,6 +824,12 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       }
       if (wave == R::kOutWave && c >= 2)
         write_tile_out(sm.Ob[(c - 2) & 1], out, bhT, (c - 2) * BT, T, lane);
+      if (REC && wave == R::kOutWave && c >= 1) {
+        const int64_t t0 = (c - 1) * BT;
+        const int rows = static_cast<int>(min<int64_t>(BT, T - t0));
+        float* dst = rec_delta + (bhT + t0) * D + lane;
+        for (int t = 0; t < rows; ++t) dst[t * D] = sm.Dt[(c - 1) & 1][lane][t];
+      }
       if constexpr (!R::kTokInSlices) {
         if (wave == R::kStageEven && live) {
           float m[4];
@@ -877,9 +892,19 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
 
 template <bool BF16, int LN, bool DUAL>
 hipError_t launch_one(const ScanArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((scan_mfma_kernel<BF16, LN, DUAL>), dim3(static_cast<unsigned>(a.B * a.H)),
+  if constexpr (!DUAL) {
+    if (a.rec_delta != nullptr) {
+      hipLaunchKernelGGL((scan_mfma_kernel<BF16, LN, false, true>),
+                         dim3(static_cast<unsigned>(a.B * a.H)), dim3(NT), 0, s, a.q, a.k, a.v,
+                         a.eta_logit, a.gate_logit, a.W0, a.gamma, a.beta, a.out, a.W_final,
+                         static_cast<int>(a.H), a.T, a.eps, a.rec_delta, a.rec_W);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((scan_mfma_kernel<BF16, LN, DUAL, false>), dim3(static_cast<unsigned>(a.B * a.H)),
                      dim3(NT), 0, s, a.q, a.k, a.v, a.eta_logit, a.gate_logit, a.W0, a.gamma,
-                     a.beta, a.out, a.W_final, static_cast<int>(a.H), a.T, a.eps);
+                     a.beta, a.out, a.W_final, static_cast<int>(a.H), a.T, a.eps,
+                     static_cast<float*>(nullptr), static_cast<float*>(nullptr));
   return hipGetLastError();
 }
 
@@ -902,7 +927,7 @@ hipError_t launch_ln(const ScanArgs& a, hipStream_t s) {
 }  // namespace
 
 bool scan_mfma_supports(const ScanArgs& a) {
-  return a.d == D && (!a.dual || a.chunk == BT);
+  return a.d == D && (!a.dual || a.chunk == BT) && (a.rec_delta == nullptr || !a.dual);
 }
 
 hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t s) {

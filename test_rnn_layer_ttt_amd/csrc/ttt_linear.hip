@@ -120,6 +120,176 @@ int32_t validate(const void* q, const void* k, const void* v, const void* eta_lo
   return TTT_OK;
 }
 
+// ---- the record of a forward pass for the backward ----
+// layout, fp32: delta [B,H,T,d] | W at every tile start [B,H,ntiles,d,d] |
+// scratch [B,H,2,d]
+struct RecordLayout {
+  int64_t delta_off, w_off, scratch_off, bytes;
+};
+
+// Checks the mode and shapes of a recording forward or a backward and fills
+// the layout.  Makes no HIP call.
+int32_t record_layout(int64_t B, int64_t H, int64_t T, int64_t d, uint32_t mode,
+                      RecordLayout* r) {
+  const uint32_t known = TTT_DUAL | TTT_LN_EXACT | TTT_IN_BF16 | TTT_NO_LN;
+  if (mode & ~known) return TTT_ERR_MODE;
+  if ((mode & TTT_LN_EXACT) && (mode & TTT_NO_LN)) return TTT_ERR_MODE;
+  if (B < 1 || H < 1 || d < 1 || T < 0) return TTT_ERR_SHAPE;
+  if ((mode & TTT_DUAL) || d != 64) return TTT_ERR_UNSUPPORTED;
+  const int64_t ntiles = (T + ttt::kRecTile - 1) / ttt::kRecTile;
+  int64_t BH, per_scan, a, b;
+  if (!mul_ok(B, H, &BH) || BH > INT32_MAX) return TTT_ERR_SHAPE;
+  if (!mul_ok(T, d, &a) || !mul_ok(ntiles, d * d, &b) || a > INT64_MAX / 2 - b)
+    return TTT_ERR_SHAPE;
+  per_scan = a + b + 2 * d;
+  int64_t elems;
+  if (!mul_ok(BH, per_scan, &elems) || elems > INT64_MAX / 4) return TTT_ERR_SHAPE;
+  r->delta_off = 0;
+  r->w_off = BH * a * 4;
+  r->scratch_off = r->w_off + BH * b * 4;
+  r->bytes = elems * 4;
+  return TTT_OK;
+}
+
+// the record's own checks, after the forward's
+int32_t validate_record(const void* record, int64_t record_bytes, int64_t B, int64_t H,
+                        int64_t T, int64_t d, uint32_t mode, RecordLayout* r) {
+  const int32_t st = record_layout(B, H, T, d, mode, r);
+  if (st != TTT_OK) return st;
+  if (record == nullptr) return TTT_ERR_NULL;
+  if (!aligned(record, 16)) return TTT_ERR_UNSUPPORTED;
+  if (record_bytes < r->bytes) return TTT_ERR_WORKSPACE;
+  return TTT_OK;
+}
+
+int32_t validate_forward_record(const void* q, const void* k, const void* v,
+                                const void* eta_logit, const void* gate_logit, const float* W0,
+                                const float* gamma, const float* beta, float* out,
+                                float* W_final, void* record, int64_t record_bytes, int64_t B,
+                                int64_t H, int64_t T, int64_t d, uint32_t mode, int64_t chunk,
+                                ttt::ScanArgs* a, RecordLayout* r) {
+  int32_t st = validate(q, k, v, eta_logit, gate_logit, W0, gamma, beta, out, W_final, B, H, T,
+                        d, mode, chunk, a);
+  if (st != TTT_OK) return st;
+  st = validate_record(record, record_bytes, B, H, T, d, mode, r);
+  if (st != TTT_OK) return st;
+  const int64_t in_size = (mode & TTT_IN_BF16) ? 2 : 4;
+  const int64_t seq = B * H * T * d, w = B * H * d * d;
+  const Range rec = span(record, r->bytes);
+  const Range others[] = {span(q, T > 0 ? seq * in_size : 0),
+                          span(k, T > 0 ? seq * in_size : 0),
+                          span(v, T > 0 ? seq * in_size : 0),
+                          span(gate_logit, T > 0 ? seq * in_size : 0),
+                          span(eta_logit, T > 0 ? B * H * T * in_size : 0),
+                          span(a->gamma, a->gamma ? H * d * 4 : 0),
+                          span(a->beta, a->beta ? H * d * 4 : 0),
+                          span(out, T > 0 ? seq * 4 : 0), span(W0, w * 4),
+                          span(W_final, W_final ? w * 4 : 0)};
+  for (const Range& o : others)
+    if (overlaps(rec, o)) return TTT_ERR_ALIAS;
+  char* base = static_cast<char*>(record);
+  a->rec_delta = reinterpret_cast<float*>(base + r->delta_off);
+  a->rec_W = reinterpret_cast<float*>(base + r->w_off);
+  return TTT_OK;
+}
+
+int32_t validate_backward(const void* q, const void* k, const void* v, const void* eta_logit,
+                          const void* gate_logit, const float* gamma, const float* beta,
+                          void* record, int64_t record_bytes, const float* dout,
+                          const float* dW_final, float* dq, float* dk, float* dv,
+                          float* deta_logit, float* dgate_logit, float* dW0, float* dgamma,
+                          float* dbeta, int64_t B, int64_t H, int64_t T, int64_t d,
+                          uint32_t mode, int64_t chunk, ttt::BwdArgs* a) {
+  // mode and shapes (the forward's rules, then the backward's coverage)
+  const uint32_t known = TTT_DUAL | TTT_LN_EXACT | TTT_IN_BF16 | TTT_NO_LN;
+  if (mode & ~known) return TTT_ERR_MODE;
+  if ((mode & TTT_LN_EXACT) && (mode & TTT_NO_LN)) return TTT_ERR_MODE;
+  if ((mode & TTT_DUAL) && chunk < 1) return TTT_ERR_MODE;
+  RecordLayout r;
+  int32_t st = record_layout(B, H, T, d, mode, &r);
+  if (st != TTT_OK) return st;
+  const bool no_ln = (mode & TTT_NO_LN) != 0;
+  const bool bf16 = (mode & TTT_IN_BF16) != 0;
+  // pointers
+  if (record == nullptr || dW0 == nullptr) return TTT_ERR_NULL;
+  if (!no_ln && (gamma == nullptr || beta == nullptr || dgamma == nullptr || dbeta == nullptr))
+    return TTT_ERR_NULL;
+  if (T > 0 && (q == nullptr || k == nullptr || v == nullptr || eta_logit == nullptr ||
+                gate_logit == nullptr || dout == nullptr || dq == nullptr || dk == nullptr ||
+                dv == nullptr || deta_logit == nullptr || dgate_logit == nullptr))
+    return TTT_ERR_NULL;
+  // alignment
+  const int64_t in_size = bf16 ? 2 : 4;
+  if (!aligned(record, 16) || !aligned(dW0, 16) || (dW_final && !aligned(dW_final, 16)))
+    return TTT_ERR_UNSUPPORTED;
+  if (!no_ln && (!aligned(gamma, 4) || !aligned(beta, 4) || !aligned(dgamma, 4) ||
+                 !aligned(dbeta, 4)))
+    return TTT_ERR_UNSUPPORTED;
+  if (T > 0) {
+    const void* a16[] = {q, k, v, gate_logit, dout, dq, dk, dv, dgate_logit};
+    for (const void* p : a16)
+      if (!aligned(p, 16)) return TTT_ERR_UNSUPPORTED;
+    if (!aligned(eta_logit, static_cast<uintptr_t>(in_size)) || !aligned(deta_logit, 4))
+      return TTT_ERR_UNSUPPORTED;
+  }
+  if (record_bytes < r.bytes) return TTT_ERR_WORKSPACE;
+  // aliasing: outputs (and the record, written as scratch) against everything
+  const int64_t seq = B * H * T * d, w = B * H * d * d, hd = no_ln ? 0 : H * d * 4;
+  const int64_t ts = T > 0 ? 1 : 0;
+  const Range outs[] = {span(dq, ts * seq * 4),          span(dk, ts * seq * 4),
+                        span(dv, ts * seq * 4),          span(dgate_logit, ts * seq * 4),
+                        span(deta_logit, ts * B * H * T * 4), span(dW0, w * 4),
+                        span(no_ln ? nullptr : dgamma, hd), span(no_ln ? nullptr : dbeta, hd),
+                        span(record, r.bytes)};
+  const Range ins[] = {span(q, ts * seq * in_size),      span(k, ts * seq * in_size),
+                       span(v, ts * seq * in_size),      span(gate_logit, ts * seq * in_size),
+                       span(eta_logit, ts * B * H * T * in_size), span(dout, ts * seq * 4),
+                       span(no_ln ? nullptr : gamma, hd), span(no_ln ? nullptr : beta, hd),
+                       span(dW_final, dW_final ? w * 4 : 0)};
+  constexpr int kOuts = sizeof(outs) / sizeof(outs[0]);
+  constexpr int kDW0 = 5;
+  constexpr int kDWFinal = sizeof(ins) / sizeof(ins[0]) - 1;
+  for (int i = 0; i < kOuts; ++i) {
+    for (int j = i + 1; j < kOuts; ++j)
+      if (overlaps(outs[i], outs[j])) return TTT_ERR_ALIAS;
+    for (int j = 0; j < static_cast<int>(sizeof(ins) / sizeof(ins[0])); ++j) {
+      if (i == kDW0 && j == kDWFinal && dW0 == dW_final) continue;   // in place
+      if (overlaps(outs[i], ins[j])) return TTT_ERR_ALIAS;
+    }
+  }
+  *a = ttt::BwdArgs{};
+  char* base = static_cast<char*>(record);
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->eta_logit = eta_logit;
+  a->gate_logit = gate_logit;
+  a->gamma = no_ln ? nullptr : gamma;
+  a->beta = no_ln ? nullptr : beta;
+  a->dout = dout;
+  a->dW_final = dW_final;
+  a->rec_delta = reinterpret_cast<const float*>(base + r.delta_off);
+  a->rec_W = reinterpret_cast<const float*>(base + r.w_off);
+  a->gb_part = reinterpret_cast<float*>(base + r.scratch_off);
+  a->dq = dq;
+  a->dk = dk;
+  a->dv = dv;
+  a->deta_logit = deta_logit;
+  a->dgate_logit = dgate_logit;
+  a->dW0 = dW0;
+  a->dgamma = no_ln ? nullptr : dgamma;
+  a->dbeta = no_ln ? nullptr : dbeta;
+  a->B = B;
+  a->H = H;
+  a->T = T;
+  a->d = d;
+  a->ln = no_ln ? ttt::kLnNone : ((mode & TTT_LN_EXACT) ? ttt::kLnExact : ttt::kLnST);
+  a->dual = false;
+  a->in_bf16 = bf16;
+  a->eps = kLnEps;
+  return TTT_OK;
+}
+
 }  // namespace
 
 extern "C" int32_t ttt_linear_validate(const void* q, const void* k, const void* v,
@@ -156,6 +326,61 @@ extern "C" int32_t ttt_linear_forward(const void* q, const void* k, const void* 
   return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
+extern "C" int32_t ttt_linear_record_bytes(int64_t B, int64_t H, int64_t T, int64_t d,
+                                           uint32_t mode, int64_t* bytes) {
+  if (bytes == nullptr) return TTT_ERR_NULL;
+  RecordLayout r;
+  const int32_t st = record_layout(B, H, T, d, mode, &r);
+  if (st == TTT_OK) *bytes = r.bytes;
+  return st;
+}
+
+extern "C" int32_t ttt_linear_forward_record(const void* q, const void* k, const void* v,
+                                             const void* eta_logit, const void* gate_logit,
+                                             const float* W0, const float* gamma,
+                                             const float* beta, float* out, float* W_final,
+                                             void* record, int64_t record_bytes, int64_t B,
+                                             int64_t H, int64_t T, int64_t d, uint32_t mode,
+                                             int64_t chunk, void* stream) {
+  ttt::ScanArgs a;
+  RecordLayout r;
+  const int32_t st = validate_forward_record(q, k, v, eta_logit, gate_logit, W0, gamma, beta,
+                                             out, W_final, record, record_bytes, B, H, T, d,
+                                             mode, chunk, &a, &r);
+  if (st != TTT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    if (W_final && W_final != W0) {
+      const size_t bytes = static_cast<size_t>(B * H * d * d) * sizeof(float);
+      if (hipMemcpyAsync(W_final, W0, bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        return TTT_ERR_HIP;
+    }
+    return TTT_OK;
+  }
+  if (!ttt::scan_mfma_supports(a)) return TTT_ERR_UNSUPPORTED;
+  return ttt::launch_scan_mfma(a, s) == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+extern "C" int32_t ttt_linear_backward(const void* q, const void* k, const void* v,
+                                       const void* eta_logit, const void* gate_logit,
+                                       const float* gamma, const float* beta, void* record,
+                                       int64_t record_bytes, const float* dout,
+                                       const float* dW_final, float* dq, float* dk, float* dv,
+                                       float* deta_logit, float* dgate_logit, float* dW0,
+                                       float* dgamma, float* dbeta, int64_t B, int64_t H,
+                                       int64_t T, int64_t d, uint32_t mode, int64_t chunk,
+                                       void* stream) {
+  ttt::BwdArgs a;
+  const int32_t st = validate_backward(q, k, v, eta_logit, gate_logit, gamma, beta, record,
+                                       record_bytes, dout, dW_final, dq, dk, dv, deta_logit,
+                                       dgate_logit, dW0, dgamma, dbeta, B, H, T, d, mode, chunk,
+                                       &a);
+  if (st != TTT_OK) return st;
+  const hipError_t err = ttt::launch_bwd_mfma(a, static_cast<hipStream_t>(stream));
+  if (err == hipErrorNotSupported) return TTT_ERR_UNSUPPORTED;
+  return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
 extern "C" const char* ttt_linear_kernel(int64_t d, uint32_t mode, int64_t chunk) {
   // a 16-byte aligned stand-in for every pointer: only the mode and sizes matter here
   alignas(16) static const float dummy[4] = {0, 0, 0, 0};
@@ -177,6 +402,7 @@ extern "C" const char* ttt_status_string(int32_t status) {
     case TTT_ERR_UNSUPPORTED: return "unsupported (d must be 16, 32, 64 or 128; pointers must be aligned)";
     case TTT_ERR_ALIAS: return "out or W_final overlaps another argument";
     case TTT_ERR_HIP: return "HIP runtime error at launch";
+    case TTT_ERR_WORKSPACE: return "record buffer smaller than ttt_linear_record_bytes";
     default: return "unknown status";
   }
 }

@@ -133,3 +133,12 @@ def make_inputs(workload: str, **overrides) -> ScanInputs:
     cfg = dict(WORKLOADS[workload])
     cfg.update(overrides)
     return make_case(name=workload, **cfg)
+
+
+def make_cotangents(B: int, H: int, T: int, d: int, seed: int, *, with_state: bool = True):
+    """Seeded loss gradients for a backward pass: ``(dout, dW_final)``, float32,
+    dout [B,H,T,d] ~ N(0,1) and dW_final [B,H,d,d] ~ N(0,1) (or None)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dout = rng.standard_normal((B, H, T, d), dtype=np.float32)
+    dWf = rng.standard_normal((B, H, d, d), dtype=np.float32) if with_state else None
+    return dout, dWf

@@ -49,7 +49,7 @@ def test_binding_constants_match_header():
 
 def test_version_and_status_strings():
     assert "ttt_linear" in ttt.ttt_version()
-    for code in range(7):
+    for code in range(8):
         assert ttt.ttt_status_string(code)
     assert ttt.ttt_status_string(99) == "unknown status"
 
