@@ -3,7 +3,10 @@
 
 One step is one call of ``ttt_linear_forward`` over the whole workload (every
 (batch, head) scan over the full sequence), with the inputs already resident
-in device memory.  W warm-up steps run untimed; then exactly K steps are
+in device memory.  With ``--pass train`` a step is one training pass instead:
+the recording forward (``ttt_linear_forward_record``) followed by the backward
+(``ttt_linear_backward``) from a fixed seeded dL/dout and dL/dW_final; the
+roofline is then that of the backward kernel.  W warm-up steps run untimed; then exactly K steps are
 timed between two device synchronisations, and each launch is also bracketed
 by events on its stream for the per-kernel duration.  Rank 0 prints one JSON
 line.
@@ -30,6 +33,8 @@ import numpy as np  # noqa: E402
 from test_rnn_layer_ttt_amd.inputs import WORKLOADS, make_inputs  # noqa: E402
 
 METRIC = "TTT-Linear scan token-heads/s at d=64 + % of HBM/FP32 roofline, 1 MI355X"
+METRIC_TRAIN = ("TTT-Linear training pass (recording forward + backward) token-heads/s at d=64 "
+                "+ % of HBM roofline of the backward kernel, 1 MI355X")
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # 256 CU x 2.4 GHz x 256 flop/clk (packed FMA), published
 FP32_MATRIX_PEAK_TFLOPS = 157.3  # MFMA fp32, published
@@ -47,6 +52,25 @@ def algorithmic_work(x):
     return n, nbytes, n * per_tok_flops
 
 
+def backward_work(x):
+    """Compulsory HBM bytes and flops of one backward launch (per token-head).
+
+    Bytes: q, k, v, gate, eta in their input type; dL/dout and the recorded
+    delta_t in fp32; the recorded W at every 16-token tile start (4 d^2 bytes
+    per tile, d^2/4 per token); dq, dk, dv, dgate (fp32) and deta out; per
+    scan dL/dW_final in and dW0 out; per head gamma, beta in and their
+    gradients out.  Flops: the 12 d^2 of the per-token gradient algebra
+    (G_t k_t, G_t^T delta_t, W_{t-1}^T dz_t, W_t^T dy_t and the two rank-one
+    updates of G).
+    """
+    B, H, T, d = x.q.shape
+    n = B * H * T
+    s_in = 2 if x.in_bf16 else 4
+    per_tok_bytes = (4 * d + 1) * s_in + 4 * d + 4 * d + (d * d) // 4 + 16 * d + 4
+    nbytes = n * per_tok_bytes + B * H * 8 * d * d + H * 16 * d
+    return n, nbytes, n * 12 * d * d
+
+
 def kernel_info(x):
     """Which kernel family runs this workload and which roof bounds it."""
     import test_rnn_layer_ttt_amd as ttt
@@ -59,9 +83,13 @@ def kernel_info(x):
     return name, ("alu" if x.in_bf16 else "hbm")
 
 
-def roofline(x, kernel_ms, traffic):
-    n, nbytes, flops = algorithmic_work(x)
-    name, bound = kernel_info(x)
+def roofline(x, kernel_ms, traffic, train=False):
+    if train:
+        n, nbytes, flops = backward_work(x)
+        name, bound = "bwd_mfma", "hbm"
+    else:
+        n, nbytes, flops = algorithmic_work(x)
+        name, bound = kernel_info(x)
     sec = kernel_ms / 1e3
     if bound == "hbm":
         achieved = nbytes / sec / 1e9
@@ -79,22 +107,37 @@ def roofline(x, kernel_ms, traffic):
 _CPU_SAMPLE = None
 
 
+_CPU_TRAIN = False
+
+
 def _oracle_worker(idx):
     from threadpoolctl import threadpool_limits
 
     import oracle
     x = _CPU_SAMPLE
+    args = (x.q[:, idx], x.k[:, idx], x.v[:, idx], x.eta_logit[:, idx], x.gate_logit[:, idx],
+            x.W0[:, idx], x.gamma[idx], x.beta[idx])
     with threadpool_limits(limits=1):
-        oracle.ttt_linear_forward(
-            x.q[:, idx], x.k[:, idx], x.v[:, idx], x.eta_logit[:, idx], x.gate_logit[:, idx],
-            x.W0[:, idx], x.gamma[idx], x.beta[idx], ln=x.ln, dual=x.dual, chunk=x.chunk)
+        oracle.ttt_linear_forward(*args, ln=x.ln, dual=x.dual, chunk=x.chunk)
+        if _CPU_TRAIN:
+            dout, dWf = _cotangents(x)
+            oracle.ttt_linear_backward(*args, dout[:, idx], dWf[:, idx], ln=x.ln, dual=x.dual,
+                                       chunk=x.chunk)
     return len(idx)
 
 
-def cpu_baseline(x, n_scans, workers):
-    """Time the oracle on ``n_scans`` scans of ``x`` (full length) over ``workers`` processes."""
+def _cotangents(x):
+    from test_rnn_layer_ttt_amd.inputs import make_cotangents
+    B, H, T, d = x.q.shape
+    return make_cotangents(B, H, T, d, seed=x.meta.get("seed", 0) + 1000)
+
+
+def cpu_baseline(x, n_scans, workers, train=False):
+    """Time the oracle on ``n_scans`` scans of ``x`` (full length) over ``workers``
+    processes; with ``train`` its forward and its backward, as one training pass."""
     import multiprocessing as mp
-    global _CPU_SAMPLE
+    global _CPU_SAMPLE, _CPU_TRAIN
+    _CPU_TRAIN = train
     B, H, T, d = x.q.shape
     n_scans = min(n_scans, B * H)
     step = max(1, (B * H) // n_scans)
@@ -110,7 +153,8 @@ def cpu_baseline(x, n_scans, workers):
     _CPU_SAMPLE = None
     return dict(value=round(done * T / sec, 1), unit="token-heads/s", cores=len(groups),
                 kind="oracle",
-                sample=f"{done} of {B * H} scans at full length T={T} (float64 NumPy, "
+                sample=f"{done} of {B * H} scans at full length T={T}"
+                       f"{', forward and backward' if train else ''} (float64 NumPy, "
                        f"{len(groups)} processes x 1 BLAS thread, {sec:.1f} s wall)")
 
 
@@ -146,8 +190,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="h1024_T4096_bf16", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-scans", type=int, default=256,
-                    help="scans of the workload the CPU oracle is timed on")
+    ap.add_argument("--pass", dest="pass_", default="forward", choices=("forward", "train"),
+                    help="forward: the scan; train: recording forward + backward")
+    ap.add_argument("--cpu-scans", type=int, default=None,
+                    help="scans of the workload the CPU oracle is timed on "
+                         "(default 256 for the forward, 128 for a training pass)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed region, run one device-to-device copy of this many "
@@ -163,11 +210,18 @@ def main():
 
     x = make_inputs(args.workload)
     B, H, T, d = x.q.shape
+    train = args.pass_ == "train"
+    if train and (x.dual or d != 64):
+        print(f"bench.py: the backward covers the per-token modes at d = 64; workload "
+              f"{args.workload} is not one", file=sys.stderr)
+        sys.exit(2)
+    if args.cpu_scans is None:
+        args.cpu_scans = 128 if train else 256
 
     # the CPU baseline runs before any GPU use (its workers are forked)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(x, args.cpu_scans, host_cores())
+        cpu = cpu_baseline(x, args.cpu_scans, host_cores(), train)
 
     import torch
 
@@ -187,36 +241,81 @@ def main():
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), el.data_ptr(), gl.data_ptr(),
             W0.data_ptr(), gamma.data_ptr(), beta.data_ptr(), out.data_ptr(), Wf.data_ptr())
 
-    def step():
+    def forward():
         st = ttt.ttt_linear_forward(*ptrs, B, H, T, d, mode, x.chunk, stream.cuda_stream)
         if st != ttt.TTT_OK:
             raise RuntimeError(f"ttt_linear_forward: {ttt.ttt_status_string(st)}")
 
+    if train:
+        st, rec_bytes = ttt.ttt_linear_record_bytes(B, H, T, d, mode)
+        ttt.check(st)
+        record = torch.empty(rec_bytes, dtype=torch.uint8, device=dev)
+        dout_np, dWf_np = _cotangents(x)
+        dout = torch.from_numpy(dout_np).to(dev)
+        dWf = torch.from_numpy(dWf_np).to(dev)
+        grads = [torch.empty((B, H, T, d), dtype=torch.float32, device=dev) for _ in range(4)]
+        deta = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+        dW0 = torch.empty_like(W0)
+        dgamma, dbeta = torch.empty_like(gamma), torch.empty_like(beta)
+        no_ln = x.ln == "none"
+        bptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), el.data_ptr(), gl.data_ptr(),
+                 None if no_ln else gamma.data_ptr(), None if no_ln else beta.data_ptr(),
+                 record.data_ptr(), rec_bytes, dout.data_ptr(), dWf.data_ptr(),
+                 *[g.data_ptr() for g in grads[:3]], deta.data_ptr(), grads[3].data_ptr(),
+                 dW0.data_ptr(), None if no_ln else dgamma.data_ptr(),
+                 None if no_ln else dbeta.data_ptr())
+
+        def forward_record():
+            st = ttt.ttt_linear_forward_record(*ptrs, record.data_ptr(), rec_bytes, B, H, T, d,
+                                               mode, 1, stream.cuda_stream)
+            if st != ttt.TTT_OK:
+                raise RuntimeError(f"ttt_linear_forward_record: {ttt.ttt_status_string(st)}")
+
+        def backward():
+            st = ttt.ttt_linear_backward(*bptrs, B, H, T, d, mode, 1, stream.cuda_stream)
+            if st != ttt.TTT_OK:
+                raise RuntimeError(f"ttt_linear_backward: {ttt.ttt_status_string(st)}")
+
     for _ in range(args.warmup):
-        step()
+        if train:
+            forward_record()
+            backward()
+        else:
+            forward()
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # events on the launch stream around the dominant kernel of each step (the
+    # backward in a training pass), and around the whole step
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    starts, ends, fstarts, fends = mk(), mk(), mk(), mk()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
+        if train:
+            fstarts[i].record(stream)
+            forward_record()
+            fends[i].record(stream)
+            starts[i].record(stream)
+            backward()
+            ends[i].record(stream)
+        else:
+            starts[i].record(stream)
+            forward()
+            ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_kernel_ms = float(np.mean(kernel_ms))
     ms_per_step = wall * 1e3 / args.steps
     n_tok = B * H * T
-    kernel, _ = kernel_info(x)
-    kname, roof = roofline(x, avg_kernel_ms, load_traffic(kernel, args.workload))
+    kernel = "bwd_mfma" if train else kernel_info(x)[0]
+    traffic_key = args.workload + ("/backward" if train else "")
+    kname, roof = roofline(x, avg_kernel_ms, load_traffic(kernel, traffic_key), train)
 
     mode_name = ("dual-form chunk %d" % x.chunk if x.dual else "per-token") + \
         {"st": "", "exact": ", exact LN Jacobian", "none": ", no LN"}[x.ln]
     line = {
-        "metric": METRIC,
+        "metric": METRIC_TRAIN if train else METRIC,
         "value": round(n_tok / (ms_per_step / 1e3), 1),
         "unit": "token-heads/s",
         "n_gpus": 1,
@@ -236,6 +335,10 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if train:
+        line["config"]["pass"] = "train: recording forward + backward"
+        fwd_ms = [s_.elapsed_time(e_) for s_, e_ in zip(fstarts, fends)]
+        line["config"]["forward_record_ms_avg"] = round(float(np.mean(fwd_ms)), 4)
     print(json.dumps(line), flush=True)
 
     if args.copy_probe_mib > 0:
