@@ -5,9 +5,9 @@
 // gradients are those of a loss L through out and W_final: reverse-mode
 // through every step of the forward.
 //
-// A forward pass first records delta_t and W at the start of every tile of 16
-// tokens.  The tiles are then walked backwards.  With W_c the weight at the
-// tile start, E_s = eta_s delta_s, H the gradient with respect to the weight
+// A recording forward stores delta_t and W at the start of every tile of 16
+// tokens.  The tiles are walked backwards.  With W_c the weight at the start
+// of tile c, E_s = eta_s delta_s, H the gradient with respect to the weight
 // after the tile, dy_t = dout_t * sigmoid(g_t), and G_t the gradient with
 // respect to W_t, the tile's algebra is (rows are tokens):
 //
@@ -15,17 +15,32 @@
 //   y_t  = W_c q_t - sum_{s<=t} (q_t.k_s) E_s          (W_t q_t)
 //   a_t  = G_t k_t = H k_t + sum_{t'>=t} (q_t'.k_t) dy_t' + sum_{t'>t} (k_t'.k_t) dz_t'
 //   d delta_t = -eta_t a_t,  d eta_t = -delta_t . a_t,  dz_t = VJP of delta(z_t)
-//   dk_t = -eta_t G_t^T delta_t + W_{t-1}^T dz_t
-//        = -eta_t [H^T delta_t + sum_{t'>=t} (delta_t.dy_t') q_t' + sum_{t'>t} (delta_t.dz_t') k_t']
+//   dk_t = -eta_t [H^T delta_t + sum_{t'>=t} (delta_t.dy_t') q_t' + sum_{t'>t} (delta_t.dz_t') k_t']
 //          + W_c^T dz_t - sum_{s<t} eta_s (delta_s.dz_t) k_s
-//   dq_t = W_t^T dy_t = W_c^T dy_t - sum_{s<=t} eta_s (delta_s.dy_t) k_s
+//   dq_t = W_c^T dy_t - sum_{s<=t} eta_s (delta_s.dy_t) k_s
 //   H   <- H + sum_t dy_t q_t^T + sum_t dz_t k_t^T          (gradient before the tile)
 //
-// Everything but the dz_t chain is a dense tile contraction on the matrix
-// cores (fp32 16x16x4, all operands from LDS, so either orientation of a
-// matrix is only a matter of addressing).  The chain (the a_t corrections and
-// the LayerNorm VJP, one wave, lane = feature) is serial.  One workgroup of 8
-// waves per (batch, head); phases separated by barriers.
+// Two rewrites let the work of neighbouring tiles overlap.  (1) The part of
+// a_t of tile c-1 that comes through H needs H before tile c, which is H
+// after it plus tile c's rank-16 terms: K_{c-1} H^T + (K_{c-1} Q_c^T) DY_c +
+// (K_{c-1} K_c^T) DZ_c; only the last term waits for tile c's chain.  (2)
+// W_c = W_{c-1} - E_{c-1}^T K_{c-1}, so DZ_c W_c is formed from the one
+// recorded W a period holds.
+//
+// One workgroup of 8 waves per (batch, head).  Period c (c = N .. 0; the
+// virtual tile N has no tokens) has two phases separated by barriers:
+//   A: wave 0 runs tile c's serial dz chain (lane = feature), then the Grams
+//      delta_c . dz_c and dz_c . E_{c-1}; the matrix-core waves form tile
+//      c-1's chain-independent products (K W^T, Q W^T, DY W, K H^T and its
+//      Grams) and delta_c H for dk of tile c; waves 4 and 7 issue the loads
+//      of tile c-2 and its W.
+//   B: what needs the chain or the Grams: tile c-1's in-tile corrections
+//      (z and its LayerNorm statistics, y -> dgate, dq, a0), tile c's
+//      remaining dk terms, d eta and the H update; waves 4 and 7 store tile
+//      c-2 and its W.
+// Every contraction is an fp32 MFMA 16x16x4 with operands from LDS.  In a
+// 64-deep contraction lane group G covers k = 16G..16G+15 (k-contiguous rows
+// load as 128-bit LDS reads); in a 16-deep (token) one, k = 4G..4G+3.
 #include "scan_common.h"
 
 namespace ttt {
@@ -44,12 +59,11 @@ __device__ __forceinline__ float sigmoidf_(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
-// D[4G + r][l16] += sum_k A[l16][k] B[k][l16] over a 4-deep k-step
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// sum over the 64 lanes, in every lane (row scan, two row broadcasts, readlane)
+// ---- wave-wide sums (lane = feature): row scans, row broadcasts, lane 63 ----
 template <int CTRL>
 __device__ __forceinline__ float dpp_add(float x) {
 #pragma clang fp contract(off)
@@ -58,42 +72,114 @@ __device__ __forceinline__ float dpp_add(float x) {
 __device__ __forceinline__ float rl63(float x) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
-__device__ __forceinline__ float wave_sum1(float a) {
-  a = dpp_add<0x111>(a);
-  a = dpp_add<0x112>(a);
-  a = dpp_add<0x114>(a);
-  a = dpp_add<0x118>(a);
-  a = dpp_add<0x142>(a);
-  a = dpp_add<0x143>(a);
-  return rl63(a);
-}
-__device__ __forceinline__ void wave_sum2(float& a, float& b) {
-  a = dpp_add<0x111>(a); b = dpp_add<0x111>(b);
-  a = dpp_add<0x112>(a); b = dpp_add<0x112>(b);
-  a = dpp_add<0x114>(a); b = dpp_add<0x114>(b);
-  a = dpp_add<0x118>(a); b = dpp_add<0x118>(b);
-  a = dpp_add<0x142>(a); b = dpp_add<0x142>(b);
-  a = dpp_add<0x143>(a); b = dpp_add<0x143>(b);
-  a = rl63(a); b = rl63(b);
-}
-__device__ __forceinline__ void wave_sum3(float& a, float& b, float& c) {
-  a = dpp_add<0x111>(a); b = dpp_add<0x111>(b); c = dpp_add<0x111>(c);
-  a = dpp_add<0x112>(a); b = dpp_add<0x112>(b); c = dpp_add<0x112>(c);
-  a = dpp_add<0x114>(a); b = dpp_add<0x114>(b); c = dpp_add<0x114>(c);
-  a = dpp_add<0x118>(a); b = dpp_add<0x118>(b); c = dpp_add<0x118>(c);
-  a = dpp_add<0x142>(a); b = dpp_add<0x142>(b); c = dpp_add<0x142>(c);
-  a = dpp_add<0x143>(a); b = dpp_add<0x143>(b); c = dpp_add<0x143>(c);
-  a = rl63(a); b = rl63(b); c = rl63(c);
+// N independent sums, interleaved step by step; wave-uniform results
+template <int N>
+__device__ __forceinline__ void wave_sums(float (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = dpp_add<0x111>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = dpp_add<0x112>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = dpp_add<0x114>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = dpp_add<0x118>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = dpp_add<0x142>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = dpp_add<0x143>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = rl63(x[i]);
 }
 
-struct alignas(16) BwdSmem {
-  float Wc[D][KP];         // W at the tile start, [i][j]
-  float Hm[2][D][KP];      // gradient w.r.t. the weight after the tile, [i][j]
-  float Q[BT][KP], K[BT][KP], V[BT][KP], DO[BT][KP], SG[BT][KP], De[BT][KP];
-  float Z[BT][KP], A0[BT][KP], DZ[BT][KP], XH[BT][KP];
-  float KK[BT][TP], QK[BT][TP], DeDY[BT][TP], DeDZ[BT][TP];
-  float ETA[BT], ELD[BT], RS[BT];   // eta, sigmoid'(eta_logit)/d, 1/sqrt(var+eps)
+// sum over the 16 lanes of a row, in every lane of it (rotations by 8, 4, 2, 1)
+template <int CTRL>
+__device__ __forceinline__ float ror_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x = ror_add<0x128>(x);
+  x = ror_add<0x124>(x);
+  x = ror_add<0x122>(x);
+  return ror_add<0x121>(x);
+}
+
+// ---- LDS layout ----
+struct alignas(16) TileIn {   // one tile of inputs (fp32); rows past the end are zero
+  float Q[BT][KP], K[BT][KP], DY[BT][KP], De[BT][KP];
+  float ETA[BT], ELD[BT];     // eta_t, sigmoid'(eta_logit_t) / d
 };
+struct alignas(16) Work {     // a tile's working set around its chain
+  float A[BT][KP];            // a0_t in, a_t out
+  float X[BT][KP];            // xhat_t in (zero without LayerNorm), dz_t out
+  float E[BT][KP];            // exact LayerNorm: e_t = gamma xhat_t + beta - v_t
+  float S[BT][8];             // rs, mean g, mean g xhat, mean gamma^2 xhat, mean gamma^2 xhat^2
+};
+struct alignas(16) Grams {
+  float KK[BT][TP], QK[BT][TP], DeDY[BT][TP];
+};
+struct alignas(16) BwdSmem {
+  TileIn ring[3];
+  float W[2][D][KP];          // recorded W at a tile start, [i][j]
+  float Hm[D][KP];            // H, [i][j]
+  Work wk[2];
+  Grams gr[2];
+  float XQ[BT][TP], XK[BT][TP], DeDZ[BT][TP], DZE[BT][TP];
+  float B2[BT][KP];           // the W-side half of dk, handed to wave 3
+};
+
+// ---- MFMA operand fragments (lane group G, row or column l16) ----
+// 64-deep: 16 consecutive k of a k-contiguous row
+__device__ __forceinline__ void frag_row64(const float* row, int G, float (&v)[16]) {
+  const float4* p = reinterpret_cast<const float4*>(row + 16 * G);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 x = p[q];
+    v[4 * q] = x.x;
+    v[4 * q + 1] = x.y;
+    v[4 * q + 2] = x.z;
+    v[4 * q + 3] = x.w;
+  }
+}
+// 64-deep: column n of a k-major array
+__device__ __forceinline__ void frag_col64(const float (*a)[KP], int n, int G, float (&v)[16]) {
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) v[ks] = a[16 * G + ks][n];
+}
+// 16-deep: 4 consecutive k of a k-contiguous row
+__device__ __forceinline__ void frag_row16(const float* row, int G, float (&v)[4]) {
+  const float4 x = *reinterpret_cast<const float4*>(row + 4 * G);
+  v[0] = x.x;
+  v[1] = x.y;
+  v[2] = x.z;
+  v[3] = x.w;
+}
+// 16-deep: column n of a k-major array
+template <int P>
+__device__ __forceinline__ void frag_col16(const float (*a)[P], int n, int G, float (&v)[4]) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) v[ks] = a[4 * G + ks][n];
+}
+template <int KS>
+__device__ __forceinline__ f32x4 mma(const float (&a)[KS], const float (&b)[KS], f32x4 acc) {
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) acc = mfma4(a[ks], b[ks], acc);
+  return acc;
+}
+// 16x16 Gram of two 16-row blocks of k-contiguous rows: G[m][n] = ra[m] . rb[n]
+template <int P1, int P2>
+__device__ __forceinline__ f32x4 gram(const float (*ra)[P1], const float (*rb)[P2], int l16,
+                                      int G) {
+  float a[16], b[16];
+  frag_row64(ra[l16], G, a);
+  frag_row64(rb[l16], G, b);
+  return mma<16>(a, b, f32x4{0, 0, 0, 0});
+}
+// an MFMA output block: rows 4G + r, column col0 + l16
+template <int P>
+__device__ __forceinline__ void store_block(float (*o)[P], int col0, f32x4 v, int l16, int G) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) o[4 * G + r][col0 + l16] = v[r];
+}
 
 template <bool BF16>
 __device__ __forceinline__ float ld_in(const void* p, int64_t i) {
@@ -103,15 +189,140 @@ __device__ __forceinline__ float ld_in(const void* p, int64_t i) {
     return static_cast<const float*>(p)[i];
 }
 
-// one 16 x 16 output block: sum over k-steps of A(m, k) B(k, n) (accessors
-// take the lane's row m = l16 and column n = l16 and the k index)
-template <typename FA, typename FB>
-__device__ __forceinline__ f32x4 block_mfma(int ksteps, FA A, FB B, f32x4 acc, int l16, int G) {
-  for (int ks = 0; ks < ksteps; ++ks) {
-    const int k = 4 * ks + G;
-    acc = mfma4(A(l16, k), B(k, l16), acc);
+// ---- state a wave keeps across a barrier ----
+// The roles share one register array, so the kernel needs registers for the
+// largest role rather than for all of them together:
+//   waves 1, 2, 5, 6: a 16x64 accumulator in [0, 16); wave 3: dk's H-side half
+//   wave 1: v in [16, 32) (exact LayerNorm); wave 5: dout in [16, 32), gate in [32, 48)
+//   wave 4: a tile of inputs in flight (LoadLayout); wave 7: its W, [0, 64)
+constexpr int kState = 80;
+__device__ __forceinline__ f32x4 blk(const float (&st)[kState], int b) {
+  return f32x4{st[4 * b], st[4 * b + 1], st[4 * b + 2], st[4 * b + 3]};
+}
+__device__ __forceinline__ void put(float (&st)[kState], int b, f32x4 v) {
+  st[4 * b] = v[0];
+  st[4 * b + 1] = v[1];
+  st[4 * b + 2] = v[2];
+  st[4 * b + 3] = v[3];
+}
+
+// wave 4's layout: lane -> token t = lane / 4, features 16 (lane % 4) .. +15.
+// q, k, gate: 16 values (fp32) or 8 words of packed bf16; then dout, delta
+// (16 fp32 each)
+template <bool BF16>
+struct LoadLayout {
+  static constexpr int kIn = BF16 ? 8 : 16;
+  static constexpr int kQ = 0, kK = kIn, kG = 2 * kIn, kDout = 3 * kIn, kDe = kDout + 16,
+                       kEnd = kDe + 16;
+  static_assert(kEnd <= kState, "loader state does not fit");
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load_in16(const void* p, int64_t base, bool in, float* dst) {
+  using L = LoadLayout<BF16>;
+  if constexpr (BF16) {
+    const uint4* q = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + base);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint4 x = in ? q[i] : uint4{0, 0, 0, 0};
+      dst[4 * i] = __uint_as_float(x.x);
+      dst[4 * i + 1] = __uint_as_float(x.y);
+      dst[4 * i + 2] = __uint_as_float(x.z);
+      dst[4 * i + 3] = __uint_as_float(x.w);
+    }
+  } else {
+    const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p) + base);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 x = in ? q[i] : float4{0, 0, 0, 0};
+      dst[4 * i] = x.x;
+      dst[4 * i + 1] = x.y;
+      dst[4 * i + 2] = x.z;
+      dst[4 * i + 3] = x.w;
+    }
   }
-  return acc;
+  (void)sizeof(L);
+}
+// element i of 16 loaded by load_in16
+template <bool BF16>
+__device__ __forceinline__ float in16(const float* src, int i) {
+  if constexpr (BF16) {
+    const uint32_t w = __float_as_uint(src[i >> 1]);
+    return __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  } else {
+    return src[i];
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void loader_issue(float (&st)[kState], float& eta, int& n,
+                                             const void* qp, const void* kp, const void* gp,
+                                             const void* ep, const float* dout_p,
+                                             const float* rec_delta, int64_t bhT, int64_t t0,
+                                             int64_t T, int lane) {
+  using L = LoadLayout<BF16>;
+  n = static_cast<int>(min<int64_t>(BT, T - t0));
+  const int t = lane >> 2, f0 = 16 * (lane & 3);
+  const bool in = t < n;
+  const int64_t base = (bhT + t0 + t) * D + f0;
+  load_in16<BF16>(qp, base, in, &st[L::kQ]);
+  load_in16<BF16>(kp, base, in, &st[L::kK]);
+  load_in16<BF16>(gp, base, in, &st[L::kG]);
+  load_in16<false>(dout_p, base, in, &st[L::kDout]);
+  load_in16<false>(rec_delta, base, in, &st[L::kDe]);
+  eta = lane < n ? ld_in<BF16>(ep, bhT + t0 + lane) : 0.0f;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void loader_store(const float (&st)[kState], float eta, int n,
+                                             TileIn& tl, int lane) {
+  using L = LoadLayout<BF16>;
+  const int t = lane >> 2, f0 = 16 * (lane & 3);
+#pragma unroll
+  for (int i = 0; i < 16; i += 4) {
+    float4 q4, k4, y4, d4;
+    float* qv = &q4.x;
+    float* kv = &k4.x;
+    float* yv = &y4.x;
+    float* dv = &d4.x;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      qv[u] = in16<BF16>(&st[L::kQ], i + u);
+      kv[u] = in16<BF16>(&st[L::kK], i + u);
+      yv[u] = t < n ? st[L::kDout + i + u] * sigmoidf_(in16<BF16>(&st[L::kG], i + u)) : 0.0f;
+      dv[u] = st[L::kDe + i + u];
+    }
+    *reinterpret_cast<float4*>(&tl.Q[t][f0 + i]) = q4;
+    *reinterpret_cast<float4*>(&tl.K[t][f0 + i]) = k4;
+    *reinterpret_cast<float4*>(&tl.DY[t][f0 + i]) = y4;
+    *reinterpret_cast<float4*>(&tl.De[t][f0 + i]) = d4;
+  }
+  if (lane < BT) {
+    const float s = lane < n ? sigmoidf_(eta) : 0.0f;
+    tl.ETA[lane] = s * (1.0f / D);
+    tl.ELD[lane] = s * (1.0f - s) * (1.0f / D);
+  }
+}
+
+// wave 7: a recorded W (64 fp32 a lane: elements 4 (lane + 64 j) .. +3)
+__device__ __forceinline__ void w_issue(float (&st)[kState], const float* w_rec, int lane) {
+  const float4* wp = reinterpret_cast<const float4*>(w_rec);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float4 x = wp[lane + 64 * j];
+    st[4 * j] = x.x;
+    st[4 * j + 1] = x.y;
+    st[4 * j + 2] = x.z;
+    st[4 * j + 3] = x.w;
+  }
+}
+__device__ __forceinline__ void w_store(const float (&st)[kState], float (*W)[KP], int lane) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int e = 4 * (lane + 64 * j);
+    *reinterpret_cast<float4*>(&W[e / D][e % D]) =
+        make_float4(st[4 * j], st[4 * j + 1], st[4 * j + 2], st[4 * j + 3]);
+  }
 }
 
 template <bool BF16, int LN>
@@ -134,253 +345,507 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   const int64_t bh = blockIdx.x;
   const int h = static_cast<int>(bh % H);
   const int64_t bhT = bh * T;
-  const int64_t ntiles = (T + BT - 1) / BT;
+  const int N = static_cast<int>((T + BT - 1) / BT);
+  auto rows = [&](int c) { return static_cast<int>(min<int64_t>(BT, T - int64_t(c) * BT)); };
+  auto wrec = [&](int c) { return (bh * N + c) * D * D; };
 
-  // H starts as dL/dW_final
-  for (int e = tid; e < D * D; e += NT) {
-    const int i = e / D, j = e % D;
-    sm.Hm[0][i][j] = dW_final != nullptr ? dW_final[bh * D * D + e] : 0.0f;
-  }
-  // serial wave: LayerNorm affine of feature `lane`, gradient accumulators
-  float gam = 1.0f, bet = 0.0f, dgam = 0.0f, dbet = 0.0f;
-  if (wave == 0 && LN != kLnNone) {
-    gam = gamma[h * D + lane];
-    bet = beta[h * D + lane];
-  }
-  int cur = 0;
-
-  for (int64_t c = ntiles - 1; c >= 0; --c) {
-    const int64_t t0 = c * BT;
-    const int n = static_cast<int>(min<int64_t>(BT, T - t0));
-    // ---- load the tile (rows past the end are zero) and W_c ----
+  // ---- prologue: H = dL/dW_final; tile N-1 and its W ----
+  for (int e = tid; e < D * D; e += NT)
+    sm.Hm[e / D][e % D] = dW_final != nullptr ? dW_final[bh * D * D + e] : 0.0f;
+  if (N > 0) {
+    const int c = N - 1, n = rows(c);
+    TileIn& tl = sm.ring[c % 3];
     for (int e = tid; e < BT * D; e += NT) {
       const int t = e / D, i = e % D;
       const bool in = t < n;
-      const int64_t g = (bhT + t0 + t) * D + i;
-      sm.Q[t][i] = in ? ld_in<BF16>(qp, g) : 0.0f;
-      sm.K[t][i] = in ? ld_in<BF16>(kp, g) : 0.0f;
-      sm.V[t][i] = in ? ld_in<BF16>(vp, g) : 0.0f;
-      sm.DO[t][i] = in ? dout[g] : 0.0f;
-      sm.SG[t][i] = in ? sigmoidf_(ld_in<BF16>(gatep, g)) : 0.0f;
-      sm.De[t][i] = in ? rec_delta[g] : 0.0f;
-      sm.DZ[t][i] = 0.0f;
+      const int64_t g = (bhT + int64_t(c) * BT + t) * D + i;
+      tl.Q[t][i] = in ? ld_in<BF16>(qp, g) : 0.0f;
+      tl.K[t][i] = in ? ld_in<BF16>(kp, g) : 0.0f;
+      tl.DY[t][i] = in ? dout[g] * sigmoidf_(ld_in<BF16>(gatep, g)) : 0.0f;
+      tl.De[t][i] = in ? rec_delta[g] : 0.0f;
     }
     if (tid < BT) {
-      const bool in = tid < n;
-      const float s = in ? sigmoidf_(ld_in<BF16>(etap, bhT + t0 + tid)) : 0.0f;
-      sm.ETA[tid] = s * (1.0f / D);
-      sm.ELD[tid] = s * (1.0f - s) * (1.0f / D);
+      const float s = tid < n ? sigmoidf_(ld_in<BF16>(etap, bhT + int64_t(c) * BT + tid)) : 0.0f;
+      tl.ETA[tid] = s * (1.0f / D);
+      tl.ELD[tid] = s * (1.0f - s) * (1.0f / D);
     }
-    for (int e = tid; e < D * D / 4; e += NT) {
-      const int i = (4 * e) / D, j = (4 * e) % D;
-      const float4 w = *reinterpret_cast<const float4*>(rec_W + ((bh * ntiles + c) * D + i) * D + j);
-      *reinterpret_cast<float4*>(&sm.Wc[i][j]) = w;
-    }
-    __syncthreads();
-    // ---- token Gram matrices KK[s][t] = k_s.k_t, QK[t][s] = q_t.k_s ----
-    if (wave < 2) {
-      const float (*A)[KP] = wave == 0 ? sm.K : sm.Q;
-      f32x4 acc = {0, 0, 0, 0};
-      acc = block_mfma(16, [&](int m, int k) { return A[m][k]; },
-                       [&](int k, int nn) { return sm.K[nn][k]; }, acc, l16, G);
-      float (*O)[TP] = wave == 0 ? sm.KK : sm.QK;
+    for (int e = tid; e < D * D; e += NT) sm.W[c & 1][e / D][e % D] = rec_W[wrec(c) + e];
+  }
+
+  // per-role constants
+  float gam = 1.0f, gam0 = 1.0f;        // wave 0: gamma of feature `lane`, mean gamma^2
+  float dgam = 0.0f, dbet = 0.0f;       // wave 0: this scan's dgamma, dbeta of feature `lane`
+  if (wave == 0 && LN != kLnNone) {
+    gam = gamma[h * D + lane];
+    float s[1] = {gam * gam};
+    wave_sums<1>(s);
+    gam0 = s[0] * (1.0f / D);
+  }
+  float cg[4] = {1, 1, 1, 1}, cb[4] = {0, 0, 0, 0};   // wave 1: features 16 fb + l16
+  if (wave == 1 && LN != kLnNone) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) O[4 * G + r][l16] = acc[r];
+    for (int fb = 0; fb < 4; ++fb) {
+      cg[fb] = gamma[h * D + 16 * fb + l16];
+      cb[fb] = beta[h * D + 16 * fb + l16];
     }
-    __syncthreads();
-    // ---- z (waves 0-3), y and dgate (waves 0-3), a0 (waves 4-7), by feature slice ----
-    {
-      const int sl = wave & 3;
-      const int f = 16 * sl + l16;
-      const float (*Hc)[KP] = sm.Hm[cur];
-      if (wave < 4) {
-        // z_t = W_c k_t - sum_{s<t} (k_s.k_t) eta_s delta_s
-        f32x4 z = {0, 0, 0, 0};
-        z = block_mfma(16, [&](int m, int k) { return sm.K[m][k]; },
-                       [&](int k, int nn) { return sm.Wc[16 * sl + nn][k]; }, z, l16, G);
-        z = block_mfma(4, [&](int m, int k) { return k < m ? -sm.KK[m][k] : 0.0f; },
-                       [&](int k, int nn) { return sm.ETA[k] * sm.De[k][16 * sl + nn]; }, z, l16, G);
-        // y_t = W_c q_t - sum_{s<=t} (q_t.k_s) eta_s delta_s
-        f32x4 y = {0, 0, 0, 0};
-        y = block_mfma(16, [&](int m, int k) { return sm.Q[m][k]; },
-                       [&](int k, int nn) { return sm.Wc[16 * sl + nn][k]; }, y, l16, G);
-        y = block_mfma(4, [&](int m, int k) { return k <= m ? -sm.QK[m][k] : 0.0f; },
-                       [&](int k, int nn) { return sm.ETA[k] * sm.De[k][16 * sl + nn]; }, y, l16, G);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 4 * G + r;
-          sm.Z[t][f] = z[r];
-          if (t < n) {
-            const float s = sm.SG[t][f];
-            dgate[(bhT + t0 + t) * D + f] = sm.DO[t][f] * y[r] * s * (1.0f - s);
-          }
-        }
-      } else {
-        // a0_t = H k_t + sum_{t'>=t} (q_t'.k_t) dy_t'
-        f32x4 a = {0, 0, 0, 0};
-        a = block_mfma(16, [&](int m, int k) { return sm.K[m][k]; },
-                       [&](int k, int nn) { return Hc[16 * sl + nn][k]; }, a, l16, G);
-        a = block_mfma(4, [&](int m, int k) { return k >= m ? sm.QK[k][m] : 0.0f; },
-                       [&](int k, int nn) { return sm.DO[k][16 * sl + nn] * sm.SG[k][16 * sl + nn]; },
-                       a, l16, G);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.A0[4 * G + r][f] = a[r];
-      }
-    }
-    __syncthreads();
-    // ---- LayerNorm statistics of z: two tokens per wave ----
-    if (LN != kLnNone) {
-      for (int t = 2 * wave; t < 2 * wave + 2; ++t) {
-        const float z = sm.Z[t][lane];
-        float s1 = z, s2 = z * z;
-        wave_sum2(s1, s2);
-        const float mu = s1 * (1.0f / D);
-        const float var = fmaf(s2, 1.0f / D, -mu * mu);
-        const float rs = __builtin_amdgcn_rsqf(fmaxf(var + eps, eps));
-        sm.XH[t][lane] = (z - mu) * rs;
-        if (lane == 0) sm.RS[t] = rs;
-      }
-    }
-    __syncthreads();
-    // ---- the serial chain, t descending (wave 0, lane = feature) ----
+  }
+  float st[kState];    // the role state kept across barriers (see above)
+  float ld_eta = 0.0f;
+  int ld_n = 0;
+  __syncthreads();
+
+  for (int c = N; c >= 0; --c) {
+    const bool prep = c >= 1;       // tile c-1 exists
+    const bool live = c < N;        // tile c exists
+    const int cm = c - 1;
+    // ============================ phase A ============================
     if (wave == 0) {
-      float dzr[BT];
+      if (live) {
+        // ---- the dz chain of tile c, t descending ----
+        const TileIn& tc = sm.ring[c % 3];
+        Work& w = sm.wk[c & 1];
+        const float(*KK)[TP] = sm.gr[c & 1].KK;
+        const int n = rows(c);
+        const int64_t t0 = int64_t(c) * BT;
+        float ac[BT];
 #pragma unroll
-      for (int t = 0; t < BT; ++t) dzr[t] = 0.0f;
+        for (int t = 0; t < BT; ++t) ac[t] = w.A[t][lane];
 #pragma unroll
-      for (int t = BT - 1; t >= 0; --t) {
-        if (t < n) {
-          float a = sm.A0[t][lane];
+        for (int t = BT - 1; t >= 0; --t) {
+          if (t < n) {
+            const float a = ac[t];
+            const float dd = -tc.ETA[t] * a;
+            float dz, dvv;
+            if constexpr (LN == kLnNone) {
+              dz = dd;
+              dvv = -dd;
+            } else if constexpr (LN == kLnST) {
+              const float x = w.X[t][lane];
+              const float rs = w.S[t][0];
+              const float ww = gam * dd;
+              float s[2] = {ww, ww * x};
+              wave_sums<2>(s);
+              dz = rs * (ww - s[0] * (1.0f / D) - x * (s[1] * (1.0f / D)));
+              dvv = -dd;
+              dgam = fmaf(dd, x, dgam);
+              dbet += dd;
+            } else {
+              // delta = rs (g - mean g - xhat mean(g xhat)), g = gamma e; one
+              // round of five sums of dd against per-token constants
+              const float x = w.X[t][lane];
+              const float e = w.E[t][lane];
+              const float4 s4 = *reinterpret_cast<const float4*>(&w.S[t][0]);
+              const float rs = s4.x, mg = s4.y, mgx = s4.z, g1 = s4.w, g2 = w.S[t][4];
+              const float g = gam * e;
+              const float P = g - mg - x * mgx;
+              const float g2d = gam * gam * dd;
+              float s[5] = {dd, dd * x, g2d, g2d * x, dd * P};
+              wave_sums<5>(s);
+              const float sdp = rs * s[0], sdpx = rs * s[1], drs = s[4];
+              const float dP = rs * dd;
+              const float dg = dP - sdp * (1.0f / D) - x * (sdpx * (1.0f / D));
+              const float de = gam * dg;
+              const float dxh = gam * de - dP * mgx - sdpx * (1.0f / D) * g;
+              const float m1 =
+                  (rs * s[2] - gam0 * sdp - g1 * sdpx - rs * mgx * s[0] - sdpx * mg) * (1.0f / D);
+              const float m2 =
+                  (rs * s[3] - g1 * sdp - g2 * sdpx - rs * mgx * s[1] - sdpx * mgx) * (1.0f / D);
+              dz = rs * (dxh - m1 - x * m2) - drs * rs * rs * x * (1.0f / D);
+              dvv = -de;
+              dgam += fmaf(e, dg, x * de);
+              dbet += de;
+            }
+            w.X[t][lane] = dz;
+            w.A[t][lane] = a;
+            dv[(bhT + t0 + t) * D + lane] = dvv;
+            // the next token needs only row t-1; the other rows' updates
+            // overlap its sums.  The scheduling fence keeps the compiler from
+            // hoisting every later token's loads into registers at once.
+            if (t > 0) ac[t - 1] = fmaf(KK[t - 1][t], dz, ac[t - 1]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int tp = t + 1; tp < BT; ++tp) a = fmaf(sm.KK[t][tp], dzr[tp], a);
-          const float eta = sm.ETA[t];
-          const float dd = -eta * a;
-          const float del = sm.De[t][lane];
-          float dz, dvv;
-          float deta_sum = -del * a;
-          if constexpr (LN == kLnNone) {
-            deta_sum = wave_sum1(deta_sum);
-            dz = dd;
-            dvv = -dd;
-          } else if constexpr (LN == kLnST) {
-            const float xh = sm.XH[t][lane];
-            const float rs = sm.RS[t];
-            const float w = gam * dd;
-            float sw = w, swx = w * xh;
-            wave_sum3(deta_sum, sw, swx);
-            dz = rs * (w - sw * (1.0f / D) - xh * (swx * (1.0f / D)));
-            dvv = -dd;
-            dgam = fmaf(dd, xh, dgam);
-            dbet += dd;
-          } else {
-            // delta = rs (g - mean g - xh mean(g xh)), g = gam e, e = gam xh + bet - v
-            const float xh = sm.XH[t][lane];
-            const float rs = sm.RS[t];
-            const float e = fmaf(gam, xh, bet - sm.V[t][lane]);
-            const float g = gam * e;
-            float mg = g, mgx = g * xh;
-            wave_sum3(mg, mgx, deta_sum);
-            mg *= (1.0f / D);
-            mgx *= (1.0f / D);
-            const float P = g - mg - xh * mgx;
-            const float dP = rs * dd;
-            float drs = dd * P, sdp = dP, sdpx = dP * xh;
-            wave_sum3(drs, sdp, sdpx);
-            const float dmgx = -sdpx;
-            const float dg = dP - sdp * (1.0f / D) + dmgx * xh * (1.0f / D);
-            float dxh = -dP * mgx + dmgx * g * (1.0f / D);
-            const float de = gam * dg;
-            dgam += fmaf(e, dg, xh * de);
-            dbet += de;
-            dvv = -de;
-            dxh = fmaf(gam, de, dxh);
-            float sx = dxh, sxx = dxh * xh;
-            wave_sum2(sx, sxx);
-            dz = rs * (dxh - sx * (1.0f / D) - xh * (sxx * (1.0f / D)))
-                 - drs * rs * rs * xh * (1.0f / D);
+            for (int s = 0; s + 1 < t; ++s) ac[s] = fmaf(KK[s][t], dz, ac[s]);
           }
-          dzr[t] = dz;
-          sm.DZ[t][lane] = dz;
-          dv[(bhT + t0 + t) * D + lane] = dvv;
-          if (lane == 0) deta[bhT + t0 + t] = deta_sum * sm.ELD[t];
+        }
+        // ---- Grams that need dz: DeDZ[s][t'] = delta_s . dz_t' and
+        //      DZE[t][s] = eta_s (dz_t . delta_s) over tile c-1's s ----
+        store_block(sm.DeDZ, 0, gram(tc.De, w.X, l16, G), l16, G);
+        if (prep) {
+          const TileIn& tm = sm.ring[cm % 3];
+          f32x4 g2 = gram(w.X, tm.De, l16, G);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) g2[r] *= tm.ETA[l16];
+          store_block(sm.DZE, 0, g2, l16, G);
+        }
+      }
+    } else if (wave == 3) {
+      if (c + 1 < N) {
+        // dk of tile c+1 = -eta b1 + B2
+        const int cp = c + 1, n = rows(cp);
+        const TileIn& tp = sm.ring[cp % 3];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 4 * G + r, j = 16 * jb + l16;
+            if (t < n)
+              dk[(bhT + int64_t(cp) * BT + t) * D + j] = fmaf(-tp.ETA[t], st[4 * jb + r], sm.B2[t][j]);
+          }
+      }
+      if (live) {
+        // delta_c H, H being the gradient after tile c
+        const TileIn& tc = sm.ring[c % 3];
+        float a[16];
+        frag_row64(tc.De[l16], G, a);
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          float b[16];
+          frag_col64(sm.Hm, 16 * jb + l16, G, b);
+          put(st, jb, mma<16>(a, b, f32x4{0, 0, 0, 0}));
+        }
+      }
+    } else if (wave != 4 && prep) {
+      const TileIn& tm = sm.ring[cm % 3];
+      const float(*Wm)[KP] = sm.W[cm & 1];
+      if (wave == 1 || wave == 5 || wave == 6) {
+        // Z' = K W^T (wave 1), Y' = Q W^T (wave 5), A0' = K H^T (wave 6)
+        const float(*Ar)[KP] = wave == 5 ? tm.Q : tm.K;
+        const float(*Br)[KP] = wave == 6 ? sm.Hm : Wm;
+        float a[16];
+        frag_row64(Ar[l16], G, a);
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb) {
+          float b[16];
+          frag_row64(Br[16 * fb + l16], G, b);
+          put(st, fb, mma<16>(a, b, f32x4{0, 0, 0, 0}));
+        }
+        // fetched for phase B: v (wave 1, exact LayerNorm), dout and gate (wave 5)
+        const int nm = rows(cm);
+        const int64_t t0 = int64_t(cm) * BT;
+        if (wave == 1 && LN == kLnExact) {
+#pragma unroll
+          for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int t = 4 * G + r;
+              st[16 + 4 * fb + r] = t < nm ? ld_in<BF16>(vp, (bhT + t0 + t) * D + 16 * fb + l16) : 0.0f;
+            }
+        }
+        if (wave == 5) {
+#pragma unroll
+          for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int t = 4 * G + r;
+              const int64_t gi = (bhT + t0 + t) * D + 16 * fb + l16;
+              st[16 + 4 * fb + r] = t < nm ? dout[gi] : 0.0f;
+              st[32 + 4 * fb + r] = t < nm ? ld_in<BF16>(gatep, gi) : 0.0f;
+            }
+        }
+      } else if (wave == 2) {
+        // dQ' = DY W
+        float a[16];
+        frag_row64(tm.DY[l16], G, a);
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          float b[16];
+          frag_col64(Wm, 16 * jb + l16, G, b);
+          put(st, jb, mma<16>(a, b, f32x4{0, 0, 0, 0}));
+        }
+      } else if (wave == 7) {
+        // the W of tile c-2 in flight; Grams of tile c-1 and its cross Grams with tile c
+        if (c >= 2) w_issue(st, rec_W + wrec(c - 2), lane);
+        Grams& gm = sm.gr[cm & 1];
+        store_block(gm.KK, 0, gram(tm.K, tm.K, l16, G), l16, G);
+        store_block(gm.QK, 0, gram(tm.Q, tm.K, l16, G), l16, G);
+        store_block(gm.DeDY, 0, gram(tm.De, tm.DY, l16, G), l16, G);
+        if (live) {
+          const TileIn& tc = sm.ring[c % 3];
+          store_block(sm.XQ, 0, gram(tm.K, tc.Q, l16, G), l16, G);
+          store_block(sm.XK, 0, gram(tm.K, tc.K, l16, G), l16, G);
         }
       }
     }
-    __syncthreads();
-    // ---- Gram matrices DeDY[s][t'] = delta_s.dy_t', DeDZ[s][t'] = delta_s.dz_t' ----
-    if (wave < 2) {
-      f32x4 acc = {0, 0, 0, 0};
-      if (wave == 0)
-        acc = block_mfma(16, [&](int m, int k) { return sm.De[m][k]; },
-                         [&](int k, int nn) { return sm.DO[nn][k] * sm.SG[nn][k]; }, acc, l16, G);
-      else
-        acc = block_mfma(16, [&](int m, int k) { return sm.De[m][k]; },
-                         [&](int k, int nn) { return sm.DZ[nn][k]; }, acc, l16, G);
-      float (*O)[TP] = wave == 0 ? sm.DeDY : sm.DeDZ;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) O[4 * G + r][l16] = acc[r];
+    if (wave == 4 && c >= 2) {
+      const int u = c - 2;
+      loader_issue<BF16>(st, ld_eta, ld_n, qp, kp, gatep, etap, dout, rec_delta, bhT,
+                         int64_t(u) * BT, T, lane);
     }
     __syncthreads();
-    // ---- dK, dQ (waves 0-3 / 4-7 by column slice) and the new H (all waves) ----
-    {
-      const int sl = wave & 3;
-      const int j = 16 * sl + l16;
-      const float (*Hc)[KP] = sm.Hm[cur];
-      if (wave < 4) {
-        f32x4 b1 = {0, 0, 0, 0}, b2 = {0, 0, 0, 0};
-        b1 = block_mfma(16, [&](int m, int k) { return sm.De[m][k]; },
-                        [&](int k, int nn) { return Hc[k][16 * sl + nn]; }, b1, l16, G);
-        b1 = block_mfma(4, [&](int m, int k) { return k >= m ? sm.DeDY[m][k] : 0.0f; },
-                        [&](int k, int nn) { return sm.Q[k][16 * sl + nn]; }, b1, l16, G);
-        b1 = block_mfma(4, [&](int m, int k) { return k > m ? sm.DeDZ[m][k] : 0.0f; },
-                        [&](int k, int nn) { return sm.K[k][16 * sl + nn]; }, b1, l16, G);
-        b2 = block_mfma(16, [&](int m, int k) { return sm.DZ[m][k]; },
-                        [&](int k, int nn) { return sm.Wc[k][16 * sl + nn]; }, b2, l16, G);
-        b2 = block_mfma(4, [&](int m, int k) { return k < m ? -sm.ETA[k] * sm.DeDZ[k][m] : 0.0f; },
-                        [&](int k, int nn) { return sm.K[k][16 * sl + nn]; }, b2, l16, G);
+    // ============================ phase B ============================
+    if (wave == 4 && c >= 2) {
+      const int u = c - 2;
+      loader_store<BF16>(st, ld_eta, ld_n, sm.ring[u % 3], lane);
+    }
+    if (wave == 7 && c >= 2) w_store(st, sm.W[(c - 2) & 1], lane);
+    if (wave == 1 && prep) {
+      // z of tile c-1 and its LayerNorm statistics -> the chain's working set
+      const TileIn& tm = sm.ring[cm % 3];
+      const Grams& gm = sm.gr[cm & 1];
+      Work& w = sm.wk[cm & 1];
+      float a[4];
+      frag_row16(gm.KK[l16], G, a);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) a[ks] = (4 * G + ks < l16) ? a[ks] : 0.0f;
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) {
+        float b[4];
+        frag_col16(tm.De, 16 * fb + l16, G, b);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) b[ks] *= -tm.ETA[4 * G + ks];
+        put(st, fb, mma<4>(a, b, blk(st, fb)));
+      }
+      if constexpr (LN != kLnNone) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 4 * G + r;
-          if (t < n) dk[(bhT + t0 + t) * D + j] = fmaf(-sm.ETA[t], b1[r], b2[r]);
+          const float mu = row16_sum(st[r] + st[4 + r] + st[8 + r] + st[12 + r]) * (1.0f / D);
+          float cz[4], ss = 0.0f;
+#pragma unroll
+          for (int fb = 0; fb < 4; ++fb) {
+            cz[fb] = st[4 * fb + r] - mu;
+            ss = fmaf(cz[fb], cz[fb], ss);
+          }
+          const float var = row16_sum(ss) * (1.0f / D);
+          const float rs = __builtin_amdgcn_rsqf(var + eps);
+          float xh[4];
+#pragma unroll
+          for (int fb = 0; fb < 4; ++fb) {
+            xh[fb] = cz[fb] * rs;
+            w.X[t][16 * fb + l16] = xh[fb];
+          }
+          if constexpr (LN == kLnExact) {
+            float sg = 0.0f, sgx = 0.0f, s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb) {
+              const float e = fmaf(cg[fb], xh[fb], cb[fb] - st[16 + 4 * fb + r]);
+              w.E[t][16 * fb + l16] = e;
+              const float g = cg[fb] * e, g2 = cg[fb] * cg[fb] * xh[fb];
+              sg += g;
+              sgx = fmaf(g, xh[fb], sgx);
+              s1 += g2;
+              s2 = fmaf(g2, xh[fb], s2);
+            }
+            sg = row16_sum(sg);
+            sgx = row16_sum(sgx);
+            s1 = row16_sum(s1);
+            s2 = row16_sum(s2);
+            if (l16 == 0) {
+              *reinterpret_cast<float4*>(&w.S[t][0]) =
+                  make_float4(rs, sg * (1.0f / D), sgx * (1.0f / D), s1 * (1.0f / D));
+              w.S[t][4] = s2 * (1.0f / D);
+            }
+          } else {
+            if (l16 == 0) w.S[t][0] = rs;
+          }
         }
       } else {
-        f32x4 q = {0, 0, 0, 0};
-        q = block_mfma(16, [&](int m, int k) { return sm.DO[m][k] * sm.SG[m][k]; },
-                       [&](int k, int nn) { return sm.Wc[k][16 * sl + nn]; }, q, l16, G);
-        q = block_mfma(4, [&](int m, int k) { return k <= m ? -sm.ETA[k] * sm.DeDY[k][m] : 0.0f; },
-                       [&](int k, int nn) { return sm.K[k][16 * sl + nn]; }, q, l16, G);
+        // no LayerNorm: the chain reads no statistics; rows past the end
+        // must still hand a zero dz on
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb) store_block(w.X, 16 * fb, f32x4{0, 0, 0, 0}, l16, G);
+      }
+    } else if (wave == 5 && prep) {
+      // y of tile c-1 -> dgate = dout y sigmoid'(gate)
+      const TileIn& tm = sm.ring[cm % 3];
+      const Grams& gm = sm.gr[cm & 1];
+      float a[4];
+      frag_row16(gm.QK[l16], G, a);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) a[ks] = (4 * G + ks <= l16) ? a[ks] : 0.0f;
+      const int nm = rows(cm);
+      const int64_t t0 = int64_t(cm) * BT;
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) {
+        float b[4];
+        frag_col16(tm.De, 16 * fb + l16, G, b);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) b[ks] *= -tm.ETA[4 * G + ks];
+        const f32x4 y = mma<4>(a, b, blk(st, fb));
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 4 * G + r;
-          if (t < n) dq[(bhT + t0 + t) * D + j] = q[r];
+          if (t < nm) {
+            const float s = sigmoidf_(st[32 + 4 * fb + r]);
+            dgate[(bhT + t0 + t) * D + 16 * fb + l16] = st[16 + 4 * fb + r] * y[r] * s * (1.0f - s);
+          }
         }
       }
-      // H_new[i][j] = H[i][j] + sum_t dy_t[i] q_t[j] + dz_t[i] k_t[j]: 16 blocks, 2 per wave
-      for (int blk = wave; blk < 16; blk += NWAVES) {
-        const int ib = blk / 4, jb = blk % 4;
-        f32x4 acc;
+    } else if (wave == 2) {
+      if (prep) {
+        // dq of tile c-1 = DY W - sum_{s<=t} eta_s (delta_s.dy_t) k_s
+        const TileIn& tm = sm.ring[cm % 3];
+        const Grams& gm = sm.gr[cm & 1];
+        float a[4];
+        frag_col16(gm.DeDY, l16, G, a);   // DeDY[s][t], k = s, m = t
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = Hc[16 * ib + 4 * G + r][16 * jb + l16];
-        acc = block_mfma(4, [&](int m, int k) { return sm.DO[k][16 * ib + m] * sm.SG[k][16 * ib + m]; },
-                         [&](int k, int nn) { return sm.Q[k][16 * jb + nn]; }, acc, l16, G);
-        acc = block_mfma(4, [&](int m, int k) { return sm.DZ[k][16 * ib + m]; },
-                         [&](int k, int nn) { return sm.K[k][16 * jb + nn]; }, acc, l16, G);
+        for (int ks = 0; ks < 4; ++ks) {
+          const int s = 4 * G + ks;
+          a[ks] = s <= l16 ? -tm.ETA[s] * a[ks] : 0.0f;
+        }
+        const int nm = rows(cm);
+        const int64_t t0 = int64_t(cm) * BT;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sm.Hm[cur ^ 1][16 * ib + 4 * G + r][16 * jb + l16] = acc[r];
+        for (int jb = 0; jb < 4; ++jb) {
+          float b[4];
+          frag_col16(tm.K, 16 * jb + l16, G, b);
+          const f32x4 v = mma<4>(a, b, blk(st, jb));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 4 * G + r;
+            if (t < nm) dq[(bhT + t0 + t) * D + 16 * jb + l16] = v[r];
+          }
+        }
+      }
+      if (live) {
+        // d eta_logit of tile c = -sigmoid'(.)/d delta_t . a_t (a Gram's diagonal)
+        const TileIn& tc = sm.ring[c % 3];
+        const f32x4 gd = gram(tc.De, sm.wk[c & 1].A, l16, G);
+        const int n = rows(c);
+        const int r = l16 - 4 * G;
+        if (r >= 0 && r < 4 && l16 < n) {
+          float v = gd[0];
+          v = r == 1 ? gd[1] : v;
+          v = r == 2 ? gd[2] : v;
+          v = r == 3 ? gd[3] : v;
+          deta[bhT + int64_t(c) * BT + l16] = -tc.ELD[l16] * v;
+        }
+      }
+    } else if (wave == 6 && prep) {
+      // a0 of tile c-1 = K H^T + (K_{c-1} Q_c^T) DY_c + (K_{c-1} K_c^T) DZ_c
+      //                  + sum_{t'>=t} (q_t'.k_t) dy_t'
+      const TileIn& tm = sm.ring[cm % 3];
+      const Grams& gm = sm.gr[cm & 1];
+      float au[4];
+      frag_col16(gm.QK, l16, G, au);    // QK[t'][t], k = t', m = t
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) au[ks] = (4 * G + ks >= l16) ? au[ks] : 0.0f;
+      float aq[4] = {0, 0, 0, 0}, ak[4] = {0, 0, 0, 0};
+      if (live) {
+        frag_row16(sm.XQ[l16], G, aq);
+        frag_row16(sm.XK[l16], G, ak);
+      }
+      Work& w = sm.wk[cm & 1];
+#pragma unroll
+      for (int fb = 0; fb < 4; ++fb) {
+        float b[4];
+        frag_col16(tm.DY, 16 * fb + l16, G, b);
+        f32x4 v = mma<4>(au, b, blk(st, fb));
+        if (live) {
+          const TileIn& tc = sm.ring[c % 3];
+          frag_col16(tc.DY, 16 * fb + l16, G, b);
+          v = mma<4>(aq, b, v);
+          frag_col16(sm.wk[c & 1].X, 16 * fb + l16, G, b);
+          v = mma<4>(ak, b, v);
+        }
+        store_block(w.A, 16 * fb, v, l16, G);
+      }
+    } else if (wave == 3 && live) {
+      // b1 += sum_{t'>=t} (delta_t.dy_t') q_t' + sum_{t'>t} (delta_t.dz_t') k_t'
+      const TileIn& tc = sm.ring[c % 3];
+      float ay[4], az[4];
+      frag_row16(sm.gr[c & 1].DeDY[l16], G, ay);
+      frag_row16(sm.DeDZ[l16], G, az);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int tp = 4 * G + ks;
+        ay[ks] = tp >= l16 ? ay[ks] : 0.0f;
+        az[ks] = tp > l16 ? az[ks] : 0.0f;
+      }
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        float b[4];
+        frag_col16(tc.Q, 16 * jb + l16, G, b);
+        put(st, jb, mma<4>(ay, b, blk(st, jb)));
+        frag_col16(tc.K, 16 * jb + l16, G, b);
+        put(st, jb, mma<4>(az, b, blk(st, jb)));
       }
     }
-    cur ^= 1;
+    if ((wave == 0 || wave == 4) && live) {
+      // B2 = DZ W_c - sum_{s<t} eta_s (delta_s.dz_t) k_s, with
+      // DZ W_c = DZ W_{c-1} - (DZ E_{c-1}^T) K_{c-1} (for c = 0 the slot holds W_0)
+      const TileIn& tc = sm.ring[c % 3];
+      const float(*Wm)[KP] = sm.W[(prep ? cm : 0) & 1];
+      float a[16];
+      frag_row64(sm.wk[c & 1].X[l16], G, a);
+      float as[4], ae[4] = {0, 0, 0, 0};
+      frag_col16(sm.DeDZ, l16, G, as);   // DeDZ[s][t], k = s, m = t
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int s = 4 * G + ks;
+        as[ks] = s < l16 ? -tc.ETA[s] * as[ks] : 0.0f;
+      }
+      if (prep) {
+        frag_row16(sm.DZE[l16], G, ae);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) ae[ks] = -ae[ks];
+      }
+      const int jb0 = wave == 0 ? 0 : 2;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int jb = jb0 + jj;
+        float b[16];
+        frag_col64(Wm, 16 * jb + l16, G, b);
+        f32x4 v = mma<16>(a, b, f32x4{0, 0, 0, 0});
+        float bk[4];
+        frag_col16(tc.K, 16 * jb + l16, G, bk);
+        v = mma<4>(as, bk, v);
+        if (prep) {
+          frag_col16(sm.ring[cm % 3].K, 16 * jb + l16, G, bk);
+          v = mma<4>(ae, bk, v);
+        }
+        store_block(sm.B2, 16 * jb, v, l16, G);
+      }
+    }
+    if (live && (wave == 7 || wave == 1 || wave == 5)) {
+      // H += DY_c^T Q_c + DZ_c^T K_c by 16x16 blocks (ib, jb): wave 7 takes
+      // block rows 0-1, wave 1 row 2, wave 5 row 3
+      const TileIn& tc = sm.ring[c % 3];
+      const float(*DZ)[KP] = sm.wk[c & 1].X;
+      const int ib0 = wave == 7 ? 0 : wave == 1 ? 2 : 3;
+      const int nib = wave == 7 ? 2 : 1;
+      for (int ii = 0; ii < nib; ++ii) {
+        const int ib = ib0 + ii;
+        float ay[4], az[4];
+        frag_col16(tc.DY, 16 * ib + l16, G, ay);
+        frag_col16(DZ, 16 * ib + l16, G, az);
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          f32x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = sm.Hm[16 * ib + 4 * G + r][16 * jb + l16];
+          float b[4];
+          frag_col16(tc.Q, 16 * jb + l16, G, b);
+          v = mma<4>(ay, b, v);
+          frag_col16(tc.K, 16 * jb + l16, G, b);
+          v = mma<4>(az, b, v);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sm.Hm[16 * ib + 4 * G + r][16 * jb + l16] = v[r];
+        }
+      }
+    }
     __syncthreads();
   }
-  // dW0 and this scan's share of dgamma, dbeta
-  for (int e = tid; e < D * D; e += NT) dW0[bh * D * D + e] = sm.Hm[cur][e / D][e % D];
+  // dk of tile 0; dW0 = H; this scan's share of dgamma, dbeta
+  if (wave == 3 && N > 0) {
+    const int n = rows(0);
+    const TileIn& tp = sm.ring[0];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 4 * G + r, j = 16 * jb + l16;
+        if (t < n) dk[bhT * D + t * D + j] = fmaf(-tp.ETA[t], st[4 * jb + r], sm.B2[t][j]);
+      }
+  }
+  for (int e = tid; e < D * D; e += NT) dW0[bh * D * D + e] = sm.Hm[e / D][e % D];
   if (wave == 0 && gb_part != nullptr) {
     gb_part[(bh * 2) * D + lane] = dgam;
     gb_part[(bh * 2 + 1) * D + lane] = dbet;
   }
 }
 
-// dgamma[h][i] = sum_b (partial), dbeta likewise (deterministic order)
+// dgamma[h][i] = sum over the batch of the per-scan parts, dbeta likewise (fixed order)
 __global__ void gamma_beta_sum_kernel(const float* __restrict__ gb_part, float* __restrict__ dgamma,
                                       float* __restrict__ dbeta, int64_t B, int64_t H) {
   const int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
