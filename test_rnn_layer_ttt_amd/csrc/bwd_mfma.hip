@@ -43,6 +43,8 @@
 // load as 128-bit LDS reads); in a 16-deep (token) one, k = 4G..4G+3.
 #include "scan_common.h"
 
+#include <type_traits>
+
 namespace ttt {
 namespace {
 
@@ -106,6 +108,7 @@ __device__ __forceinline__ float row16_sum(float x) {
 // ---- LDS layout ----
 struct alignas(16) TileIn {   // one tile of inputs (fp32); rows past the end are zero
   float Q[BT][KP], K[BT][KP], DY[BT][KP], De[BT][KP];
+  float G2[BT][KP];           // dout sigmoid'(gate): dgate = y G2
   float ETA[BT], ELD[BT];     // eta_t, sigmoid'(eta_logit_t) / d
 };
 struct alignas(16) Work {     // a tile's working set around its chain
@@ -193,7 +196,7 @@ __device__ __forceinline__ float ld_in(const void* p, int64_t i) {
 // The roles share one register array, so the kernel needs registers for the
 // largest role rather than for all of them together:
 //   waves 1, 2, 5, 6: a 16x64 accumulator in [0, 16); wave 3: dk's H-side half
-//   wave 1: v in [16, 32) (exact LayerNorm); wave 5: dout in [16, 32), gate in [32, 48)
+//   wave 1: v in [16, 32) (exact LayerNorm)
 //   wave 4: a tile of inputs in flight (LoadLayout); wave 7: its W, [0, 64)
 constexpr int kState = 80;
 __device__ __forceinline__ f32x4 blk(const float (&st)[kState], int b) {
@@ -280,21 +283,25 @@ __device__ __forceinline__ void loader_store(const float (&st)[kState], float et
   const int t = lane >> 2, f0 = 16 * (lane & 3);
 #pragma unroll
   for (int i = 0; i < 16; i += 4) {
-    float4 q4, k4, y4, d4;
+    float4 q4, k4, y4, d4, g4;
     float* qv = &q4.x;
     float* kv = &k4.x;
     float* yv = &y4.x;
     float* dv = &d4.x;
+    float* gv = &g4.x;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       qv[u] = in16<BF16>(&st[L::kQ], i + u);
       kv[u] = in16<BF16>(&st[L::kK], i + u);
-      yv[u] = t < n ? st[L::kDout + i + u] * sigmoidf_(in16<BF16>(&st[L::kG], i + u)) : 0.0f;
+      const float sg = sigmoidf_(in16<BF16>(&st[L::kG], i + u));
+      yv[u] = t < n ? st[L::kDout + i + u] * sg : 0.0f;
+      gv[u] = yv[u] * (1.0f - sg);
       dv[u] = st[L::kDe + i + u];
     }
     *reinterpret_cast<float4*>(&tl.Q[t][f0 + i]) = q4;
     *reinterpret_cast<float4*>(&tl.K[t][f0 + i]) = k4;
     *reinterpret_cast<float4*>(&tl.DY[t][f0 + i]) = y4;
+    *reinterpret_cast<float4*>(&tl.G2[t][f0 + i]) = g4;
     *reinterpret_cast<float4*>(&tl.De[t][f0 + i]) = d4;
   }
   if (lane < BT) {
@@ -361,7 +368,9 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       const int64_t g = (bhT + int64_t(c) * BT + t) * D + i;
       tl.Q[t][i] = in ? ld_in<BF16>(qp, g) : 0.0f;
       tl.K[t][i] = in ? ld_in<BF16>(kp, g) : 0.0f;
-      tl.DY[t][i] = in ? dout[g] * sigmoidf_(ld_in<BF16>(gatep, g)) : 0.0f;
+      const float sg = in ? sigmoidf_(ld_in<BF16>(gatep, g)) : 0.0f;
+      tl.DY[t][i] = in ? dout[g] * sg : 0.0f;
+      tl.G2[t][i] = tl.DY[t][i] * (1.0f - sg);
       tl.De[t][i] = in ? rec_delta[g] : 0.0f;
     }
     if (tid < BT) {
@@ -392,6 +401,9 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   float st[kState];    // the role state kept across barriers (see above)
   float ld_eta = 0.0f;
   int ld_n = 0;
+  // every prologue load complete: otherwise the token guards of the chain
+  // leave the gamma load pending and each token waits on the memory counter
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int c = N; c >= 0; --c) {
@@ -410,62 +422,89 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         float ac[BT];
 #pragma unroll
         for (int t = 0; t < BT; ++t) ac[t] = w.A[t][lane];
+        // a token's inputs from LDS, read one token ahead so that their
+        // latency hides behind the previous token's sums
+        struct Tok {
+          float eta, x, e, rs, mg, mgx, g1, g2;
+          float kk[BT];   // KK[s][t], s < t
+        };
+        auto fetch = [&](int t, Tok& k) {
+          k.eta = tc.ETA[t];
+          if constexpr (LN != kLnNone) {
+            k.x = w.X[t][lane];
+            if constexpr (LN == kLnExact) {
+              k.e = w.E[t][lane];
+              const float4 s4 = *reinterpret_cast<const float4*>(&w.S[t][0]);
+              k.rs = s4.x;
+              k.mg = s4.y;
+              k.mgx = s4.z;
+              k.g1 = s4.w;
+              k.g2 = w.S[t][4];
+            } else {
+              k.rs = w.S[t][0];
+            }
+          }
+#pragma unroll
+          for (int s = 0; s < BT; ++s)
+            if (s < t) k.kk[s] = KK[s][t];
+        };
+        Tok cur, nxt;
+        fetch(BT - 1, nxt);
 #pragma unroll
         for (int t = BT - 1; t >= 0; --t) {
+          cur = nxt;
+          if (t > 0) fetch(t - 1, nxt);
           if (t < n) {
             const float a = ac[t];
-            const float dd = -tc.ETA[t] * a;
+            const float dd = -cur.eta * a;
             float dz, dvv;
             if constexpr (LN == kLnNone) {
               dz = dd;
               dvv = -dd;
             } else if constexpr (LN == kLnST) {
-              const float x = w.X[t][lane];
-              const float rs = w.S[t][0];
+              const float x = cur.x, rs = cur.rs;
               const float ww = gam * dd;
-              float s[2] = {ww, ww * x};
-              wave_sums<2>(s);
-              dz = rs * (ww - s[0] * (1.0f / D) - x * (s[1] * (1.0f / D)));
+              float sm2[2] = {ww, ww * x};
+              wave_sums<2>(sm2);
+              dz = rs * (ww - sm2[0] * (1.0f / D) - x * (sm2[1] * (1.0f / D)));
               dvv = -dd;
               dgam = fmaf(dd, x, dgam);
               dbet += dd;
             } else {
               // delta = rs (g - mean g - xhat mean(g xhat)), g = gamma e; one
               // round of five sums of dd against per-token constants
-              const float x = w.X[t][lane];
-              const float e = w.E[t][lane];
-              const float4 s4 = *reinterpret_cast<const float4*>(&w.S[t][0]);
-              const float rs = s4.x, mg = s4.y, mgx = s4.z, g1 = s4.w, g2 = w.S[t][4];
+              const float x = cur.x, e = cur.e, rs = cur.rs, mg = cur.mg, mgx = cur.mgx;
+              const float g1 = cur.g1, g2 = cur.g2;
               const float g = gam * e;
               const float P = g - mg - x * mgx;
               const float g2d = gam * gam * dd;
-              float s[5] = {dd, dd * x, g2d, g2d * x, dd * P};
-              wave_sums<5>(s);
-              const float sdp = rs * s[0], sdpx = rs * s[1], drs = s[4];
+              float sm5[5] = {dd, dd * x, g2d, g2d * x, dd * P};
+              wave_sums<5>(sm5);
+              const float sdp = rs * sm5[0], sdpx = rs * sm5[1], drs = sm5[4];
               const float dP = rs * dd;
               const float dg = dP - sdp * (1.0f / D) - x * (sdpx * (1.0f / D));
               const float de = gam * dg;
               const float dxh = gam * de - dP * mgx - sdpx * (1.0f / D) * g;
-              const float m1 =
-                  (rs * s[2] - gam0 * sdp - g1 * sdpx - rs * mgx * s[0] - sdpx * mg) * (1.0f / D);
-              const float m2 =
-                  (rs * s[3] - g1 * sdp - g2 * sdpx - rs * mgx * s[1] - sdpx * mgx) * (1.0f / D);
+              const float m1 = (rs * sm5[2] - gam0 * sdp - g1 * sdpx - rs * mgx * sm5[0] -
+                                sdpx * mg) * (1.0f / D);
+              const float m2 = (rs * sm5[3] - g1 * sdp - g2 * sdpx - rs * mgx * sm5[1] -
+                                sdpx * mgx) * (1.0f / D);
               dz = rs * (dxh - m1 - x * m2) - drs * rs * rs * x * (1.0f / D);
               dvv = -de;
               dgam += fmaf(e, dg, x * de);
               dbet += de;
             }
+            // the next token needs only row t-1; the other rows' updates
+            // overlap its sums
+            if (t > 0) ac[t - 1] = fmaf(cur.kk[t - 1], dz, ac[t - 1]);
             w.X[t][lane] = dz;
             w.A[t][lane] = a;
             dv[(bhT + t0 + t) * D + lane] = dvv;
-            // the next token needs only row t-1; the other rows' updates
-            // overlap its sums.  The scheduling fence keeps the compiler from
-            // hoisting every later token's loads into registers at once.
-            if (t > 0) ac[t - 1] = fmaf(KK[t - 1][t], dz, ac[t - 1]);
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int s = 0; s + 1 < t; ++s) ac[s] = fmaf(KK[s][t], dz, ac[s]);
+            for (int s = 0; s + 1 < t; ++s) ac[s] = fmaf(cur.kk[s], dz, ac[s]);
           }
+          // keeps each token's loads one token ahead rather than all hoisted
+          __builtin_amdgcn_sched_barrier(0);
         }
         // ---- Grams that need dz: DeDZ[s][t'] = delta_s . dz_t' and
         //      DZE[t][s] = eta_s (dz_t . delta_s) over tile c-1's s ----
@@ -478,30 +517,54 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
           store_block(sm.DZE, 0, g2, l16, G);
         }
       }
-    } else if (wave == 3) {
-      if (c + 1 < N) {
-        // dk of tile c+1 = -eta b1 + B2
-        const int cp = c + 1, n = rows(cp);
-        const TileIn& tp = sm.ring[cp % 3];
+    } else if (wave == 3 || wave == 2) {
+      // dk's H-side half b1, column blocks j0, j0+1 (wave 3: 0-1 in state
+      // slots 0-1; wave 2: 2-3 in slots 4-5, beside its DY W product)
+      auto half = [&](auto s0c) {
+        constexpr int s0 = decltype(s0c)::value;
+        const int j0 = s0 == 0 ? 0 : 2;
+        if (c + 1 < N) {
+          // dk of tile c+1 = -eta b1 + B2
+          const int cp = c + 1, n = rows(cp);
+          const TileIn& tp = sm.ring[cp % 3];
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
+          for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 4 * G + r, j = 16 * jb + l16;
-            if (t < n)
-              dk[(bhT + int64_t(cp) * BT + t) * D + j] = fmaf(-tp.ETA[t], st[4 * jb + r], sm.B2[t][j]);
+            for (int r = 0; r < 4; ++r) {
+              const int t = 4 * G + r, j = 16 * (j0 + jj) + l16;
+              if (t < n)
+                dk[(bhT + int64_t(cp) * BT + t) * D + j] =
+                    fmaf(-tp.ETA[t], st[4 * (s0 + jj) + r], sm.B2[t][j]);
+            }
+        }
+        if (live) {
+          // delta_c H, H being the gradient after tile c
+          const TileIn& tc = sm.ring[c % 3];
+          float a[16];
+          frag_row64(tc.De[l16], G, a);
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            float bb[16];
+            frag_col64(sm.Hm, 16 * (j0 + jj) + l16, G, bb);
+            put(st, s0 + jj, mma<16>(a, bb, f32x4{0, 0, 0, 0}));
           }
-      }
-      if (live) {
-        // delta_c H, H being the gradient after tile c
-        const TileIn& tc = sm.ring[c % 3];
+        }
+      };
+      if (wave == 3)
+        half(std::integral_constant<int, 0>{});
+      else
+        half(std::integral_constant<int, 4>{});
+      if (wave == 2 && prep) {
+        // dQ' = DY W of tile c-1
+        const TileIn& tm = sm.ring[cm % 3];
+        const float(*Wm)[KP] = sm.W[cm & 1];
         float a[16];
-        frag_row64(tc.De[l16], G, a);
+        frag_row64(tm.DY[l16], G, a);
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
-          float b[16];
-          frag_col64(sm.Hm, 16 * jb + l16, G, b);
-          put(st, jb, mma<16>(a, b, f32x4{0, 0, 0, 0}));
+          float bb[16];
+          frag_col64(Wm, 16 * jb + l16, G, bb);
+          put(st, jb, mma<16>(a, bb, f32x4{0, 0, 0, 0}));
         }
       }
     } else if (wave != 4 && prep) {
@@ -519,7 +582,7 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
           frag_row64(Br[16 * fb + l16], G, b);
           put(st, fb, mma<16>(a, b, f32x4{0, 0, 0, 0}));
         }
-        // fetched for phase B: v (wave 1, exact LayerNorm), dout and gate (wave 5)
+        // fetched for phase B: v (wave 1, exact LayerNorm)
         const int nm = rows(cm);
         const int64_t t0 = int64_t(cm) * BT;
         if (wave == 1 && LN == kLnExact) {
@@ -530,27 +593,6 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
               const int t = 4 * G + r;
               st[16 + 4 * fb + r] = t < nm ? ld_in<BF16>(vp, (bhT + t0 + t) * D + 16 * fb + l16) : 0.0f;
             }
-        }
-        if (wave == 5) {
-#pragma unroll
-          for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int t = 4 * G + r;
-              const int64_t gi = (bhT + t0 + t) * D + 16 * fb + l16;
-              st[16 + 4 * fb + r] = t < nm ? dout[gi] : 0.0f;
-              st[32 + 4 * fb + r] = t < nm ? ld_in<BF16>(gatep, gi) : 0.0f;
-            }
-        }
-      } else if (wave == 2) {
-        // dQ' = DY W
-        float a[16];
-        frag_row64(tm.DY[l16], G, a);
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-          float b[16];
-          frag_col64(Wm, 16 * jb + l16, G, b);
-          put(st, jb, mma<16>(a, b, f32x4{0, 0, 0, 0}));
         }
       } else if (wave == 7) {
         // the W of tile c-2 in flight; Grams of tile c-1 and its cross Grams with tile c
@@ -646,7 +688,7 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         for (int fb = 0; fb < 4; ++fb) store_block(w.X, 16 * fb, f32x4{0, 0, 0, 0}, l16, G);
       }
     } else if (wave == 5 && prep) {
-      // y of tile c-1 -> dgate = dout y sigmoid'(gate)
+      // y of tile c-1 -> dgate = y dout sigmoid'(gate)
       const TileIn& tm = sm.ring[cm % 3];
       const Grams& gm = sm.gr[cm & 1];
       float a[4];
@@ -665,10 +707,7 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 4 * G + r;
-          if (t < nm) {
-            const float s = sigmoidf_(st[32 + 4 * fb + r]);
-            dgate[(bhT + t0 + t) * D + 16 * fb + l16] = st[16 + 4 * fb + r] * y[r] * s * (1.0f - s);
-          }
+          if (t < nm) dgate[(bhT + t0 + t) * D + 16 * fb + l16] = y[r] * tm.G2[t][16 * fb + l16];
         }
       }
     } else if (wave == 2) {
@@ -740,7 +779,8 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         }
         store_block(w.A, 16 * fb, v, l16, G);
       }
-    } else if (wave == 3 && live) {
+    }
+    if ((wave == 3 || wave == 2) && live) {
       // b1 += sum_{t'>=t} (delta_t.dy_t') q_t' + sum_{t'>t} (delta_t.dz_t') k_t'
       const TileIn& tc = sm.ring[c % 3];
       float ay[4], az[4];
@@ -752,16 +792,25 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         ay[ks] = tp >= l16 ? ay[ks] : 0.0f;
         az[ks] = tp > l16 ? az[ks] : 0.0f;
       }
+      auto half = [&](auto s0c) {
+        constexpr int s0 = decltype(s0c)::value;
+        const int j0 = s0 == 0 ? 0 : 2;
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        float b[4];
-        frag_col16(tc.Q, 16 * jb + l16, G, b);
-        put(st, jb, mma<4>(ay, b, blk(st, jb)));
-        frag_col16(tc.K, 16 * jb + l16, G, b);
-        put(st, jb, mma<4>(az, b, blk(st, jb)));
-      }
+        for (int jj = 0; jj < 2; ++jj) {
+          const int jb = j0 + jj;
+          float bb[4];
+          frag_col16(tc.Q, 16 * jb + l16, G, bb);
+          put(st, s0 + jj, mma<4>(ay, bb, blk(st, s0 + jj)));
+          frag_col16(tc.K, 16 * jb + l16, G, bb);
+          put(st, s0 + jj, mma<4>(az, bb, blk(st, s0 + jj)));
+        }
+      };
+      if (wave == 3)
+        half(std::integral_constant<int, 0>{});
+      else
+        half(std::integral_constant<int, 4>{});
     }
-    if ((wave == 0 || wave == 4) && live) {
+    if ((wave == 0 || wave == 4 || wave == 3) && live) {
       // B2 = DZ W_c - sum_{s<t} eta_s (delta_s.dz_t) k_s, with
       // DZ W_c = DZ W_{c-1} - (DZ E_{c-1}^T) K_{c-1} (for c = 0 the slot holds W_0)
       const TileIn& tc = sm.ring[c % 3];
@@ -780,9 +829,10 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) ae[ks] = -ae[ks];
       }
-      const int jb0 = wave == 0 ? 0 : 2;
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
+      // column blocks: wave 0 takes 0 and 1, wave 4 block 2, wave 3 block 3
+      const int jb0 = wave == 0 ? 0 : wave == 4 ? 2 : 3;
+      const int njb = wave == 0 ? 2 : 1;
+      for (int jj = 0; jj < njb; ++jj) {
         const int jb = jb0 + jj;
         float b[16];
         frag_col64(Wm, 16 * jb + l16, G, b);
@@ -797,46 +847,64 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         store_block(sm.B2, 16 * jb, v, l16, G);
       }
     }
-    if (live && (wave == 7 || wave == 1 || wave == 5)) {
-      // H += DY_c^T Q_c + DZ_c^T K_c by 16x16 blocks (ib, jb): wave 7 takes
-      // block rows 0-1, wave 1 row 2, wave 5 row 3
+    if (live && (wave == 7 || wave == 0 || wave == 1 || wave == 5 || wave == 3)) {
+      // H += DY_c^T Q_c + DZ_c^T K_c by 16x16 blocks b = 4 ib + jb, in pairs
+      // whose loads and MFMAs interleave: wave 7 takes pairs 0-2, wave 0
+      // pair 3, wave 1 pairs 4-5, wave 5 pair 6, wave 3 pair 7
       const TileIn& tc = sm.ring[c % 3];
       const float(*DZ)[KP] = sm.wk[c & 1].X;
-      const int ib0 = wave == 7 ? 0 : wave == 1 ? 2 : 3;
-      const int nib = wave == 7 ? 2 : 1;
-      for (int ii = 0; ii < nib; ++ii) {
-        const int ib = ib0 + ii;
+      const int p0 = wave == 7 ? 0 : wave == 0 ? 3 : wave == 1 ? 4 : wave == 5 ? 6 : 7;
+      const int p1 = p0 + (wave == 7 ? 3 : wave == 1 ? 2 : 1);
+      for (int pr = p0; pr < p1; ++pr) {
+        const int ib = pr >> 1, jb0 = 2 * (pr & 1);
         float ay[4], az[4];
         frag_col16(tc.DY, 16 * ib + l16, G, ay);
         frag_col16(DZ, 16 * ib + l16, G, az);
+        f32x4 v[2];
+        float bq[2][4], bk[2][4];
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-          f32x4 v;
+        for (int u = 0; u < 2; ++u) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = sm.Hm[16 * ib + 4 * G + r][16 * jb + l16];
-          float b[4];
-          frag_col16(tc.Q, 16 * jb + l16, G, b);
-          v = mma<4>(ay, b, v);
-          frag_col16(tc.K, 16 * jb + l16, G, b);
-          v = mma<4>(az, b, v);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sm.Hm[16 * ib + 4 * G + r][16 * jb + l16] = v[r];
+          for (int r = 0; r < 4; ++r) v[u][r] = sm.Hm[16 * ib + 4 * G + r][16 * (jb0 + u) + l16];
+          frag_col16(tc.Q, 16 * (jb0 + u) + l16, G, bq[u]);
+          frag_col16(tc.K, 16 * (jb0 + u) + l16, G, bk[u]);
         }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) v[u] = mfma4(ay[ks], bq[u][ks], v[u]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) v[u] = mfma4(az[ks], bk[u][ks], v[u]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sm.Hm[16 * ib + 4 * G + r][16 * (jb0 + u) + l16] = v[u][r];
       }
     }
     __syncthreads();
   }
   // dk of tile 0; dW0 = H; this scan's share of dgamma, dbeta
-  if (wave == 3 && N > 0) {
-    const int n = rows(0);
-    const TileIn& tp = sm.ring[0];
+  if ((wave == 3 || wave == 2) && N > 0) {
+    auto half = [&](auto s0c) {
+      constexpr int s0 = decltype(s0c)::value;
+      const int j0 = s0 == 0 ? 0 : 2;
+      const int n = rows(0);
+      const TileIn& tp = sm.ring[0];
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
+      for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 4 * G + r, j = 16 * jb + l16;
-        if (t < n) dk[bhT * D + t * D + j] = fmaf(-tp.ETA[t], st[4 * jb + r], sm.B2[t][j]);
-      }
+        for (int r = 0; r < 4; ++r) {
+          const int t = 4 * G + r, j = 16 * (j0 + jj) + l16;
+          if (t < n)
+            dk[bhT * D + t * D + j] = fmaf(-tp.ETA[t], st[4 * (s0 + jj) + r], sm.B2[t][j]);
+        }
+    };
+    if (wave == 3)
+      half(std::integral_constant<int, 0>{});
+    else
+      half(std::integral_constant<int, 4>{});
   }
   for (int e = tid; e < D * D; e += NT) dW0[bh * D * D + e] = sm.Hm[e / D][e % D];
   if (wave == 0 && gb_part != nullptr) {
