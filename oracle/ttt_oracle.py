@@ -118,7 +118,7 @@ def inner_grad_vector(z, v, gamma, beta, ln: str, eps: float = EPS):
 
 def ttt_linear_forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None,
                        *, ln: str = LN_ST, dual: bool = False, chunk: int = 16,
-                       eps: float = EPS, dtype=np.float64):
+                       eps: float = EPS, dtype=np.float64, update_mask=None):
     """The TTT-Linear scan, token by token.
 
     Shapes (row-major): q, k, v, gate_logit [B,H,T,d]; eta_logit [B,H,T];
@@ -137,9 +137,16 @@ def ttt_linear_forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None
       W       = W - eta_t * delta_t k_t^T
       o_t     = (W q_t) * sigmoid(gate_logit_t)    (updated W, sigmoid gate)
 
+    ``update_mask`` (dual mode only): [B,H,ceil(T/chunk)], one SKIP (0) /
+    UPDATE (nonzero) decision per chunk ("PonderTTT", "Core Idea" and
+    "Technical Architecture": learned SKIP/UPDATE decisions per input
+    chunk).  A skipped chunk applies no update: its tokens take eta_t = 0, so
+    W passes the chunk unchanged and the chunk's outputs read W_c q_t.
+
     Parity: pinned (eta -> 0 closed form, delta-rule unrolled product,
     autograd inner-gradient steps, finite differences, dual-form special
-    cases, overwrite and cancellation identities, resume, independence).
+    cases, overwrite and cancellation identities, resume, independence; the
+    mask against eta_logit = -inf on its skipped chunks).
     """
     f = lambda a: None if a is None else np.asarray(a, dtype=dtype)
     q, k, v, eta_logit, gate_logit, W0 = map(f, (q, k, v, eta_logit, gate_logit, W0))
@@ -149,6 +156,13 @@ def ttt_linear_forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None
         beta = f(beta)[None, :, :]
     if dual and chunk < 1:
         raise ValueError("chunk must be >= 1 in dual mode")
+    keep = None
+    if update_mask is not None:
+        if not dual:
+            raise ValueError("update_mask needs dual mode")
+        keep = np.asarray(update_mask) != 0
+        if keep.shape != (B, H, -(-T // chunk)):
+            raise ValueError(f"update_mask must be [B,H,ceil(T/chunk)], got {keep.shape}")
 
     W = W0.copy()
     out = np.zeros((B, H, T, d), dtype=dtype)
@@ -163,6 +177,8 @@ def ttt_linear_forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None
         z = np.matmul(P, kt[..., None])[..., 0]
         delta = inner_grad_vector(z, v[:, :, t, :], gamma, beta, ln, eps)
         eta = eta_all[:, :, t][..., None, None]
+        if keep is not None:
+            eta = np.where(keep[:, :, t // chunk][..., None, None], eta, dtype(0))
         W = W - eta * (delta[..., :, None] * kt[..., None, :])
         out[:, :, t, :] = np.matmul(W, q[:, :, t, :][..., None])[..., 0] * gate_all[:, :, t, :]
     return out, W

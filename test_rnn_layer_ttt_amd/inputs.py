@@ -142,3 +142,11 @@ def make_cotangents(B: int, H: int, T: int, d: int, seed: int, *, with_state: bo
     dout = rng.standard_normal((B, H, T, d), dtype=np.float32)
     dWf = rng.standard_normal((B, H, d, d), dtype=np.float32) if with_state else None
     return dout, dWf
+
+
+def make_update_mask(B: int, H: int, T: int, chunk: int, rate: float, seed: int) -> np.ndarray:
+    """Seeded SKIP (0) / UPDATE (1) decisions, one per chunk: uint8
+    [B,H,ceil(T/chunk)], each 1 with probability ``rate``."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n = -(-T // chunk) if T > 0 else 0
+    return (rng.random((B, H, n)) < rate).astype(np.uint8)
