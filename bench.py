@@ -41,15 +41,26 @@ FP32_MATRIX_PEAK_TFLOPS = 157.3  # MFMA fp32, published
 BF16_MATRIX_PEAK_TFLOPS = 2500.0  # dense MFMA bf16, published
 
 
-def algorithmic_work(x):
-    """Compulsory HBM bytes and flops of one launch (counted per token-head)."""
+def algorithmic_work(x, mask=None):
+    """Compulsory HBM bytes and flops of one launch (counted per token-head).
+
+    With a SKIP/UPDATE mask a skipped chunk's tokens need only q and gate in
+    and out written (2 d^2 flops for W_c q); the mask itself is read once."""
     B, H, T, d = x.q.shape
     n = B * H * T
     s_in = 2 if x.in_bf16 else 4
     per_tok_bytes = (4 * d + 1) * s_in + 4 * d        # q,k,v,gate,eta in; out fp32
-    nbytes = n * per_tok_bytes + B * H * 8 * d * d + H * 8 * d
     per_tok_flops = 6 * d * d + (4 * x.chunk * d if x.dual else 0)
-    return n, nbytes, n * per_tok_flops
+    n_skip, extra = 0, 0
+    if mask is not None:
+        skip_tok = np.repeat(mask == 0, x.chunk, axis=-1)[..., :T]
+        n_skip = int(skip_tok.sum())
+        extra = mask.size
+    skip_bytes = 2 * d * s_in + 4 * d
+    nbytes = ((n - n_skip) * per_tok_bytes + n_skip * skip_bytes + B * H * 8 * d * d + H * 8 * d
+              + extra)
+    flops = (n - n_skip) * per_tok_flops + n_skip * 2 * d * d
+    return n, nbytes, flops
 
 
 def backward_work(x):
@@ -83,12 +94,12 @@ def kernel_info(x):
     return name, ("alu" if x.in_bf16 else "hbm")
 
 
-def roofline(x, kernel_ms, traffic, train=False):
+def roofline(x, kernel_ms, traffic, train=False, mask=None):
     if train:
         n, nbytes, flops = backward_work(x)
         name, bound = "bwd_mfma", "hbm"
     else:
-        n, nbytes, flops = algorithmic_work(x)
+        n, nbytes, flops = algorithmic_work(x, mask)
         name, bound = kernel_info(x)
     sec = kernel_ms / 1e3
     if bound == "hbm":
@@ -108,6 +119,7 @@ _CPU_SAMPLE = None
 
 
 _CPU_TRAIN = False
+_CPU_MASK = None
 
 
 def _oracle_worker(idx):
@@ -118,7 +130,8 @@ def _oracle_worker(idx):
     args = (x.q[:, idx], x.k[:, idx], x.v[:, idx], x.eta_logit[:, idx], x.gate_logit[:, idx],
             x.W0[:, idx], x.gamma[idx], x.beta[idx])
     with threadpool_limits(limits=1):
-        oracle.ttt_linear_forward(*args, ln=x.ln, dual=x.dual, chunk=x.chunk)
+        m = None if _CPU_MASK is None else _CPU_MASK[:, idx]
+        oracle.ttt_linear_forward(*args, ln=x.ln, dual=x.dual, chunk=x.chunk, update_mask=m)
         if _CPU_TRAIN:
             dout, dWf = _cotangents(x)
             oracle.ttt_linear_backward(*args, dout[:, idx], dWf[:, idx], ln=x.ln, dual=x.dual,
@@ -132,17 +145,19 @@ def _cotangents(x):
     return make_cotangents(B, H, T, d, seed=x.meta.get("seed", 0) + 1000)
 
 
-def cpu_baseline(x, n_scans, workers, train=False):
+def cpu_baseline(x, n_scans, workers, train=False, mask=None):
     """Time the oracle on ``n_scans`` scans of ``x`` (full length) over ``workers``
     processes; with ``train`` its forward and its backward, as one training pass."""
     import multiprocessing as mp
-    global _CPU_SAMPLE, _CPU_TRAIN
+    global _CPU_SAMPLE, _CPU_TRAIN, _CPU_MASK
     _CPU_TRAIN = train
     B, H, T, d = x.q.shape
     n_scans = min(n_scans, B * H)
     step = max(1, (B * H) // n_scans)
     pairs = [(i // H, i % H) for i in range(0, B * H, step)][:n_scans]
     _CPU_SAMPLE = x.subset(pairs)
+    _CPU_MASK = None if mask is None else np.ascontiguousarray(
+        mask[[p[0] for p in pairs], [p[1] for p in pairs]][None])
     groups = [list(range(w, n_scans, workers)) for w in range(workers)]
     groups = [g for g in groups if g]
     ctx = mp.get_context("fork")
@@ -192,6 +207,9 @@ def main():
     ap.add_argument("--workload", default="h1024_T4096_bf16", choices=sorted(WORKLOADS))
     ap.add_argument("--pass", dest="pass_", default="forward", choices=("forward", "train"),
                     help="forward: the scan; train: recording forward + backward")
+    ap.add_argument("--update-rate", type=float, default=None,
+                    help="dual-form workloads: seeded SKIP/UPDATE decisions per chunk, each "
+                         "UPDATE with this probability (ttt_linear_forward_masked)")
     ap.add_argument("--cpu-scans", type=int, default=None,
                     help="scans of the workload the CPU oracle is timed on "
                          "(default 256 for the forward, 128 for a training pass)")
@@ -217,11 +235,20 @@ def main():
         sys.exit(2)
     if args.cpu_scans is None:
         args.cpu_scans = 128 if train else 256
+    mask_np = None
+    if args.update_rate is not None:
+        if train or not x.dual:
+            print("bench.py: --update-rate needs a dual-form workload and the forward pass",
+                  file=sys.stderr)
+            sys.exit(2)
+        from test_rnn_layer_ttt_amd.inputs import make_update_mask
+        mask_np = make_update_mask(B, H, T, x.chunk, args.update_rate,
+                                   seed=x.meta.get("seed", 0) + 2000)
 
     # the CPU baseline runs before any GPU use (its workers are forked)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(x, args.cpu_scans, host_cores(), train)
+        cpu = cpu_baseline(x, args.cpu_scans, host_cores(), train, mask_np)
 
     import torch
 
@@ -241,10 +268,20 @@ def main():
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), el.data_ptr(), gl.data_ptr(),
             W0.data_ptr(), gamma.data_ptr(), beta.data_ptr(), out.data_ptr(), Wf.data_ptr())
 
-    def forward():
-        st = ttt.ttt_linear_forward(*ptrs, B, H, T, d, mode, x.chunk, stream.cuda_stream)
-        if st != ttt.TTT_OK:
-            raise RuntimeError(f"ttt_linear_forward: {ttt.ttt_status_string(st)}")
+    if mask_np is None:
+        def forward():
+            st = ttt.ttt_linear_forward(*ptrs, B, H, T, d, mode, x.chunk, stream.cuda_stream)
+            if st != ttt.TTT_OK:
+                raise RuntimeError(f"ttt_linear_forward: {ttt.ttt_status_string(st)}")
+    else:
+        mask_dev = torch.from_numpy(mask_np).to(dev)
+        mptrs = ptrs[:8] + (mask_dev.data_ptr(),) + ptrs[8:]
+
+        def forward():
+            st = ttt.ttt_linear_forward_masked(*mptrs, B, H, T, d, mode, x.chunk,
+                                               stream.cuda_stream)
+            if st != ttt.TTT_OK:
+                raise RuntimeError(f"ttt_linear_forward_masked: {ttt.ttt_status_string(st)}")
 
     if train:
         st, rec_bytes = ttt.ttt_linear_record_bytes(B, H, T, d, mode)
@@ -310,7 +347,9 @@ def main():
     n_tok = B * H * T
     kernel = "bwd_mfma" if train else kernel_info(x)[0]
     traffic_key = args.workload + ("/backward" if train else "")
-    kname, roof = roofline(x, avg_kernel_ms, load_traffic(kernel, traffic_key), train)
+    if mask_np is not None:
+        traffic_key = args.workload + f"/update{args.update_rate:g}"
+    kname, roof = roofline(x, avg_kernel_ms, load_traffic(kernel, traffic_key), train, mask_np)
 
     mode_name = ("dual-form chunk %d" % x.chunk if x.dual else "per-token") + \
         {"st": "", "exact": ", exact LN Jacobian", "none": ", no LN"}[x.ln]
@@ -335,6 +374,9 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if mask_np is not None:
+        line["config"]["update_rate"] = args.update_rate
+        line["config"]["chunks_updated"] = float(np.mean(mask_np != 0))
     if train:
         line["config"]["pass"] = "train: recording forward + backward"
         fwd_ms = [s_.elapsed_time(e_) for s_, e_ in zip(fstarts, fends)]

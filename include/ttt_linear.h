@@ -111,6 +111,25 @@ int32_t ttt_linear_validate(const void* q, const void* k, const void* v,
 const char* ttt_linear_kernel(int64_t d, uint32_t mode, int64_t chunk);
 
 /*
+ * The dual-form scan with one SKIP/UPDATE decision per chunk ("PonderTTT",
+ * "Core Idea" and "Technical Architecture": instead of updating on every
+ * chunk, learned SKIP/UPDATE decisions pick the chunks that update).
+ * update_mask is [B,H,ceil(T/chunk)] uint8 in device memory: 0 = SKIP, any
+ * other value = UPDATE.  A skipped chunk applies no update: its tokens take
+ * eta = 0 (exactly what eta_logit = -inf gives), so W passes the chunk
+ * unchanged and its outputs are (W_c q_t) * sigmoid(gate).  Every other
+ * argument is as in ttt_linear_forward.  mode must include TTT_DUAL
+ * (TTT_ERR_MODE otherwise); update_mask may be NULL only when T == 0 and must
+ * not overlap out or W_final (TTT_ERR_ALIAS).  update_mask is read-only.
+ */
+int32_t ttt_linear_forward_masked(const void* q, const void* k, const void* v,
+                                  const void* eta_logit, const void* gate_logit,
+                                  const float* W0, const float* gamma, const float* beta,
+                                  const uint8_t* update_mask, float* out, float* W_final,
+                                  int64_t B, int64_t H, int64_t T, int64_t d,
+                                  uint32_t mode, int64_t chunk, void* stream);
+
+/*
  * ---- Training: a recording forward and the backward pass ----
  *
  * The backward gives the gradients of a scalar loss L with respect to every

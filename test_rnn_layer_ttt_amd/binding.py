@@ -31,7 +31,8 @@ TTT_ERR_HIP = 6
 TTT_ERR_WORKSPACE = 7
 
 #: every symbol the header declares
-EXPORTED = ("ttt_linear_backward", "ttt_linear_forward", "ttt_linear_forward_record",
+EXPORTED = ("ttt_linear_backward", "ttt_linear_forward", "ttt_linear_forward_masked",
+            "ttt_linear_forward_record",
             "ttt_linear_kernel", "ttt_linear_record_bytes", "ttt_linear_validate",
             "ttt_status_string", "ttt_version")
 
@@ -70,6 +71,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ttt_status_string.argtypes = [ctypes.c_int32]
     lib.ttt_version.restype = ctypes.c_char_p
     lib.ttt_version.argtypes = []
+    lib.ttt_linear_forward_masked.restype = ctypes.c_int32
+    lib.ttt_linear_forward_masked.argtypes = [ctypes.c_void_p] * 11 + [ctypes.c_int64] * 4 + [
+        ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p]
     lib.ttt_linear_record_bytes.restype = ctypes.c_int32
     lib.ttt_linear_record_bytes.argtypes = [ctypes.c_int64] * 4 + [
         ctypes.c_uint32, ctypes.POINTER(ctypes.c_int64)]
@@ -119,6 +123,17 @@ def ttt_linear_validate(q, k, v, eta_logit, gate_logit, W0, gamma, beta, out, W_
     return int(lib.ttt_linear_validate(
         p(q), p(k), p(v), p(eta_logit), p(gate_logit), p(W0), p(gamma), p(beta), p(out),
         p(W_final), int(B), int(H), int(T), int(d), ctypes.c_uint32(int(mode)), int(chunk)))
+
+
+def ttt_linear_forward_masked(q, k, v, eta_logit, gate_logit, W0, gamma, beta, update_mask,
+                              out, W_final, B, H, T, d, mode, chunk, stream) -> int:
+    """The dual-form scan with per-chunk SKIP/UPDATE decisions (raw pointers)."""
+    lib = load_library()
+    p = lambda x: None if x is None else ctypes.c_void_p(int(x))
+    return int(lib.ttt_linear_forward_masked(
+        p(q), p(k), p(v), p(eta_logit), p(gate_logit), p(W0), p(gamma), p(beta), p(update_mask),
+        p(out), p(W_final), int(B), int(H), int(T), int(d), ctypes.c_uint32(int(mode)),
+        int(chunk), p(stream)))
 
 
 def ttt_linear_record_bytes(B, H, T, d, mode):
@@ -179,14 +194,16 @@ def mode_bits(ln: str = "st", dual: bool = False, in_bf16: bool = False) -> int:
 
 
 def forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln: str = "st",
-            dual: bool = False, chunk: int = 16, out=None, W_final=None, stream=None):
+            dual: bool = False, chunk: int = 16, out=None, W_final=None, stream=None,
+            update_mask=None):
     """Run the scan on torch device tensors; returns ``(out, W_final)``.
 
     q, k, v, gate_logit: [B,H,T,d] and eta_logit: [B,H,T], all float32 or all
     bfloat16; W0: [B,H,d,d] float32; gamma, beta: [H,d] float32 (not needed
     with ``ln="none"``).  ``out`` and ``W_final`` are allocated when not given
     (``W_final=W0`` updates the state in place).  Runs on ``stream`` (a
-    ``torch.cuda.Stream``) or on the current stream.
+    ``torch.cuda.Stream``) or on the current stream.  ``update_mask`` (dual
+    form only): uint8 [B,H,ceil(T/chunk)], 0 = SKIP the chunk's updates.
     """
     import torch
 
@@ -197,12 +214,22 @@ def forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln: st
         W_final = torch.empty_like(W0)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    status = ttt_linear_forward(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(eta_logit), _ptr(gate_logit), W0.data_ptr(),
-        _ptr(gamma) if ln != "none" else None, _ptr(beta) if ln != "none" else None,
-        _ptr(out), W_final.data_ptr(), B, H, T, d,
-        mode_bits(ln, dual, q.dtype == torch.bfloat16), chunk if dual else 1,
-        stream.cuda_stream)
+    mode = mode_bits(ln, dual, q.dtype == torch.bfloat16)
+    gb = (_ptr(gamma) if ln != "none" else None, _ptr(beta) if ln != "none" else None)
+    if update_mask is not None:
+        nc = -(-T // chunk) if T > 0 else 0
+        if (update_mask.dtype != torch.uint8 or tuple(update_mask.shape) != (B, H, nc)
+                or not update_mask.is_contiguous() or not update_mask.is_cuda):
+            raise ValueError(f"update_mask must be a contiguous uint8 device tensor [B,H,{nc}]")
+        status = ttt_linear_forward_masked(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(eta_logit), _ptr(gate_logit), W0.data_ptr(), *gb,
+            _ptr(update_mask), _ptr(out), W_final.data_ptr(), B, H, T, d, mode, chunk,
+            stream.cuda_stream)
+    else:
+        status = ttt_linear_forward(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(eta_logit), _ptr(gate_logit), W0.data_ptr(), *gb,
+            _ptr(out), W_final.data_ptr(), B, H, T, d, mode, chunk if dual else 1,
+            stream.cuda_stream)
     check(status)
     return out, W_final
 

@@ -31,6 +31,9 @@ struct ScanArgs {
   // nullptr: not recorded
   float* rec_delta = nullptr;
   float* rec_W = nullptr;
+  // dual form: one SKIP (0) / UPDATE (nonzero) decision per chunk,
+  // [B,H,ceil(T/chunk)]; a skipped chunk's tokens take eta = 0.  nullptr: all update
+  const uint8_t* upd_mask = nullptr;
 };
 
 // One validated backward call (d = 64, per-token modes).

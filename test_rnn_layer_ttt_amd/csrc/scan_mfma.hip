@@ -204,7 +204,7 @@ struct Stage {
 template <bool BF16>
 __device__ __forceinline__ void load_tile(Stage<BF16>& st, const void* const src[4],
                                           const void* etap, int64_t bhT, int64_t t0, int64_t T,
-                                          int lane) {
+                                          int lane, const uint8_t* mrow) {
   using In = typename std::conditional<BF16, uint16_t, float>::type;
   using S = Stage<BF16>;
 #pragma unroll
@@ -225,6 +225,9 @@ __device__ __forceinline__ void load_tile(Stage<BF16>& st, const void* const src
       st.eta = *e;
     else
       st.eta = __float_as_uint(*e);
+    // a skipped chunk (the dual form's chunk is the tile): eta_logit = -inf,
+    // whose sigmoid is exactly 0
+    if (mrow != nullptr && mrow[t0 / BT] == 0) st.eta = BF16 ? 0xFF80u : 0xFF800000u;
   }
 }
 
@@ -642,7 +645,8 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
                  const void* __restrict__ gatep, const float* __restrict__ W0,
                  const float* __restrict__ gamma, const float* __restrict__ beta,
                  float* __restrict__ out, float* __restrict__ W_final, int H, int64_t T,
-                 float eps, float* __restrict__ rec_delta, float* __restrict__ rec_W) {
+                 float eps, float* __restrict__ rec_delta, float* __restrict__ rec_W,
+                 const uint8_t* __restrict__ upd_mask) {
   static_assert(!(REC && DUAL), "the record is kept for the per-token modes");
   __shared__ Smem<BF16> sm;
   const int tid = threadIdx.x;
@@ -656,6 +660,7 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   const void* const src[4] = {qp, kp, vp, gatep};
   const int64_t ntiles = (T + BT - 1) / BT;
   using R = Roles<BF16, DUAL>;
+  const uint8_t* mrow = (DUAL && upd_mask != nullptr) ? upd_mask + bh * ntiles : nullptr;
   const int slice = R::slice_of(wave);
   const int irow = 16 * slice + l16;   // W row (feature i) held by this lane, slice waves
 
@@ -695,10 +700,10 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   if (stage_parity >= 0) {
     const int u = stage_parity;
     if (u < ntiles) {
-      load_tile<BF16>(st, src, etap, bhT, u * BT, T, lane);
+      load_tile<BF16>(st, src, etap, bhT, u * BT, T, lane, mrow);
       store_tile<BF16, LN>(st, sm.ring[u], u * BT, T, lane, sb);
     }
-    if (u + 2 < ntiles) load_tile<BF16>(st, src, etap, bhT, (u + 2) * BT, T, lane);
+    if (u + 2 < ntiles) load_tile<BF16>(st, src, etap, bhT, (u + 2) * BT, T, lane, mrow);
   }
   __syncthreads();
   // z of tile 0 and its coefficients
@@ -819,7 +824,7 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
           if (c + 2 < ntiles)
             store_tile<BF16, LN>(st, sm.ring[(c + 2) % RING], (c + 2) * BT, T, lane, sb);
         } else if (c + 3 < ntiles) {
-          load_tile<BF16>(st, src, etap, bhT, (c + 3) * BT, T, lane);
+          load_tile<BF16>(st, src, etap, bhT, (c + 3) * BT, T, lane, mrow);
         }
       }
       if (wave == R::kOutWave && c >= 2)
@@ -897,14 +902,15 @@ hipError_t launch_one(const ScanArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((scan_mfma_kernel<BF16, LN, false, true>),
                          dim3(static_cast<unsigned>(a.B * a.H)), dim3(NT), 0, s, a.q, a.k, a.v,
                          a.eta_logit, a.gate_logit, a.W0, a.gamma, a.beta, a.out, a.W_final,
-                         static_cast<int>(a.H), a.T, a.eps, a.rec_delta, a.rec_W);
+                         static_cast<int>(a.H), a.T, a.eps, a.rec_delta, a.rec_W,
+                         static_cast<const uint8_t*>(nullptr));
       return hipGetLastError();
     }
   }
   hipLaunchKernelGGL((scan_mfma_kernel<BF16, LN, DUAL, false>), dim3(static_cast<unsigned>(a.B * a.H)),
                      dim3(NT), 0, s, a.q, a.k, a.v, a.eta_logit, a.gate_logit, a.W0, a.gamma,
                      a.beta, a.out, a.W_final, static_cast<int>(a.H), a.T, a.eps,
-                     static_cast<float*>(nullptr), static_cast<float*>(nullptr));
+                     static_cast<float*>(nullptr), static_cast<float*>(nullptr), a.upd_mask);
   return hipGetLastError();
 }
 

@@ -82,7 +82,8 @@ scan_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
                  const void* __restrict__ gatep, const float* __restrict__ W0,
                  const float* __restrict__ gamma, const float* __restrict__ beta,
                  float* __restrict__ out, float* __restrict__ W_final,
-                 int H, int64_t T, int64_t chunk, float eps) {
+                 int H, int64_t T, int64_t chunk, float eps,
+                 const uint8_t* __restrict__ upd_mask) {
   using In = typename std::conditional<BF16, uint16_t, float>::type;
   constexpr int NT = 4 * D;               // threads
   constexpr int NW = NT / 64;             // waves
@@ -115,6 +116,9 @@ scan_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
                       static_cast<const In*>(vp) + bh * T * D,
                       static_cast<const In*>(gatep) + bh * T * D};
   const In* eta = static_cast<const In*>(etap) + bh * T;
+  // dual form: SKIP (0) / UPDATE decisions of this scan's chunks
+  const uint8_t* mrow =
+      (DUAL && upd_mask != nullptr) ? upd_mask + bh * ((T + chunk - 1) / chunk) : nullptr;
   float* dst_out = out + bh * T * D;
 
   float W[C];
@@ -158,6 +162,8 @@ scan_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
           x = __uint_as_float(static_cast<uint32_t>(eta[t]) << 16);
         else
           x = eta[t];
+        // a skipped chunk: eta_logit = -inf, whose sigmoid is exactly 0
+        if (mrow != nullptr && mrow[t / chunk] == 0) x = -__builtin_huge_valf();
       }
       pre_eta[r] = x;
     }
@@ -304,7 +310,8 @@ hipError_t launch_one(const ScanArgs& a, hipStream_t s) {
   const dim3 block(4 * D);
   hipLaunchKernelGGL((scan_valu_kernel<D, BF16, LN, DUAL>), grid, block, 0, s, a.q, a.k, a.v,
                      a.eta_logit, a.gate_logit, a.W0, a.gamma, a.beta, a.out, a.W_final,
-                     static_cast<int>(a.H), a.T, a.dual ? a.chunk : int64_t(1), a.eps);
+                     static_cast<int>(a.H), a.T, a.dual ? a.chunk : int64_t(1), a.eps,
+                     a.upd_mask);
   return hipGetLastError();
 }
 

@@ -326,6 +326,40 @@ extern "C" int32_t ttt_linear_forward(const void* q, const void* k, const void* 
   return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
+extern "C" int32_t ttt_linear_forward_masked(const void* q, const void* k, const void* v,
+                                             const void* eta_logit, const void* gate_logit,
+                                             const float* W0, const float* gamma,
+                                             const float* beta, const uint8_t* update_mask,
+                                             float* out, float* W_final, int64_t B, int64_t H,
+                                             int64_t T, int64_t d, uint32_t mode, int64_t chunk,
+                                             void* stream) {
+  ttt::ScanArgs a;
+  const int32_t st = validate(q, k, v, eta_logit, gate_logit, W0, gamma, beta, out, W_final,
+                              B, H, T, d, mode, chunk, &a);
+  if (st != TTT_OK) return st;
+  if (!(mode & TTT_DUAL)) return TTT_ERR_MODE;
+  if (T > 0 && update_mask == nullptr) return TTT_ERR_NULL;
+  // validate() bounded B*H*T*d, so these products cannot overflow
+  const int64_t mask_bytes = T > 0 ? B * H * ((T + chunk - 1) / chunk) : 0;
+  const Range r_mask = span(update_mask, mask_bytes);
+  if (overlaps(r_mask, span(out, T > 0 ? B * H * T * d * 4 : 0)) ||
+      overlaps(r_mask, span(W_final, W_final ? B * H * d * d * 4 : 0)))
+    return TTT_ERR_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    if (W_final && W_final != W0) {
+      const size_t bytes = static_cast<size_t>(B * H * d * d) * sizeof(float);
+      if (hipMemcpyAsync(W_final, W0, bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        return TTT_ERR_HIP;
+    }
+    return TTT_OK;
+  }
+  a.upd_mask = update_mask;
+  const hipError_t err = ttt::scan_mfma_supports(a) ? ttt::launch_scan_mfma(a, s)
+                                                    : ttt::launch_scan_valu(a, s);
+  return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
 extern "C" int32_t ttt_linear_record_bytes(int64_t B, int64_t H, int64_t T, int64_t d,
                                            uint32_t mode, int64_t* bytes) {
   if (bytes == nullptr) return TTT_ERR_NULL;
