@@ -63,6 +63,19 @@ def sigmoid(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def silu(x: np.ndarray) -> np.ndarray:
+    """SiLU, x * sigmoid(x): the activation the `:mlp` variant of
+    "Edifice.Recurrent.TTT" (Options, `:variant`) applies to keys and queries
+    before the inner model.  Pinned against torch's silu."""
+    return np.asarray(x) * sigmoid(x)
+
+
+def silu_grad(x: np.ndarray) -> np.ndarray:
+    """d silu / dx = sigmoid(x) (1 + x (1 - sigmoid(x))).  Pinned by autograd."""
+    s = sigmoid(x)
+    return s * (1.0 + np.asarray(x) * (1.0 - s))
+
+
 def layer_norm(z: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float = EPS):
     """Learnable LayerNorm over the last axis.
 
@@ -118,7 +131,8 @@ def inner_grad_vector(z, v, gamma, beta, ln: str, eps: float = EPS):
 
 def ttt_linear_forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None,
                        *, ln: str = LN_ST, dual: bool = False, chunk: int = 16,
-                       eps: float = EPS, dtype=np.float64, update_mask=None):
+                       eps: float = EPS, dtype=np.float64, update_mask=None,
+                       silu_qk: bool = False):
     """The TTT-Linear scan, token by token.
 
     Shapes (row-major): q, k, v, gate_logit [B,H,T,d]; eta_logit [B,H,T];
@@ -137,6 +151,11 @@ def ttt_linear_forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None
       W       = W - eta_t * delta_t k_t^T
       o_t     = (W q_t) * sigmoid(gate_logit_t)    (updated W, sigmoid gate)
 
+    ``silu_qk``: the `:mlp` variant of "Edifice.Recurrent.TTT" (Options,
+    `:variant`): SiLU is applied to k_t and q_t before the inner model, so
+    z_t = W silu(k_t) and o_t = (W_t silu(q_t)) * sigmoid(g_t); silu(k_t) also
+    takes k_t's place in the update.
+
     ``update_mask`` (dual mode only): [B,H,ceil(T/chunk)], one SKIP (0) /
     UPDATE (nonzero) decision per chunk ("PonderTTT", "Core Idea" and
     "Technical Architecture": learned SKIP/UPDATE decisions per input
@@ -150,6 +169,8 @@ def ttt_linear_forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None
     """
     f = lambda a: None if a is None else np.asarray(a, dtype=dtype)
     q, k, v, eta_logit, gate_logit, W0 = map(f, (q, k, v, eta_logit, gate_logit, W0))
+    if silu_qk:
+        q, k = silu(q), silu(k)
     B, H, T, d = q.shape
     if ln != LN_NONE:
         gamma = f(gamma)[None, :, :]   # [1,H,d], broadcast over batch
@@ -245,7 +266,7 @@ def inner_grad_vector_vjp(dd, z, v, gamma, beta, ln: str, eps: float = EPS):
 
 def ttt_linear_backward(q, k, v, eta_logit, gate_logit, W0, gamma, beta, dout, dW_final=None,
                         *, ln: str = LN_ST, dual: bool = False, chunk: int = 16,
-                        eps: float = EPS, dtype=np.float64):
+                        eps: float = EPS, dtype=np.float64, silu_qk: bool = False):
     """Gradients of the scan: reverse-mode through ``ttt_linear_forward``.
 
     For a loss L with dL/d out = ``dout`` [B,H,T,d] and dL/d W_final =
@@ -269,11 +290,16 @@ def ttt_linear_backward(q, k, v, eta_logit, gate_logit, W0, gamma, beta, dout, d
         -> dP += dz_t k_t^T,  dk_t += P^T dz_t
 
     In the dual form dP accumulates over the chunk and joins dW at the
-    chunk's first token.  Parity: pinned by central finite differences of
-    the forward and by autograd (``tests/test_oracle_backward.py``).
+    chunk's first token.  With ``silu_qk`` the walk runs on silu(q), silu(k)
+    and the last step multiplies dq, dk by silu'(q), silu'(k).  Parity: pinned
+    by central finite differences of the forward and by autograd
+    (``tests/test_oracle_backward.py``, ``tests/test_oracle_silu.py``).
     """
     f = lambda a: None if a is None else np.asarray(a, dtype=dtype)
     q, k, v, eta_logit, gate_logit, W0, dout = map(f, (q, k, v, eta_logit, gate_logit, W0, dout))
+    q_in, k_in = q, k
+    if silu_qk:
+        q, k = silu(q), silu(k)
     B, H, T, d = q.shape
     has_ln = ln != LN_NONE
     if has_ln:
@@ -340,6 +366,9 @@ def ttt_linear_backward(q, k, v, eta_logit, gate_logit, W0, gamma, beta, dout, d
                 dP = np.zeros_like(dP)
         else:
             dW = dW + outer(dz, kt)
+    if silu_qk:
+        g["dq"] = g["dq"] * silu_grad(q_in)
+        g["dk"] = g["dk"] * silu_grad(k_in)
     g["dW0"] = dW
     g["dgamma"] = dgamma.sum(axis=0) if has_ln else None
     g["dbeta"] = dbeta.sum(axis=0) if has_ln else None

@@ -58,11 +58,14 @@ def test_backward_matches_finite_differences(ln, dual, chunk):
         assert err < 1e-6, f"{name}: finite-difference mismatch {err:.2e}"
 
 
-def _torch_forward(x, ln, dual, chunk, eps=oracle.EPS):
+def _torch_forward(x, ln, dual, chunk, eps=oracle.EPS, silu_qk=False):
     """An independent float64 forward: LayerNorm from torch, the exact inner
-    gradient by autograd, the dual form by an explicit chunk-start copy."""
+    gradient by autograd, the dual form by an explicit chunk-start copy; with
+    ``silu_qk`` torch's silu on keys and queries first."""
     t = {n: torch.tensor(a, dtype=torch.float64, requires_grad=True) for n, a in x.items()}
     q, k, v, el, gl, W = t["q"], t["k"], t["v"], t["eta_logit"], t["gate_logit"], t["W0"]
+    if silu_qk:
+        q, k = torch.nn.functional.silu(q), torch.nn.functional.silu(k)
     B, H, T, d = q.shape
     gam, bet = t["gamma"], t["beta"]
     outs = []
