@@ -120,6 +120,7 @@ _CPU_SAMPLE = None
 
 _CPU_TRAIN = False
 _CPU_MASK = None
+_CPU_SILU = False
 
 
 def _oracle_worker(idx):
@@ -131,11 +132,12 @@ def _oracle_worker(idx):
             x.W0[:, idx], x.gamma[idx], x.beta[idx])
     with threadpool_limits(limits=1):
         m = None if _CPU_MASK is None else _CPU_MASK[:, idx]
-        oracle.ttt_linear_forward(*args, ln=x.ln, dual=x.dual, chunk=x.chunk, update_mask=m)
+        oracle.ttt_linear_forward(*args, ln=x.ln, dual=x.dual, chunk=x.chunk, update_mask=m,
+                                  silu_qk=_CPU_SILU)
         if _CPU_TRAIN:
             dout, dWf = _cotangents(x)
             oracle.ttt_linear_backward(*args, dout[:, idx], dWf[:, idx], ln=x.ln, dual=x.dual,
-                                       chunk=x.chunk)
+                                       chunk=x.chunk, silu_qk=_CPU_SILU)
     return len(idx)
 
 
@@ -207,6 +209,8 @@ def main():
     ap.add_argument("--workload", default="h1024_T4096_bf16", choices=sorted(WORKLOADS))
     ap.add_argument("--pass", dest="pass_", default="forward", choices=("forward", "train"),
                     help="forward: the scan; train: recording forward + backward")
+    ap.add_argument("--silu-qk", action="store_true",
+                    help="the :mlp variant: SiLU on q and k before the inner model")
     ap.add_argument("--update-rate", type=float, default=None,
                     help="dual-form workloads: seeded SKIP/UPDATE decisions per chunk, each "
                          "UPDATE with this probability (ttt_linear_forward_masked)")
@@ -218,6 +222,8 @@ def main():
                     help="after the timed region, run one device-to-device copy of this many "
                          "MiB: a kernel of known traffic that scales the HBM byte counters")
     args = ap.parse_args()
+    global _CPU_SILU
+    _CPU_SILU = args.silu_qk
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -264,7 +270,7 @@ def main():
     out = torch.empty((B, H, T, d), dtype=torch.float32, device=dev)
     Wf = torch.empty_like(W0)
     stream = torch.cuda.current_stream(dev)
-    mode = ttt.mode_bits(x.ln, x.dual, x.in_bf16)
+    mode = ttt.mode_bits(x.ln, x.dual, x.in_bf16, args.silu_qk)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), el.data_ptr(), gl.data_ptr(),
             W0.data_ptr(), gamma.data_ptr(), beta.data_ptr(), out.data_ptr(), Wf.data_ptr())
 
@@ -349,6 +355,8 @@ def main():
     traffic_key = args.workload + ("/backward" if train else "")
     if mask_np is not None:
         traffic_key = args.workload + f"/update{args.update_rate:g}"
+    if args.silu_qk:
+        traffic_key += "/silu"
     kname, roof = roofline(x, avg_kernel_ms, load_traffic(kernel, traffic_key), train, mask_np)
 
     mode_name = ("dual-form chunk %d" % x.chunk if x.dual else "per-token") + \
@@ -374,6 +382,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if args.silu_qk:
+        line["config"]["variant"] = "mlp (SiLU on q and k)"
     if mask_np is not None:
         line["config"]["update_rate"] = args.update_rate
         line["config"]["chunks_updated"] = float(np.mean(mask_np != 0))

@@ -61,6 +61,12 @@ extern "C" {
 #define TTT_LN_EXACT  2u  /* LayerNorm Jacobian applied to the error */
 #define TTT_IN_BF16   4u  /* q, k, v, eta_logit, gate_logit are bf16 */
 #define TTT_NO_LN     8u  /* inner LayerNorm removed (delta rule); excludes TTT_LN_EXACT */
+#define TTT_SILU_QK  16u  /* the :mlp variant of "Edifice.Recurrent.TTT" (Options,
+                             :variant): SiLU on k and q before the inner model, so
+                             z_t = P silu(k_t), the update uses silu(k_t) and
+                             out = (W silu(q_t)) * sigmoid(gate); gradients are
+                             with respect to the raw q and k.  On the bf16-input
+                             matrix-core path silu(q), silu(k) are rounded to bf16 */
 
 /* status codes */
 #define TTT_OK               0

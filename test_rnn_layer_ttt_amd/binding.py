@@ -20,6 +20,7 @@ TTT_DUAL = 1
 TTT_LN_EXACT = 2
 TTT_IN_BF16 = 4
 TTT_NO_LN = 8
+TTT_SILU_QK = 16
 
 TTT_OK = 0
 TTT_ERR_NULL = 1
@@ -178,8 +179,9 @@ def check(status: int) -> None:
     raise TTTArgumentError(status, msg)
 
 
-def mode_bits(ln: str = "st", dual: bool = False, in_bf16: bool = False) -> int:
-    m = 0
+def mode_bits(ln: str = "st", dual: bool = False, in_bf16: bool = False,
+              silu_qk: bool = False) -> int:
+    m = TTT_SILU_QK if silu_qk else 0
     if dual:
         m |= TTT_DUAL
     if in_bf16:
@@ -195,7 +197,7 @@ def mode_bits(ln: str = "st", dual: bool = False, in_bf16: bool = False) -> int:
 
 def forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln: str = "st",
             dual: bool = False, chunk: int = 16, out=None, W_final=None, stream=None,
-            update_mask=None):
+            update_mask=None, silu_qk: bool = False):
     """Run the scan on torch device tensors; returns ``(out, W_final)``.
 
     q, k, v, gate_logit: [B,H,T,d] and eta_logit: [B,H,T], all float32 or all
@@ -204,6 +206,7 @@ def forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln: st
     (``W_final=W0`` updates the state in place).  Runs on ``stream`` (a
     ``torch.cuda.Stream``) or on the current stream.  ``update_mask`` (dual
     form only): uint8 [B,H,ceil(T/chunk)], 0 = SKIP the chunk's updates.
+    ``silu_qk``: the :mlp variant (SiLU on q and k before the inner model).
     """
     import torch
 
@@ -214,7 +217,7 @@ def forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln: st
         W_final = torch.empty_like(W0)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    mode = mode_bits(ln, dual, q.dtype == torch.bfloat16)
+    mode = mode_bits(ln, dual, q.dtype == torch.bfloat16, silu_qk)
     gb = (_ptr(gamma) if ln != "none" else None, _ptr(beta) if ln != "none" else None)
     if update_mask is not None:
         nc = -(-T // chunk) if T > 0 else 0
@@ -268,13 +271,14 @@ def _check_inputs(q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln):
 
 
 def forward_record(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *,
-                   ln: str = "st", out=None, W_final=None, record=None, stream=None):
+                   ln: str = "st", out=None, W_final=None, record=None, stream=None,
+                   silu_qk: bool = False):
     """:func:`forward` (per-token modes, d = 64) that also returns the record the
     backward reads: ``(out, W_final, record)``, the record a uint8 device tensor."""
     import torch
 
     B, H, T, d = _check_inputs(q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln)
-    mode = mode_bits(ln, False, q.dtype == torch.bfloat16)
+    mode = mode_bits(ln, False, q.dtype == torch.bfloat16, silu_qk)
     st, nbytes = ttt_linear_record_bytes(B, H, T, d, mode)
     check(st)
     if out is None:
@@ -294,7 +298,7 @@ def forward_record(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *,
 
 
 def backward(q, k, v, eta_logit, gate_logit, gamma, beta, record, dout, dW_final=None, *,
-             ln: str = "st", stream=None):
+             ln: str = "st", stream=None, silu_qk: bool = False):
     """Gradients from a record of :func:`forward_record` and dL/dout (float32
     [B,H,T,d]), dL/dW_final (float32 [B,H,d,d] or None).  Returns a dict with
     dq, dk, dv, dgate_logit, deta_logit, dW0, dgamma, dbeta (float32; the last
@@ -323,14 +327,15 @@ def backward(q, k, v, eta_logit, gate_logit, gamma, beta, record, dout, dW_final
         None if dW_final is None else dW_final.data_ptr(), _ptr(g["dq"]), _ptr(g["dk"]),
         _ptr(g["dv"]), _ptr(g["deta_logit"]), _ptr(g["dgate_logit"]), g["dW0"].data_ptr(),
         _ptr(g["dgamma"]), _ptr(g["dbeta"]), B, H, T, d,
-        mode_bits(ln, False, q.dtype == torch.bfloat16), 1, stream.cuda_stream))
+        mode_bits(ln, False, q.dtype == torch.bfloat16, silu_qk), 1, stream.cuda_stream))
     return g
 
 
 _autograd_fn = None
 
 
-def ttt_linear(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln: str = "st"):
+def ttt_linear(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln: str = "st",
+               silu_qk: bool = False):
     """Differentiable scan for torch autograd: ``(out, W_final)``.
 
     The forward is :func:`forward_record`; the backward is :func:`backward`
@@ -343,10 +348,11 @@ def ttt_linear(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln:
 
         class TTTLinearFunction(torch.autograd.Function):
             @staticmethod
-            def forward(ctx, q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln):
+            def forward(ctx, q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln, silu_qk):
                 out, W_final, record = forward_record(q, k, v, eta_logit, gate_logit, W0, gamma,
-                                                      beta, ln=ln)
+                                                      beta, ln=ln, silu_qk=silu_qk)
                 ctx.ln = ln
+                ctx.silu_qk = silu_qk
                 ctx.save_for_backward(q, k, v, eta_logit, gate_logit, gamma, beta, record)
                 return out, W_final
 
@@ -359,11 +365,11 @@ def ttt_linear(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln:
                 g = backward(q, k, v, eta_logit, gate_logit, gamma, beta, record,
                              dout.contiguous().float(),
                              None if dW_final is None else dW_final.contiguous().float(),
-                             ln=ctx.ln)
+                             ln=ctx.ln, silu_qk=ctx.silu_qk)
                 return (g["dq"], g["dk"], g["dv"], g["deta_logit"], g["dgate_logit"], g["dW0"],
-                        g["dgamma"], g["dbeta"], None)
+                        g["dgamma"], g["dbeta"], None, None)
 
         _autograd_fn = TTTLinearFunction
     if ln == "none":
         gamma = beta = None
-    return _autograd_fn.apply(q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln)
+    return _autograd_fn.apply(q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln, silu_qk)

@@ -184,6 +184,20 @@ __device__ __forceinline__ void store_block(float (*o)[P], int col0, f32x4 v, in
   for (int r = 0; r < 4; ++r) o[4 * G + r][col0 + l16] = v[r];
 }
 
+// The :mlp variant's SiLU on q and k, as the forward applies it: in fp32, and
+// on the bf16-input path rounded back to bf16 (to nearest even), so that the
+// backward differentiates the function the forward computed.
+template <bool BF16>
+__device__ __forceinline__ float silu_in(float x) {
+  const float y = x * sigmoidf_(x);
+  if constexpr (BF16) {
+    const __bf16 b = static_cast<__bf16>(y);
+    return __uint_as_float(static_cast<uint32_t>(__builtin_bit_cast(unsigned short, b)) << 16);
+  } else {
+    return y;
+  }
+}
+
 template <bool BF16>
 __device__ __forceinline__ float ld_in(const void* p, int64_t i) {
   if constexpr (BF16)
@@ -278,7 +292,7 @@ __device__ __forceinline__ void loader_issue(float (&st)[kState], float& eta, in
 
 template <bool BF16>
 __device__ __forceinline__ void loader_store(const float (&st)[kState], float eta, int n,
-                                             TileIn& tl, int lane) {
+                                             TileIn& tl, int lane, bool silu) {
   using L = LoadLayout<BF16>;
   const int t = lane >> 2, f0 = 16 * (lane & 3);
 #pragma unroll
@@ -293,6 +307,10 @@ __device__ __forceinline__ void loader_store(const float (&st)[kState], float et
     for (int u = 0; u < 4; ++u) {
       qv[u] = in16<BF16>(&st[L::kQ], i + u);
       kv[u] = in16<BF16>(&st[L::kK], i + u);
+      if (silu) {
+        qv[u] = silu_in<BF16>(qv[u]);
+        kv[u] = silu_in<BF16>(kv[u]);
+      }
       const float sg = sigmoidf_(in16<BF16>(&st[L::kG], i + u));
       yv[u] = t < n ? st[L::kDout + i + u] * sg : 0.0f;
       gv[u] = yv[u] * (1.0f - sg);
@@ -342,7 +360,7 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
                 const float* __restrict__ rec_W, float* __restrict__ dq, float* __restrict__ dk,
                 float* __restrict__ dv, float* __restrict__ deta, float* __restrict__ dgate,
                 float* __restrict__ dW0, float* __restrict__ gb_part, int H, int64_t T,
-                float eps) {
+                float eps, int silu) {
   __shared__ BwdSmem sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -366,8 +384,10 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       const int t = e / D, i = e % D;
       const bool in = t < n;
       const int64_t g = (bhT + int64_t(c) * BT + t) * D + i;
-      tl.Q[t][i] = in ? ld_in<BF16>(qp, g) : 0.0f;
-      tl.K[t][i] = in ? ld_in<BF16>(kp, g) : 0.0f;
+      const float qv = in ? ld_in<BF16>(qp, g) : 0.0f;
+      const float kv = in ? ld_in<BF16>(kp, g) : 0.0f;
+      tl.Q[t][i] = silu ? silu_in<BF16>(qv) : qv;
+      tl.K[t][i] = silu ? silu_in<BF16>(kv) : kv;
       const float sg = in ? sigmoidf_(ld_in<BF16>(gatep, g)) : 0.0f;
       tl.DY[t][i] = in ? dout[g] * sg : 0.0f;
       tl.G2[t][i] = tl.DY[t][i] * (1.0f - sg);
@@ -617,7 +637,7 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
     // ============================ phase B ============================
     if (wave == 4 && c >= 2) {
       const int u = c - 2;
-      loader_store<BF16>(st, ld_eta, ld_n, sm.ring[u % 3], lane);
+      loader_store<BF16>(st, ld_eta, ld_n, sm.ring[u % 3], lane, silu != 0);
     }
     if (wave == 7 && c >= 2) w_store(st, sm.W[(c - 2) & 1], lane);
     if (wave == 1 && prep) {
@@ -913,6 +933,19 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   }
 }
 
+// the :mlp variant: the gradients computed for silu(q), silu(k) times
+// silu'(x) = sigmoid(x) (1 + x (1 - sigmoid(x))) at the raw inputs
+template <bool BF16>
+__global__ void silu_grad_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
+                                 float* __restrict__ dq, float* __restrict__ dk, int64_t n) {
+  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (i >= n) return;
+  const float q = ld_in<BF16>(qp, i), k = ld_in<BF16>(kp, i);
+  const float sq = sigmoidf_(q), sk = sigmoidf_(k);
+  dq[i] *= sq * fmaf(q, 1.0f - sq, 1.0f);
+  dk[i] *= sk * fmaf(k, 1.0f - sk, 1.0f);
+}
+
 // dgamma[h][i] = sum over the batch of the per-scan parts, dbeta likewise (fixed order)
 __global__ void gamma_beta_sum_kernel(const float* __restrict__ gb_part, float* __restrict__ dgamma,
                                       float* __restrict__ dbeta, int64_t B, int64_t H) {
@@ -934,9 +967,17 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
                      0, s, a.q, a.k, a.v, a.eta_logit, a.gate_logit, a.gamma, a.beta, a.dout,
                      a.dW_final, a.rec_delta, a.rec_W, a.dq, a.dk, a.dv, a.deta_logit,
                      a.dgate_logit, a.dW0, LN == kLnNone ? nullptr : a.gb_part,
-                     static_cast<int>(a.H), a.T, a.eps);
+                     static_cast<int>(a.H), a.T, a.eps, a.silu_qk ? 1 : 0);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || LN == kLnNone) return err;
+  if (err != hipSuccess) return err;
+  if (a.silu_qk && a.T > 0) {
+    const int64_t n = a.B * a.H * a.T * D;
+    hipLaunchKernelGGL((silu_grad_kernel<BF16>), dim3(static_cast<unsigned>((n + 255) / 256)),
+                       dim3(256), 0, s, a.q, a.k, a.dq, a.dk, n);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (LN == kLnNone) return hipSuccess;
   const int64_t n = a.H * D;
   hipLaunchKernelGGL(gamma_beta_sum_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
                      0, s, a.gb_part, a.dgamma, a.dbeta, a.B, a.H);

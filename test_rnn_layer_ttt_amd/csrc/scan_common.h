@@ -34,6 +34,8 @@ struct ScanArgs {
   // dual form: one SKIP (0) / UPDATE (nonzero) decision per chunk,
   // [B,H,ceil(T/chunk)]; a skipped chunk's tokens take eta = 0.  nullptr: all update
   const uint8_t* upd_mask = nullptr;
+  // the :mlp variant: SiLU applied to q and k before the inner model
+  bool silu_qk = false;
 };
 
 // One validated backward call (d = 64, per-token modes).
@@ -63,6 +65,7 @@ struct BwdArgs {
   bool dual;
   bool in_bf16;
   float eps;
+  bool silu_qk = false;   // the :mlp variant (SiLU on q and k)
 };
 
 // Tokens per tile of the recorded W (and of the backward's reverse walk).

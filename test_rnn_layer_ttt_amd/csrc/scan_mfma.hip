@@ -233,10 +233,20 @@ __device__ __forceinline__ void load_tile(Stage<BF16>& st, const void* const src
 
 // sb[e]: beta of feature j0 + e (the same features for every vector of a
 // lane), or 0 without LayerNorm, where VB holds v itself.
+// silu(x) = x sigmoid(x) on two packed bf16 values, each result rounded to bf16
+__device__ __forceinline__ uint32_t silu_bf16x2(uint32_t w) {
+  const float a = __uint_as_float(w << 16), b = __uint_as_float(w & 0xFFFF0000u);
+  return static_cast<uint32_t>(bf16_bits(a * fast_sigmoid(a))) |
+         (static_cast<uint32_t>(bf16_bits(b * fast_sigmoid(b))) << 16);
+}
+
+// silu: the :mlp variant's SiLU on q and k (on the bf16 path the activated
+// values are rounded back to bf16, the matrix cores' operand type)
 template <bool BF16, int LN>
 __device__ __forceinline__ void store_tile(const Stage<BF16>& st,
                                            typename Smem<BF16>::Tile& tl, int64_t t0, int64_t T,
-                                           int lane, const float (&sb)[Stage<BF16>::kVE]) {
+                                           int lane, const float (&sb)[Stage<BF16>::kVE],
+                                           bool silu) {
   using S = Stage<BF16>;
   auto vb = [&](float v, int e) { return LN == kLnNone ? v : sb[e] - v; };
 #pragma unroll
@@ -246,8 +256,10 @@ __device__ __forceinline__ void store_tile(const Stage<BF16>& st,
       const int vid = lane + 64 * r;
       const int t = (vid * S::kVE) / D;
       const int j0 = (vid * S::kVE) % D;
-      const uint4 x = st.v[a][r];
+      uint4 x = st.v[a][r];
       if constexpr (BF16) {
+        if (silu && a <= 1)
+          x = make_uint4(silu_bf16x2(x.x), silu_bf16x2(x.y), silu_bf16x2(x.z), silu_bf16x2(x.w));
         const uint32_t w[4] = {x.x, x.y, x.z, x.w};
         if (a <= 1) {
           uint16_t(*dst)[64][8] = (a == 0) ? tl.QA : tl.KA;
@@ -278,8 +290,11 @@ __device__ __forceinline__ void store_tile(const Stage<BF16>& st,
           *reinterpret_cast<float4*>(&tl.SG[t][j0 + 4]) = make_float4(f[4], f[5], f[6], f[7]);
         }
       } else {
-        const float4 f = make_float4(__uint_as_float(x.x), __uint_as_float(x.y),
-                                     __uint_as_float(x.z), __uint_as_float(x.w));
+        float4 f = make_float4(__uint_as_float(x.x), __uint_as_float(x.y),
+                               __uint_as_float(x.z), __uint_as_float(x.w));
+        if (silu && a <= 1)
+          f = make_float4(f.x * fast_sigmoid(f.x), f.y * fast_sigmoid(f.y),
+                          f.z * fast_sigmoid(f.z), f.w * fast_sigmoid(f.w));
         if (a == 0) *reinterpret_cast<float4*>(&tl.Q[t][j0]) = f;
         if (a == 1) *reinterpret_cast<float4*>(&tl.K[t][j0]) = f;
         if (a == 2) {
@@ -646,7 +661,7 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
                  const float* __restrict__ gamma, const float* __restrict__ beta,
                  float* __restrict__ out, float* __restrict__ W_final, int H, int64_t T,
                  float eps, float* __restrict__ rec_delta, float* __restrict__ rec_W,
-                 const uint8_t* __restrict__ upd_mask) {
+                 const uint8_t* __restrict__ upd_mask, int silu) {
   static_assert(!(REC && DUAL), "the record is kept for the per-token modes");
   __shared__ Smem<BF16> sm;
   const int tid = threadIdx.x;
@@ -701,7 +716,7 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
     const int u = stage_parity;
     if (u < ntiles) {
       load_tile<BF16>(st, src, etap, bhT, u * BT, T, lane, mrow);
-      store_tile<BF16, LN>(st, sm.ring[u], u * BT, T, lane, sb);
+      store_tile<BF16, LN>(st, sm.ring[u], u * BT, T, lane, sb, silu != 0);
     }
     if (u + 2 < ntiles) load_tile<BF16>(st, src, etap, bhT, (u + 2) * BT, T, lane, mrow);
   }
@@ -822,7 +837,8 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         // the last wave's arrival.
         if ((c & 1) == stage_parity) {
           if (c + 2 < ntiles)
-            store_tile<BF16, LN>(st, sm.ring[(c + 2) % RING], (c + 2) * BT, T, lane, sb);
+            store_tile<BF16, LN>(st, sm.ring[(c + 2) % RING], (c + 2) * BT, T, lane, sb,
+                                 silu != 0);
         } else if (c + 3 < ntiles) {
           load_tile<BF16>(st, src, etap, bhT, (c + 3) * BT, T, lane, mrow);
         }
@@ -903,14 +919,15 @@ hipError_t launch_one(const ScanArgs& a, hipStream_t s) {
                          dim3(static_cast<unsigned>(a.B * a.H)), dim3(NT), 0, s, a.q, a.k, a.v,
                          a.eta_logit, a.gate_logit, a.W0, a.gamma, a.beta, a.out, a.W_final,
                          static_cast<int>(a.H), a.T, a.eps, a.rec_delta, a.rec_W,
-                         static_cast<const uint8_t*>(nullptr));
+                         static_cast<const uint8_t*>(nullptr), a.silu_qk ? 1 : 0);
       return hipGetLastError();
     }
   }
   hipLaunchKernelGGL((scan_mfma_kernel<BF16, LN, DUAL, false>), dim3(static_cast<unsigned>(a.B * a.H)),
                      dim3(NT), 0, s, a.q, a.k, a.v, a.eta_logit, a.gate_logit, a.W0, a.gamma,
                      a.beta, a.out, a.W_final, static_cast<int>(a.H), a.T, a.eps,
-                     static_cast<float*>(nullptr), static_cast<float*>(nullptr), a.upd_mask);
+                     static_cast<float*>(nullptr), static_cast<float*>(nullptr), a.upd_mask,
+                     a.silu_qk ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -83,7 +83,7 @@ scan_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
                  const float* __restrict__ gamma, const float* __restrict__ beta,
                  float* __restrict__ out, float* __restrict__ W_final,
                  int H, int64_t T, int64_t chunk, float eps,
-                 const uint8_t* __restrict__ upd_mask) {
+                 const uint8_t* __restrict__ upd_mask, int silu) {
   using In = typename std::conditional<BF16, uint16_t, float>::type;
   constexpr int NT = 4 * D;               // threads
   constexpr int NW = NT / 64;             // waves
@@ -181,6 +181,11 @@ scan_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
           if (a == 3) {
 #pragma unroll
             for (int j = 0; j < VE; ++j) f[j] = fast_sigmoid(f[j]);
+          }
+          if (silu && a <= 1) {
+            // the :mlp variant: SiLU on q and k before the inner model
+#pragma unroll
+            for (int j = 0; j < VE; ++j) f[j] = f[j] * fast_sigmoid(f[j]);
           }
 #pragma unroll
           for (int j = 0; j < VE; j += 4)
@@ -311,7 +316,7 @@ hipError_t launch_one(const ScanArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((scan_valu_kernel<D, BF16, LN, DUAL>), grid, block, 0, s, a.q, a.k, a.v,
                      a.eta_logit, a.gate_logit, a.W0, a.gamma, a.beta, a.out, a.W_final,
                      static_cast<int>(a.H), a.T, a.dual ? a.chunk : int64_t(1), a.eps,
-                     a.upd_mask);
+                     a.upd_mask, a.silu_qk ? 1 : 0);
   return hipGetLastError();
 }
 

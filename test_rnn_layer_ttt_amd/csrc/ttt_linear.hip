@@ -45,7 +45,7 @@ int32_t validate(const void* q, const void* k, const void* v, const void* eta_lo
                  const float* beta, float* out, float* W_final, int64_t B, int64_t H,
                  int64_t T, int64_t d, uint32_t mode, int64_t chunk, ttt::ScanArgs* a) {
   // ---- mode ----
-  const uint32_t known = TTT_DUAL | TTT_LN_EXACT | TTT_IN_BF16 | TTT_NO_LN;
+  const uint32_t known = TTT_DUAL | TTT_LN_EXACT | TTT_IN_BF16 | TTT_NO_LN | TTT_SILU_QK;
   if (mode & ~known) return TTT_ERR_MODE;
   if ((mode & TTT_LN_EXACT) && (mode & TTT_NO_LN)) return TTT_ERR_MODE;
   const bool dual = (mode & TTT_DUAL) != 0;
@@ -117,6 +117,7 @@ int32_t validate(const void* q, const void* k, const void* v, const void* eta_lo
   a->chunk = dual ? chunk : 1;
   a->in_bf16 = bf16;
   a->eps = kLnEps;
+  a->silu_qk = (mode & TTT_SILU_QK) != 0;
   return TTT_OK;
 }
 
@@ -131,7 +132,7 @@ struct RecordLayout {
 // the layout.  Makes no HIP call.
 int32_t record_layout(int64_t B, int64_t H, int64_t T, int64_t d, uint32_t mode,
                       RecordLayout* r) {
-  const uint32_t known = TTT_DUAL | TTT_LN_EXACT | TTT_IN_BF16 | TTT_NO_LN;
+  const uint32_t known = TTT_DUAL | TTT_LN_EXACT | TTT_IN_BF16 | TTT_NO_LN | TTT_SILU_QK;
   if (mode & ~known) return TTT_ERR_MODE;
   if ((mode & TTT_LN_EXACT) && (mode & TTT_NO_LN)) return TTT_ERR_MODE;
   if (B < 1 || H < 1 || d < 1 || T < 0) return TTT_ERR_SHAPE;
@@ -201,7 +202,7 @@ int32_t validate_backward(const void* q, const void* k, const void* v, const voi
                           float* dbeta, int64_t B, int64_t H, int64_t T, int64_t d,
                           uint32_t mode, int64_t chunk, ttt::BwdArgs* a) {
   // mode and shapes (the forward's rules, then the backward's coverage)
-  const uint32_t known = TTT_DUAL | TTT_LN_EXACT | TTT_IN_BF16 | TTT_NO_LN;
+  const uint32_t known = TTT_DUAL | TTT_LN_EXACT | TTT_IN_BF16 | TTT_NO_LN | TTT_SILU_QK;
   if (mode & ~known) return TTT_ERR_MODE;
   if ((mode & TTT_LN_EXACT) && (mode & TTT_NO_LN)) return TTT_ERR_MODE;
   if ((mode & TTT_DUAL) && chunk < 1) return TTT_ERR_MODE;
@@ -287,6 +288,7 @@ int32_t validate_backward(const void* q, const void* k, const void* v, const voi
   a->dual = false;
   a->in_bf16 = bf16;
   a->eps = kLnEps;
+  a->silu_qk = (mode & TTT_SILU_QK) != 0;
   return TTT_OK;
 }
 

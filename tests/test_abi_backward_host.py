@@ -38,7 +38,7 @@ def test_record_bytes_independent_of_dtype_and_ln(mode):
     (dict(mode=ttt.TTT_DUAL), ttt.TTT_ERR_UNSUPPORTED),
     (dict(d=32), ttt.TTT_ERR_UNSUPPORTED),
     (dict(d=128), ttt.TTT_ERR_UNSUPPORTED),
-    (dict(mode=16), ttt.TTT_ERR_MODE),
+    (dict(mode=32), ttt.TTT_ERR_MODE),
     (dict(mode=ttt.TTT_LN_EXACT | ttt.TTT_NO_LN), ttt.TTT_ERR_MODE),
     (dict(B=0), ttt.TTT_ERR_SHAPE),
     (dict(T=-1), ttt.TTT_ERR_SHAPE),

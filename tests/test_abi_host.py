@@ -108,7 +108,7 @@ def test_bad_shape(over):
     assert call(**over) == ttt.TTT_ERR_SHAPE
 
 
-@pytest.mark.parametrize("mode", [16, 32, 0x80000000, ttt.TTT_LN_EXACT | ttt.TTT_NO_LN])
+@pytest.mark.parametrize("mode", [32, 64, 0x80000000, ttt.TTT_LN_EXACT | ttt.TTT_NO_LN])
 def test_bad_mode(mode):
     assert call(mode=mode) == ttt.TTT_ERR_MODE
 
@@ -168,7 +168,7 @@ def test_empty_sequence_allows_null_sequence_pointers():
 
 
 @pytest.mark.parametrize("d", [16, 32, 64, 128])
-@pytest.mark.parametrize("mode", [0, 1, 2, 4, 8, 5, 7, 13])
+@pytest.mark.parametrize("mode", [0, 1, 2, 4, 8, 5, 7, 13, 16, 23, 29])
 def test_supported_combinations_validate(d, mode):
     assert call(d=d, mode=mode) == ttt.TTT_OK
 
