@@ -446,7 +446,7 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         // latency hides behind the previous token's sums
         struct Tok {
           float eta, x, e, rs, mg, mgx, g1, g2;
-          float kk[BT];   // KK[s][t], s < t
+          float kk[BT];   // k_s . k_t, s < t
         };
         auto fetch = [&](int t, Tok& k) {
           k.eta = tc.ETA[t];
@@ -466,7 +466,7 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
           }
 #pragma unroll
           for (int s = 0; s < BT; ++s)
-            if (s < t) k.kk[s] = KK[s][t];
+            if (s < t) k.kk[s] = KK[t][s];   // KK is symmetric: row t reads contiguously
         };
         Tok cur, nxt;
         fetch(BT - 1, nxt);
