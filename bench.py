@@ -82,6 +82,12 @@ def backward_work(x):
     return n, nbytes, n * 12 * d * d
 
 
+def ttt_record_chunk():
+    """Tokens per tile of the training record (the dual form's chunk must match)."""
+    from test_rnn_layer_ttt_amd.binding import RECORD_CHUNK
+    return RECORD_CHUNK
+
+
 def kernel_info(x):
     """Which kernel family runs this workload and which roof bounds it."""
     import test_rnn_layer_ttt_amd as ttt
@@ -235,9 +241,9 @@ def main():
     x = make_inputs(args.workload)
     B, H, T, d = x.q.shape
     train = args.pass_ == "train"
-    if train and (x.dual or d != 64):
-        print(f"bench.py: the backward covers the per-token modes at d = 64; workload "
-              f"{args.workload} is not one", file=sys.stderr)
+    if train and ((x.dual and x.chunk != ttt_record_chunk()) or d != 64):
+        print(f"bench.py: the backward covers d = 64, per-token or dual form with chunks of "
+              f"{ttt_record_chunk()}; workload {args.workload} is not one", file=sys.stderr)
         sys.exit(2)
     if args.cpu_scans is None:
         args.cpu_scans = 128 if train else 256
@@ -310,12 +316,14 @@ def main():
 
         def forward_record():
             st = ttt.ttt_linear_forward_record(*ptrs, record.data_ptr(), rec_bytes, B, H, T, d,
-                                               mode, 1, stream.cuda_stream)
+                                               mode, x.chunk if x.dual else 1,
+                                               stream.cuda_stream)
             if st != ttt.TTT_OK:
                 raise RuntimeError(f"ttt_linear_forward_record: {ttt.ttt_status_string(st)}")
 
         def backward():
-            st = ttt.ttt_linear_backward(*bptrs, B, H, T, d, mode, 1, stream.cuda_stream)
+            st = ttt.ttt_linear_backward(*bptrs, B, H, T, d, mode, x.chunk if x.dual else 1,
+                                         stream.cuda_stream)
             if st != ttt.TTT_OK:
                 raise RuntimeError(f"ttt_linear_backward: {ttt.ttt_status_string(st)}")
 

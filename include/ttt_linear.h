@@ -147,7 +147,12 @@ int32_t ttt_linear_forward_masked(const void* q, const void* k, const void* v,
  * tile (16 KiB per tile and (b,h) at d = 64).
  *
  * Supported: d = 64, the per-token modes (straight-through, TTT_LN_EXACT,
- * TTT_NO_LN), fp32 or bf16 inputs.  TTT_DUAL gives TTT_ERR_UNSUPPORTED.
+ * TTT_NO_LN) and the dual form with chunk == 16 (its chunks are then the
+ * tiles: every z of a chunk is taken at the chunk's first W, "TTT-Linear",
+ * dual form), fp32 or bf16 inputs.  TTT_DUAL with another chunk gives
+ * TTT_ERR_UNSUPPORTED.  A chunk that ttt_linear_forward_masked would skip is
+ * trained by giving its tokens eta_logit = -inf in both calls: the step size
+ * sigmoid(-inf) = 0 makes the forward identical, and its deta_logit is 0.
  *
  * The record is one caller-owned device buffer of ttt_linear_record_bytes()
  * bytes, 16-byte aligned; its contents are private to the library.  The
@@ -159,8 +164,9 @@ int32_t ttt_linear_forward_masked(const void* q, const void* k, const void* v,
 
 /*
  * The record size for these sizes and mode, in *bytes:
- * 4 * B*H * (T*d + ceil(T/16)*d*d + 2*d).  Checks the shapes and mode as
- * ttt_linear_forward_record does.  Makes no HIP call.
+ * 4 * B*H * (T*d + ceil(T/16)*d*d + 2*d), the same with or without TTT_DUAL.
+ * Checks the shapes and mode as ttt_linear_forward_record does (the chunk of
+ * the dual form is checked by the two calls that take it).  Makes no HIP call.
  */
 int32_t ttt_linear_record_bytes(int64_t B, int64_t H, int64_t T, int64_t d, uint32_t mode,
                                 int64_t* bytes);

@@ -31,6 +31,9 @@ TTT_ERR_ALIAS = 5
 TTT_ERR_HIP = 6
 TTT_ERR_WORKSPACE = 7
 
+# tokens per tile of the record; the dual form records only with chunks of this size
+RECORD_CHUNK = 16
+
 #: every symbol the header declares
 EXPORTED = ("ttt_linear_backward", "ttt_linear_forward", "ttt_linear_forward_masked",
             "ttt_linear_forward_record",
@@ -272,13 +275,14 @@ def _check_inputs(q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln):
 
 def forward_record(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *,
                    ln: str = "st", out=None, W_final=None, record=None, stream=None,
-                   silu_qk: bool = False):
-    """:func:`forward` (per-token modes, d = 64) that also returns the record the
-    backward reads: ``(out, W_final, record)``, the record a uint8 device tensor."""
+                   silu_qk: bool = False, dual: bool = False):
+    """:func:`forward` (d = 64; per-token modes, or ``dual=True`` with chunks of
+    16) that also returns the record the backward reads: ``(out, W_final,
+    record)``, the record a uint8 device tensor."""
     import torch
 
     B, H, T, d = _check_inputs(q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln)
-    mode = mode_bits(ln, False, q.dtype == torch.bfloat16, silu_qk)
+    mode = mode_bits(ln, dual, q.dtype == torch.bfloat16, silu_qk)
     st, nbytes = ttt_linear_record_bytes(B, H, T, d, mode)
     check(st)
     if out is None:
@@ -293,16 +297,17 @@ def forward_record(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *,
         _ptr(q), _ptr(k), _ptr(v), _ptr(eta_logit), _ptr(gate_logit), W0.data_ptr(),
         _ptr(gamma) if ln != "none" else None, _ptr(beta) if ln != "none" else None,
         _ptr(out), W_final.data_ptr(), record.data_ptr(), record.numel() * record.element_size(),
-        B, H, T, d, mode, 1, stream.cuda_stream))
+        B, H, T, d, mode, RECORD_CHUNK if dual else 1, stream.cuda_stream))
     return out, W_final, record
 
 
 def backward(q, k, v, eta_logit, gate_logit, gamma, beta, record, dout, dW_final=None, *,
-             ln: str = "st", stream=None, silu_qk: bool = False):
-    """Gradients from a record of :func:`forward_record` and dL/dout (float32
-    [B,H,T,d]), dL/dW_final (float32 [B,H,d,d] or None).  Returns a dict with
-    dq, dk, dv, dgate_logit, deta_logit, dW0, dgamma, dbeta (float32; the last
-    two None with ``ln="none"``)."""
+             ln: str = "st", stream=None, silu_qk: bool = False, dual: bool = False):
+    """Gradients from a record of :func:`forward_record` (same ``ln``,
+    ``silu_qk`` and ``dual``) and dL/dout (float32 [B,H,T,d]), dL/dW_final
+    (float32 [B,H,d,d] or None).  Returns a dict with dq, dk, dv, dgate_logit,
+    deta_logit, dW0, dgamma, dbeta (float32; the last two None with
+    ``ln="none"``)."""
     import torch
 
     B, H, T, d = _check_inputs(q, k, v, eta_logit, gate_logit, None, gamma, beta, ln)
@@ -327,7 +332,8 @@ def backward(q, k, v, eta_logit, gate_logit, gamma, beta, record, dout, dW_final
         None if dW_final is None else dW_final.data_ptr(), _ptr(g["dq"]), _ptr(g["dk"]),
         _ptr(g["dv"]), _ptr(g["deta_logit"]), _ptr(g["dgate_logit"]), g["dW0"].data_ptr(),
         _ptr(g["dgamma"]), _ptr(g["dbeta"]), B, H, T, d,
-        mode_bits(ln, False, q.dtype == torch.bfloat16, silu_qk), 1, stream.cuda_stream))
+        mode_bits(ln, dual, q.dtype == torch.bfloat16, silu_qk), RECORD_CHUNK if dual else 1,
+        stream.cuda_stream))
     return g
 
 
@@ -335,12 +341,13 @@ _autograd_fn = None
 
 
 def ttt_linear(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln: str = "st",
-               silu_qk: bool = False):
+               silu_qk: bool = False, dual: bool = False):
     """Differentiable scan for torch autograd: ``(out, W_final)``.
 
     The forward is :func:`forward_record`; the backward is :func:`backward`
-    on the saved record.  Per-token modes at d = 64.  Gradients come back in
-    float32 (autograd casts them to a bf16 input's dtype).
+    on the saved record.  d = 64: per-token modes, or the dual form with
+    chunks of 16 tokens.  Gradients come back in float32 (autograd casts them
+    to a bf16 input's dtype).
     """
     global _autograd_fn
     if _autograd_fn is None:
@@ -348,11 +355,12 @@ def ttt_linear(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln:
 
         class TTTLinearFunction(torch.autograd.Function):
             @staticmethod
-            def forward(ctx, q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln, silu_qk):
+            def forward(ctx, q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln, silu_qk, dual):
                 out, W_final, record = forward_record(q, k, v, eta_logit, gate_logit, W0, gamma,
-                                                      beta, ln=ln, silu_qk=silu_qk)
+                                                      beta, ln=ln, silu_qk=silu_qk, dual=dual)
                 ctx.ln = ln
                 ctx.silu_qk = silu_qk
+                ctx.dual = dual
                 ctx.save_for_backward(q, k, v, eta_logit, gate_logit, gamma, beta, record)
                 return out, W_final
 
@@ -365,11 +373,11 @@ def ttt_linear(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln:
                 g = backward(q, k, v, eta_logit, gate_logit, gamma, beta, record,
                              dout.contiguous().float(),
                              None if dW_final is None else dW_final.contiguous().float(),
-                             ln=ctx.ln, silu_qk=ctx.silu_qk)
+                             ln=ctx.ln, silu_qk=ctx.silu_qk, dual=ctx.dual)
                 return (g["dq"], g["dk"], g["dv"], g["deta_logit"], g["dgate_logit"], g["dW0"],
-                        g["dgamma"], g["dbeta"], None, None)
+                        g["dgamma"], g["dbeta"], None, None, None)
 
         _autograd_fn = TTTLinearFunction
     if ln == "none":
         gamma = beta = None
-    return _autograd_fn.apply(q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln, silu_qk)
+    return _autograd_fn.apply(q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln, silu_qk, dual)

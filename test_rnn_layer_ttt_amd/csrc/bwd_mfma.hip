@@ -350,7 +350,7 @@ __device__ __forceinline__ void w_store(const float (&st)[kState], float (*W)[KP
   }
 }
 
-template <bool BF16, int LN>
+template <bool BF16, int LN, bool DUAL>
 __global__ void __launch_bounds__(NT)
 bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
                 const void* __restrict__ vp, const void* __restrict__ etap,
@@ -464,9 +464,11 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
               k.rs = w.S[t][0];
             }
           }
+          if constexpr (!DUAL) {
 #pragma unroll
-          for (int s = 0; s < BT; ++s)
-            if (s < t) k.kk[s] = KK[t][s];   // KK is symmetric: row t reads contiguously
+            for (int s = 0; s < BT; ++s)
+              if (s < t) k.kk[s] = KK[t][s];   // KK is symmetric: row t reads contiguously
+          }
         };
         Tok cur, nxt;
         fetch(BT - 1, nxt);
@@ -515,20 +517,25 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
               dbet += de;
             }
             // the next token needs only row t-1; the other rows' updates
-            // overlap its sums
-            if (t > 0) ac[t - 1] = fmaf(cur.kk[t - 1], dz, ac[t - 1]);
+            // overlap its sums.  The dual form: z of every token of the tile
+            // is taken at the tile's first W, so no dz flows back within it.
+            if constexpr (!DUAL)
+              if (t > 0) ac[t - 1] = fmaf(cur.kk[t - 1], dz, ac[t - 1]);
             w.X[t][lane] = dz;
             w.A[t][lane] = a;
             dv[(bhT + t0 + t) * D + lane] = dvv;
+            if constexpr (!DUAL) {
 #pragma unroll
-            for (int s = 0; s + 1 < t; ++s) ac[s] = fmaf(cur.kk[s], dz, ac[s]);
+              for (int s = 0; s + 1 < t; ++s) ac[s] = fmaf(cur.kk[s], dz, ac[s]);
+            }
           }
           // keeps each token's loads one token ahead rather than all hoisted
-          __builtin_amdgcn_sched_barrier(0);
+          // (the dual form's tokens are independent: let their sums overlap)
+          if constexpr (!DUAL) __builtin_amdgcn_sched_barrier(0);
         }
         // ---- Grams that need dz: DeDZ[s][t'] = delta_s . dz_t' and
         //      DZE[t][s] = eta_s (dz_t . delta_s) over tile c-1's s ----
-        store_block(sm.DeDZ, 0, gram(tc.De, w.X, l16, G), l16, G);
+        if constexpr (!DUAL) store_block(sm.DeDZ, 0, gram(tc.De, w.X, l16, G), l16, G);
         if (prep) {
           const TileIn& tm = sm.ring[cm % 3];
           f32x4 g2 = gram(w.X, tm.De, l16, G);
@@ -645,17 +652,21 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       const TileIn& tm = sm.ring[cm % 3];
       const Grams& gm = sm.gr[cm & 1];
       Work& w = sm.wk[cm & 1];
-      float a[4];
-      frag_row16(gm.KK[l16], G, a);
+      if constexpr (!DUAL) {
+        // z_t = W_c k_t - sum_{s<t} eta_s (k_s . k_t) delta_s (the dual form
+        // takes every z of the tile at W_c)
+        float a[4];
+        frag_row16(gm.KK[l16], G, a);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) a[ks] = (4 * G + ks < l16) ? a[ks] : 0.0f;
+        for (int ks = 0; ks < 4; ++ks) a[ks] = (4 * G + ks < l16) ? a[ks] : 0.0f;
 #pragma unroll
-      for (int fb = 0; fb < 4; ++fb) {
-        float b[4];
-        frag_col16(tm.De, 16 * fb + l16, G, b);
+        for (int fb = 0; fb < 4; ++fb) {
+          float b[4];
+          frag_col16(tm.De, 16 * fb + l16, G, b);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) b[ks] *= -tm.ETA[4 * G + ks];
-        put(st, fb, mma<4>(a, b, blk(st, fb)));
+          for (int ks = 0; ks < 4; ++ks) b[ks] *= -tm.ETA[4 * G + ks];
+          put(st, fb, mma<4>(a, b, blk(st, fb)));
+        }
       }
       if constexpr (LN != kLnNone) {
 #pragma unroll
@@ -802,10 +813,11 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
     }
     if ((wave == 3 || wave == 2) && live) {
       // b1 += sum_{t'>=t} (delta_t.dy_t') q_t' + sum_{t'>t} (delta_t.dz_t') k_t'
+      // (the dual form: no dz term within the tile)
       const TileIn& tc = sm.ring[c % 3];
-      float ay[4], az[4];
+      float ay[4], az[4] = {0, 0, 0, 0};
       frag_row16(sm.gr[c & 1].DeDY[l16], G, ay);
-      frag_row16(sm.DeDZ[l16], G, az);
+      if constexpr (!DUAL) frag_row16(sm.DeDZ[l16], G, az);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int tp = 4 * G + ks;
@@ -821,8 +833,10 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
           float bb[4];
           frag_col16(tc.Q, 16 * jb + l16, G, bb);
           put(st, s0 + jj, mma<4>(ay, bb, blk(st, s0 + jj)));
-          frag_col16(tc.K, 16 * jb + l16, G, bb);
-          put(st, s0 + jj, mma<4>(az, bb, blk(st, s0 + jj)));
+          if constexpr (!DUAL) {
+            frag_col16(tc.K, 16 * jb + l16, G, bb);
+            put(st, s0 + jj, mma<4>(az, bb, blk(st, s0 + jj)));
+          }
         }
       };
       if (wave == 3)
@@ -832,17 +846,20 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
     }
     if ((wave == 0 || wave == 4 || wave == 3) && live) {
       // B2 = DZ W_c - sum_{s<t} eta_s (delta_s.dz_t) k_s, with
-      // DZ W_c = DZ W_{c-1} - (DZ E_{c-1}^T) K_{c-1} (for c = 0 the slot holds W_0)
+      // DZ W_c = DZ W_{c-1} - (DZ E_{c-1}^T) K_{c-1} (for c = 0 the slot holds W_0);
+      // the dual form has no in-tile sum
       const TileIn& tc = sm.ring[c % 3];
       const float(*Wm)[KP] = sm.W[(prep ? cm : 0) & 1];
       float a[16];
       frag_row64(sm.wk[c & 1].X[l16], G, a);
-      float as[4], ae[4] = {0, 0, 0, 0};
-      frag_col16(sm.DeDZ, l16, G, as);   // DeDZ[s][t], k = s, m = t
+      float as[4] = {0, 0, 0, 0}, ae[4] = {0, 0, 0, 0};
+      if constexpr (!DUAL) {
+        frag_col16(sm.DeDZ, l16, G, as);   // DeDZ[s][t], k = s, m = t
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int s = 4 * G + ks;
-        as[ks] = s < l16 ? -tc.ETA[s] * as[ks] : 0.0f;
+        for (int ks = 0; ks < 4; ++ks) {
+          const int s = 4 * G + ks;
+          as[ks] = s < l16 ? -tc.ETA[s] * as[ks] : 0.0f;
+        }
       }
       if (prep) {
         frag_row16(sm.DZE[l16], G, ae);
@@ -858,8 +875,10 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         frag_col64(Wm, 16 * jb + l16, G, b);
         f32x4 v = mma<16>(a, b, f32x4{0, 0, 0, 0});
         float bk[4];
-        frag_col16(tc.K, 16 * jb + l16, G, bk);
-        v = mma<4>(as, bk, v);
+        if constexpr (!DUAL) {
+          frag_col16(tc.K, 16 * jb + l16, G, bk);
+          v = mma<4>(as, bk, v);
+        }
         if (prep) {
           frag_col16(sm.ring[cm % 3].K, 16 * jb + l16, G, bk);
           v = mma<4>(ae, bk, v);
@@ -961,9 +980,9 @@ __global__ void gamma_beta_sum_kernel(const float* __restrict__ gb_part, float* 
   dbeta[e] = sb;
 }
 
-template <bool BF16, int LN>
+template <bool BF16, int LN, bool DUAL>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_mfma_kernel<BF16, LN>), dim3(static_cast<unsigned>(a.B * a.H)), dim3(NT),
+  hipLaunchKernelGGL((bwd_mfma_kernel<BF16, LN, DUAL>), dim3(static_cast<unsigned>(a.B * a.H)), dim3(NT),
                      0, s, a.q, a.k, a.v, a.eta_logit, a.gate_logit, a.gamma, a.beta, a.dout,
                      a.dW_final, a.rec_delta, a.rec_W, a.dq, a.dk, a.dv, a.deta_logit,
                      a.dgate_logit, a.dW0, LN == kLnNone ? nullptr : a.gb_part,
@@ -986,20 +1005,20 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t s) {
-  if (a.d != D || a.dual) return hipErrorNotSupported;
-  if (a.in_bf16) {
-    switch (a.ln) {
-      case kLnST: return launch_bwd<true, kLnST>(a, s);
-      case kLnExact: return launch_bwd<true, kLnExact>(a, s);
-      default: return launch_bwd<true, kLnNone>(a, s);
-    }
-  }
+template <bool BF16, bool DUAL>
+hipError_t launch_ln(const BwdArgs& a, hipStream_t s) {
   switch (a.ln) {
-    case kLnST: return launch_bwd<false, kLnST>(a, s);
-    case kLnExact: return launch_bwd<false, kLnExact>(a, s);
-    default: return launch_bwd<false, kLnNone>(a, s);
+    case kLnST: return launch_bwd<BF16, kLnST, DUAL>(a, s);
+    case kLnExact: return launch_bwd<BF16, kLnExact, DUAL>(a, s);
+    default: return launch_bwd<BF16, kLnNone, DUAL>(a, s);
   }
+}
+
+hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t s) {
+  // the dual form's chunks must be the tiles
+  if (a.d != D || (a.dual && a.chunk != BT)) return hipErrorNotSupported;
+  if (a.in_bf16) return a.dual ? launch_ln<true, true>(a, s) : launch_ln<true, false>(a, s);
+  return a.dual ? launch_ln<false, true>(a, s) : launch_ln<false, false>(a, s);
 }
 
 }  // namespace ttt

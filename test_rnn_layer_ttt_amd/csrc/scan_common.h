@@ -63,6 +63,7 @@ struct BwdArgs {
   int64_t B, H, T, d;
   int ln;
   bool dual;
+  int64_t chunk;       // the dual form's chunk (must be kRecTile); 1 otherwise
   bool in_bf16;
   float eps;
   bool silu_qk = false;   // the :mlp variant (SiLU on q and k)
@@ -81,8 +82,9 @@ hipError_t launch_scan_valu(const ScanArgs& a, hipStream_t stream);
 hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t stream);
 bool scan_mfma_supports(const ScanArgs& a);
 
-// Backward of the per-token scan for d = 64 from a record; hipErrorNotSupported
-// for anything else.
+// Backward of the per-token scan, and of the dual form with chunks of
+// kRecTile tokens, for d = 64 from a record; hipErrorNotSupported for
+// anything else.
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace ttt

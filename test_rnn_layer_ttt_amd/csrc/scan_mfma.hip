@@ -652,7 +652,8 @@ __device__ __forceinline__ void write_tile_out(const float (*ob)[KPAD], float* o
 }
 
 // ---------------------------------------------------------------------------
-// REC: also record delta_t and W at the start of every tile (for the backward)
+// REC: also record delta_t and W at the start of every tile (for the backward;
+// in the dual form the tiles are the chunks)
 template <bool BF16, int LN, bool DUAL, bool REC>
 __global__ void __launch_bounds__(NT)
 scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
@@ -662,7 +663,6 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
                  float* __restrict__ out, float* __restrict__ W_final, int H, int64_t T,
                  float eps, float* __restrict__ rec_delta, float* __restrict__ rec_W,
                  const uint8_t* __restrict__ upd_mask, int silu) {
-  static_assert(!(REC && DUAL), "the record is kept for the per-token modes");
   __shared__ Smem<BF16> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -913,15 +913,13 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
 
 template <bool BF16, int LN, bool DUAL>
 hipError_t launch_one(const ScanArgs& a, hipStream_t s) {
-  if constexpr (!DUAL) {
-    if (a.rec_delta != nullptr) {
-      hipLaunchKernelGGL((scan_mfma_kernel<BF16, LN, false, true>),
-                         dim3(static_cast<unsigned>(a.B * a.H)), dim3(NT), 0, s, a.q, a.k, a.v,
-                         a.eta_logit, a.gate_logit, a.W0, a.gamma, a.beta, a.out, a.W_final,
-                         static_cast<int>(a.H), a.T, a.eps, a.rec_delta, a.rec_W,
-                         static_cast<const uint8_t*>(nullptr), a.silu_qk ? 1 : 0);
-      return hipGetLastError();
-    }
+  if (a.rec_delta != nullptr) {
+    hipLaunchKernelGGL((scan_mfma_kernel<BF16, LN, DUAL, true>),
+                       dim3(static_cast<unsigned>(a.B * a.H)), dim3(NT), 0, s, a.q, a.k, a.v,
+                       a.eta_logit, a.gate_logit, a.W0, a.gamma, a.beta, a.out, a.W_final,
+                       static_cast<int>(a.H), a.T, a.eps, a.rec_delta, a.rec_W, a.upd_mask,
+                       a.silu_qk ? 1 : 0);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL((scan_mfma_kernel<BF16, LN, DUAL, false>), dim3(static_cast<unsigned>(a.B * a.H)),
                      dim3(NT), 0, s, a.q, a.k, a.v, a.eta_logit, a.gate_logit, a.W0, a.gamma,
@@ -950,7 +948,7 @@ hipError_t launch_ln(const ScanArgs& a, hipStream_t s) {
 }  // namespace
 
 bool scan_mfma_supports(const ScanArgs& a) {
-  return a.d == D && (!a.dual || a.chunk == BT) && (a.rec_delta == nullptr || !a.dual);
+  return a.d == D && (!a.dual || a.chunk == BT);
 }
 
 hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t s) {

@@ -136,7 +136,7 @@ int32_t record_layout(int64_t B, int64_t H, int64_t T, int64_t d, uint32_t mode,
   if (mode & ~known) return TTT_ERR_MODE;
   if ((mode & TTT_LN_EXACT) && (mode & TTT_NO_LN)) return TTT_ERR_MODE;
   if (B < 1 || H < 1 || d < 1 || T < 0) return TTT_ERR_SHAPE;
-  if ((mode & TTT_DUAL) || d != 64) return TTT_ERR_UNSUPPORTED;
+  if (d != 64) return TTT_ERR_UNSUPPORTED;
   const int64_t ntiles = (T + ttt::kRecTile - 1) / ttt::kRecTile;
   int64_t BH, per_scan, a, b;
   if (!mul_ok(B, H, &BH) || BH > INT32_MAX) return TTT_ERR_SHAPE;
@@ -174,6 +174,7 @@ int32_t validate_forward_record(const void* q, const void* k, const void* v,
   if (st != TTT_OK) return st;
   st = validate_record(record, record_bytes, B, H, T, d, mode, r);
   if (st != TTT_OK) return st;
+  if (a->dual && a->chunk != ttt::kRecTile) return TTT_ERR_UNSUPPORTED;   // chunks = tiles
   const int64_t in_size = (mode & TTT_IN_BF16) ? 2 : 4;
   const int64_t seq = B * H * T * d, w = B * H * d * d;
   const Range rec = span(record, r->bytes);
@@ -209,6 +210,8 @@ int32_t validate_backward(const void* q, const void* k, const void* v, const voi
   RecordLayout r;
   int32_t st = record_layout(B, H, T, d, mode, &r);
   if (st != TTT_OK) return st;
+  const bool dual = (mode & TTT_DUAL) != 0;
+  if (dual && chunk != ttt::kRecTile) return TTT_ERR_UNSUPPORTED;
   const bool no_ln = (mode & TTT_NO_LN) != 0;
   const bool bf16 = (mode & TTT_IN_BF16) != 0;
   // pointers
@@ -285,7 +288,8 @@ int32_t validate_backward(const void* q, const void* k, const void* v, const voi
   a->T = T;
   a->d = d;
   a->ln = no_ln ? ttt::kLnNone : ((mode & TTT_LN_EXACT) ? ttt::kLnExact : ttt::kLnST);
-  a->dual = false;
+  a->dual = dual;
+  a->chunk = dual ? chunk : 1;
   a->in_bf16 = bf16;
   a->eps = kLnEps;
   a->silu_qk = (mode & TTT_SILU_QK) != 0;

@@ -29,13 +29,14 @@ def test_record_bytes_formula(B_, H_, T_):
 
 
 @pytest.mark.parametrize("mode", [0, ttt.TTT_LN_EXACT, ttt.TTT_NO_LN, ttt.TTT_IN_BF16,
-                                  ttt.TTT_IN_BF16 | ttt.TTT_LN_EXACT])
-def test_record_bytes_independent_of_dtype_and_ln(mode):
+                                  ttt.TTT_IN_BF16 | ttt.TTT_LN_EXACT, ttt.TTT_DUAL,
+                                  ttt.TTT_DUAL | ttt.TTT_IN_BF16 | ttt.TTT_NO_LN,
+                                  ttt.TTT_DUAL | ttt.TTT_SILU_QK])
+def test_record_bytes_independent_of_dtype_ln_and_form(mode):
     assert rec_bytes(mode=mode) == rec_bytes()
 
 
 @pytest.mark.parametrize("over,code", [
-    (dict(mode=ttt.TTT_DUAL), ttt.TTT_ERR_UNSUPPORTED),
     (dict(d=32), ttt.TTT_ERR_UNSUPPORTED),
     (dict(d=128), ttt.TTT_ERR_UNSUPPORTED),
     (dict(mode=32), ttt.TTT_ERR_MODE),
@@ -81,7 +82,9 @@ needs_no_gpu = pytest.mark.skipif(_GPU, reason="sends unlaunchable arguments to 
     (dict(record=A + 2 * S + 4096), ttt.TTT_ERR_ALIAS),     # record inside v
     (dict(record=A + 9 * S), ttt.TTT_ERR_ALIAS),            # record == W_final
     (dict(record=A + 5 * S), ttt.TTT_ERR_ALIAS),            # record == W0
-    (dict(mode=ttt.TTT_DUAL), ttt.TTT_ERR_UNSUPPORTED),
+    (dict(mode=ttt.TTT_DUAL, chunk=8), ttt.TTT_ERR_UNSUPPORTED),    # chunks must be the tiles
+    (dict(mode=ttt.TTT_DUAL, chunk=32), ttt.TTT_ERR_UNSUPPORTED),
+    (dict(mode=ttt.TTT_DUAL, chunk=0), ttt.TTT_ERR_MODE),
     (dict(d=32), ttt.TTT_ERR_UNSUPPORTED),
     (dict(q=None), ttt.TTT_ERR_NULL),                       # the forward's own checks first
     (dict(out=A), ttt.TTT_ERR_ALIAS),
@@ -155,7 +158,8 @@ def test_backward_alias_rejected(over):
 
 @needs_no_gpu
 @pytest.mark.parametrize("over,code", [
-    (dict(mode=ttt.TTT_DUAL), ttt.TTT_ERR_UNSUPPORTED),
+    (dict(mode=ttt.TTT_DUAL, chunk=8), ttt.TTT_ERR_UNSUPPORTED),
+    (dict(mode=ttt.TTT_DUAL, chunk=1), ttt.TTT_ERR_UNSUPPORTED),
     (dict(mode=ttt.TTT_DUAL, chunk=0), ttt.TTT_ERR_MODE),
     (dict(d=16), ttt.TTT_ERR_UNSUPPORTED),
     (dict(record_bytes=rec_bytes() - 4), ttt.TTT_ERR_WORKSPACE),

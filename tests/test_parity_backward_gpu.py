@@ -15,7 +15,8 @@ import numpy as np
 import pytest
 
 import oracle
-from test_rnn_layer_ttt_amd.inputs import make_case, make_cotangents, make_inputs
+from test_rnn_layer_ttt_amd.inputs import (make_case, make_cotangents, make_inputs,
+                                           make_update_mask)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -42,22 +43,23 @@ def cot(a):
     return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def gpu_bwd(x, dout, dWf, ln=None):
+def gpu_bwd(x, dout, dWf, ln=None, dual=False, silu_qk=False):
     ln = x.ln if ln is None else ln
     t = dev(x)
     gam = None if ln == "none" else t["gamma"]
     bet = None if ln == "none" else t["beta"]
     out, Wf, rec = ttt.forward_record(t["q"], t["k"], t["v"], t["eta_logit"], t["gate_logit"],
-                                      t["W0"], gam, bet, ln=ln)
+                                      t["W0"], gam, bet, ln=ln, dual=dual, silu_qk=silu_qk)
     g = ttt.backward(t["q"], t["k"], t["v"], t["eta_logit"], t["gate_logit"], gam, bet, rec,
-                     cot(dout), cot(dWf), ln=ln)
+                     cot(dout), cot(dWf), ln=ln, dual=dual, silu_qk=silu_qk)
     torch.cuda.synchronize()
     return {k: None if v is None else v.cpu().numpy() for k, v in g.items()}
 
 
-def ref_bwd(x, dout, dWf, ln=None):
+def ref_bwd(x, dout, dWf, ln=None, dual=False, silu_qk=False):
     return oracle.ttt_linear_backward(x.q, x.k, x.v, x.eta_logit, x.gate_logit, x.W0, x.gamma,
-                                      x.beta, dout, dWf, ln=x.ln if ln is None else ln)
+                                      x.beta, dout, dWf, ln=x.ln if ln is None else ln,
+                                      dual=dual, chunk=16, silu_qk=silu_qk)
 
 
 def assert_close(got, ref, tol, what):
@@ -255,3 +257,117 @@ def test_full_size_exact_backward_tail():
                                    ln="exact")
     for key in ("dq", "dk", "dv", "dgate_logit", "deta_logit"):
         assert_close(tail(g[key][bs, hs][None]), r[key], 1e-4, key)
+
+
+# ---------------------------------------------------------------------------
+# the dual form: chunks of 16 tokens (the tiles), every z of a chunk at the
+# chunk's first W
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("ln", ["st", "exact", "none"])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_dual_small_backward_parity(ln, bf16):
+    T = 3 * 16 + 5
+    say(f"case dual backward ln={ln} bf16={bf16} T={T}")
+    x = make_case(2, 3, T, 64, seed=400 + T, ln=ln, dual=True, chunk=16, in_bf16=bf16,
+                  random_affine=True)
+    dout, dWf = make_cotangents(2, 3, T, 64, seed=401)
+    compare(gpu_bwd(x, dout, dWf, dual=True), ref_bwd(x, dout, dWf, dual=True), TOL[bf16])
+
+
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 33, 100])
+def test_dual_short_and_ragged_backward(T):
+    say(f"case dual backward T={T}")
+    x = make_case(2, 2, T, 64, seed=410 + T, dual=True, chunk=16, random_affine=True)
+    dout, dWf = make_cotangents(2, 2, T, 64, seed=411 + T)
+    compare(gpu_bwd(x, dout, dWf, dual=True), ref_bwd(x, dout, dWf, dual=True), 1e-4)
+
+
+def test_dual_backward_differs_from_per_token():
+    # the two forms' gradients are not interchangeable: the per-token backward
+    # on a dual record would be a silent error, so the forms must differ here
+    say("case dual vs per-token gradients")
+    x = make_case(1, 2, 40, 64, seed=420, dual=True, chunk=16, random_affine=True)
+    dout, dWf = make_cotangents(1, 2, 40, 64, seed=421)
+    g = gpu_bwd(x, dout, dWf, dual=True)
+    r_tok = ref_bwd(x, dout, dWf, dual=False)
+    assert oracle.rel_max_err(g["dk"], r_tok["dk"]) > 1e-2
+
+
+def test_dual_record_forward_matches_plain_forward_bitwise():
+    say("case dual forward_record == forward")
+    for ln, bf16 in (("st", True), ("exact", False), ("none", False)):
+        x = make_case(2, 3, 70, 64, seed=430, ln=ln, dual=True, chunk=16, in_bf16=bf16,
+                      random_affine=True)
+        t = dev(x)
+        gam = None if ln == "none" else t["gamma"]
+        bet = None if ln == "none" else t["beta"]
+        o1, W1 = ttt.forward(t["q"], t["k"], t["v"], t["eta_logit"], t["gate_logit"], t["W0"],
+                             gam, bet, ln=ln, dual=True, chunk=16)
+        o2, W2, _ = ttt.forward_record(t["q"], t["k"], t["v"], t["eta_logit"],
+                                       t["gate_logit"], t["W0"], gam, bet, ln=ln, dual=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(W1, W2), (ln, bf16)
+
+
+def test_dual_skipped_chunks_as_minus_inf_step_size():
+    # a chunk the masked forward skips trains as eta_logit = -inf on its
+    # tokens: the recording forward then equals the masked forward bit for bit,
+    # and the gradients match the oracle's, with d eta_logit = 0 on those tokens
+    say("case dual backward, skipped chunks")
+    B, H, T = 2, 3, 90
+    x = make_case(B, H, T, 64, seed=440, dual=True, chunk=16, in_bf16=True, random_affine=True)
+    mask = make_update_mask(B, H, T, 16, 0.5, seed=441)
+    skip = np.repeat(mask == 0, 16, axis=2)[:, :, :T]
+    t = dev(x)
+    o1, W1 = ttt.forward(t["q"], t["k"], t["v"], t["eta_logit"], t["gate_logit"], t["W0"],
+                         t["gamma"], t["beta"], dual=True, chunk=16,
+                         update_mask=torch.from_numpy(mask).cuda())
+    x.eta_logit[skip] = -np.inf
+    t = dev(x)
+    o2, W2, _ = ttt.forward_record(t["q"], t["k"], t["v"], t["eta_logit"], t["gate_logit"],
+                                   t["W0"], t["gamma"], t["beta"], dual=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(W1, W2)
+    dout, dWf = make_cotangents(B, H, T, 64, seed=442)
+    g = gpu_bwd(x, dout, dWf, dual=True)
+    assert np.all(g["deta_logit"][skip] == 0.0)
+    compare(g, ref_bwd(x, dout, dWf, dual=True), TOL[True])
+
+
+def test_dual_silu_backward():
+    say("case dual backward silu_qk")
+    x = make_case(2, 2, 50, 64, seed=450, dual=True, chunk=16, in_bf16=True, random_affine=True)
+    dout, dWf = make_cotangents(2, 2, 50, 64, seed=451)
+    compare(gpu_bwd(x, dout, dWf, dual=True, silu_qk=True),
+            ref_bwd(x, dout, dWf, dual=True, silu_qk=True), TOL[True])
+
+
+def test_dual_autograd_function_matches_backward():
+    say("case dual autograd")
+    x = make_case(2, 2, 33, 64, seed=460, dual=True, chunk=16, random_affine=True)
+    dout, dWf = make_cotangents(2, 2, 33, 64, seed=461)
+    t = dev(x)
+    leaves = {k: v.clone().requires_grad_() for k, v in t.items()}
+    out, Wf = ttt.ttt_linear(*[leaves[k] for k in ("q", "k", "v", "eta_logit", "gate_logit",
+                                                   "W0", "gamma", "beta")], ln="st", dual=True)
+    ((out * cot(dout)).sum() + (Wf * cot(dWf)).sum()).backward()
+    r = ref_bwd(x, dout, dWf, dual=True)
+    names = dict(q="dq", k="dk", v="dv", eta_logit="deta_logit", gate_logit="dgate_logit",
+                 W0="dW0", gamma="dgamma", beta="dbeta")
+    for leaf, key in names.items():
+        assert_close(leaves[leaf].grad.cpu().numpy(), r[key], 1e-4, f"autograd {key}")
+
+
+def test_full_size_dual_backward_sampled():
+    workload, head = "h2048_T8192_dual16_bf16", 11
+    say(f"case dual backward full size {workload} head {head}")
+    x = make_inputs(workload)
+    B, H, T, d = x.q.shape
+    dout, dWf = make_cotangents(B, H, T, d, seed=470)
+    g = gpu_bwd(x, dout, dWf, dual=True)
+    xs, ds, dWs, (bs, hs) = _sampled(x, dout, dWf, head)
+    r = ref_bwd(xs, ds, dWs, dual=True)
+    for key in ("dq", "dk", "dv", "dgate_logit", "deta_logit", "dW0"):
+        assert_close(g[key][bs, hs][None], r[key], TOL[True], key)
+    assert_close(g["dgamma"][head], r["dgamma"].sum(axis=0), TOL[True], "dgamma")
+    assert_close(g["dbeta"][head], r["dbeta"].sum(axis=0), TOL[True], "dbeta")
