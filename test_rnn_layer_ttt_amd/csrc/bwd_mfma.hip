@@ -1,4 +1,5 @@
-// Backward of the per-token TTT-Linear scan for d = 64 (gfx950).
+// Backward of the TTT-Linear scan for d = 64 (gfx950): the per-token scan,
+// and the dual form with chunks of 16 tokens (the tiles below).
 //
 // Recurrence: "Edifice.Recurrent.TTT", "Equations (TTT-Linear)"; exact
 // LayerNorm gradient: "Error Correction in Trained TTT Layers", abstract.  The
@@ -19,6 +20,11 @@
 //          + W_c^T dz_t - sum_{s<t} eta_s (delta_s.dz_t) k_s
 //   dq_t = W_c^T dy_t - sum_{s<=t} eta_s (delta_s.dy_t) k_s
 //   H   <- H + sum_t dy_t q_t^T + sum_t dz_t k_t^T          (gradient before the tile)
+//
+// The dual form ("PonderTTT", dual-form chunk updates) takes every z of a tile
+// at W_c: z_t = W_c k_t, so the two sums over dz inside the tile (in a_t and
+// in dk_t) and the z correction drop out and the tokens' VJPs are independent;
+// the terms that couple neighbouring tiles are unchanged.
 //
 // Two rewrites let the work of neighbouring tiles overlap.  (1) The part of
 // a_t of tile c-1 that comes through H needs H before tile c, which is H
@@ -953,16 +959,49 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
 }
 
 // the :mlp variant: the gradients computed for silu(q), silu(k) times
-// silu'(x) = sigmoid(x) (1 + x (1 - sigmoid(x))) at the raw inputs
+// silu'(x) = sigmoid(x) (1 + x (1 - sigmoid(x))) at the raw inputs; eight
+// elements per thread (n is a multiple of d = 64; every pointer is 16-byte
+// aligned), as 16-byte loads and stores
+__device__ __forceinline__ float silu_grad(float x) {
+  const float s = sigmoidf_(x);
+  return s * fmaf(x, 1.0f - s, 1.0f);
+}
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* p, int64_t i, float (&x)[8]) {
+  if constexpr (BF16) {
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(u[e] << 16);
+      x[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* f = reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    const float4 a = f[0], b = f[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+}
+__device__ __forceinline__ void scale8(float* g, int64_t i, const float (&x)[8]) {
+  float4* p = reinterpret_cast<float4*>(g + i);
+  float4 a = p[0], b = p[1];
+  a.x *= silu_grad(x[0]); a.y *= silu_grad(x[1]); a.z *= silu_grad(x[2]); a.w *= silu_grad(x[3]);
+  b.x *= silu_grad(x[4]); b.y *= silu_grad(x[5]); b.z *= silu_grad(x[6]); b.w *= silu_grad(x[7]);
+  p[0] = a;
+  p[1] = b;
+}
 template <bool BF16>
 __global__ void silu_grad_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
-                                 float* __restrict__ dq, float* __restrict__ dk, int64_t n) {
-  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
-  if (i >= n) return;
-  const float q = ld_in<BF16>(qp, i), k = ld_in<BF16>(kp, i);
-  const float sq = sigmoidf_(q), sk = sigmoidf_(k);
-  dq[i] *= sq * fmaf(q, 1.0f - sq, 1.0f);
-  dk[i] *= sk * fmaf(k, 1.0f - sk, 1.0f);
+                                 float* __restrict__ dq, float* __restrict__ dk, int64_t n8) {
+  const int64_t v = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (v >= n8) return;
+  const int64_t i = 8 * v;
+  float x[8];
+  load8<BF16>(qp, i, x);
+  scale8(dq, i, x);
+  load8<BF16>(kp, i, x);
+  scale8(dk, i, x);
 }
 
 // dgamma[h][i] = sum over the batch of the per-scan parts, dbeta likewise (fixed order)
@@ -990,9 +1029,9 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (a.silu_qk && a.T > 0) {
-    const int64_t n = a.B * a.H * a.T * D;
-    hipLaunchKernelGGL((silu_grad_kernel<BF16>), dim3(static_cast<unsigned>((n + 255) / 256)),
-                       dim3(256), 0, s, a.q, a.k, a.dq, a.dk, n);
+    const int64_t n8 = a.B * a.H * a.T * (D / 8);
+    hipLaunchKernelGGL((silu_grad_kernel<BF16>), dim3(static_cast<unsigned>((n8 + 255) / 256)),
+                       dim3(256), 0, s, a.q, a.k, a.dq, a.dk, n8);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
