@@ -202,7 +202,7 @@ def load_traffic(kernel, workload):
     if not rec:
         return None
     from test_rnn_layer_ttt_amd.build import source_digest
-    if rec.get("source_digest") != source_digest():
+    if rec.get("source_digest") != source_digest(kernel):
         return None        # the kernel changed since the counters were taken
     return rec.get("traffic_bytes")
 
@@ -233,7 +233,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only; the scans of a workload shard "
+        print("bench.py: measures one GPU only; the scans of a workload shard "
               "over GPUs by (batch, head) with no communication, and no multi-GPU figure "
               "is produced.", file=sys.stderr)
         sys.exit(2)

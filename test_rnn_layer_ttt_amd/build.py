@@ -27,15 +27,22 @@ CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
           "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
-def source_digest() -> str:
-    """SHA-256 over the library's sources and header (identifies a kernel build)."""
+def source_digest(kernel: str | None = None) -> str:
+    """SHA-256 identifying a build: over one kernel's source and the shared
+    kernel header (``kernel`` = "scan_mfma", "bwd_mfma", "scan_valu"), or over
+    every source and the public header (``kernel`` = None)."""
     import hashlib
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    if kernel is not None:
+        names = [kernel + ".hip", "scan_common.h"]
+    else:
+        names = sorted(os.listdir(CSRC))
+    for name in names:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
-    with open(os.path.join(INCLUDE, "ttt_linear.h"), "rb") as f:
-        h.update(f.read())
+    if kernel is None:
+        with open(os.path.join(INCLUDE, "ttt_linear.h"), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 

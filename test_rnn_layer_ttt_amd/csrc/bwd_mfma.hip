@@ -215,7 +215,8 @@ __device__ __forceinline__ float ld_in(const void* p, int64_t i) {
 // ---- state a wave keeps across a barrier ----
 // The roles share one register array, so the kernel needs registers for the
 // largest role rather than for all of them together:
-//   waves 1, 2, 5, 6: a 16x64 accumulator in [0, 16); wave 3: dk's H-side half
+//   waves 1, 5, 6: a 16x64 accumulator in [0, 16); waves 2 and 3: half of
+//   DY W and dk's H-side half ([0, 8) and [16, 24); [8, 16) and [0, 8))
 //   wave 1: v in [16, 32) (exact LayerNorm)
 //   wave 4: a tile of inputs in flight (LoadLayout); wave 7: its W, [0, 64)
 constexpr int kState = 80;
@@ -552,7 +553,7 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       }
     } else if (wave == 3 || wave == 2) {
       // dk's H-side half b1, column blocks j0, j0+1 (wave 3: 0-1 in state
-      // slots 0-1; wave 2: 2-3 in slots 4-5, beside its DY W product)
+      // slots 0-1; wave 2: 2-3 in slots 4-5), beside half of DY W each
       auto half = [&](auto s0c) {
         constexpr int s0 = decltype(s0c)::value;
         const int j0 = s0 == 0 ? 0 : 2;
@@ -583,22 +584,27 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
           }
         }
       };
-      if (wave == 3)
-        half(std::integral_constant<int, 0>{});
-      else
-        half(std::integral_constant<int, 4>{});
-      if (wave == 2 && prep) {
-        // dQ' = DY W of tile c-1
+      // dQ' = DY W of tile c-1, column blocks j0, j0+1 into state slots
+      // j0, j0+1 (wave 2: blocks 0-1; wave 3: blocks 2-3)
+      auto dqw = [&](auto j0c) {
+        constexpr int j0 = decltype(j0c)::value;
         const TileIn& tm = sm.ring[cm % 3];
         const float(*Wm)[KP] = sm.W[cm & 1];
         float a[16];
         frag_row64(tm.DY[l16], G, a);
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
+        for (int jb = j0; jb < j0 + 2; ++jb) {
           float bb[16];
           frag_col64(Wm, 16 * jb + l16, G, bb);
           put(st, jb, mma<16>(a, bb, f32x4{0, 0, 0, 0}));
         }
+      };
+      if (wave == 3) {
+        half(std::integral_constant<int, 0>{});
+        if (prep) dqw(std::integral_constant<int, 2>{});
+      } else {
+        half(std::integral_constant<int, 4>{});
+        if (prep) dqw(std::integral_constant<int, 0>{});
       }
     } else if (wave != 4 && prep) {
       const TileIn& tm = sm.ring[cm % 3];
@@ -648,6 +654,34 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
     }
     __syncthreads();
     // ============================ phase B ============================
+    // dq of tile c-1 = DY W - sum_{s<=t} eta_s (delta_s.dy_t) k_s, column
+    // blocks j0, j0+1 from DY W in state slots j0, j0+1 (wave 2: blocks 0-1,
+    // wave 3: blocks 2-3)
+    auto dq_blocks = [&](auto j0c) {
+      constexpr int j0 = decltype(j0c)::value;
+      const TileIn& tm = sm.ring[cm % 3];
+      const Grams& gm = sm.gr[cm & 1];
+      float a[4];
+      frag_col16(gm.DeDY, l16, G, a);   // DeDY[s][t], k = s, m = t
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int s = 4 * G + ks;
+        a[ks] = s <= l16 ? -tm.ETA[s] * a[ks] : 0.0f;
+      }
+      const int nm = rows(cm);
+      const int64_t t0 = int64_t(cm) * BT;
+#pragma unroll
+      for (int jb = j0; jb < j0 + 2; ++jb) {
+        float b[4];
+        frag_col16(tm.K, 16 * jb + l16, G, b);
+        const f32x4 v = mma<4>(a, b, blk(st, jb));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 4 * G + r;
+          if (t < nm) dq[(bhT + t0 + t) * D + 16 * jb + l16] = v[r];
+        }
+      }
+    };
     if (wave == 4 && c >= 2) {
       const int u = c - 2;
       loader_store<BF16>(st, ld_eta, ld_n, sm.ring[u % 3], lane, silu != 0);
@@ -747,32 +781,10 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
           if (t < nm) dgate[(bhT + t0 + t) * D + 16 * fb + l16] = y[r] * tm.G2[t][16 * fb + l16];
         }
       }
+    } else if (wave == 3) {
+      if (prep) dq_blocks(std::integral_constant<int, 2>{});
     } else if (wave == 2) {
-      if (prep) {
-        // dq of tile c-1 = DY W - sum_{s<=t} eta_s (delta_s.dy_t) k_s
-        const TileIn& tm = sm.ring[cm % 3];
-        const Grams& gm = sm.gr[cm & 1];
-        float a[4];
-        frag_col16(gm.DeDY, l16, G, a);   // DeDY[s][t], k = s, m = t
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int s = 4 * G + ks;
-          a[ks] = s <= l16 ? -tm.ETA[s] * a[ks] : 0.0f;
-        }
-        const int nm = rows(cm);
-        const int64_t t0 = int64_t(cm) * BT;
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-          float b[4];
-          frag_col16(tm.K, 16 * jb + l16, G, b);
-          const f32x4 v = mma<4>(a, b, blk(st, jb));
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 4 * G + r;
-            if (t < nm) dq[(bhT + t0 + t) * D + 16 * jb + l16] = v[r];
-          }
-        }
-      }
+      if (prep) dq_blocks(std::integral_constant<int, 0>{});
       if (live) {
         // d eta_logit of tile c = -sigmoid'(.)/d delta_t . a_t (a Gram's diagonal)
         const TileIn& tc = sm.ring[c % 3];
@@ -892,10 +904,10 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         store_block(sm.B2, 16 * jb, v, l16, G);
       }
     }
-    if (live && (wave == 7 || wave == 0 || wave == 1 || wave == 5 || wave == 3)) {
+    if (live && (wave == 7 || wave == 0 || wave == 1 || wave == 5 || wave == 6)) {
       // H += DY_c^T Q_c + DZ_c^T K_c by 16x16 blocks b = 4 ib + jb, in pairs
       // whose loads and MFMAs interleave: wave 7 takes pairs 0-2, wave 0
-      // pair 3, wave 1 pairs 4-5, wave 5 pair 6, wave 3 pair 7
+      // pair 3, wave 1 pairs 4-5, wave 5 pair 6, wave 6 pair 7
       const TileIn& tc = sm.ring[c % 3];
       const float(*DZ)[KP] = sm.wk[c & 1].X;
       const int p0 = wave == 7 ? 0 : wave == 0 ? 3 : wave == 1 ? 4 : wave == 5 ? 6 : 7;
