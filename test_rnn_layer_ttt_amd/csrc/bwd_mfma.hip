@@ -71,6 +71,32 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// 16-deep token contractions with bf16 operands (16x16x16 MFMA, lane group G
+// holding k = 4G..4G+3, the k of mfma4's four steps): an fp32 operand is split
+// into bf16 hi + lo (round to nearest each; |x - hi - lo| <= 2^-17 |x|), a
+// bf16-exact one (the bf16 inputs q, k) is taken as is
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ unsigned short bf16_rne(float x) {
+  return __builtin_bit_cast(unsigned short, static_cast<__bf16>(x));
+}
+__device__ __forceinline__ void split4(const float (&x)[4], i16x4& hi, i16x4& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const unsigned short h = bf16_rne(x[e]);
+    hi[e] = static_cast<short>(h);
+    lo[e] = static_cast<short>(bf16_rne(x[e] - __uint_as_float(static_cast<uint32_t>(h) << 16)));
+  }
+}
+__device__ __forceinline__ i16x4 exact4(const float (&x)[4]) {
+  i16x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = static_cast<short>(__float_as_uint(x[e]) >> 16);
+  return r;
+}
+__device__ __forceinline__ f32x4 mfma16(const i16x4& a, const i16x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
 // ---- wave-wide sums (lane = feature): row scans, row broadcasts, lane 63 ----
 template <int CTRL>
 __device__ __forceinline__ float dpp_add(float x) {
@@ -926,14 +952,29 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
           frag_col16(tc.Q, 16 * (jb0 + u) + l16, G, bq[u]);
           frag_col16(tc.K, 16 * (jb0 + u) + l16, G, bk[u]);
         }
+        if constexpr (BF16) {
+          // q and k are bf16 values: dy and dz split into hi + lo
+          i16x4 yh, yl, zh, zl;
+          split4(ay, yh, yl);
+          split4(az, zh, zl);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+          for (int u = 0; u < 2; ++u) {
+            const i16x4 q16 = exact4(bq[u]), k16 = exact4(bk[u]);
+            v[u] = mfma16(yh, q16, v[u]);
+            v[u] = mfma16(zh, k16, v[u]);
+            v[u] = mfma16(yl, q16, v[u]);
+            v[u] = mfma16(zl, k16, v[u]);
+          }
+        } else {
 #pragma unroll
-          for (int u = 0; u < 2; ++u) v[u] = mfma4(ay[ks], bq[u][ks], v[u]);
+          for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+            for (int u = 0; u < 2; ++u) v[u] = mfma4(ay[ks], bq[u][ks], v[u]);
 #pragma unroll
-          for (int u = 0; u < 2; ++u) v[u] = mfma4(az[ks], bk[u][ks], v[u]);
+          for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) v[u] = mfma4(az[ks], bk[u][ks], v[u]);
+        }
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
