@@ -3,12 +3,12 @@
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  It shares no code with the GPU path.
 """
-from .ttt_oracle import (EPS, LN_EXACT, LN_NONE, LN_ST, inner_grad_vector,
+from .ttt_oracle import (EPS, LN_EXACT, LN_NONE, LN_ST, inner_grad_vector, input_projections,
                          inner_grad_vector_vjp, layer_norm, ln_jacobian,
                          ln_jacobian_derivative, rel_max_err, sigmoid, silu, silu_grad,
                          ttt_linear_backward, ttt_linear_forward)
 
-__all__ = ["EPS", "LN_EXACT", "LN_NONE", "LN_ST", "inner_grad_vector",
+__all__ = ["EPS", "LN_EXACT", "LN_NONE", "LN_ST", "inner_grad_vector", "input_projections",
            "inner_grad_vector_vjp", "layer_norm", "ln_jacobian", "ln_jacobian_derivative",
            "rel_max_err", "sigmoid", "silu", "silu_grad", "ttt_linear_backward",
            "ttt_linear_forward"]

@@ -375,6 +375,40 @@ def ttt_linear_backward(q, k, v, eta_logit, gate_logit, W0, gamma, beta, dout, d
     return g
 
 
+def input_projections(x, w_proj, b_proj=None):
+    """The layer's input projections, the step before the scan.
+
+    "Edifice.Recurrent.TTT", "Equations (TTT-Linear)" (the projection lines:
+    q_t = W_q x_t, k_t = W_k x_t, v_t = W_v x_t, and the learning-rate gate
+    from W_eta x_t) and "Architecture" (the TTT layer projects its input to
+    Q, K, V, eta and gate).  One matrix product per head; the gate and the
+    eta logit come out before any sigmoid (the scan applies it).
+
+    x: [B, T, hidden].  w_proj: [H, 4d+1, hidden], the rows of one head
+    stacked as W_q (d rows), W_k (d), W_v (d), W_gate (d), W_eta (1) (a layout
+    choice; the pages give no order).  b_proj: [H, 4d+1] or None; the pages
+    write the projections without a bias, so None is their reading and a
+    bias is an option.  Returns q, k, v, eta_logit, gate_logit in the scan's
+    layouts ([B, H, T, d], eta_logit [B, H, T]), float64.
+
+    Parity: pinned by tests/test_oracle_projection.py (a brute-force loop on
+    tiny inputs, one-hot weight rows that pick out coordinates of x, the
+    bias alone, linearity).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w_proj, dtype=np.float64)
+    H, R, hidden = w.shape
+    d = (R - 1) // 4
+    if R != 4 * d + 1 or x.shape[-1] != hidden:
+        raise ValueError("w_proj must be [H, 4d+1, hidden] with x [B, T, hidden]")
+    y = np.einsum("btk,hrk->bhtr", x, w)
+    if b_proj is not None:
+        y = y + np.asarray(b_proj, dtype=np.float64)[None, :, None, :]
+    q, k, v, gate = (np.ascontiguousarray(y[..., i * d:(i + 1) * d]) for i in range(4))
+    eta = np.ascontiguousarray(y[..., 4 * d])
+    return q, k, v, eta, gate
+
+
 def rel_max_err(got, ref) -> float:
     """Relative max error of one output tensor: max|got - ref| / max|ref|."""
     got = np.asarray(got, dtype=np.float64)

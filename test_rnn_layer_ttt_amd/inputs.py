@@ -150,3 +150,23 @@ def make_update_mask(B: int, H: int, T: int, chunk: int, rate: float, seed: int)
     rng = np.random.Generator(np.random.PCG64(seed))
     n = -(-T // chunk) if T > 0 else 0
     return (rng.random((B, H, n)) < rate).astype(np.uint8)
+
+
+def make_projection_case(B: int, T: int, hidden: int, H: int, d: int, seed: int, *,
+                         with_bias: bool = False):
+    """Seeded input of the layer's input projections: ``(x, w_proj, b_proj)``.
+
+    x [B,T,hidden] ~ N(0,1) and w_proj [H,4d+1,hidden] ~ N(0, 1/hidden) (so
+    that each projection is ~ N(0,1), the scale of the scan's own inputs),
+    both rounded to bf16 (nearest even) and handed out as float32 holding the
+    bf16 values; b_proj [H,4d+1] ~ N(0, 0.1^2) in float32, or None.  Draw
+    order x, w_proj, b_proj.  The rows of one head are stacked q (d), k (d),
+    v (d), gate (d), eta (1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = round_to_bf16(rng.standard_normal((B, T, hidden), dtype=np.float32))
+    w = rng.standard_normal((H, 4 * d + 1, hidden), dtype=np.float32)
+    w = round_to_bf16(_f32(w.astype(np.float64) / np.sqrt(hidden)))
+    b = None
+    if with_bias:
+        b = _f32(rng.standard_normal((H, 4 * d + 1), dtype=np.float32).astype(np.float64) * 0.1)
+    return x, w, b
