@@ -33,6 +33,8 @@ import numpy as np  # noqa: E402
 from test_rnn_layer_ttt_amd.inputs import WORKLOADS, make_inputs  # noqa: E402
 
 METRIC = "TTT-Linear scan token-heads/s at d=64 + % of HBM/FP32 roofline, 1 MI355X"
+METRIC_PROJECT = ("TTT-Linear layer (input projections + scan) token-heads/s at d=64 "
+                  "+ % of bf16 MFMA roofline of the projection kernel, 1 MI355X")
 METRIC_TRAIN = ("TTT-Linear training pass (recording forward + backward) token-heads/s at d=64 "
                 "+ % of HBM roofline of the backward kernel, 1 MI355X")
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
@@ -100,7 +102,25 @@ def kernel_info(x):
     return name, ("alu" if x.in_bf16 else "hbm")
 
 
-def roofline(x, kernel_ms, traffic, train=False, mask=None):
+def projection_work(x):
+    """Flops and compulsory HBM bytes of one projection launch: x [B,T,hidden]
+    and the weights [H,4d+1,hidden] in bf16, the five results out in the
+    scan's input type; 2 flops per product of hidden = H d terms."""
+    B, H, T, d = x.q.shape
+    hidden, rows = H * d, H * (4 * d + 1)
+    out_size = 2 if x.in_bf16 else 4
+    nbytes = B * T * hidden * 2 + rows * hidden * 2 + B * T * rows * out_size
+    return B * H * T, nbytes, 2 * B * T * hidden * rows
+
+
+def roofline(x, kernel_ms, traffic, train=False, mask=None, project=False):
+    if project:
+        n, nbytes, flops = projection_work(x)
+        achieved = flops / (kernel_ms / 1e3) / 1e12
+        return "proj_mfma", dict(bound="mfma", achieved=round(achieved, 1),
+                                 peak=BF16_MATRIX_PEAK_TFLOPS, unit="TFLOP/s",
+                                 frac=round(achieved / BF16_MATRIX_PEAK_TFLOPS, 4),
+                                 traffic=traffic)
     if train:
         n, nbytes, flops = backward_work(x)
         name, bound = "bwd_mfma", "hbm"
@@ -126,6 +146,7 @@ _CPU_SAMPLE = None
 
 _CPU_TRAIN = False
 _CPU_MASK = None
+_CPU_PROJ = None   # (x, w_proj) of the layer-pass workload, float32 holding bf16 values
 _CPU_SILU = False
 
 
@@ -134,9 +155,21 @@ def _oracle_worker(idx):
 
     import oracle
     x = _CPU_SAMPLE
-    args = (x.q[:, idx], x.k[:, idx], x.v[:, idx], x.eta_logit[:, idx], x.gate_logit[:, idx],
-            x.W0[:, idx], x.gamma[idx], x.beta[idx])
     with threadpool_limits(limits=1):
+        if _CPU_PROJ is not None:
+            # the oracle's projections of the sampled scans, in the scan's input type
+            from test_rnn_layer_ttt_amd.inputs import round_to_bf16
+            xs, ws = _CPU_PROJ
+            pairs = x.meta["subset"]
+            outs = [oracle.input_projections(xs[pairs[i][0]][None], ws[pairs[i][1]][None])
+                    for i in idx]
+            cat = [np.concatenate([o[j] for o in outs], axis=1) for j in range(5)]
+            if x.in_bf16:
+                cat = [round_to_bf16(a.astype(np.float32)) for a in cat]
+            args = (*cat, x.W0[:, idx], x.gamma[idx], x.beta[idx])
+        else:
+            args = (x.q[:, idx], x.k[:, idx], x.v[:, idx], x.eta_logit[:, idx],
+                    x.gate_logit[:, idx], x.W0[:, idx], x.gamma[idx], x.beta[idx])
         m = None if _CPU_MASK is None else _CPU_MASK[:, idx]
         oracle.ttt_linear_forward(*args, ln=x.ln, dual=x.dual, chunk=x.chunk, update_mask=m,
                                   silu_qk=_CPU_SILU)
@@ -153,12 +186,14 @@ def _cotangents(x):
     return make_cotangents(B, H, T, d, seed=x.meta.get("seed", 0) + 1000)
 
 
-def cpu_baseline(x, n_scans, workers, train=False, mask=None):
+def cpu_baseline(x, n_scans, workers, train=False, mask=None, proj=None):
     """Time the oracle on ``n_scans`` scans of ``x`` (full length) over ``workers``
-    processes; with ``train`` its forward and its backward, as one training pass."""
+    processes; with ``train`` its forward and its backward, as one training pass;
+    with ``proj`` = (x, w_proj) its input projections of each scan, then the scan."""
     import multiprocessing as mp
-    global _CPU_SAMPLE, _CPU_TRAIN, _CPU_MASK
+    global _CPU_SAMPLE, _CPU_TRAIN, _CPU_MASK, _CPU_PROJ
     _CPU_TRAIN = train
+    _CPU_PROJ = proj
     B, H, T, d = x.q.shape
     n_scans = min(n_scans, B * H)
     step = max(1, (B * H) // n_scans)
@@ -174,10 +209,13 @@ def cpu_baseline(x, n_scans, workers, train=False, mask=None):
         done = sum(pool.map(_oracle_worker, groups))
     sec = time.perf_counter() - t0
     _CPU_SAMPLE = None
+    _CPU_PROJ = None
+    what = (", forward and backward" if train else
+            ", input projections then the scan" if proj is not None else "")
     return dict(value=round(done * T / sec, 1), unit="token-heads/s", cores=len(groups),
                 kind="oracle",
                 sample=f"{done} of {B * H} scans at full length T={T}"
-                       f"{', forward and backward' if train else ''} (float64 NumPy, "
+                       f"{what} (float64 NumPy, "
                        f"{len(groups)} processes x 1 BLAS thread, {sec:.1f} s wall)")
 
 
@@ -213,8 +251,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="h1024_T4096_bf16", choices=sorted(WORKLOADS))
-    ap.add_argument("--pass", dest="pass_", default="forward", choices=("forward", "train"),
-                    help="forward: the scan; train: recording forward + backward")
+    ap.add_argument("--pass", dest="pass_", default="forward",
+                    choices=("forward", "train", "project"),
+                    help="forward: the scan; train: recording forward + backward; "
+                         "project: the layer's input projections from x, then the scan")
     ap.add_argument("--silu-qk", action="store_true",
                     help="the :mlp variant: SiLU on q and k before the inner model")
     ap.add_argument("--update-rate", type=float, default=None,
@@ -241,12 +281,16 @@ def main():
     x = make_inputs(args.workload)
     B, H, T, d = x.q.shape
     train = args.pass_ == "train"
+    project = args.pass_ == "project"
+    if project and (d != 64 or args.update_rate is not None or args.silu_qk):
+        print("bench.py: --pass project covers d = 64 and the plain scan", file=sys.stderr)
+        sys.exit(2)
     if train and ((x.dual and x.chunk != ttt_record_chunk()) or d != 64):
         print(f"bench.py: the backward covers d = 64, per-token or dual form with chunks of "
               f"{ttt_record_chunk()}; workload {args.workload} is not one", file=sys.stderr)
         sys.exit(2)
     if args.cpu_scans is None:
-        args.cpu_scans = 128 if train else 256
+        args.cpu_scans = 128 if train else 32 if project else 256
     mask_np = None
     if args.update_rate is not None:
         if train or not x.dual:
@@ -257,10 +301,17 @@ def main():
         mask_np = make_update_mask(B, H, T, x.chunk, args.update_rate,
                                    seed=x.meta.get("seed", 0) + 2000)
 
+    proj_np = None
+    if project:
+        from test_rnn_layer_ttt_amd.inputs import make_projection_case
+        xp, wp, _ = make_projection_case(B, T, H * d, H, d, seed=x.meta.get("seed", 0) + 3000)
+        proj_np = (xp, wp)
+
     # the CPU baseline runs before any GPU use (its workers are forked)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(x, args.cpu_scans, host_cores(), train, mask_np)
+        cpu = cpu_baseline(x, args.cpu_scans, host_cores(), train, mask_np,
+                           proj_np if project else None)
 
     import torch
 
@@ -279,6 +330,19 @@ def main():
     mode = ttt.mode_bits(x.ln, x.dual, x.in_bf16, args.silu_qk)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), el.data_ptr(), gl.data_ptr(),
             W0.data_ptr(), gamma.data_ptr(), beta.data_ptr(), out.data_ptr(), Wf.data_ptr())
+    if project:
+        # the projections overwrite q, k, v, eta and gate, which the scan then reads
+        xt = torch.from_numpy(proj_np[0]).to(dev).to(torch.bfloat16)
+        wt = torch.from_numpy(proj_np[1]).to(dev).to(torch.bfloat16)
+        proj_np = None
+
+        def projection():
+            st = ttt.ttt_linear_project(xt.data_ptr(), wt.data_ptr(), None, q.data_ptr(),
+                                        k.data_ptr(), v.data_ptr(), el.data_ptr(),
+                                        gl.data_ptr(), B, T, H * d, H, d, mode,
+                                        stream.cuda_stream)
+            if st != ttt.TTT_OK:
+                raise RuntimeError(f"ttt_linear_project: {ttt.ttt_status_string(st)}")
 
     if mask_np is None:
         def forward():
@@ -331,6 +395,9 @@ def main():
         if train:
             forward_record()
             backward()
+        elif project:
+            projection()
+            forward()
         else:
             forward()
     torch.cuda.synchronize()
@@ -349,6 +416,13 @@ def main():
             starts[i].record(stream)
             backward()
             ends[i].record(stream)
+        elif project:
+            starts[i].record(stream)
+            projection()
+            ends[i].record(stream)
+            fstarts[i].record(stream)
+            forward()
+            fends[i].record(stream)
         else:
             starts[i].record(stream)
             forward()
@@ -359,18 +433,19 @@ def main():
     avg_kernel_ms = float(np.mean(kernel_ms))
     ms_per_step = wall * 1e3 / args.steps
     n_tok = B * H * T
-    kernel = "bwd_mfma" if train else kernel_info(x)[0]
-    traffic_key = args.workload + ("/backward" if train else "")
+    kernel = "bwd_mfma" if train else "proj_mfma" if project else kernel_info(x)[0]
+    traffic_key = args.workload + ("/backward" if train else "/project" if project else "")
     if mask_np is not None:
         traffic_key = args.workload + f"/update{args.update_rate:g}"
     if args.silu_qk:
         traffic_key += "/silu"
-    kname, roof = roofline(x, avg_kernel_ms, load_traffic(kernel, traffic_key), train, mask_np)
+    kname, roof = roofline(x, avg_kernel_ms, load_traffic(kernel, traffic_key), train, mask_np,
+                           project)
 
     mode_name = ("dual-form chunk %d" % x.chunk if x.dual else "per-token") + \
         {"st": "", "exact": ", exact LN Jacobian", "none": ", no LN"}[x.ln]
     line = {
-        "metric": METRIC_TRAIN if train else METRIC,
+        "metric": METRIC_TRAIN if train else METRIC_PROJECT if project else METRIC,
         "value": round(n_tok / (ms_per_step / 1e3), 1),
         "unit": "token-heads/s",
         "n_gpus": 1,
@@ -399,6 +474,11 @@ def main():
         line["config"]["pass"] = "train: recording forward + backward"
         fwd_ms = [s_.elapsed_time(e_) for s_, e_ in zip(fstarts, fends)]
         line["config"]["forward_record_ms_avg"] = round(float(np.mean(fwd_ms)), 4)
+    if project:
+        line["config"]["pass"] = ("layer: input projections from x [B,T,hidden] bf16, "
+                                  "then the scan")
+        scan_ms = [s_.elapsed_time(e_) for s_, e_ in zip(fstarts, fends)]
+        line["config"]["scan_ms_avg"] = round(float(np.mean(scan_ms)), 4)
     print(json.dumps(line), flush=True)
 
     if args.copy_probe_mib > 0:

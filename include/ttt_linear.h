@@ -212,6 +212,37 @@ int32_t ttt_linear_backward(const void* q, const void* k, const void* v,
                             int64_t B, int64_t H, int64_t T, int64_t d,
                             uint32_t mode, int64_t chunk, void* stream);
 
+/*
+ * ---- The layer's input projections ----
+ *
+ * q_t = W_q x_t, k_t = W_k x_t, v_t = W_v x_t, and the learning-rate and gate
+ * logits W_eta x_t, W_gate x_t of every head ("Edifice.Recurrent.TTT",
+ * "Equations (TTT-Linear)" and "Architecture": the layer projects its input
+ * to Q, K, V, eta and gate before the scan), in one launch that reads x once
+ * and writes the five results in the layouts ttt_linear_forward reads.
+ *
+ *   x          [B,T,hidden]   bf16
+ *   w_proj     [H,4d+1,hidden] bf16; the 4d+1 rows of head h are W_q (d rows),
+ *                             W_k (d), W_v (d), W_gate (d), W_eta (1)
+ *   b_proj     [H,4d+1] fp32, added to the products, or NULL (no bias, as the
+ *                             pages write the projections)
+ *   q, k, v, gate_logit [B,H,T,d] and eta_logit [B,H,T]: outputs, bf16 when
+ *              mode has TTT_IN_BF16 (rounded to nearest even from the fp32
+ *              sums), else fp32
+ *
+ * mode is the scan's mode word (only TTT_IN_BF16 is read here), so one mode
+ * serves both calls.  Supported: d = 64, hidden a multiple of 32 (otherwise
+ * TTT_ERR_UNSUPPORTED).  x, w_proj and q, k, v, gate_logit 16-byte aligned,
+ * eta_logit and b_proj element-aligned.  The outputs must not overlap one
+ * another or the inputs.  T == 0 writes nothing.  Runs asynchronously on
+ * `stream`; the accumulation order is fixed, so repeated calls give
+ * identical bits.
+ */
+int32_t ttt_linear_project(const void* x, const void* w_proj, const float* b_proj,
+                           void* q, void* k, void* v, void* eta_logit, void* gate_logit,
+                           int64_t B, int64_t T, int64_t hidden, int64_t H, int64_t d,
+                           uint32_t mode, void* stream);
+
 /* A static, human-readable description of a status code (never NULL). */
 const char* ttt_status_string(int32_t status);
 

@@ -36,7 +36,7 @@ RECORD_CHUNK = 16
 
 #: every symbol the header declares
 EXPORTED = ("ttt_linear_backward", "ttt_linear_forward", "ttt_linear_forward_masked",
-            "ttt_linear_forward_record",
+            "ttt_linear_forward_record", "ttt_linear_project",
             "ttt_linear_kernel", "ttt_linear_record_bytes", "ttt_linear_validate",
             "ttt_status_string", "ttt_version")
 
@@ -88,6 +88,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ttt_linear_backward.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.c_int64] +
                                         [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 4 +
                                         [ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p])
+    lib.ttt_linear_project.restype = ctypes.c_int32
+    lib.ttt_linear_project.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int64] * 5 + [
+        ctypes.c_uint32, ctypes.c_void_p]
     _lib = lib
     return lib
 
@@ -170,6 +173,16 @@ def ttt_linear_backward(q, k, v, eta_logit, gate_logit, gamma, beta, record, rec
         int(record_bytes), p(dout), p(dW_final), p(dq), p(dk), p(dv), p(deta_logit),
         p(dgate_logit), p(dW0), p(dgamma), p(dbeta), int(B), int(H), int(T), int(d),
         ctypes.c_uint32(int(mode)), int(chunk), p(stream)))
+
+
+def ttt_linear_project(x, w_proj, b_proj, q, k, v, eta_logit, gate_logit, B, T, hidden, H, d,
+                       mode, stream) -> int:
+    """The input projections with raw pointers; returns the status code."""
+    lib = load_library()
+    p = lambda x_: None if x_ is None else ctypes.c_void_p(int(x_))
+    return int(lib.ttt_linear_project(
+        p(x), p(w_proj), p(b_proj), p(q), p(k), p(v), p(eta_logit), p(gate_logit), int(B),
+        int(T), int(hidden), int(H), int(d), ctypes.c_uint32(int(mode)), p(stream)))
 
 
 def check(status: int) -> None:
@@ -271,6 +284,42 @@ def _check_inputs(q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("every tensor must be a contiguous device tensor")
     return B, H, T, d
+
+
+def project(x, w_proj, b_proj=None, *, out_bf16: bool = True, stream=None):
+    """The layer's input projections (:func:`ttt_linear_project`) on torch
+    device tensors: x bfloat16 [B,T,hidden], w_proj bfloat16 [H,4d+1,hidden]
+    (rows q, k, v, gate, eta per head), b_proj float32 [H,4d+1] or None.
+    Returns ``(q, k, v, eta_logit, gate_logit)`` in the scan's layouts,
+    bfloat16 (``out_bf16``) or float32, ready for :func:`forward`."""
+    import torch
+
+    if x.dim() != 3 or w_proj.dim() != 3 or x.shape[2] != w_proj.shape[2]:
+        raise ValueError("x must be [B,T,hidden] and w_proj [H,4d+1,hidden]")
+    if x.dtype != torch.bfloat16 or w_proj.dtype != torch.bfloat16:
+        raise ValueError("x and w_proj must be bfloat16")
+    B, T, hidden = x.shape
+    H, rows, _ = w_proj.shape
+    d = (rows - 1) // 4
+    if rows != 4 * d + 1:
+        raise ValueError("w_proj must have 4d+1 rows per head")
+    if b_proj is not None and (b_proj.dtype != torch.float32 or tuple(b_proj.shape) != (H, rows)):
+        raise ValueError("b_proj must be float32 [H,4d+1]")
+    for t in (x, w_proj) + (() if b_proj is None else (b_proj,)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("every tensor must be a contiguous device tensor")
+    dt = torch.bfloat16 if out_bf16 else torch.float32
+    opt = dict(dtype=dt, device=x.device)
+    q, k, v, gate = (torch.empty((B, H, T, d), **opt) for _ in range(4))
+    eta = torch.empty((B, H, T), **opt)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    mode = TTT_IN_BF16 if out_bf16 else 0
+    check(ttt_linear_project(x.data_ptr(), w_proj.data_ptr(),
+                             None if b_proj is None else b_proj.data_ptr(), _ptr(q), _ptr(k),
+                             _ptr(v), _ptr(eta), _ptr(gate), B, T, hidden, H, d, mode,
+                             stream.cuda_stream))
+    return q, k, v, eta, gate
 
 
 def forward_record(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *,

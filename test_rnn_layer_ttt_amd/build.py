@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libttt_linear.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["ttt_linear.hip", "scan_valu.hip", "scan_mfma.hip", "bwd_mfma.hip"]
+SOURCES = ["ttt_linear.hip", "scan_valu.hip", "scan_mfma.hip", "bwd_mfma.hip", "proj_mfma.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

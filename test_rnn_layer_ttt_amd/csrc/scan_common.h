@@ -82,6 +82,25 @@ hipError_t launch_scan_valu(const ScanArgs& a, hipStream_t stream);
 hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t stream);
 bool scan_mfma_supports(const ScanArgs& a);
 
+// The layer's input projections: x [B,T,hidden] bf16 times the stacked
+// weights w [H,4d+1,hidden] bf16 (+ bias [H,4d+1] fp32), into q, k, v, gate
+// [B,H,T,d] and eta [B,H,T], bf16 or fp32.
+struct ProjArgs {
+  const void* x;
+  const void* w;
+  const float* bias;   // nullptr: none
+  void* q;
+  void* k;
+  void* v;
+  void* eta;
+  void* gate;
+  int64_t B, T, hidden, H, d;
+  bool out_bf16;
+};
+// MFMA projection kernel for d = 64 and hidden a multiple of 32.
+bool proj_mfma_supports(const ProjArgs& a);
+hipError_t launch_proj_mfma(const ProjArgs& a, hipStream_t stream);
+
 // Backward of the per-token scan, and of the dual form with chunks of
 // kRecTile tokens, for d = 64 from a record; hipErrorNotSupported for
 // anything else.

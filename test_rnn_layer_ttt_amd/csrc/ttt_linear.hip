@@ -296,7 +296,69 @@ int32_t validate_backward(const void* q, const void* k, const void* v, const voi
   return TTT_OK;
 }
 
+// Every argument check of ttt_linear_project; fills *a.  Makes no HIP call.
+int32_t validate_project(const void* x, const void* w_proj, const float* b_proj, void* q,
+                         void* k, void* v, void* eta_logit, void* gate_logit, int64_t B,
+                         int64_t T, int64_t hidden, int64_t H, int64_t d, uint32_t mode,
+                         ttt::ProjArgs* a) {
+  const uint32_t known = TTT_DUAL | TTT_LN_EXACT | TTT_IN_BF16 | TTT_NO_LN | TTT_SILU_QK;
+  if (mode & ~known) return TTT_ERR_MODE;
+  if (B < 1 || H < 1 || d < 1 || hidden < 1 || T < 0) return TTT_ERR_SHAPE;
+  int64_t BT, x_elems, rows, w_elems, BH, BHT, out_elems;
+  if (!mul_ok(B, T, &BT) || !mul_ok(BT, hidden, &x_elems) || x_elems > INT64_MAX / 2)
+    return TTT_ERR_SHAPE;
+  if (!mul_ok(d, 4, &rows) || !mul_ok(H, rows + 1, &rows) || !mul_ok(rows, hidden, &w_elems) ||
+      w_elems > INT64_MAX / 2)
+    return TTT_ERR_SHAPE;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, T, &BHT) || !mul_ok(BHT, d, &out_elems) ||
+      out_elems > INT64_MAX / 4 || hidden > INT32_MAX || H > INT32_MAX / 2)
+    return TTT_ERR_SHAPE;
+  if (d != 64 || hidden % 32 != 0) return TTT_ERR_UNSUPPORTED;
+  if (T > 0 && (x == nullptr || w_proj == nullptr || q == nullptr || k == nullptr ||
+                v == nullptr || eta_logit == nullptr || gate_logit == nullptr))
+    return TTT_ERR_NULL;
+  const bool bf16 = (mode & TTT_IN_BF16) != 0;
+  const int64_t osz = bf16 ? 2 : 4;
+  if (T > 0) {
+    if (!aligned(x, 16) || !aligned(w_proj, 16) || (b_proj && !aligned(b_proj, 4)))
+      return TTT_ERR_UNSUPPORTED;
+    const void* outs16[] = {q, k, v, gate_logit};
+    for (const void* p : outs16)
+      if (!aligned(p, 16)) return TTT_ERR_UNSUPPORTED;
+    if (!aligned(eta_logit, static_cast<uintptr_t>(osz))) return TTT_ERR_UNSUPPORTED;
+    const int64_t ts = 1;
+    const Range outs[] = {span(q, ts * out_elems * osz), span(k, ts * out_elems * osz),
+                          span(v, ts * out_elems * osz), span(gate_logit, ts * out_elems * osz),
+                          span(eta_logit, ts * BHT * osz)};
+    const Range ins[] = {span(x, x_elems * 2), span(w_proj, w_elems * 2),
+                         span(b_proj, b_proj ? rows * 4 : 0)};
+    constexpr int kOuts = sizeof(outs) / sizeof(outs[0]);
+    for (int i = 0; i < kOuts; ++i) {
+      for (int j = i + 1; j < kOuts; ++j)
+        if (overlaps(outs[i], outs[j])) return TTT_ERR_ALIAS;
+      for (const Range& r : ins)
+        if (overlaps(outs[i], r)) return TTT_ERR_ALIAS;
+    }
+  }
+  *a = ttt::ProjArgs{x, w_proj, b_proj, q, k, v, eta_logit, gate_logit, B, T, hidden, H, d, bf16};
+  return TTT_OK;
+}
+
 }  // namespace
+
+extern "C" int32_t ttt_linear_project(const void* x, const void* w_proj, const float* b_proj,
+                                      void* q, void* k, void* v, void* eta_logit,
+                                      void* gate_logit, int64_t B, int64_t T, int64_t hidden,
+                                      int64_t H, int64_t d, uint32_t mode, void* stream) {
+  ttt::ProjArgs a;
+  const int32_t st = validate_project(x, w_proj, b_proj, q, k, v, eta_logit, gate_logit, B, T,
+                                      hidden, H, d, mode, &a);
+  if (st != TTT_OK) return st;
+  if (T == 0) return TTT_OK;
+  const hipError_t err = ttt::launch_proj_mfma(a, static_cast<hipStream_t>(stream));
+  if (err == hipErrorNotSupported) return TTT_ERR_UNSUPPORTED;
+  return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
 
 extern "C" int32_t ttt_linear_validate(const void* q, const void* k, const void* v,
                                        const void* eta_logit, const void* gate_logit,

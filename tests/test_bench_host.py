@@ -73,3 +73,21 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_projection_work_and_its_matrix_roofline():
+    a = make_case(2, 4, 32, 64, seed=4, in_bf16=True)
+    b = make_case(2, 4, 64, 64, seed=4, in_bf16=True)
+    c = make_case(2, 4, 32, 64, seed=4)
+    _, by_a, fl_a = bench.projection_work(a)
+    _, by_b, fl_b = bench.projection_work(b)
+    _, by_c, _ = bench.projection_work(c)
+    hidden, rows = 4 * 64, 4 * (4 * 64 + 1)
+    assert fl_b == 2 * fl_a == 2 * (2 * 2 * 32 * hidden * rows)
+    # 32 more tokens of 2 batches: their x rows in and their results out (bf16)
+    assert by_b - by_a == 2 * 32 * (hidden * 2 + rows * 2)
+    assert by_c - by_a == 2 * 32 * rows * 2          # fp32 results are twice as wide
+    name, roof = bench.roofline(a, kernel_ms=1e-3, traffic=None, project=True)
+    assert name == "proj_mfma" and roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s"
+    assert roof["peak"] == bench.BF16_MATRIX_PEAK_TFLOPS
+    assert roof["achieved"] == pytest.approx(fl_a / 1e-6 / 1e12, rel=1e-3)
