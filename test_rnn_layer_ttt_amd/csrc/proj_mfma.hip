@@ -15,8 +15,12 @@
 // tiles holding the eta rows of up to 128 heads.  K runs in steps of 32
 // through double-buffered LDS; four waves each own a 64 x 64 block of 4 x 4
 // MFMA tiles.  In a 32-deep step lane group G holds k = 8G..8G+7 of its row
-// for both operands, so every operand fetch is one 16-byte LDS read and the
-// 64 lanes of a wave read 1 KiB of consecutive bytes.
+// for both operands, so every operand fetch is one 16-byte LDS read; LDS rows
+// are padded to 80 bytes so that the 16-byte reads of neighbouring rows fall
+// in different banks.  The global loads of the next step are issued before a
+// step's MFMAs and are unconditional (a row past the end reads row 0 and is
+// replaced by zeros when it is stored to LDS), so their wait comes after the
+// MFMAs.
 #include "scan_common.h"
 
 #include <cstdint>
@@ -29,6 +33,7 @@ constexpr int R = 4 * D + 1;    // weight rows per head
 constexpr int TM = 128;         // tokens per tile
 constexpr int TN = 128;         // weight rows per tile
 constexpr int TK = 32;          // k per step
+constexpr int KPAD = TK + 8;    // padded LDS row (bf16): 80 bytes
 constexpr int NT = 256;         // threads: four waves
 constexpr int NXCD = 8;         // workgroups are dealt round-robin over the XCDs
 
@@ -36,8 +41,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 struct alignas(16) ProjSmem {
-  uint16_t A[2][TM][TK];   // x rows (tokens), k-contiguous
-  uint16_t B[2][TN][TK];   // weight rows, k-contiguous
+  uint16_t A[2][TM][KPAD];   // x rows (tokens), k-contiguous
+  uint16_t B[2][TN][KPAD];   // weight rows, k-contiguous
 };
 
 __device__ __forceinline__ uint16_t to_bf16(float x) {
@@ -49,16 +54,19 @@ __global__ void __launch_bounds__(NT)
 proj_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                  const float* __restrict__ bias, void* __restrict__ q, void* __restrict__ k,
                  void* __restrict__ v, void* __restrict__ gate, void* __restrict__ eta,
-                 int64_t M, int64_t T, int hidden, int H, int ntn, int64_t ntiles,
-                 int64_t per_xcd) {
+                 int64_t M, int64_t T, int hidden, int H, int ntn, int64_t mtiles) {
   __shared__ ProjSmem sm;
-  // the tiles of one XCD are consecutive, N fastest: tiles that share x rows
-  // run on the same L2
-  const int64_t L = blockIdx.x;
-  const int64_t tile = (L % NXCD) * per_xcd + L / NXCD;
-  if (tile >= ntiles) return;
-  const int64_t mt = tile / ntn;
-  const int nt = static_cast<int>(tile % ntn);
+  // XCD x (workgroups are dealt to the XCDs round-robin) takes the weight
+  // tiles nt = x, x + 8, ... for every token tile: its share of the weights
+  // stays in its L2 while x streams through, and consecutive workgroups on it
+  // share their x rows
+  const int xcd = static_cast<int>(blockIdx.x % NXCD);
+  const int64_t slot = blockIdx.x / NXCD;
+  const int cx = (ntn - xcd + NXCD - 1) / NXCD;     // weight tiles of this XCD
+  if (cx == 0) return;
+  const int64_t mt = slot / cx;
+  if (mt >= mtiles) return;
+  const int nt = xcd + NXCD * static_cast<int>(slot % cx);
   const int64_t m0 = mt * TM;
   const bool eta_tile = nt >= 2 * H;
   const int h = eta_tile ? 0 : nt >> 1;        // head of a q/k or v/gate tile
@@ -74,6 +82,7 @@ proj_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
   // global -> LDS: 512 chunks of 16 bytes per operand and step, two per thread
   const uint16_t* arow[2];
   const uint16_t* brow[2];
+  bool aok[2], bok[2];
   int crow[2], cpart[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -81,28 +90,32 @@ proj_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     crow[j] = c >> 2;
     cpart[j] = c & 3;
     const int64_t m = m0 + crow[j];
-    arow[j] = m < M ? x + m * hidden + 8 * cpart[j] : nullptr;
+    aok[j] = m < M;
+    arow[j] = x + (aok[j] ? m : 0) * hidden + 8 * cpart[j];
     int64_t wr = -1;
     if (!eta_tile) {
       wr = int64_t(h) * R + TN * pair + crow[j];
     } else if (e0 + crow[j] < H) {
       wr = int64_t(e0 + crow[j]) * R + 4 * D;
     }
-    brow[j] = wr >= 0 ? w + wr * hidden + 8 * cpart[j] : nullptr;
+    bok[j] = wr >= 0;
+    brow[j] = w + (bok[j] ? wr : 0) * hidden + 8 * cpart[j];
   }
   uint4 ra[2], rb[2];
   auto fetch = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      ra[j] = arow[j] ? *reinterpret_cast<const uint4*>(arow[j] + k0) : uint4{0, 0, 0, 0};
-      rb[j] = brow[j] ? *reinterpret_cast<const uint4*>(brow[j] + k0) : uint4{0, 0, 0, 0};
+      ra[j] = *reinterpret_cast<const uint4*>(arow[j] + k0);
+      rb[j] = *reinterpret_cast<const uint4*>(brow[j] + k0);
     }
   };
   auto stash = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      *reinterpret_cast<uint4*>(&sm.A[buf][crow[j]][8 * cpart[j]]) = ra[j];
-      *reinterpret_cast<uint4*>(&sm.B[buf][crow[j]][8 * cpart[j]]) = rb[j];
+      // rows past the end read a valid row; their data is replaced by zeros here,
+      // after this step's MFMAs, so the loads' latency stays hidden
+      *reinterpret_cast<uint4*>(&sm.A[buf][crow[j]][8 * cpart[j]]) = aok[j] ? ra[j] : uint4{0, 0, 0, 0};
+      *reinterpret_cast<uint4*>(&sm.B[buf][crow[j]][8 * cpart[j]]) = bok[j] ? rb[j] : uint4{0, 0, 0, 0};
     }
   };
 
@@ -181,20 +194,20 @@ hipError_t launch_proj_mfma(const ProjArgs& a, hipStream_t s) {
   const int64_t M = a.B * a.T;
   if (M == 0) return hipSuccess;
   const int ntn = static_cast<int>(2 * a.H + (a.H + TN - 1) / TN);
-  const int64_t ntiles = ((M + TM - 1) / TM) * ntn;
-  const int64_t per_xcd = (ntiles + NXCD - 1) / NXCD;
-  const int64_t grid = per_xcd * NXCD;
+  const int64_t mtiles = (M + TM - 1) / TM;
+  const int64_t cmax = (ntn + NXCD - 1) / NXCD;     // weight tiles of the busiest XCD
+  const int64_t grid = NXCD * cmax * mtiles;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   const uint16_t* w = static_cast<const uint16_t*>(a.w);
   if (a.out_bf16)
     hipLaunchKernelGGL((proj_mfma_kernel<true>), dim3(static_cast<unsigned>(grid)), dim3(NT), 0, s,
                        x, w, a.bias, a.q, a.k, a.v, a.gate, a.eta, M, a.T,
-                       static_cast<int>(a.hidden), static_cast<int>(a.H), ntn, ntiles, per_xcd);
+                       static_cast<int>(a.hidden), static_cast<int>(a.H), ntn, mtiles);
   else
     hipLaunchKernelGGL((proj_mfma_kernel<false>), dim3(static_cast<unsigned>(grid)), dim3(NT), 0,
                        s, x, w, a.bias, a.q, a.k, a.v, a.gate, a.eta, M, a.T,
-                       static_cast<int>(a.hidden), static_cast<int>(a.H), ntn, ntiles, per_xcd);
+                       static_cast<int>(a.hidden), static_cast<int>(a.H), ntn, mtiles);
   return hipGetLastError();
 }
 
