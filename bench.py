@@ -6,7 +6,10 @@ One step is one call of ``ttt_linear_forward`` over the whole workload (every
 in device memory.  With ``--pass train`` a step is one training pass instead:
 the recording forward (``ttt_linear_forward_record``) followed by the backward
 (``ttt_linear_backward``) from a fixed seeded dL/dout and dL/dW_final; the
-roofline is then that of the backward kernel.  W warm-up steps run untimed; then exactly K steps are
+roofline is then that of the backward kernel.  With ``--pass project`` a step
+is the layer's input projections (``ttt_linear_project``, from a seeded bf16 x
+[B,T,H*d] and stacked weights) followed by the scan; the roofline is the
+projection kernel's (bf16 MFMA).  W warm-up steps run untimed; then exactly K steps are
 timed between two device synchronisations, and each launch is also bracketed
 by events on its stream for the per-kernel duration.  Rank 0 prints one JSON
 line.
