@@ -12,15 +12,15 @@
 //
 // x is read once for all five projections of all heads.  Output tiles are
 // 128 tokens x 128 weight rows of one head (q with k, or v with gate), plus
-// tiles holding the eta rows of up to 128 heads.  K runs in steps of 32
-// through double-buffered LDS; four waves each own a 64 x 64 block of 4 x 4
-// MFMA tiles.  In a 32-deep step lane group G holds k = 8G..8G+7 of its row
-// for both operands, so every operand fetch is one 16-byte LDS read; LDS rows
-// are padded to 80 bytes so that the 16-byte reads of neighbouring rows fall
-// in different banks.  The global loads of the next step are issued before a
-// step's MFMAs and are unconditional (a row past the end reads row 0 and is
-// replaced by zeros when it is stored to LDS), so their wait comes after the
-// MFMAs.
+// tiles holding the eta rows of up to 128 heads.  Four waves each own a
+// 64 x 64 block of 4 x 4 MFMA tiles; in a 32-deep step lane group G holds
+// k = 8G..8G+7 of its row for both operands, so every operand fetch is one
+// 16-byte LDS read.  Operands go from global memory straight into LDS
+// (global_load_lds, 16 bytes per lane, a wave filling 1 KiB of consecutive
+// LDS) through a ring of three K steps: the loads of step ks+2 are issued
+// while step ks is computed, without holding registers.  LDS rows are 64
+// bytes; the 16-byte chunks of a row are XOR-swizzled with the row index so
+// that the reads of neighbouring rows fall in different banks.
 #include "scan_common.h"
 
 #include <cstdint>
@@ -33,7 +33,7 @@ constexpr int R = 4 * D + 1;    // weight rows per head
 constexpr int TM = 128;         // tokens per tile
 constexpr int TN = 128;         // weight rows per tile
 constexpr int TK = 32;          // k per step
-constexpr int KPAD = TK + 8;    // padded LDS row (bf16): 80 bytes
+constexpr int NSTAGE = 3;       // LDS ring of K steps in flight
 constexpr int NT = 256;         // threads: four waves
 constexpr int NXCD = 8;         // workgroups are dealt round-robin over the XCDs
 
@@ -41,9 +41,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 struct alignas(16) ProjSmem {
-  uint16_t A[2][TM][KPAD];   // x rows (tokens), k-contiguous
-  uint16_t B[2][TN][KPAD];   // weight rows, k-contiguous
+  uint16_t A[NSTAGE][TM][TK];   // x rows (tokens), k-contiguous, 16-byte chunks swizzled
+  uint16_t B[NSTAGE][TN][TK];   // weight rows, likewise
 };
+// the 16-byte chunk of row r that holds k = 8c .. 8c+7
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 3); }
 
 __device__ __forceinline__ uint16_t to_bf16(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
@@ -79,43 +81,32 @@ proj_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
   const int l16 = lane & 15;
   const int G = lane >> 4;
 
-  // global -> LDS: 512 chunks of 16 bytes per operand and step, two per thread
-  const uint16_t* arow[2];
-  const uint16_t* brow[2];
-  bool aok[2], bok[2];
-  int crow[2], cpart[2];
+  // global -> LDS: the lanes of a wave fill 1 KiB of consecutive LDS (16 rows
+  // of 64 bytes); the lane at physical chunk p of row r loads the chunk
+  // swz(r, p) of that row.  Rows past the end load a valid row whose results
+  // are never stored.
+  const uint16_t* asrc[2];
+  const uint16_t* bsrc[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int c = tid + NT * j;
-    crow[j] = c >> 2;
-    cpart[j] = c & 3;
-    const int64_t m = m0 + crow[j];
-    aok[j] = m < M;
-    arow[j] = x + (aok[j] ? m : 0) * hidden + 8 * cpart[j];
-    int64_t wr = -1;
-    if (!eta_tile) {
-      wr = int64_t(h) * R + TN * pair + crow[j];
-    } else if (e0 + crow[j] < H) {
-      wr = int64_t(e0 + crow[j]) * R + 4 * D;
-    }
-    bok[j] = wr >= 0;
-    brow[j] = w + (bok[j] ? wr : 0) * hidden + 8 * cpart[j];
+    const int c = tid + NT * j;          // LDS chunk: row c / 4, physical chunk c % 4
+    const int row = c >> 2, lc = swz(row, c & 3);
+    const int64_t m = m0 + row;
+    asrc[j] = x + (m < M ? m : 0) * hidden + 8 * lc;   // rows past the end read row 0
+    int64_t wr = 0;
+    if (!eta_tile)
+      wr = int64_t(h) * R + TN * pair + row;
+    else if (e0 + row < H)
+      wr = int64_t(e0 + row) * R + 4 * D;
+    bsrc[j] = w + wr * hidden + 8 * lc;
   }
-  uint4 ra[2], rb[2];
-  auto fetch = [&](int k0) {
+  auto issue = [&](int stage, int k0) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      ra[j] = *reinterpret_cast<const uint4*>(arow[j] + k0);
-      rb[j] = *reinterpret_cast<const uint4*>(brow[j] + k0);
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      // rows past the end read a valid row; their data is replaced by zeros here,
-      // after this step's MFMAs, so the loads' latency stays hidden
-      *reinterpret_cast<uint4*>(&sm.A[buf][crow[j]][8 * cpart[j]]) = aok[j] ? ra[j] : uint4{0, 0, 0, 0};
-      *reinterpret_cast<uint4*>(&sm.B[buf][crow[j]][8 * cpart[j]]) = bok[j] ? rb[j] : uint4{0, 0, 0, 0};
+      // the wave's 1 KiB block of this load: chunks (tid - lane) + NT j onward
+      const int cb = (tid - lane) + NT * j;
+      __builtin_amdgcn_global_load_lds(asrc[j] + k0, &sm.A[stage][cb >> 2][0], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bsrc[j] + k0, &sm.B[stage][cb >> 2][0], 16, 0, 0);
     }
   };
 
@@ -127,25 +118,39 @@ proj_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
 
   const int nk = hidden / TK;
-  fetch(0);
-  stash(0);
-  __syncthreads();
+  issue(0, 0);
+  if (nk > 1) issue(1, TK);
   for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nk) fetch((ks + 1) * TK);   // in flight during this step's MFMAs
+    const int st = ks % NSTAGE;
+    // this thread's loads of step ks are done (the 4 of step ks+1 may still run)
+    if (ks + 1 < nk)
+      __builtin_amdgcn_s_waitcnt(0x0074);   // vmcnt(4), lgkmcnt(0)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0)
+    // everyone's loads of step ks landed; everyone is done reading step ks-1.
+    // A bare barrier (the waits above are explicit): a fence would wait for
+    // the loads of step ks+1 as well.  The empty asm statements keep the
+    // compiler from moving memory accesses across it.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (ks + 2 < nk) issue((ks + 2) % NSTAGE, (ks + 2) * TK);
     bf16x8 a[4], b[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(&sm.A[buf][wm + 16 * i + l16][8 * G]);
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm + 16 * i + l16;
+      a[i] = *reinterpret_cast<const bf16x8*>(&sm.A[st][r][8 * swz(r, G)]);
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8*>(&sm.B[buf][wn + 16 * j + l16][8 * G]);
+    for (int j = 0; j < 4; ++j) {
+      const int r = wn + 16 * j + l16;
+      b[j] = *reinterpret_cast<const bf16x8*>(&sm.B[st][r][8 * swz(r, G)]);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    // the other buffer was last read in the previous step, before its barrier
-    if (ks + 1 < nk) stash(buf ^ 1);
-    __syncthreads();
   }
 
   // epilogue: D[4G + r][l16] of MFMA tile (i, j) is output row
