@@ -192,7 +192,21 @@ proj_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
 
 }  // namespace
 
-bool proj_mfma_supports(const ProjArgs& a) { return a.d == D && a.hidden % TK == 0; }
+// workgroups of a launch: 8 XCDs x the weight tiles of the busiest XCD x the token tiles
+static int64_t proj_grid(int64_t B, int64_t T, int64_t H) {
+  const int64_t ntn = 2 * H + (H + TN - 1) / TN;
+  const int64_t mtiles = (B * T + TM - 1) / TM;
+  return NXCD * ((ntn + NXCD - 1) / NXCD) * mtiles;
+}
+
+bool proj_mfma_grid_fits(int64_t B, int64_t T, int64_t H) {
+  return B <= INT32_MAX && T <= INT32_MAX && H <= INT32_MAX / 4 &&
+         proj_grid(B, T, H) <= INT32_MAX;
+}
+
+bool proj_mfma_supports(const ProjArgs& a) {
+  return a.d == D && a.hidden % TK == 0 && proj_mfma_grid_fits(a.B, a.T, a.H);
+}
 
 hipError_t launch_proj_mfma(const ProjArgs& a, hipStream_t s) {
   if (!proj_mfma_supports(a)) return hipErrorNotSupported;
@@ -200,9 +214,7 @@ hipError_t launch_proj_mfma(const ProjArgs& a, hipStream_t s) {
   if (M == 0) return hipSuccess;
   const int ntn = static_cast<int>(2 * a.H + (a.H + TN - 1) / TN);
   const int64_t mtiles = (M + TM - 1) / TM;
-  const int64_t cmax = (ntn + NXCD - 1) / NXCD;     // weight tiles of the busiest XCD
-  const int64_t grid = NXCD * cmax * mtiles;
-  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  const int64_t grid = proj_grid(a.B, a.T, a.H);
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   const uint16_t* w = static_cast<const uint16_t*>(a.w);
   if (a.out_bf16)

@@ -97,8 +97,10 @@ struct ProjArgs {
   int64_t B, T, hidden, H, d;
   bool out_bf16;
 };
-// MFMA projection kernel for d = 64 and hidden a multiple of 32.
+// MFMA projection kernel for d = 64 and hidden a multiple of 32; its grid of
+// one workgroup per output tile must fit a launch (B*T tokens, H heads).
 bool proj_mfma_supports(const ProjArgs& a);
+bool proj_mfma_grid_fits(int64_t B, int64_t T, int64_t H);
 hipError_t launch_proj_mfma(const ProjArgs& a, hipStream_t stream);
 
 // Backward of the per-token scan, and of the dual form with chunks of

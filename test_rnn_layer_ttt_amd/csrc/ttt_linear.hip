@@ -304,16 +304,18 @@ int32_t validate_project(const void* x, const void* w_proj, const float* b_proj,
   const uint32_t known = TTT_DUAL | TTT_LN_EXACT | TTT_IN_BF16 | TTT_NO_LN | TTT_SILU_QK;
   if (mode & ~known) return TTT_ERR_MODE;
   if (B < 1 || H < 1 || d < 1 || hidden < 1 || T < 0) return TTT_ERR_SHAPE;
-  int64_t BT, x_elems, rows, w_elems, BH, BHT, out_elems;
+  int64_t BT, x_elems, per_head, rows, w_elems, BH, BHT, out_elems;
   if (!mul_ok(B, T, &BT) || !mul_ok(BT, hidden, &x_elems) || x_elems > INT64_MAX / 2)
     return TTT_ERR_SHAPE;
-  if (!mul_ok(d, 4, &rows) || !mul_ok(H, rows + 1, &rows) || !mul_ok(rows, hidden, &w_elems) ||
-      w_elems > INT64_MAX / 2)
+  // weight rows: 4d + 1 per head (q, k, v, gate, eta)
+  if (!mul_ok(d, 4, &per_head) || !mul_ok(H, per_head + 1, &rows) ||
+      !mul_ok(rows, hidden, &w_elems) || w_elems > INT64_MAX / 2)
     return TTT_ERR_SHAPE;
   if (!mul_ok(B, H, &BH) || !mul_ok(BH, T, &BHT) || !mul_ok(BHT, d, &out_elems) ||
       out_elems > INT64_MAX / 4 || hidden > INT32_MAX || H > INT32_MAX / 2)
     return TTT_ERR_SHAPE;
-  if (d != 64 || hidden % 32 != 0) return TTT_ERR_UNSUPPORTED;
+  if (d != 64 || hidden % 32 != 0 || !ttt::proj_mfma_grid_fits(B, T, H))
+    return TTT_ERR_UNSUPPORTED;
   if (T > 0 && (x == nullptr || w_proj == nullptr || q == nullptr || k == nullptr ||
                 v == nullptr || eta_logit == nullptr || gate_logit == nullptr))
     return TTT_ERR_NULL;
@@ -326,10 +328,9 @@ int32_t validate_project(const void* x, const void* w_proj, const float* b_proj,
     for (const void* p : outs16)
       if (!aligned(p, 16)) return TTT_ERR_UNSUPPORTED;
     if (!aligned(eta_logit, static_cast<uintptr_t>(osz))) return TTT_ERR_UNSUPPORTED;
-    const int64_t ts = 1;
-    const Range outs[] = {span(q, ts * out_elems * osz), span(k, ts * out_elems * osz),
-                          span(v, ts * out_elems * osz), span(gate_logit, ts * out_elems * osz),
-                          span(eta_logit, ts * BHT * osz)};
+    const Range outs[] = {span(q, out_elems * osz), span(k, out_elems * osz),
+                          span(v, out_elems * osz), span(gate_logit, out_elems * osz),
+                          span(eta_logit, BHT * osz)};
     const Range ins[] = {span(x, x_elems * 2), span(w_proj, w_elems * 2),
                          span(b_proj, b_proj ? rows * 4 : 0)};
     constexpr int kOuts = sizeof(outs) / sizeof(outs[0]);

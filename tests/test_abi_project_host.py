@@ -41,6 +41,7 @@ needs_no_gpu = pytest.mark.skipif(_GPU, reason="sends unlaunchable arguments to 
     (dict(B=1 << 40, T=1 << 40), ttt.TTT_ERR_SHAPE),
     (dict(d=32), ttt.TTT_ERR_UNSUPPORTED),
     (dict(hidden=48), ttt.TTT_ERR_UNSUPPORTED),   # not a multiple of 32
+    (dict(T=1 << 33), ttt.TTT_ERR_UNSUPPORTED),   # more workgroups than a launch takes
     (dict(x=None), ttt.TTT_ERR_NULL),
     (dict(w_proj=None), ttt.TTT_ERR_NULL),
     (dict(eta_logit=None), ttt.TTT_ERR_NULL),
