@@ -231,8 +231,8 @@ int32_t ttt_linear_backward(const void* q, const void* k, const void* v,
  *              sums), else fp32
  *
  * mode is the scan's mode word (only TTT_IN_BF16 is read here), so one mode
- * serves both calls.  Supported: d = 64, hidden a multiple of 32 (otherwise
- * TTT_ERR_UNSUPPORTED).  x, w_proj and q, k, v, gate_logit 16-byte aligned,
+ * serves both calls.  Supported: d = 64, hidden a multiple of 32 and at most
+ * 65536 (otherwise TTT_ERR_UNSUPPORTED).  x, w_proj and q, k, v, gate_logit 16-byte aligned,
  * eta_logit and b_proj element-aligned.  The outputs must not overlap one
  * another or the inputs.  T == 0 writes nothing.  Runs asynchronously on
  * `stream`; the accumulation order is fixed, so repeated calls give

@@ -10,32 +10,45 @@
 // accumulate in fp32 on the 16x16x32 bf16 MFMA; an optional fp32 bias is added
 // and the result is stored as bf16 (the scan's bf16 inputs) or fp32.
 //
-// x is read once for all five projections of all heads.  Output tiles are
-// 128 tokens x 128 weight rows of one head (q with k, or v with gate), plus
-// tiles holding the eta rows of up to 128 heads.  Four waves each own a
-// 64 x 64 block of 4 x 4 MFMA tiles; in a 32-deep step lane group G holds
-// k = 8G..8G+7 of its row for both operands, so every operand fetch is one
-// 16-byte LDS read.  Operands go from global memory straight into LDS
-// (global_load_lds, 16 bytes per lane, a wave filling 1 KiB of consecutive
-// LDS) through a ring of three K steps: the loads of step ks+2 are issued
-// while step ks is computed, without holding registers.  LDS rows are 64
-// bytes; the 16-byte chunks of a row are XOR-swizzled with the row index so
-// that the reads of neighbouring rows fall in different banks.
+// Tiles are 256 tokens x the 256 q, k, v, gate rows of one head, plus tiles
+// of 256 tokens x the eta rows of up to 256 heads, which come last in the
+// grid.  Eight waves (two per SIMD) each own 64 tokens x 128 weight rows
+// (4 x 8 MFMA tiles).  K runs in steps of 32: operands go from global memory
+// straight into LDS (global_load_lds, 16 bytes per lane, a wave filling 1 KiB
+// of consecutive LDS) through a ring of three steps, so the loads of step
+// ks+2 are in flight while step ks is computed.  Within a step each wave
+// reads the next step's fragments from LDS between its MFMAs (b fragments
+// double-buffered, each a fragment replaced once its row of MFMAs is
+// issued).  In a 32-deep step lane group G holds k = 8G..8G+7 of its row for
+// both operands, so every fragment is one 16-byte LDS read; LDS rows are 64
+// bytes, their 16-byte chunks XOR-swizzled with the row so that the reads of
+// neighbouring rows fall in different banks.  The weights are the MFMA's
+// first operand, so a lane ends with four consecutive features of one token
+// and stores them as one 8-byte (bf16) or 16-byte (fp32) write.
 #include "scan_common.h"
 
 #include <cstdint>
+#include <type_traits>
 
 namespace ttt {
 namespace {
 
 constexpr int D = 64;
 constexpr int R = 4 * D + 1;    // weight rows per head
-constexpr int TM = 128;         // tokens per tile
-constexpr int TN = 128;         // weight rows per tile
+constexpr int TM = 256;         // tokens per tile
+constexpr int TN = 256;         // weight rows per tile: q, k, v, gate of a head, or eta of 256 heads
 constexpr int TK = 32;          // k per step
-constexpr int NSTAGE = 3;       // LDS ring of K steps in flight
-constexpr int NT = 256;         // threads: four waves
-constexpr int NXCD = 8;         // workgroups are dealt round-robin over the XCDs
+constexpr int NSTAGE = 3;       // LDS ring of K steps
+constexpr int NT = 512;         // threads: eight waves
+constexpr int FI = 4;           // MFMA tiles per wave along tokens (64 tokens)
+constexpr int FJ = 8;           // along weight rows (128 rows)
+constexpr int ACH = TM * TK / 8 / NT;   // 16-byte chunks per thread and step: x
+constexpr int BCH = TN * TK / 8 / NT;   // weights
+constexpr int VM_STEP = ACH + BCH;      // global loads per thread and step
+constexpr int ROWS_PER_CH = NT / 4;     // rows covered by one chunk index j
+constexpr int64_t kMaxHidden = 65536;   // keeps the per-lane byte offsets in 32 bits
+static_assert(TM == 4 * FI * 16 && TN == 2 * FJ * 16, "4 x 2 waves");
+static_assert(VM_STEP < 16, "one vmcnt step");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -52,28 +65,29 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
 }
 
 template <bool OUT_BF16>
-__global__ void __launch_bounds__(NT)
+__global__ void __launch_bounds__(NT, 1)
 proj_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                  const float* __restrict__ bias, void* __restrict__ q, void* __restrict__ k,
                  void* __restrict__ v, void* __restrict__ gate, void* __restrict__ eta,
-                 int64_t M, int64_t T, int hidden, int H, int ntn, int64_t mtiles) {
+                 int64_t M, int64_t T, int hidden, int H, int ne, int64_t head_blocks) {
   __shared__ ProjSmem sm;
-  // XCD x (workgroups are dealt to the XCDs round-robin) takes the weight
-  // tiles nt = x, x + 8, ... for every token tile: its share of the weights
-  // stays in its L2 while x streams through, and consecutive workgroups on it
-  // share their x rows
-  const int xcd = static_cast<int>(blockIdx.x % NXCD);
-  const int64_t slot = blockIdx.x / NXCD;
-  const int cx = (ntn - xcd + NXCD - 1) / NXCD;     // weight tiles of this XCD
-  if (cx == 0) return;
-  const int64_t mt = slot / cx;
-  if (mt >= mtiles) return;
-  const int nt = xcd + NXCD * static_cast<int>(slot % cx);
+  // Blocks [0, head_blocks) are (token tile, head) in token-tile-major order:
+  // blocks are dealt round-robin over the 8 XCDs, so when H is a multiple of
+  // 8 XCD x takes heads x, x + 8, ... of every token tile, its share of the
+  // weights stays in its L2 and consecutive blocks on it share their x rows.
+  // The eta tiles follow, (token tile, group of 256 heads).
+  const bool eta_tile = int64_t(blockIdx.x) >= head_blocks;
+  int64_t mt;
+  int h = 0, e0 = 0;
+  if (!eta_tile) {
+    mt = int64_t(blockIdx.x) / H;
+    h = static_cast<int>(int64_t(blockIdx.x) % H);
+  } else {
+    const int64_t e = int64_t(blockIdx.x) - head_blocks;
+    mt = e / ne;
+    e0 = static_cast<int>(e % ne) * TN;
+  }
   const int64_t m0 = mt * TM;
-  const bool eta_tile = nt >= 2 * H;
-  const int h = eta_tile ? 0 : nt >> 1;        // head of a q/k or v/gate tile
-  const int pair = nt & 1;                     // 0: q, k rows; 1: v, gate rows
-  const int e0 = eta_tile ? (nt - 2 * H) * TN : 0;   // first head of an eta tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -81,110 +95,193 @@ proj_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
   const int l16 = lane & 15;
   const int G = lane >> 4;
 
-  // global -> LDS: the lanes of a wave fill 1 KiB of consecutive LDS (16 rows
-  // of 64 bytes); the lane at physical chunk p of row r loads the chunk
-  // swz(r, p) of that row.  Rows past the end load a valid row whose results
-  // are never stored.
-  const uint16_t* asrc[2];
-  const uint16_t* bsrc[2];
+  // global -> LDS: chunk c = tid + NT j is physical chunk c % 4 of tile row
+  // c / 4 and loads that row's chunk swz(row, c % 4).  Each source is a base
+  // per chunk index j (rows ROWS_PER_CH j onward, scalar registers) plus a
+  // 32-bit byte offset per lane.  Rows past the end load a valid row whose
+  // results are never stored.
+  const char* const abase = reinterpret_cast<const char*>(x + m0 * hidden);
+  const char* bbase[BCH];
+  uint32_t aoff[ACH], boff[BCH];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = tid + NT * j;          // LDS chunk: row c / 4, physical chunk c % 4
+  for (int j = 0; j < ACH; ++j) {
+    const int c = tid + NT * j;
     const int row = c >> 2, lc = swz(row, c & 3);
-    const int64_t m = m0 + row;
-    asrc[j] = x + (m < M ? m : 0) * hidden + 8 * lc;   // rows past the end read row 0
-    int64_t wr = 0;
-    if (!eta_tile)
-      wr = int64_t(h) * R + TN * pair + row;
-    else if (e0 + row < H)
-      wr = int64_t(e0 + row) * R + 4 * D;
-    bsrc[j] = w + wr * hidden + 8 * lc;
+    aoff[j] = (m0 + row < M ? uint32_t(row) * hidden * 2 : 0u) + 16u * lc;
+  }
+#pragma unroll
+  for (int j = 0; j < BCH; ++j) {
+    const int c = tid + NT * j;
+    const int row = c >> 2, lc = swz(row, c & 3);
+    const int rel = row - ROWS_PER_CH * j;
+    if (!eta_tile) {
+      bbase[j] = reinterpret_cast<const char*>(w + (int64_t(h) * R + ROWS_PER_CH * j) * hidden);
+      boff[j] = uint32_t(rel) * hidden * 2 + 16u * lc;
+    } else {
+      // eta row of head e0 + row: row (e0 + row) R + 4d of w_proj
+      int jb = e0 + ROWS_PER_CH * j;
+      if (jb >= H) jb = e0;
+      bbase[j] = reinterpret_cast<const char*>(w + (int64_t(jb) * R + 4 * D) * hidden);
+      boff[j] = (e0 + row < H ? uint32_t(e0 + row - jb) * uint32_t(R) * hidden * 2 : 0u) + 16u * lc;
+    }
   }
   auto issue = [&](int stage, int k0) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < ACH; ++j) {
       // the wave's 1 KiB block of this load: chunks (tid - lane) + NT j onward
       const int cb = (tid - lane) + NT * j;
-      __builtin_amdgcn_global_load_lds(asrc[j] + k0, &sm.A[stage][cb >> 2][0], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(bsrc[j] + k0, &sm.B[stage][cb >> 2][0], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(abase + 2 * k0 + aoff[j], &sm.A[stage][cb >> 2][0], 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < BCH; ++j) {
+      const int cb = (tid - lane) + NT * j;
+      __builtin_amdgcn_global_load_lds(bbase[j] + 2 * k0 + boff[j], &sm.B[stage][cb >> 2][0], 16, 0, 0);
     }
   };
 
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-  f32x4 acc[4][4];
+  const int wm = (wave >> 1) * (FI * 16), wn = (wave & 1) * (FJ * 16);
+  f32x4 acc[FI][FJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+    for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
 
-  const int nk = hidden / TK;
-  issue(0, 0);
-  if (nk > 1) issue(1, TK);
-  for (int ks = 0; ks < nk; ++ks) {
-    const int st = ks % NSTAGE;
-    // this thread's loads of step ks are done (the 4 of step ks+1 may still run)
-    if (ks + 1 < nk)
-      __builtin_amdgcn_s_waitcnt(0x0074);   // vmcnt(4), lgkmcnt(0)
-    else
-      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0)
-    // everyone's loads of step ks landed; everyone is done reading step ks-1.
-    // A bare barrier (the waits above are explicit): a fence would wait for
-    // the loads of step ks+1 as well.  The empty asm statements keep the
-    // compiler from moving memory accesses across it.
+  auto read_a = [&](int st, int i) {
+    const int r = wm + 16 * i + l16;
+    return *reinterpret_cast<const bf16x8*>(&sm.A[st][r][8 * swz(r, G)]);
+  };
+  auto read_b = [&](int st, int j) {
+    const int r = wn + 16 * j + l16;
+    return *reinterpret_cast<const bf16x8*>(&sm.B[st][r][8 * swz(r, G)]);
+  };
+  // A bare barrier (the waits are explicit): a fence would also wait for the
+  // loads still in flight.  The empty asm statements keep the compiler from
+  // moving memory accesses across it.
+  auto bar = [&]() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (ks + 2 < nk) issue((ks + 2) % NSTAGE, (ks + 2) * TK);
-    bf16x8 a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm + 16 * i + l16;
-      a[i] = *reinterpret_cast<const bf16x8*>(&sm.A[st][r][8 * swz(r, G)]);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wn + 16 * j + l16;
-      b[j] = *reinterpret_cast<const bf16x8*>(&sm.B[st][r][8 * swz(r, G)]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
+  };
+  constexpr int kWaitStep = 0x0070 | VM_STEP;   // vmcnt(VM_STEP), lgkmcnt(0)
+  constexpr int kWaitAll = 0x0070;              // vmcnt(0), lgkmcnt(0)
 
-  // epilogue: D[4G + r][l16] of MFMA tile (i, j) is output row
-  // m0 + wm + 16i + 4G + r, weight row wn + 16j + l16 of the tile
-  void* const dst4[4] = {q, k, v, gate};
+  const int nk = hidden / TK;
+  bf16x8 a[FI];
+  // One K step.  Its fragments are a and cb; the next step's b fragments go
+  // into nb and its a fragments replace a[i] once row i's MFMAs are issued.
+  // FULL: steps ks+1 .. ks+3 exist, so the step has no branches and the
+  // compiler's own waits do not drain the reads of the next fragments.
+  auto step = [&](auto full, int ks, bf16x8 (&cb)[FJ], bf16x8 (&nb)[FJ]) {
+    constexpr bool FULL = decltype(full)::value;
+    const bool more = FULL || ks + 1 < nk;
+    if (more) {
+      // this thread's loads of step ks+1 are done (those of ks+2 may run) and
+      // its reads of step ks are done
+      if (FULL || ks + 2 < nk)
+        __builtin_amdgcn_s_waitcnt(kWaitStep);
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitAll);
+      // step ks+1 is in LDS for everyone, and everyone has read step ks, so
+      // its stage takes step ks+3
+      bar();
+      if (FULL || ks + 3 < nk) issue(ks % NSTAGE, (ks + 3) * TK);
+    }
+    const int sn = (ks + 1) % NSTAGE;
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+      for (int j = 0; j < FJ; ++j) nb[j] = read_b(sn, j);
+    }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t m = m0 + wm + 16 * i + 4 * G + r;
-      if (m >= M) continue;
-      const int64_t bb = m / T, t = m % T;
+    for (int i = 0; i < FI; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = wn + 16 * j + l16;
-        float y = acc[i][j][r];
-        int64_t off;
-        void* dst;
-        if (!eta_tile) {
-          const int kind = 2 * pair + (col >> 6);
-          if (bias) y += bias[int64_t(h) * R + TN * pair + col];
-          dst = dst4[kind];
-          off = ((bb * H + h) * T + t) * D + (col & 63);
-        } else {
-          const int hh = e0 + col;
-          if (hh >= H) continue;
-          if (bias) y += bias[int64_t(hh) * R + 4 * D];
-          dst = eta;
-          off = (bb * H + hh) * T + t;
+      for (int j = 0; j < FJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cb[j], a[i], acc[i][j], 0, 0, 0);
+      if (more) a[i] = read_a(sn, i);
+    }
+    if constexpr (FULL) {
+      // the b reads over the first 2 FJ MFMAs, then one a read per
+      // FJ (FI - 2) / FI MFMAs (a[i] only after its row's MFMAs)
+#pragma unroll
+      for (int g = 0; g < FJ; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);     // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // LDS read
+      }
+#pragma unroll
+      for (int g = 0; g < FI; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, FJ * (FI - 2) / FI, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using full_t = std::integral_constant<bool, true>;
+  using tail_t = std::integral_constant<bool, false>;
+  bf16x8 b0[FJ], b1[FJ];
+  issue(0, 0);
+  if (nk > 1) issue(1, TK);
+  if (nk > 1)
+    __builtin_amdgcn_s_waitcnt(kWaitStep);
+  else
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+  bar();
+  if (nk > 2) issue(2, 2 * TK);
+#pragma unroll
+  for (int i = 0; i < FI; ++i) a[i] = read_a(0, i);
+#pragma unroll
+  for (int j = 0; j < FJ; ++j) b0[j] = read_b(0, j);
+  int ks = 0;
+  for (; ks + 4 < nk; ks += 2) {
+    step(full_t{}, ks, b0, b1);
+    step(full_t{}, ks + 1, b1, b0);
+  }
+  // the last one to four steps
+  step(tail_t{}, ks, b0, b1);
+  if (ks + 1 < nk) step(tail_t{}, ks + 1, b1, b0);
+  if (ks + 2 < nk) step(tail_t{}, ks + 2, b0, b1);
+  if (ks + 3 < nk) step(tail_t{}, ks + 3, b1, b0);
+
+  // epilogue: D[4G + r][l16] of MFMA tile (i, j) is token m0 + wm + 16i + l16,
+  // weight row wn + 16j + 4G + r of the tile
+#pragma unroll
+  for (int i = 0; i < FI; ++i) {
+    const int64_t m = m0 + wm + 16 * i + l16;
+    if (m >= M) continue;
+    const int64_t bb = m / T, t = m % T;
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) {
+      const int col0 = wn + 16 * j + 4 * G;
+      float y[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      if (!eta_tile) {
+        if (bias) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) y[r] += bias[int64_t(h) * R + col0 + r];
         }
-        if constexpr (OUT_BF16)
-          static_cast<uint16_t*>(dst)[off] = to_bf16(y);
-        else
-          static_cast<float*>(dst)[off] = y;
+        // rows 0-63 q, 64-127 k, 128-191 v, 192-255 gate; one output per (wave, j)
+        const int kind = (wn + 16 * j) >> 6;
+        void* const dst = kind == 0 ? q : kind == 1 ? k : kind == 2 ? v : gate;
+        const int64_t off = ((bb * H + h) * T + t) * D + (col0 & (D - 1));
+        if constexpr (OUT_BF16) {
+          uint2 pk;
+          pk.x = uint32_t(to_bf16(y[0])) | (uint32_t(to_bf16(y[1])) << 16);
+          pk.y = uint32_t(to_bf16(y[2])) | (uint32_t(to_bf16(y[3])) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(dst) + off) = pk;
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(dst) + off) = float4{y[0], y[1], y[2], y[3]};
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int hh = e0 + col0 + r;
+          if (hh >= H) continue;
+          float yy = y[r];
+          if (bias) yy += bias[int64_t(hh) * R + 4 * D];
+          const int64_t off = (bb * H + hh) * T + t;
+          if constexpr (OUT_BF16)
+            static_cast<uint16_t*>(eta)[off] = to_bf16(yy);
+          else
+            static_cast<float*>(eta)[off] = yy;
+        }
       }
     }
   }
@@ -192,11 +289,11 @@ proj_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
 
 }  // namespace
 
-// workgroups of a launch: 8 XCDs x the weight tiles of the busiest XCD x the token tiles
+// token tiles, and the blocks of a launch: one per (token tile, head), then
+// one per (token tile, group of TN heads) for the eta rows
+static int64_t proj_mtiles(int64_t B, int64_t T) { return (B * T + TM - 1) / TM; }
 static int64_t proj_grid(int64_t B, int64_t T, int64_t H) {
-  const int64_t ntn = 2 * H + (H + TN - 1) / TN;
-  const int64_t mtiles = (B * T + TM - 1) / TM;
-  return NXCD * ((ntn + NXCD - 1) / NXCD) * mtiles;
+  return proj_mtiles(B, T) * (H + (H + TN - 1) / TN);
 }
 
 bool proj_mfma_grid_fits(int64_t B, int64_t T, int64_t H) {
@@ -205,26 +302,27 @@ bool proj_mfma_grid_fits(int64_t B, int64_t T, int64_t H) {
 }
 
 bool proj_mfma_supports(const ProjArgs& a) {
-  return a.d == D && a.hidden % TK == 0 && proj_mfma_grid_fits(a.B, a.T, a.H);
+  return a.d == D && a.hidden % TK == 0 && a.hidden <= kMaxHidden &&
+         proj_mfma_grid_fits(a.B, a.T, a.H);
 }
 
 hipError_t launch_proj_mfma(const ProjArgs& a, hipStream_t s) {
   if (!proj_mfma_supports(a)) return hipErrorNotSupported;
   const int64_t M = a.B * a.T;
   if (M == 0) return hipSuccess;
-  const int ntn = static_cast<int>(2 * a.H + (a.H + TN - 1) / TN);
-  const int64_t mtiles = (M + TM - 1) / TM;
+  const int ne = static_cast<int>((a.H + TN - 1) / TN);
+  const int64_t head_blocks = proj_mtiles(a.B, a.T) * a.H;
   const int64_t grid = proj_grid(a.B, a.T, a.H);
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   const uint16_t* w = static_cast<const uint16_t*>(a.w);
   if (a.out_bf16)
     hipLaunchKernelGGL((proj_mfma_kernel<true>), dim3(static_cast<unsigned>(grid)), dim3(NT), 0, s,
                        x, w, a.bias, a.q, a.k, a.v, a.gate, a.eta, M, a.T,
-                       static_cast<int>(a.hidden), static_cast<int>(a.H), ntn, mtiles);
+                       static_cast<int>(a.hidden), static_cast<int>(a.H), ne, head_blocks);
   else
     hipLaunchKernelGGL((proj_mfma_kernel<false>), dim3(static_cast<unsigned>(grid)), dim3(NT), 0,
                        s, x, w, a.bias, a.q, a.k, a.v, a.gate, a.eta, M, a.T,
-                       static_cast<int>(a.hidden), static_cast<int>(a.H), ntn, mtiles);
+                       static_cast<int>(a.hidden), static_cast<int>(a.H), ne, head_blocks);
   return hipGetLastError();
 }
 

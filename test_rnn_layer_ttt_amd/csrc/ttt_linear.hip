@@ -314,12 +314,14 @@ int32_t validate_project(const void* x, const void* w_proj, const float* b_proj,
   if (!mul_ok(B, H, &BH) || !mul_ok(BH, T, &BHT) || !mul_ok(BHT, d, &out_elems) ||
       out_elems > INT64_MAX / 4 || hidden > INT32_MAX || H > INT32_MAX / 2)
     return TTT_ERR_SHAPE;
-  if (d != 64 || hidden % 32 != 0 || !ttt::proj_mfma_grid_fits(B, T, H))
-    return TTT_ERR_UNSUPPORTED;
+  // d = 64, hidden a multiple of 32 and at most 65536, a grid that fits a launch
+  const bool bf16 = (mode & TTT_IN_BF16) != 0;
+  const ttt::ProjArgs pa{x, w_proj, b_proj, q, k, v, eta_logit, gate_logit,
+                         B, T, hidden, H, d, bf16};
+  if (!ttt::proj_mfma_supports(pa)) return TTT_ERR_UNSUPPORTED;
   if (T > 0 && (x == nullptr || w_proj == nullptr || q == nullptr || k == nullptr ||
                 v == nullptr || eta_logit == nullptr || gate_logit == nullptr))
     return TTT_ERR_NULL;
-  const bool bf16 = (mode & TTT_IN_BF16) != 0;
   const int64_t osz = bf16 ? 2 : 4;
   if (T > 0) {
     if (!aligned(x, 16) || !aligned(w_proj, 16) || (b_proj && !aligned(b_proj, 4)))
@@ -341,7 +343,7 @@ int32_t validate_project(const void* x, const void* w_proj, const float* b_proj,
         if (overlaps(outs[i], r)) return TTT_ERR_ALIAS;
     }
   }
-  *a = ttt::ProjArgs{x, w_proj, b_proj, q, k, v, eta_logit, gate_logit, B, T, hidden, H, d, bf16};
+  *a = pa;
   return TTT_OK;
 }
 

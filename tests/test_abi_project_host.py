@@ -41,7 +41,9 @@ needs_no_gpu = pytest.mark.skipif(_GPU, reason="sends unlaunchable arguments to 
     (dict(B=1 << 40, T=1 << 40), ttt.TTT_ERR_SHAPE),
     (dict(d=32), ttt.TTT_ERR_UNSUPPORTED),
     (dict(hidden=48), ttt.TTT_ERR_UNSUPPORTED),   # not a multiple of 32
-    (dict(T=1 << 33), ttt.TTT_ERR_UNSUPPORTED),   # more workgroups than a launch takes
+    (dict(hidden=65536 + 32), ttt.TTT_ERR_UNSUPPORTED),   # beyond 32-bit lane offsets
+    (dict(T=1 << 33), ttt.TTT_ERR_UNSUPPORTED),   # T beyond 32 bits
+    (dict(B=1 << 20, T=1 << 30), ttt.TTT_ERR_UNSUPPORTED),   # more workgroups than a launch takes
     (dict(x=None), ttt.TTT_ERR_NULL),
     (dict(w_proj=None), ttt.TTT_ERR_NULL),
     (dict(eta_logit=None), ttt.TTT_ERR_NULL),
@@ -70,6 +72,12 @@ def test_empty_sequence_is_a_no_op_with_null_pointers():
     st = ttt.ttt_linear_project(None, None, None, None, None, None, None, None, 2, 0, 128, 3,
                                 64, ttt.TTT_IN_BF16, None)
     assert st == ttt.TTT_OK
+
+
+@needs_no_gpu
+def test_hidden_65536_is_supported():
+    # passes the size rules; q == x then trips the alias check
+    assert call(hidden=65536, q=A) == ttt.TTT_ERR_ALIAS
 
 
 def test_bias_is_optional():

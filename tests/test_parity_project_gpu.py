@@ -65,13 +65,24 @@ def test_small_projection_parity(hidden, H, out_bf16, with_bias):
     compare(gpu_project(x, w, b, out_bf16), oracle.input_projections(x, w, b), out_bf16)
 
 
-@pytest.mark.parametrize("B,T,H", [(3, 200, 2), (1, 129, 130), (2, 1, 5)])
+@pytest.mark.parametrize("B,T,H", [(3, 200, 2), (1, 129, 260), (2, 1, 5), (2, 300, 8)])
 def test_ragged_tiles_and_many_heads(B, T, H):
-    # token tiles across batch boundaries and a ragged last tile; more than 128
-    # heads puts the eta rows in two tiles, the second one mostly empty
+    # token tiles (256 tokens) across batch boundaries and a ragged last tile;
+    # more than 256 heads puts the eta rows in two tiles, the second one mostly
+    # empty
     say(f"case project B={B} T={T} H={H}")
     x, w, b = make_projection_case(B, T, 64, H, 64, seed=510 + T, with_bias=True)
     compare(gpu_project(x, w, b, False), oracle.input_projections(x, w, b), False)
+
+
+@pytest.mark.parametrize("hidden", [64, 128, 160, 192])
+def test_step_counts_around_the_ring(hidden):
+    # 2, 4, 5 and 6 K steps of 32: no steady-state step, and one pair of them
+    # followed by three or four closing steps
+    B, T, H = 1, 300, 2
+    say(f"case project hidden={hidden} (K steps {hidden // 32})")
+    x, w, b = make_projection_case(B, T, hidden, H, 64, seed=550 + hidden, with_bias=True)
+    compare(gpu_project(x, w, b, True), oracle.input_projections(x, w, b), True)
 
 
 def test_one_hot_rows_route_every_output():
