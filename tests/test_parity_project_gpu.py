@@ -132,13 +132,13 @@ def test_projection_then_scan_matches_the_oracle_chain():
     assert e_o <= 2e-2 and e_w <= 2e-2
 
 
-def test_full_size_sampled_tokens():
-    # the hidden-1024 workload's shape (B=16, T=4096, hidden=1024, H=16), as
-    # the benchmark launches it; the oracle checks 64 sampled tokens of every
-    # batch and head
-    B, T, hidden, H, d = 16, 4096, 1024, 16, 64
-    say("case project full size")
-    x, w, _ = make_projection_case(B, T, hidden, H, d, seed=540)
+@pytest.mark.parametrize("B,T,hidden,H", [(16, 4096, 1024, 16), (8, 8192, 2048, 32)])
+def test_full_size_sampled_tokens(B, T, hidden, H):
+    # the hidden-1024 and hidden-2048 workloads' shapes, as the benchmark
+    # launches them; the oracle checks 64 sampled tokens of every head
+    d = 64
+    say(f"case project full size B={B} T={T} hidden={hidden} H={H}")
+    x, w, _ = make_projection_case(B, T, hidden, H, d, seed=540 + H)
     got = gpu_project(x, w, None, True)
     rng = np.random.default_rng(541)
     bs = rng.integers(0, B, 64)
