@@ -23,8 +23,11 @@
 // both operands, so every fragment is one 16-byte LDS read; LDS rows are 64
 // bytes, their 16-byte chunks XOR-swizzled with the row so that the reads of
 // neighbouring rows fall in different banks.  The weights are the MFMA's
-// first operand, so a lane ends with four consecutive features of one token
-// and stores them as one 8-byte (bf16) or 16-byte (fp32) write.
+// first operand, so a lane ends with four consecutive features of one token.
+// bf16 results of a head tile go through LDS: each wave stages one output
+// (64 tokens x 64 features) at a time and writes whole 128-byte token rows
+// with 16-byte stores; fp32 results and eta tiles are stored directly (four
+// features per lane in one 16-byte write, or single values).
 #include "scan_common.h"
 
 #include <cstdint>
@@ -242,7 +245,58 @@ proj_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
   if (ks + 3 < nk) step(tail_t{}, ks + 3, b1, b0);
 
   // epilogue: D[4G + r][l16] of MFMA tile (i, j) is token m0 + wm + 16i + l16,
-  // weight row wn + 16j + 4G + r of the tile
+  // weight row wn + 16j + 4G + r of the tile.
+  if constexpr (OUT_BF16) {
+    if (!eta_tile) {
+      // bf16 q, k, v, gate: each wave stages one output (64 tokens x 64
+      // features) at a time in its own LDS rows, then writes whole 128-byte
+      // token rows with 16-byte stores (8 lanes per row, 8 rows per store)
+      __syncthreads();   // every wave is done with the operand ring
+      constexpr int SROW = 2 * D + 16;   // staged row: 64 bf16 + 16 bytes of padding
+      char* const stage = reinterpret_cast<char*>(&sm) + wave * (FI * 16 * SROW);
+      const int64_t mb = m0 + wm;        // this wave's first token
+      const int64_t bb0 = mb / T, t0 = mb % T;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int kind = (wn >> 6) + p;   // 0 q, 1 k, 2 v, 3 gate
+        uint16_t* const dst = static_cast<uint16_t*>(kind == 0 ? q : kind == 1 ? k : kind == 2 ? v : gate);
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int f0 = 16 * jj + 4 * G;
+            float y[4] = {acc[i][4 * p + jj][0], acc[i][4 * p + jj][1], acc[i][4 * p + jj][2],
+                          acc[i][4 * p + jj][3]};
+            if (bias) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) y[r] += bias[int64_t(h) * R + 64 * kind + f0 + r];
+            }
+            uint2 pk;
+            pk.x = uint32_t(to_bf16(y[0])) | (uint32_t(to_bf16(y[1])) << 16);
+            pk.y = uint32_t(to_bf16(y[2])) | (uint32_t(to_bf16(y[3])) << 16);
+            *reinterpret_cast<uint2*>(stage + (16 * i + l16) * SROW + 2 * f0) = pk;
+          }
+        // the same wave reads the rows back (its LDS accesses stay in order)
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          const int row = (lane >> 3) + 8 * n, ch = lane & 7;
+          const uint4 val = *reinterpret_cast<const uint4*>(stage + row * SROW + 16 * ch);
+          if (mb + row >= M) continue;
+          int64_t bb, t;
+          if (T >= FI * 16) {   // at most one sequence boundary inside the wave's rows
+            t = t0 + row;
+            bb = bb0;
+            if (t >= T) { t -= T; ++bb; }
+          } else {
+            bb = (mb + row) / T;
+            t = (mb + row) % T;
+          }
+          *reinterpret_cast<uint4*>(dst + ((bb * H + h) * T + t) * D + 8 * ch) = val;
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < FI; ++i) {
     const int64_t m = m0 + wm + 16 * i + l16;

@@ -65,14 +65,17 @@ def test_small_projection_parity(hidden, H, out_bf16, with_bias):
     compare(gpu_project(x, w, b, out_bf16), oracle.input_projections(x, w, b), out_bf16)
 
 
-@pytest.mark.parametrize("B,T,H", [(3, 200, 2), (1, 129, 260), (2, 1, 5), (2, 300, 8)])
-def test_ragged_tiles_and_many_heads(B, T, H):
-    # token tiles (256 tokens) across batch boundaries and a ragged last tile;
-    # more than 256 heads puts the eta rows in two tiles, the second one mostly
-    # empty
-    say(f"case project B={B} T={T} H={H}")
+@pytest.mark.parametrize("out_bf16", [False, True])
+@pytest.mark.parametrize("B,T,H", [(3, 200, 2), (1, 129, 260), (2, 1, 5), (2, 300, 8),
+                                   (5, 70, 3)])
+def test_ragged_tiles_and_many_heads(B, T, H, out_bf16):
+    # token tiles (256 tokens) across batch boundaries and a ragged last tile
+    # (with bf16 results also sequence boundaries inside a wave's 64 staged
+    # rows, for T below and above 64); more than 256 heads puts the eta rows
+    # in two tiles, the second one mostly empty
+    say(f"case project B={B} T={T} H={H} bf16={out_bf16}")
     x, w, b = make_projection_case(B, T, 64, H, 64, seed=510 + T, with_bias=True)
-    compare(gpu_project(x, w, b, False), oracle.input_projections(x, w, b), False)
+    compare(gpu_project(x, w, b, out_bf16), oracle.input_projections(x, w, b), out_bf16)
 
 
 @pytest.mark.parametrize("hidden", [64, 128, 160, 192])
