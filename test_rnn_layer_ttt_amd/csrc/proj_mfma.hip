@@ -27,7 +27,8 @@
 // bf16 results of a head tile go through LDS: each wave stages one output
 // (64 tokens x 64 features) at a time and writes whole 128-byte token rows
 // with 16-byte stores; fp32 results and eta tiles are stored directly (four
-// features per lane in one 16-byte write, or single values).
+// features per lane in one 16-byte write, or single values).  Eta tiles run
+// a plain K loop that issues the MFMAs of their real rows only.
 #include "scan_common.h"
 
 #include <cstdint>
@@ -220,6 +221,38 @@ proj_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
   };
   using full_t = std::integral_constant<bool, true>;
   using tail_t = std::integral_constant<bool, false>;
+  if (eta_tile) {
+    // eta tiles hold up to 256 heads' eta rows, mostly fewer: a plain K loop
+    // on the same ring that issues the MFMAs of the real rows only (column
+    // tiles j < nj of this wave)
+    const int n_eta = H - e0 < TN ? H - e0 : TN;
+    const int nj = max(0, min(FJ, (n_eta - wn + 15) / 16));
+    issue(0, 0);
+    if (nk > 1) issue(1, TK);
+    for (int ks = 0; ks < nk; ++ks) {
+      if (ks + 1 < nk)
+        __builtin_amdgcn_s_waitcnt(kWaitStep);
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitAll);
+      bar();
+      if (ks + 2 < nk) issue((ks + 2) % NSTAGE, (ks + 2) * TK);
+      const int st = ks % NSTAGE;
+      if (nj > 0) {
+        bf16x8 af[FI];
+#pragma unroll
+        for (int i = 0; i < FI; ++i) af[i] = read_a(st, i);
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+          if (j < nj) {
+            const bf16x8 bf = read_b(st, j);
+#pragma unroll
+            for (int i = 0; i < FI; ++i)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, af[i], acc[i][j], 0, 0, 0);
+          }
+        }
+      }
+    }
+  } else {
   bf16x8 b0[FJ], b1[FJ];
   issue(0, 0);
   if (nk > 1) issue(1, TK);
@@ -243,6 +276,7 @@ proj_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
   if (ks + 1 < nk) step(tail_t{}, ks + 1, b1, b0);
   if (ks + 2 < nk) step(tail_t{}, ks + 2, b0, b1);
   if (ks + 3 < nk) step(tail_t{}, ks + 3, b1, b0);
+  }
 
   // epilogue: D[4G + r][l16] of MFMA tile (i, j) is token m0 + wm + 16i + l16,
   // weight row wn + 16j + 4G + r of the tile.
