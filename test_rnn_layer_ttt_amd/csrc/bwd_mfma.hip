@@ -395,6 +395,11 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
                 float* __restrict__ dW0, float* __restrict__ gb_part, int H, int64_t T,
                 float eps, int silu) {
   __shared__ BwdSmem sm;
+  // the wave that forms B2's third column block in phase B: with bf16 inputs
+  // (outside the exact LayerNorm) wave 1, whose phase B is short there, so
+  // that the loader's store is the only long task of its phase; else the
+  // loader (measured: each choice slower by 6-12% where it is not used)
+  constexpr int kB2Wave = (BF16 && LN != kLnExact) ? 1 : 4;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -888,7 +893,7 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       else
         half(std::integral_constant<int, 4>{});
     }
-    if ((wave == 0 || wave == 4 || wave == 3) && live) {
+    if ((wave == 0 || wave == kB2Wave || wave == 3) && live) {
       // B2 = DZ W_c - sum_{s<t} eta_s (delta_s.dz_t) k_s, with
       // DZ W_c = DZ W_{c-1} - (DZ E_{c-1}^T) K_{c-1} (for c = 0 the slot holds W_0);
       // the dual form has no in-tile sum
@@ -910,8 +915,8 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) ae[ks] = -ae[ks];
       }
-      // column blocks: wave 0 takes 0 and 1, wave 4 block 2, wave 3 block 3
-      const int jb0 = wave == 0 ? 0 : wave == 4 ? 2 : 3;
+      // column blocks: wave 0 takes 0 and 1, kB2Wave block 2, wave 3 block 3
+      const int jb0 = wave == 0 ? 0 : wave == kB2Wave ? 2 : 3;
       const int njb = wave == 0 ? 2 : 1;
       for (int jj = 0; jj < njb; ++jj) {
         const int jb = jb0 + jj;
