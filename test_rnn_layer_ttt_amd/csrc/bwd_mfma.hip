@@ -400,6 +400,11 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   // that the loader's store is the only long task of its phase; else the
   // loader (measured: each choice slower by 6-12% where it is not used)
   constexpr int kB2Wave = (BF16 && LN != kLnExact) ? 1 : 4;
+  // the dual form's chain is short: its wave and the loader each take one of
+  // the four DY W blocks (and its dq block) from waves 2 and 3 (bf16 inputs,
+  // where the loader's state leaves slot 14 free)
+  constexpr bool kSpreadDq = DUAL && BF16 && LN != kLnExact;
+  static_assert(!kSpreadDq || LoadLayout<BF16>::kEnd <= 56, "slot 14 must be free");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -469,6 +474,21 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
     const bool live = c < N;        // tile c exists
     const int cm = c - 1;
     // ============================ phase A ============================
+    // dQ' = DY W of tile c-1, column block jb into state slot sl
+    auto dqw1 = [&](auto jbc, auto slc) {
+      constexpr int jb = decltype(jbc)::value, sl = decltype(slc)::value;
+      const TileIn& tm = sm.ring[cm % 3];
+      const float(*Wm)[KP] = sm.W[cm & 1];
+      float a[16], bb[16];
+      frag_row64(tm.DY[l16], G, a);
+      frag_col64(Wm, 16 * jb + l16, G, bb);
+      put(st, sl, mma<16>(a, bb, f32x4{0, 0, 0, 0}));
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I14 = std::integral_constant<int, 14>;
     if (wave == 0) {
       if (live) {
         // ---- the dz chain of tile c, t descending ----
@@ -582,6 +602,9 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
           store_block(sm.DZE, 0, g2, l16, G);
         }
       }
+      if constexpr (kSpreadDq) {
+        if (prep) dqw1(I1{}, I0{});
+      }
     } else if (wave == 3 || wave == 2) {
       // dk's H-side half b1, column blocks j0, j0+1 (wave 3: 0-1 in state
       // slots 0-1; wave 2: 2-3 in slots 4-5), beside half of DY W each
@@ -632,10 +655,18 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       };
       if (wave == 3) {
         half(std::integral_constant<int, 0>{});
-        if (prep) dqw(std::integral_constant<int, 2>{});
+        if constexpr (kSpreadDq) {
+          if (prep) dqw1(I2{}, I2{});
+        } else {
+          if (prep) dqw(std::integral_constant<int, 2>{});
+        }
       } else {
         half(std::integral_constant<int, 4>{});
-        if (prep) dqw(std::integral_constant<int, 0>{});
+        if constexpr (kSpreadDq) {
+          if (prep) dqw1(I0{}, I0{});
+        } else {
+          if (prep) dqw(std::integral_constant<int, 0>{});
+        }
       }
     } else if (wave != 4 && prep) {
       const TileIn& tm = sm.ring[cm % 3];
@@ -678,6 +709,9 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         }
       }
     }
+    if constexpr (kSpreadDq) {
+      if (wave == 4 && prep) dqw1(I3{}, I14{});
+    }
     if (wave == 4 && c >= 2) {
       const int u = c - 2;
       loader_issue<BF16>(st, ld_eta, ld_n, qp, kp, gatep, etap, dout, rec_delta, bhT,
@@ -716,6 +750,33 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
     if (wave == 4 && c >= 2) {
       const int u = c - 2;
       loader_store<BF16>(st, ld_eta, ld_n, sm.ring[u % 3], lane, silu != 0);
+    }
+    // dq of tile c-1, column block jb from state slot sl (as dq_blocks)
+    auto dq1 = [&](auto jbc, auto slc) {
+      constexpr int jb = decltype(jbc)::value, sl = decltype(slc)::value;
+      const TileIn& tm = sm.ring[cm % 3];
+      const Grams& gm = sm.gr[cm & 1];
+      float a[4];
+      frag_col16(gm.DeDY, l16, G, a);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int s = 4 * G + ks;
+        a[ks] = s <= l16 ? -tm.ETA[s] * a[ks] : 0.0f;
+      }
+      const int nm = rows(cm);
+      const int64_t t0 = int64_t(cm) * BT;
+      float b[4];
+      frag_col16(tm.K, 16 * jb + l16, G, b);
+      const f32x4 v = mma<4>(a, b, blk(st, sl));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 4 * G + r;
+        if (t < nm) dq[(bhT + t0 + t) * D + 16 * jb + l16] = v[r];
+      }
+    };
+    if constexpr (kSpreadDq) {
+      if (prep && wave == 0) dq1(I1{}, I0{});
+      if (prep && wave == 4) dq1(I3{}, I14{});
     }
     if (wave == 7 && c >= 2) w_store(st, sm.W[(c - 2) & 1], lane);
     if (wave == 1 && prep) {
@@ -813,9 +874,17 @@ bwd_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         }
       }
     } else if (wave == 3) {
-      if (prep) dq_blocks(std::integral_constant<int, 2>{});
+      if constexpr (kSpreadDq) {
+        if (prep) dq1(I2{}, I2{});
+      } else {
+        if (prep) dq_blocks(std::integral_constant<int, 2>{});
+      }
     } else if (wave == 2) {
-      if (prep) dq_blocks(std::integral_constant<int, 0>{});
+      if constexpr (kSpreadDq) {
+        if (prep) dq1(I0{}, I0{});
+      } else {
+        if (prep) dq_blocks(std::integral_constant<int, 0>{});
+      }
       if (live) {
         // d eta_logit of tile c = -sigmoid'(.)/d delta_t . a_t (a Gram's diagonal)
         const TileIn& tc = sm.ring[c % 3];
