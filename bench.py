@@ -93,16 +93,26 @@ def ttt_record_chunk():
     return RECORD_CHUNK
 
 
-def kernel_info(x):
-    """Which kernel family runs this workload and which roof bounds it."""
+def kernel_name(x, force_valu=False):
+    """Which kernel family runs this workload."""
     import test_rnn_layer_ttt_amd as ttt
     d = x.q.shape[-1]
-    name = ttt.ttt_linear_kernel(d, ttt.mode_bits(x.ln, x.dual, x.in_bf16), x.chunk)
-    if name == "scan_mfma":
-        # the d^2 work runs on the matrix cores: the HBM stream is the binding roof
-        return name, "hbm"
-    # vector-ALU scan: bf16 inputs put it above the FP32-vector ridge, fp32 inputs below
-    return name, ("alu" if x.in_bf16 else "hbm")
+    return ttt.ttt_linear_kernel(d, ttt.mode_bits(x.ln, x.dual, x.in_bf16,
+                                                  force_valu=force_valu), x.chunk)
+
+
+def precision(x, kernel):
+    """What the arithmetic of a forward launch is, in words."""
+    if kernel == "scan_valu":
+        return ("bf16 inputs widened to fp32; " if x.in_bf16 else "fp32 inputs; ") + \
+            "fp32 vector-ALU arithmetic, fp32 state and output"
+    if x.in_bf16:
+        return ("bf16 inputs; d x d products on bf16 MFMA (16x16x32, 16x16x16) with the fp32 "
+                "operands (W, delta, eta-scaled Gram entries) split into bf16 hi + lo and only "
+                "the lo*lo term (~2^-17 relative) dropped; fp32 accumulation, fp32 LayerNorm "
+                "pass, fp32 state and output")
+    return ("fp32 inputs; d x d products on fp32 MFMA (16x16x4); fp32 LayerNorm pass, "
+            "fp32 state and output")
 
 
 def projection_work(x):
@@ -116,29 +126,50 @@ def projection_work(x):
     return B * H * T, nbytes, 2 * B * T * hidden * rows
 
 
-def roofline(x, kernel_ms, traffic, train=False, mask=None, project=False):
+def roofline(x, kernel_ms, traffic, train=False, mask=None, project=False,
+             hbm_measured_gbs=None, kernel=None):
+    """Both ceilings of one launch and the fraction of the binding one.
+
+    t_hbm = algorithmic bytes / the HBM peak and t_compute = algorithmic flops /
+    the compute peak of that arithmetic: fp32 (157.3 TFLOP/s) for the per-token
+    scan and the backward, whose flops are fp32 arithmetic; dense bf16 MFMA for
+    the dual form's chunk contractions and the projections.  The binding roof
+    is the one with the larger time; ``frac`` is measured against it, and
+    ``frac_hbm`` / ``frac_compute`` give both.  With ``hbm_measured_gbs`` (a
+    device copy timed in the same run) the HBM fraction is also given against
+    that measured ceiling."""
     if project:
         n, nbytes, flops = projection_work(x)
-        achieved = flops / (kernel_ms / 1e3) / 1e12
-        return "proj_mfma", dict(bound="mfma", achieved=round(achieved, 1),
-                                 peak=BF16_MATRIX_PEAK_TFLOPS, unit="TFLOP/s",
-                                 frac=round(achieved / BF16_MATRIX_PEAK_TFLOPS, 4),
-                                 traffic=traffic)
-    if train:
+        name, cbound, cpeak = "proj_mfma", "mfma", BF16_MATRIX_PEAK_TFLOPS
+    elif train:
         n, nbytes, flops = backward_work(x)
-        name, bound = "bwd_mfma", "hbm"
+        name, cbound, cpeak = "bwd_mfma", "alu", FP32_VECTOR_PEAK_TFLOPS
     else:
         n, nbytes, flops = algorithmic_work(x, mask)
-        name, bound = kernel_info(x)
+        name = kernel or kernel_name(x)
+        if x.dual and name == "scan_mfma":
+            cbound, cpeak = "mfma", BF16_MATRIX_PEAK_TFLOPS
+        else:
+            cbound, cpeak = "alu", FP32_VECTOR_PEAK_TFLOPS
     sec = kernel_ms / 1e3
-    if bound == "hbm":
-        achieved = nbytes / sec / 1e9
-        return name, dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
-                          unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic)
-    achieved = flops / sec / 1e12
-    return name, dict(bound="alu", achieved=round(achieved, 2), peak=FP32_VECTOR_PEAK_TFLOPS,
-                      unit="TFLOP/s", frac=round(achieved / FP32_VECTOR_PEAK_TFLOPS, 4),
-                      traffic=traffic)
+    gbs = nbytes / sec / 1e9
+    tfs = flops / sec / 1e12
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_cmp = flops / (cpeak * 1e12)
+    if t_hbm >= t_cmp:
+        roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(gbs / HBM_PEAK_GBS, 4))
+    else:
+        roof = dict(bound=cbound, achieved=round(tfs, 2), peak=cpeak, unit="TFLOP/s",
+                    frac=round(tfs / cpeak, 4))
+    roof.update(traffic=traffic, frac_hbm=round(gbs / HBM_PEAK_GBS, 4),
+                frac_compute=round(tfs / cpeak, 4), compute_peak_tflops=cpeak,
+                t_hbm_us=round(t_hbm * 1e6, 1), t_compute_us=round(t_cmp * 1e6, 1),
+                algorithmic_bytes=nbytes, algorithmic_flops=flops)
+    if hbm_measured_gbs:
+        roof.update(hbm_measured_gbs=round(hbm_measured_gbs, 1),
+                    frac_hbm_measured=round(gbs / hbm_measured_gbs, 4))
+    return name, roof
 
 
 # ---------------------------------------------------------------------------
@@ -267,6 +298,12 @@ def main():
                     help="scans of the workload the CPU oracle is timed on "
                          "(default 256 for the forward, 128 for a training pass)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="launches of the dominant kernel timed with a cache flush before each")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="MiB written between cold launches (L2 and the 256 MB MALL)")
+    ap.add_argument("--valu-steps", type=int, default=5,
+                    help="launches of the vector-ALU kernel timed beside the matrix-core one")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed region, run one device-to-device copy of this many "
                          "MiB: a kernel of known traffic that scales the HBM byte counters")
@@ -366,6 +403,9 @@ def main():
         st, rec_bytes = ttt.ttt_linear_record_bytes(B, H, T, d, mode)
         ttt.check(st)
         record = torch.empty(rec_bytes, dtype=torch.uint8, device=dev)
+        st, ws_bytes = ttt.ttt_linear_backward_workspace_bytes(B, H, d, mode)
+        ttt.check(st)
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
         dout_np, dWf_np = _cotangents(x)
         dout = torch.from_numpy(dout_np).to(dev)
         dWf = torch.from_numpy(dWf_np).to(dev)
@@ -376,7 +416,8 @@ def main():
         no_ln = x.ln == "none"
         bptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), el.data_ptr(), gl.data_ptr(),
                  None if no_ln else gamma.data_ptr(), None if no_ln else beta.data_ptr(),
-                 record.data_ptr(), rec_bytes, dout.data_ptr(), dWf.data_ptr(),
+                 record.data_ptr(), rec_bytes, workspace.data_ptr(), ws_bytes,
+                 dout.data_ptr(), dWf.data_ptr(),
                  *[g.data_ptr() for g in grads[:3]], deta.data_ptr(), grads[3].data_ptr(),
                  dW0.data_ptr(), None if no_ln else dgamma.data_ptr(),
                  None if no_ln else dbeta.data_ptr())
@@ -394,59 +435,83 @@ def main():
             if st != ttt.TTT_OK:
                 raise RuntimeError(f"ttt_linear_backward: {ttt.ttt_status_string(st)}")
 
+    # the dominant kernel of a step (the one the roofline is about) and the rest
+    if train:
+        steps = [("record", forward_record), ("main", backward)]
+    elif project:
+        steps = [("main", projection), ("scan", forward)]
+    else:
+        steps = [("main", forward)]
+
     for _ in range(args.warmup):
-        if train:
-            forward_record()
-            backward()
-        elif project:
-            projection()
-            forward()
-        else:
-            forward()
+        for _, fn in steps:
+            fn()
     torch.cuda.synchronize()
 
-    # events on the launch stream around the dominant kernel of each step (the
-    # backward in a training pass), and around the whole step
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    starts, ends, fstarts, fends = mk(), mk(), mk(), mk()
+    # ---- timed region: exactly K back-to-back steps between two device syncs;
+    # events on the launch stream around every launch (warm caches: a step's
+    # inputs may still sit in L2 / the MALL from the step before)
+    ev = {tag: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)] for tag, _ in steps}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        if train:
-            fstarts[i].record(stream)
-            forward_record()
-            fends[i].record(stream)
-            starts[i].record(stream)
-            backward()
-            ends[i].record(stream)
-        elif project:
-            starts[i].record(stream)
-            projection()
-            ends[i].record(stream)
-            fstarts[i].record(stream)
-            forward()
-            fends[i].record(stream)
-        else:
-            starts[i].record(stream)
-            forward()
-            ends[i].record(stream)
+        for tag, fn in steps:
+            ev[tag][i][0].record(stream)
+            fn()
+            ev[tag][i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms = {tag: [a.elapsed_time(b) for a, b in ev[tag]] for tag, _ in steps}
+    kernel_ms = ms["main"]
     avg_kernel_ms = float(np.mean(kernel_ms))
     ms_per_step = wall * 1e3 / args.steps
+
+    # ---- cold: the dominant kernel again, with >= 512 MiB written between
+    # launches (outside the events) so that neither L2 nor the 256 MB MALL
+    # holds its inputs
+    cold_ms = []
+    if args.cold_steps > 0:
+        flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev)
+        main_fn = dict(steps)["main"]
+        for i in range(args.cold_steps):
+            flush.fill_(i & 0xFF)
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            main_fn()
+            b_.record(stream)
+            b_.synchronize()
+            cold_ms.append(a_.elapsed_time(b_))
+        del flush
+
+    # ---- the measured HBM ceiling: a 1 GiB device-to-device copy (1 GiB read,
+    # 1 GiB written), median of five
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    copy_ms = []
+    for _ in range(6):
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record(stream)
+        dst.copy_(src)
+        b_.record(stream)
+        b_.synchronize()
+        copy_ms.append(a_.elapsed_time(b_))
+    del src, dst
+    copy_gbs = 2 * (1 << 30) / (float(np.median(copy_ms[1:])) / 1e3) / 1e9
+
     n_tok = B * H * T
-    kernel = "bwd_mfma" if train else "proj_mfma" if project else kernel_info(x)[0]
+    kernel = "bwd_mfma" if train else "proj_mfma" if project else kernel_name(x)
     traffic_key = args.workload + ("/backward" if train else "/project" if project else "")
     if mask_np is not None:
         traffic_key = args.workload + f"/update{args.update_rate:g}"
     if args.silu_qk:
         traffic_key += "/silu"
     kname, roof = roofline(x, avg_kernel_ms, load_traffic(kernel, traffic_key), train, mask_np,
-                           project)
+                           project, hbm_measured_gbs=copy_gbs)
 
     mode_name = ("dual-form chunk %d" % x.chunk if x.dual else "per-token") + \
         {"st": "", "exact": ", exact LN Jacobian", "none": ", no LN"}[x.ln]
+    med = lambda a: round(float(np.median(a)), 4)
     line = {
         "metric": METRIC_TRAIN if train else METRIC_PROJECT if project else METRIC,
         "value": round(n_tok / (ms_per_step / 1e3), 1),
@@ -458,16 +523,31 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if x.in_bf16 else "f32",
         "data": "synthetic",
+        "cache": "warm",
         "config": {"workload": args.workload, "B": B, "H": H, "T": T, "d": d,
                    "hidden": H * d, "mode": mode_name,
                    "inputs": "bf16" if x.in_bf16 else "fp32", "state": "fp32",
+                   "precision": precision(x, kname) if not (train or project) else
+                   ("bf16 inputs" if x.in_bf16 else "fp32 inputs") +
+                   "; fp32 accumulation, fp32 gradients",
                    "kernel": kname, "kernel_ms_avg": round(avg_kernel_ms, 4),
-                   "kernel_ms_min": round(min(kernel_ms), 4)},
+                   "kernel_ms_median": med(kernel_ms),
+                   "kernel_ms_min": round(min(kernel_ms), 4),
+                   "cu_occupied": f"{min(B * H, 256)}/256" if not project else "all",
+                   "timing": "value from the wall clock of the K back-to-back steps (warm "
+                             "caches); roofline from the events' average over them; cold = "
+                             f"{args.flush_mib} MiB written between launches"},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if cold_ms:
+        line["config"]["cold"] = {"kernel_ms_median": med(cold_ms),
+                                  "kernel_ms_min": round(min(cold_ms), 4),
+                                  "launches": len(cold_ms), "flush_mib": args.flush_mib,
+                                  "token_heads_per_s": round(n_tok / (np.median(cold_ms) / 1e3),
+                                                             1)}
     if args.silu_qk:
         line["config"]["variant"] = "mlp (SiLU on q and k)"
     if mask_np is not None:
@@ -475,13 +555,38 @@ def main():
         line["config"]["chunks_updated"] = float(np.mean(mask_np != 0))
     if train:
         line["config"]["pass"] = "train: recording forward + backward"
-        fwd_ms = [s_.elapsed_time(e_) for s_, e_ in zip(fstarts, fends)]
-        line["config"]["forward_record_ms_avg"] = round(float(np.mean(fwd_ms)), 4)
+        line["config"]["forward_record_ms_avg"] = round(float(np.mean(ms["record"])), 4)
     if project:
         line["config"]["pass"] = ("layer: input projections from x [B,T,hidden] bf16, "
                                   "then the scan")
-        scan_ms = [s_.elapsed_time(e_) for s_, e_ in zip(fstarts, fends)]
-        line["config"]["scan_ms_avg"] = round(float(np.mean(scan_ms)), 4)
+        line["config"]["scan_ms_avg"] = round(float(np.mean(ms["scan"])), 4)
+
+    # ---- the vector-ALU per-token kernel on the same inputs, for comparison
+    # (the matrix-core kernel is what a call at d = 64 runs)
+    if (not train and not project and mask_np is None and args.valu_steps > 0
+            and kname == "scan_mfma"):
+        vmode = mode | ttt.TTT_FORCE_VALU
+
+        def valu():
+            st = ttt.ttt_linear_forward(*ptrs, B, H, T, d, vmode, x.chunk, stream.cuda_stream)
+            if st != ttt.TTT_OK:
+                raise RuntimeError(f"ttt_linear_forward: {ttt.ttt_status_string(st)}")
+        valu()
+        torch.cuda.synchronize()
+        vms = []
+        for _ in range(args.valu_steps):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            valu()
+            b_.record(stream)
+            b_.synchronize()
+            vms.append(a_.elapsed_time(b_))
+        _, vroof = roofline(x, float(np.median(vms)), None, kernel="scan_valu")
+        line["config"]["valu_kernel"] = {
+            "kernel": "scan_valu", "kernel_ms_median": med(vms),
+            "token_heads_per_s": round(n_tok / (np.median(vms) / 1e3), 1),
+            "bound": vroof["bound"], "frac": vroof["frac"], "frac_hbm": vroof["frac_hbm"],
+            "frac_compute": vroof["frac_compute"], "precision": precision(x, "scan_valu")}
     print(json.dumps(line), flush=True)
 
     if args.copy_probe_mib > 0:

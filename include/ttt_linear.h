@@ -67,6 +67,11 @@ extern "C" {
                              out = (W silu(q_t)) * sigmoid(gate); gradients are
                              with respect to the raw q and k.  On the bf16-input
                              matrix-core path silu(q), silu(k) are rounded to bf16 */
+#define TTT_FORCE_VALU 32u /* run the vector-ALU per-token kernel even where the
+                             matrix-core kernel applies (d = 64): the kernel the
+                             scan's specification names for the per-token mode,
+                             kept callable for comparison; same results within
+                             rounding.  Not accepted by the recording forward */
 
 /* status codes */
 #define TTT_OK               0
@@ -76,7 +81,7 @@ extern "C" {
 #define TTT_ERR_UNSUPPORTED  4  /* d not in {16, 32, 64, 128}, or a misaligned pointer */
 #define TTT_ERR_ALIAS        5  /* out overlaps an argument, or W_final partially overlaps */
 #define TTT_ERR_HIP          6  /* the HIP runtime reported an error at launch */
-#define TTT_ERR_WORKSPACE    7  /* record_bytes is below what ttt_linear_record_bytes gives */
+#define TTT_ERR_WORKSPACE    7  /* record_bytes or workspace_bytes below the size query's value */
 
 /*
  * Run the scan over all B*H (batch, head) pairs.
@@ -156,15 +161,16 @@ int32_t ttt_linear_forward_masked(const void* q, const void* k, const void* v,
  *
  * The record is one caller-owned device buffer of ttt_linear_record_bytes()
  * bytes, 16-byte aligned; its contents are private to the library.  The
- * backward also uses a small tail of it as scratch (the per-(b,h) LayerNorm
- * parameter gradients before their sum over the batch), so two backward calls
- * on one record must not run at the same time; the recorded part is only read
- * and may be used by any number of backward calls in sequence.
+ * backward only reads it, so any number of backward calls may use one record,
+ * also at the same time on different streams.  The backward's own scratch (the
+ * per-(b,h) LayerNorm parameter gradients before their sum over the batch)
+ * lives in a separate caller-owned workspace of
+ * ttt_linear_backward_workspace_bytes() bytes.
  */
 
 /*
  * The record size for these sizes and mode, in *bytes:
- * 4 * B*H * (T*d + ceil(T/16)*d*d + 2*d), the same with or without TTT_DUAL.
+ * 4 * B*H * (T*d + ceil(T/16)*d*d), the same with or without TTT_DUAL.
  * Checks the shapes and mode as ttt_linear_forward_record does (the chunk of
  * the dual form is checked by the two calls that take it).  Makes no HIP call.
  */
@@ -195,7 +201,11 @@ int32_t ttt_linear_forward_record(const void* q, const void* k, const void* v,
  *     dgamma, dbeta             [H,d]       summed over the batch and the tokens;
  *                                           unused, may be NULL, with TTT_NO_LN
  * Every output is overwritten, not accumulated into.  Outputs must not overlap
- * one another, the inputs or the record (except dW0 == dW_final).  Pointer
+ * one another, the inputs, the record or the workspace (except dW0 ==
+ * dW_final).  `workspace` is caller-owned device scratch of at least
+ * ttt_linear_backward_workspace_bytes() bytes, 16-byte aligned (it may be NULL
+ * when that size is 0); its contents on entry do not matter and on return are
+ * unspecified, and two calls that overlap in time need two workspaces.  Pointer
  * alignment as in ttt_linear_forward; deta_logit, dgamma and dbeta need 4
  * bytes.  With T == 0 only dW0 (= dW_final, or zero), dgamma and dbeta (zero)
  * are written, and the per-token pointers may be NULL.  Runs asynchronously on
@@ -205,12 +215,22 @@ int32_t ttt_linear_forward_record(const void* q, const void* k, const void* v,
 int32_t ttt_linear_backward(const void* q, const void* k, const void* v,
                             const void* eta_logit, const void* gate_logit,
                             const float* gamma, const float* beta,
-                            void* record, int64_t record_bytes,
+                            const void* record, int64_t record_bytes,
+                            void* workspace, int64_t workspace_bytes,
                             const float* dout, const float* dW_final,
                             float* dq, float* dk, float* dv, float* deta_logit,
                             float* dgate_logit, float* dW0, float* dgamma, float* dbeta,
                             int64_t B, int64_t H, int64_t T, int64_t d,
                             uint32_t mode, int64_t chunk, void* stream);
+
+/*
+ * The workspace size of ttt_linear_backward for these sizes and mode, in
+ * *bytes: 4 * B*H * 2*d with the LayerNorm (per-(b,h) dgamma, dbeta before the
+ * batch sum), 0 with TTT_NO_LN.  Checks the shapes and mode as
+ * ttt_linear_record_bytes does.  Makes no HIP call.
+ */
+int32_t ttt_linear_backward_workspace_bytes(int64_t B, int64_t H, int64_t d, uint32_t mode,
+                                            int64_t* bytes);
 
 /*
  * ---- The layer's input projections ----
@@ -246,7 +266,9 @@ int32_t ttt_linear_project(const void* x, const void* w_proj, const float* b_pro
 /* A static, human-readable description of a status code (never NULL). */
 const char* ttt_status_string(int32_t status);
 
-/* A static version string of the library (never NULL). */
+/* A static version string of the library (never NULL).  It ends with
+ * "src=<16 hex digits>", a digest of the sources the library was built from,
+ * so a caller can tell a stale build from a current one. */
 const char* ttt_version(void);
 
 #ifdef __cplusplus

@@ -132,7 +132,7 @@ def inner_grad_vector(z, v, gamma, beta, ln: str, eps: float = EPS):
 def ttt_linear_forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None,
                        *, ln: str = LN_ST, dual: bool = False, chunk: int = 16,
                        eps: float = EPS, dtype=np.float64, update_mask=None,
-                       silu_qk: bool = False):
+                       silu_qk: bool = False, return_ln_stats: bool = False):
     """The TTT-Linear scan, token by token.
 
     Shapes (row-major): q, k, v, gate_logit [B,H,T,d]; eta_logit [B,H,T];
@@ -162,6 +162,12 @@ def ttt_linear_forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None
     chunk).  A skipped chunk applies no update: its tokens take eta_t = 0, so
     W passes the chunk unchanged and the chunk's outputs read W_c q_t.
 
+    ``return_ln_stats``: also return ``{"mean": [B,H,T], "std": [B,H,T],
+    "delta": [B,H,T,d]}``: the mean and the (biased) standard deviation over
+    the d features of every z_t that enters the LayerNorm (a diagnostic of how
+    far off-centre the LayerNorm's inputs are; zeros without LayerNorm), and
+    every inner-gradient vector delta_t.
+
     Parity: pinned (eta -> 0 closed form, delta-rule unrolled product,
     autograd inner-gradient steps, finite differences, dual-form special
     cases, overwrite and cancellation identities, resume, independence; the
@@ -187,6 +193,9 @@ def ttt_linear_forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None
 
     W = W0.copy()
     out = np.zeros((B, H, T, d), dtype=dtype)
+    z_mean = np.zeros((B, H, T), dtype=dtype)
+    z_std = np.zeros((B, H, T), dtype=dtype)
+    deltas = np.zeros((B, H, T, d), dtype=dtype) if return_ln_stats else None
     eta_all = sigmoid(eta_logit) / dtype(d)
     gate_all = sigmoid(gate_logit)
     Wc = W
@@ -196,12 +205,19 @@ def ttt_linear_forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None
         P = Wc if dual else W
         kt = k[:, :, t, :]
         z = np.matmul(P, kt[..., None])[..., 0]
+        if return_ln_stats and ln != LN_NONE:
+            z_mean[:, :, t] = z.mean(axis=-1)
+            z_std[:, :, t] = np.sqrt(((z - z_mean[:, :, t][..., None]) ** 2).mean(axis=-1))
         delta = inner_grad_vector(z, v[:, :, t, :], gamma, beta, ln, eps)
+        if return_ln_stats:
+            deltas[:, :, t, :] = delta
         eta = eta_all[:, :, t][..., None, None]
         if keep is not None:
             eta = np.where(keep[:, :, t // chunk][..., None, None], eta, dtype(0))
         W = W - eta * (delta[..., :, None] * kt[..., None, :])
         out[:, :, t, :] = np.matmul(W, q[:, :, t, :][..., None])[..., 0] * gate_all[:, :, t, :]
+    if return_ln_stats:
+        return out, W, dict(mean=z_mean, std=z_std, delta=deltas)
     return out, W
 
 
@@ -410,9 +426,14 @@ def input_projections(x, w_proj, b_proj=None):
 
 
 def rel_max_err(got, ref) -> float:
-    """Relative max error of one output tensor: max|got - ref| / max|ref|."""
+    """Relative max error of one output tensor: max|got - ref| / max|ref|
+    (max|got - ref| when ref is all zero).  The two tensors must have the same
+    shape.  Pinned by tests/test_oracle_checker.py (hand-worked values, the
+    zero and empty cases, non-finite results)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
+    if got.shape != ref.shape:
+        raise ValueError(f"shape mismatch: {got.shape} vs {ref.shape}")
     den = np.max(np.abs(ref)) if ref.size else 0.0
     num = np.max(np.abs(got - ref)) if ref.size else 0.0
     if den == 0.0:

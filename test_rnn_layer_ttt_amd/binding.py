@@ -21,6 +21,7 @@ TTT_LN_EXACT = 2
 TTT_IN_BF16 = 4
 TTT_NO_LN = 8
 TTT_SILU_QK = 16
+TTT_FORCE_VALU = 32
 
 TTT_OK = 0
 TTT_ERR_NULL = 1
@@ -35,7 +36,8 @@ TTT_ERR_WORKSPACE = 7
 RECORD_CHUNK = 16
 
 #: every symbol the header declares
-EXPORTED = ("ttt_linear_backward", "ttt_linear_forward", "ttt_linear_forward_masked",
+EXPORTED = ("ttt_linear_backward", "ttt_linear_backward_workspace_bytes",
+            "ttt_linear_forward", "ttt_linear_forward_masked",
             "ttt_linear_forward_record", "ttt_linear_project",
             "ttt_linear_kernel", "ttt_linear_record_bytes", "ttt_linear_validate",
             "ttt_status_string", "ttt_version")
@@ -53,8 +55,10 @@ class TTTArgumentError(TTTError, ValueError):
     pass
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load the shared library (once).  Raises if it has not been built."""
+def load_library(path: str = LIB_PATH, check_digest: bool = True) -> ctypes.CDLL:
+    """Load the shared library (once).  Raises if it has not been built, or if
+    it was built from other sources than the ones next to it (the digest that
+    ``ttt_version()`` carries must match ``build.source_digest()``)."""
     global _lib
     if _lib is not None:
         return _lib
@@ -63,6 +67,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             f"HIP library {path} is missing: build it first "
             "(python -c 'import __graft_entry__ as g; g.build()')")
     lib = ctypes.CDLL(path)
+    lib.ttt_version.restype = ctypes.c_char_p
+    lib.ttt_version.argtypes = []
+    if check_digest:
+        from .build import source_digest
+        version = lib.ttt_version().decode()
+        want = source_digest()
+        if not version.endswith("src=" + want):
+            raise RuntimeError(
+                f"HIP library {path} is stale ({version!r}; the sources' digest is {want}): "
+                "rebuild it (python -c 'import __graft_entry__ as g; g.build()')")
     lib.ttt_linear_forward.restype = ctypes.c_int32
     lib.ttt_linear_forward.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 4 + [
         ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p]
@@ -73,8 +87,6 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ttt_linear_kernel.argtypes = [ctypes.c_int64, ctypes.c_uint32, ctypes.c_int64]
     lib.ttt_status_string.restype = ctypes.c_char_p
     lib.ttt_status_string.argtypes = [ctypes.c_int32]
-    lib.ttt_version.restype = ctypes.c_char_p
-    lib.ttt_version.argtypes = []
     lib.ttt_linear_forward_masked.restype = ctypes.c_int32
     lib.ttt_linear_forward_masked.argtypes = [ctypes.c_void_p] * 11 + [ctypes.c_int64] * 4 + [
         ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p]
@@ -86,8 +98,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p]
     lib.ttt_linear_backward.restype = ctypes.c_int32
     lib.ttt_linear_backward.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.c_int64] +
+                                        [ctypes.c_void_p] + [ctypes.c_int64] +
                                         [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 4 +
                                         [ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p])
+    lib.ttt_linear_backward_workspace_bytes.restype = ctypes.c_int32
+    lib.ttt_linear_backward_workspace_bytes.argtypes = [ctypes.c_int64] * 3 + [
+        ctypes.c_uint32, ctypes.POINTER(ctypes.c_int64)]
     lib.ttt_linear_project.restype = ctypes.c_int32
     lib.ttt_linear_project.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int64] * 5 + [
         ctypes.c_uint32, ctypes.c_void_p]
@@ -151,6 +167,14 @@ def ttt_linear_record_bytes(B, H, T, d, mode):
     return st, int(n.value)
 
 
+def ttt_linear_backward_workspace_bytes(B, H, d, mode):
+    """Returns ``(status, bytes)`` of the workspace a backward call needs."""
+    n = ctypes.c_int64(0)
+    st = int(load_library().ttt_linear_backward_workspace_bytes(
+        int(B), int(H), int(d), ctypes.c_uint32(int(mode)), ctypes.byref(n)))
+    return st, int(n.value)
+
+
 def ttt_linear_forward_record(q, k, v, eta_logit, gate_logit, W0, gamma, beta, out, W_final,
                               record, record_bytes, B, H, T, d, mode, chunk, stream) -> int:
     """The recording forward with raw pointers; returns the status code."""
@@ -163,14 +187,15 @@ def ttt_linear_forward_record(q, k, v, eta_logit, gate_logit, W0, gamma, beta, o
 
 
 def ttt_linear_backward(q, k, v, eta_logit, gate_logit, gamma, beta, record, record_bytes,
-                        dout, dW_final, dq, dk, dv, deta_logit, dgate_logit, dW0, dgamma, dbeta,
-                        B, H, T, d, mode, chunk, stream) -> int:
+                        workspace, workspace_bytes, dout, dW_final, dq, dk, dv, deta_logit,
+                        dgate_logit, dW0, dgamma, dbeta, B, H, T, d, mode, chunk, stream) -> int:
     """The backward with raw pointers; returns the status code."""
     lib = load_library()
     p = lambda x: None if x is None else ctypes.c_void_p(int(x))
     return int(lib.ttt_linear_backward(
         p(q), p(k), p(v), p(eta_logit), p(gate_logit), p(gamma), p(beta), p(record),
-        int(record_bytes), p(dout), p(dW_final), p(dq), p(dk), p(dv), p(deta_logit),
+        int(record_bytes), p(workspace), int(workspace_bytes), p(dout), p(dW_final), p(dq),
+        p(dk), p(dv), p(deta_logit),
         p(dgate_logit), p(dW0), p(dgamma), p(dbeta), int(B), int(H), int(T), int(d),
         ctypes.c_uint32(int(mode)), int(chunk), p(stream)))
 
@@ -196,8 +221,10 @@ def check(status: int) -> None:
 
 
 def mode_bits(ln: str = "st", dual: bool = False, in_bf16: bool = False,
-              silu_qk: bool = False) -> int:
+              silu_qk: bool = False, force_valu: bool = False) -> int:
     m = TTT_SILU_QK if silu_qk else 0
+    if force_valu:
+        m |= TTT_FORCE_VALU
     if dual:
         m |= TTT_DUAL
     if in_bf16:
@@ -213,7 +240,7 @@ def mode_bits(ln: str = "st", dual: bool = False, in_bf16: bool = False,
 
 def forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln: str = "st",
             dual: bool = False, chunk: int = 16, out=None, W_final=None, stream=None,
-            update_mask=None, silu_qk: bool = False):
+            update_mask=None, silu_qk: bool = False, force_valu: bool = False):
     """Run the scan on torch device tensors; returns ``(out, W_final)``.
 
     q, k, v, gate_logit: [B,H,T,d] and eta_logit: [B,H,T], all float32 or all
@@ -223,6 +250,7 @@ def forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln: st
     ``torch.cuda.Stream``) or on the current stream.  ``update_mask`` (dual
     form only): uint8 [B,H,ceil(T/chunk)], 0 = SKIP the chunk's updates.
     ``silu_qk``: the :mlp variant (SiLU on q and k before the inner model).
+    ``force_valu``: run the vector-ALU kernel even at d = 64.
     """
     import torch
 
@@ -233,7 +261,7 @@ def forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln: st
         W_final = torch.empty_like(W0)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    mode = mode_bits(ln, dual, q.dtype == torch.bfloat16, silu_qk)
+    mode = mode_bits(ln, dual, q.dtype == torch.bfloat16, silu_qk, force_valu)
     gb = (_ptr(gamma) if ln != "none" else None, _ptr(beta) if ln != "none" else None)
     if update_mask is not None:
         nc = -(-T // chunk) if T > 0 else 0
@@ -351,12 +379,14 @@ def forward_record(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *,
 
 
 def backward(q, k, v, eta_logit, gate_logit, gamma, beta, record, dout, dW_final=None, *,
-             ln: str = "st", stream=None, silu_qk: bool = False, dual: bool = False):
+             ln: str = "st", stream=None, silu_qk: bool = False, dual: bool = False,
+             workspace=None):
     """Gradients from a record of :func:`forward_record` (same ``ln``,
     ``silu_qk`` and ``dual``) and dL/dout (float32 [B,H,T,d]), dL/dW_final
     (float32 [B,H,d,d] or None).  Returns a dict with dq, dk, dv, dgate_logit,
     deta_logit, dW0, dgamma, dbeta (float32; the last two None with
-    ``ln="none"``)."""
+    ``ln="none"``).  ``workspace``: a uint8 device tensor of at least
+    ``ttt_linear_backward_workspace_bytes`` bytes (allocated when None)."""
     import torch
 
     B, H, T, d = _check_inputs(q, k, v, eta_logit, gate_logit, None, gamma, beta, ln)
@@ -374,14 +404,19 @@ def backward(q, k, v, eta_logit, gate_logit, gamma, beta, record, dout, dW_final
              dbeta=None if ln == "none" else torch.empty((H, d), **f32))
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    mode = mode_bits(ln, dual, q.dtype == torch.bfloat16, silu_qk)
+    st, ws_bytes = ttt_linear_backward_workspace_bytes(B, H, d, mode)
+    check(st)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     check(ttt_linear_backward(
         _ptr(q), _ptr(k), _ptr(v), _ptr(eta_logit), _ptr(gate_logit),
         _ptr(gamma) if ln != "none" else None, _ptr(beta) if ln != "none" else None,
-        record.data_ptr(), record.numel() * record.element_size(), _ptr(dout),
+        record.data_ptr(), record.numel() * record.element_size(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _ptr(dout),
         None if dW_final is None else dW_final.data_ptr(), _ptr(g["dq"]), _ptr(g["dk"]),
         _ptr(g["dv"]), _ptr(g["deta_logit"]), _ptr(g["dgate_logit"]), g["dW0"].data_ptr(),
-        _ptr(g["dgamma"]), _ptr(g["dbeta"]), B, H, T, d,
-        mode_bits(ln, dual, q.dtype == torch.bfloat16, silu_qk), RECORD_CHUNK if dual else 1,
+        _ptr(g["dgamma"]), _ptr(g["dbeta"]), B, H, T, d, mode, RECORD_CHUNK if dual else 1,
         stream.cuda_stream))
     return g
 

@@ -59,7 +59,10 @@ def build(verbose: bool = False) -> str:
     """Compile every source and link the library; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-    cmds = [[HIPCC, *CFLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    # the digest of the sources goes into ttt_version(), so a stale library can be told apart
+    digest = [f'-DTTT_SOURCE_DIGEST="{source_digest()}"']
+    cmds = [[HIPCC, *CFLAGS, *digest, "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
     with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():

@@ -36,6 +36,8 @@ struct ScanArgs {
   const uint8_t* upd_mask = nullptr;
   // the :mlp variant: SiLU applied to q and k before the inner model
   bool silu_qk = false;
+  // run the vector-ALU kernel even where the matrix-core one applies
+  bool force_valu = false;
 };
 
 // One validated backward call (d = 64, per-token modes).
@@ -51,7 +53,7 @@ struct BwdArgs {
   const float* dW_final;     // nullptr: zero
   const float* rec_delta;    // [B,H,T,d]
   const float* rec_W;        // [B,H,ntiles,d,d]
-  float* gb_part;            // [B,H,2,d] scratch: per-scan dgamma, dbeta
+  float* gb_part;            // [B,H,2,d] caller workspace: per-scan dgamma, dbeta
   float* dq;
   float* dk;
   float* dv;

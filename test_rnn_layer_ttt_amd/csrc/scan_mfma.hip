@@ -336,6 +336,13 @@ __device__ __forceinline__ float red_step(float x) {
 __device__ __forceinline__ float lane63(float x) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
+// x minus its value in lane 0: the LayerNorm is invariant to a common shift of
+// z, and a shift by one of the token's own entries keeps the sums of the
+// shifted values within a few standard deviations of zero, so that the
+// one-pass variance E[y^2] - E[y]^2 does not cancel when |mean(z)| >> std(z)
+__device__ __forceinline__ float shift_by_lane0(float x) {
+  return x - __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
 
 // Two independent wave sums, interleaved step by step; wave-uniform results.
 __device__ __forceinline__ void wave_total2(float& a, float& b) {
@@ -349,10 +356,12 @@ __device__ __forceinline__ void wave_total2(float& a, float& b) {
   b = lane63(b);
 }
 
-// delta for one token from z (lane = feature i) and the wave sums s1 = sum z,
-// s2 = sum z^2; gz = gamma_i z, bv = beta_i - v_t[i].  With a = s1/d (the
-// mean) and b = s2/d + eps, var + eps = b - a^2; the terms that do not depend
-// on the sums (gz, b) are formed off the critical path.
+// delta for one token from y (lane = feature i) and the wave sums s1 = sum y,
+// s2 = sum y^2, where y = z - c is z shifted by one of its own entries c (the
+// LayerNorm of y equals that of z); gz = gamma_i y, bv = beta_i - v_t[i].  With
+// a = s1/d (the mean of y) and b = s2/d + eps, var + eps = b - a^2, and |a| is
+// a few standard deviations at most, so the difference does not cancel; the
+// terms that do not depend on the sums (gz, b) are formed off the critical path.
 template <int LN>
 __device__ __forceinline__ float delta_from_sums(float z, float gz, float s1, float s2, float bv,
                                                  float gam, float eps) {
@@ -377,9 +386,10 @@ __device__ __forceinline__ float token_delta(float z, float bv, float gam, float
   if constexpr (LN == kLnNone) {
     return z - bv;
   } else {
-    float s1 = z, s2 = z * z;
+    const float y = shift_by_lane0(z);
+    float s1 = y, s2 = y * y;
     wave_total2(s1, s2);
-    return delta_from_sums<LN>(z, gam * z, s1, s2, bv, gam, eps);
+    return delta_from_sums<LN>(y, gam * y, s1, s2, bv, gam, eps);
   }
 }
 
@@ -388,7 +398,10 @@ __device__ __forceinline__ float token_delta(float z, float bv, float gam, float
 // eta_s (k_s . k_{s+1}) in registers.  Token s's delta is applied to row s+1 at
 // once; its updates of rows s+2.. are spread over the reduction steps of token
 // s+1, where they fill the DPP wait states, with coefficient rows read two
-// tokens ahead of their use.
+// tokens ahead of their use.  Row s+1 is shifted by its lane-0 entry (before
+// token s's own correction, so off the dependency chain) once every earlier
+// delta but token s's has reached it; the LayerNorm of token s+1 then runs on
+// the shifted row.
 template <int LN>
 __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[BT],
                                             const float (*cc)[BT],
@@ -405,6 +418,7 @@ __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[B
   };
   load_row(0);
   load_row(1);
+  if constexpr (LN != kLnNone) zr[0] = shift_by_lane0(zr[0]);
   float dprev = 0.0f;
 #pragma unroll
   for (int s = 0; s < BT; ++s) {
@@ -437,6 +451,7 @@ __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[B
       a = red_step<3>(a); b = red_step<3>(b); fill(3);
       a = red_step<4>(a); b = red_step<4>(b); fill(4);
       a = red_step<5>(a); b = red_step<5>(b); fill(5);
+      if (s + 1 < BT) zr[s + 1] = shift_by_lane0(zr[s + 1]);
       dl = delta_from_sums<LN>(z, gz, lane63(a), lane63(b), bv[s], gam, eps);
     }
     dr[s] = dl;

@@ -10,7 +10,9 @@
 // W k and W q need only a two-step quad reduction.  The LayerNorm statistics
 // of z = W k are reduced over the rows with DPP row rotations, a cross-row
 // shuffle and, with more than one wave, one LDS exchange and barrier per token
-// (two in exact mode).  Inputs are staged through LDS in tiles of 2048
+// (two in exact mode); each wave sums its rows shifted by one of its own
+// entries and the waves' means and squared deviations combine exactly, so the
+// variance does not cancel when the mean of z is large against its spread.  Inputs are staged through LDS in tiles of 2048
 // elements per array, prefetched into registers one tile ahead, converted to
 // fp32 and passed through their sigmoids on the way in; outputs are staged in
 // LDS and written back as 16-byte stores.
@@ -202,6 +204,42 @@ scan_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   };
 
   int par = 0;
+  // Mean and biased variance of z over the d rows; every thread gets them.
+  // Each wave shifts its 16 rows by one of its own entries, sums the shifted
+  // values and their squares, and turns them into the wave's mean and its sum
+  // of squared deviations from that mean; the waves' parts then combine in the
+  // parallel form of the variance (the spread of the wave means is added
+  // explicitly).  No E[z^2] - E[z]^2 of a large mean is ever formed, so the
+  // statistic does not cancel when |mean(z)| >> std(z).
+  constexpr int kRowsPerWave = 16;
+  auto ln_stats = [&](float z) -> float2 {
+    const float c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(z)));
+    const float y = z - c;
+    const float a = quads_sum(y);
+    const float b = quads_sum(y * y);
+    const float mw = fmaf(a, 1.0f / kRowsPerWave, c);
+    const float m2w = fmaxf(fmaf(-a, a * (1.0f / kRowsPerWave), b), 0.0f);
+    if constexpr (NW == 1) {
+      return make_float2(mw, m2w * kInvD);
+    } else {
+      if (lane == 0) sRed[0][par][wave] = make_float2(mw, m2w);
+      __syncthreads();
+      float mu = 0.0f, m2 = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float2 x = sRed[0][par][w];
+        mu += x.x;
+        m2 += x.y;
+      }
+      mu *= 1.0f / NW;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float dm = sRed[0][par][w].x - mu;
+        m2 = fmaf(kRowsPerWave * dm, dm, m2);
+      }
+      return make_float2(mu, m2 * kInvD);
+    }
+  };
   // Sum of two per-row values over all d rows; every thread gets the result.
   auto rows_sum2 = [&](float a, float b, int red) -> float2 {
     a = quads_sum(a);
@@ -269,10 +307,9 @@ scan_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       if constexpr (LN == kLnNone) {
         delta = z - vi;
       } else {
-        const float2 s = rows_sum2(z, z * z, 0);
-        const float mu = s.x * kInvD;
-        const float var = fmaxf(s.y * kInvD - mu * mu, 0.0f);
-        const float rs = __builtin_amdgcn_rsqf(var + eps);
+        const float2 st = ln_stats(z);
+        const float mu = st.x;
+        const float rs = __builtin_amdgcn_rsqf(st.y + eps);
         const float xh = (z - mu) * rs;
         const float e = fmaf(gam, xh, bet) - vi;
         if constexpr (LN == kLnST) {

@@ -12,6 +12,13 @@
 namespace {
 
 constexpr float kLnEps = 1e-6f;  // cortex_rust ttt.rs, TTT_NORM_EPS
+constexpr uint32_t kKnownModes =
+    TTT_DUAL | TTT_LN_EXACT | TTT_IN_BF16 | TTT_NO_LN | TTT_SILU_QK | TTT_FORCE_VALU;
+
+// digest of the sources this library was built from (set by the build)
+#ifndef TTT_SOURCE_DIGEST
+#define TTT_SOURCE_DIGEST "unknown"
+#endif
 
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)
@@ -45,8 +52,7 @@ int32_t validate(const void* q, const void* k, const void* v, const void* eta_lo
                  const float* beta, float* out, float* W_final, int64_t B, int64_t H,
                  int64_t T, int64_t d, uint32_t mode, int64_t chunk, ttt::ScanArgs* a) {
   // ---- mode ----
-  const uint32_t known = TTT_DUAL | TTT_LN_EXACT | TTT_IN_BF16 | TTT_NO_LN | TTT_SILU_QK;
-  if (mode & ~known) return TTT_ERR_MODE;
+  if (mode & ~kKnownModes) return TTT_ERR_MODE;
   if ((mode & TTT_LN_EXACT) && (mode & TTT_NO_LN)) return TTT_ERR_MODE;
   const bool dual = (mode & TTT_DUAL) != 0;
   if (dual && chunk < 1) return TTT_ERR_MODE;
@@ -118,22 +124,24 @@ int32_t validate(const void* q, const void* k, const void* v, const void* eta_lo
   a->in_bf16 = bf16;
   a->eps = kLnEps;
   a->silu_qk = (mode & TTT_SILU_QK) != 0;
+  a->force_valu = (mode & TTT_FORCE_VALU) != 0;
   return TTT_OK;
 }
 
+// the kernel a validated forward call runs
+bool runs_mfma(const ttt::ScanArgs& a) { return !a.force_valu && ttt::scan_mfma_supports(a); }
+
 // ---- the record of a forward pass for the backward ----
-// layout, fp32: delta [B,H,T,d] | W at every tile start [B,H,ntiles,d,d] |
-// scratch [B,H,2,d]
+// layout, fp32: delta [B,H,T,d] | W at every tile start [B,H,ntiles,d,d]
 struct RecordLayout {
-  int64_t delta_off, w_off, scratch_off, bytes;
+  int64_t delta_off, w_off, bytes;
 };
 
 // Checks the mode and shapes of a recording forward or a backward and fills
 // the layout.  Makes no HIP call.
 int32_t record_layout(int64_t B, int64_t H, int64_t T, int64_t d, uint32_t mode,
                       RecordLayout* r) {
-  const uint32_t known = TTT_DUAL | TTT_LN_EXACT | TTT_IN_BF16 | TTT_NO_LN | TTT_SILU_QK;
-  if (mode & ~known) return TTT_ERR_MODE;
+  if (mode & ~kKnownModes) return TTT_ERR_MODE;
   if ((mode & TTT_LN_EXACT) && (mode & TTT_NO_LN)) return TTT_ERR_MODE;
   if (B < 1 || H < 1 || d < 1 || T < 0) return TTT_ERR_SHAPE;
   if (d != 64) return TTT_ERR_UNSUPPORTED;
@@ -142,14 +150,18 @@ int32_t record_layout(int64_t B, int64_t H, int64_t T, int64_t d, uint32_t mode,
   if (!mul_ok(B, H, &BH) || BH > INT32_MAX) return TTT_ERR_SHAPE;
   if (!mul_ok(T, d, &a) || !mul_ok(ntiles, d * d, &b) || a > INT64_MAX / 2 - b)
     return TTT_ERR_SHAPE;
-  per_scan = a + b + 2 * d;
+  per_scan = a + b;
   int64_t elems;
   if (!mul_ok(BH, per_scan, &elems) || elems > INT64_MAX / 4) return TTT_ERR_SHAPE;
   r->delta_off = 0;
   r->w_off = BH * a * 4;
-  r->scratch_off = r->w_off + BH * b * 4;
   r->bytes = elems * 4;
   return TTT_OK;
+}
+
+// bytes of the backward's scratch: per-(b,h) dgamma, dbeta before the batch sum
+int64_t backward_workspace(int64_t B, int64_t H, int64_t d, uint32_t mode) {
+  return (mode & TTT_NO_LN) ? 0 : B * H * 2 * d * 4;
 }
 
 // the record's own checks, after the forward's
@@ -175,6 +187,7 @@ int32_t validate_forward_record(const void* q, const void* k, const void* v,
   st = validate_record(record, record_bytes, B, H, T, d, mode, r);
   if (st != TTT_OK) return st;
   if (a->dual && a->chunk != ttt::kRecTile) return TTT_ERR_UNSUPPORTED;   // chunks = tiles
+  if (a->force_valu) return TTT_ERR_UNSUPPORTED;   // the record is the matrix-core kernel's
   const int64_t in_size = (mode & TTT_IN_BF16) ? 2 : 4;
   const int64_t seq = B * H * T * d, w = B * H * d * d;
   const Range rec = span(record, r->bytes);
@@ -197,14 +210,14 @@ int32_t validate_forward_record(const void* q, const void* k, const void* v,
 
 int32_t validate_backward(const void* q, const void* k, const void* v, const void* eta_logit,
                           const void* gate_logit, const float* gamma, const float* beta,
-                          void* record, int64_t record_bytes, const float* dout,
+                          const void* record, int64_t record_bytes, void* workspace,
+                          int64_t workspace_bytes, const float* dout,
                           const float* dW_final, float* dq, float* dk, float* dv,
                           float* deta_logit, float* dgate_logit, float* dW0, float* dgamma,
                           float* dbeta, int64_t B, int64_t H, int64_t T, int64_t d,
                           uint32_t mode, int64_t chunk, ttt::BwdArgs* a) {
   // mode and shapes (the forward's rules, then the backward's coverage)
-  const uint32_t known = TTT_DUAL | TTT_LN_EXACT | TTT_IN_BF16 | TTT_NO_LN | TTT_SILU_QK;
-  if (mode & ~known) return TTT_ERR_MODE;
+  if (mode & ~kKnownModes) return TTT_ERR_MODE;
   if ((mode & TTT_LN_EXACT) && (mode & TTT_NO_LN)) return TTT_ERR_MODE;
   if ((mode & TTT_DUAL) && chunk < 1) return TTT_ERR_MODE;
   RecordLayout r;
@@ -236,20 +249,23 @@ int32_t validate_backward(const void* q, const void* k, const void* v, const voi
     if (!aligned(eta_logit, static_cast<uintptr_t>(in_size)) || !aligned(deta_logit, 4))
       return TTT_ERR_UNSUPPORTED;
   }
-  if (record_bytes < r.bytes) return TTT_ERR_WORKSPACE;
-  // aliasing: outputs (and the record, written as scratch) against everything
+  const int64_t ws_bytes = backward_workspace(B, H, d, mode);
+  if (ws_bytes > 0 && workspace == nullptr) return TTT_ERR_NULL;
+  if (ws_bytes > 0 && !aligned(workspace, 16)) return TTT_ERR_UNSUPPORTED;
+  if (record_bytes < r.bytes || workspace_bytes < ws_bytes) return TTT_ERR_WORKSPACE;
+  // aliasing: outputs (and the workspace) against one another and every input
   const int64_t seq = B * H * T * d, w = B * H * d * d, hd = no_ln ? 0 : H * d * 4;
   const int64_t ts = T > 0 ? 1 : 0;
   const Range outs[] = {span(dq, ts * seq * 4),          span(dk, ts * seq * 4),
                         span(dv, ts * seq * 4),          span(dgate_logit, ts * seq * 4),
                         span(deta_logit, ts * B * H * T * 4), span(dW0, w * 4),
                         span(no_ln ? nullptr : dgamma, hd), span(no_ln ? nullptr : dbeta, hd),
-                        span(record, r.bytes)};
+                        span(ws_bytes > 0 ? workspace : nullptr, ws_bytes)};
   const Range ins[] = {span(q, ts * seq * in_size),      span(k, ts * seq * in_size),
                        span(v, ts * seq * in_size),      span(gate_logit, ts * seq * in_size),
                        span(eta_logit, ts * B * H * T * in_size), span(dout, ts * seq * 4),
                        span(no_ln ? nullptr : gamma, hd), span(no_ln ? nullptr : beta, hd),
-                       span(dW_final, dW_final ? w * 4 : 0)};
+                       span(record, r.bytes), span(dW_final, dW_final ? w * 4 : 0)};
   constexpr int kOuts = sizeof(outs) / sizeof(outs[0]);
   constexpr int kDW0 = 5;
   constexpr int kDWFinal = sizeof(ins) / sizeof(ins[0]) - 1;
@@ -262,7 +278,7 @@ int32_t validate_backward(const void* q, const void* k, const void* v, const voi
     }
   }
   *a = ttt::BwdArgs{};
-  char* base = static_cast<char*>(record);
+  const char* base = static_cast<const char*>(record);
   a->q = q;
   a->k = k;
   a->v = v;
@@ -274,7 +290,7 @@ int32_t validate_backward(const void* q, const void* k, const void* v, const voi
   a->dW_final = dW_final;
   a->rec_delta = reinterpret_cast<const float*>(base + r.delta_off);
   a->rec_W = reinterpret_cast<const float*>(base + r.w_off);
-  a->gb_part = reinterpret_cast<float*>(base + r.scratch_off);
+  a->gb_part = ws_bytes > 0 ? static_cast<float*>(workspace) : nullptr;
   a->dq = dq;
   a->dk = dk;
   a->dv = dv;
@@ -301,8 +317,7 @@ int32_t validate_project(const void* x, const void* w_proj, const float* b_proj,
                          void* k, void* v, void* eta_logit, void* gate_logit, int64_t B,
                          int64_t T, int64_t hidden, int64_t H, int64_t d, uint32_t mode,
                          ttt::ProjArgs* a) {
-  const uint32_t known = TTT_DUAL | TTT_LN_EXACT | TTT_IN_BF16 | TTT_NO_LN | TTT_SILU_QK;
-  if (mode & ~known) return TTT_ERR_MODE;
+  if (mode & ~kKnownModes) return TTT_ERR_MODE;
   if (B < 1 || H < 1 || d < 1 || hidden < 1 || T < 0) return TTT_ERR_SHAPE;
   int64_t BT, x_elems, per_head, rows, w_elems, BH, BHT, out_elems;
   if (!mul_ok(B, T, &BT) || !mul_ok(BT, hidden, &x_elems) || x_elems > INT64_MAX / 2)
@@ -392,8 +407,7 @@ extern "C" int32_t ttt_linear_forward(const void* q, const void* k, const void* 
     }
     return TTT_OK;
   }
-  const hipError_t err = ttt::scan_mfma_supports(a) ? ttt::launch_scan_mfma(a, s)
-                                                    : ttt::launch_scan_valu(a, s);
+  const hipError_t err = runs_mfma(a) ? ttt::launch_scan_mfma(a, s) : ttt::launch_scan_valu(a, s);
   return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
@@ -426,8 +440,7 @@ extern "C" int32_t ttt_linear_forward_masked(const void* q, const void* k, const
     return TTT_OK;
   }
   a.upd_mask = update_mask;
-  const hipError_t err = ttt::scan_mfma_supports(a) ? ttt::launch_scan_mfma(a, s)
-                                                    : ttt::launch_scan_valu(a, s);
+  const hipError_t err = runs_mfma(a) ? ttt::launch_scan_mfma(a, s) : ttt::launch_scan_valu(a, s);
   return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
@@ -437,6 +450,15 @@ extern "C" int32_t ttt_linear_record_bytes(int64_t B, int64_t H, int64_t T, int6
   RecordLayout r;
   const int32_t st = record_layout(B, H, T, d, mode, &r);
   if (st == TTT_OK) *bytes = r.bytes;
+  return st;
+}
+
+extern "C" int32_t ttt_linear_backward_workspace_bytes(int64_t B, int64_t H, int64_t d,
+                                                       uint32_t mode, int64_t* bytes) {
+  if (bytes == nullptr) return TTT_ERR_NULL;
+  RecordLayout r;
+  const int32_t st = record_layout(B, H, 0, d, mode, &r);
+  if (st == TTT_OK) *bytes = backward_workspace(B, H, d, mode);
   return st;
 }
 
@@ -468,8 +490,10 @@ extern "C" int32_t ttt_linear_forward_record(const void* q, const void* k, const
 
 extern "C" int32_t ttt_linear_backward(const void* q, const void* k, const void* v,
                                        const void* eta_logit, const void* gate_logit,
-                                       const float* gamma, const float* beta, void* record,
-                                       int64_t record_bytes, const float* dout,
+                                       const float* gamma, const float* beta,
+                                       const void* record, int64_t record_bytes,
+                                       void* workspace, int64_t workspace_bytes,
+                                       const float* dout,
                                        const float* dW_final, float* dq, float* dk, float* dv,
                                        float* deta_logit, float* dgate_logit, float* dW0,
                                        float* dgamma, float* dbeta, int64_t B, int64_t H,
@@ -477,9 +501,9 @@ extern "C" int32_t ttt_linear_backward(const void* q, const void* k, const void*
                                        void* stream) {
   ttt::BwdArgs a;
   const int32_t st = validate_backward(q, k, v, eta_logit, gate_logit, gamma, beta, record,
-                                       record_bytes, dout, dW_final, dq, dk, dv, deta_logit,
-                                       dgate_logit, dW0, dgamma, dbeta, B, H, T, d, mode, chunk,
-                                       &a);
+                                       record_bytes, workspace, workspace_bytes, dout, dW_final,
+                                       dq, dk, dv, deta_logit, dgate_logit, dW0, dgamma, dbeta,
+                                       B, H, T, d, mode, chunk, &a);
   if (st != TTT_OK) return st;
   const hipError_t err = ttt::launch_bwd_mfma(a, static_cast<hipStream_t>(stream));
   if (err == hipErrorNotSupported) return TTT_ERR_UNSUPPORTED;
@@ -495,7 +519,7 @@ extern "C" const char* ttt_linear_kernel(int64_t d, uint32_t mode, int64_t chunk
   if (validate(p, p, p, p, p, dummy, dummy, dummy, o, nullptr, 1, 1, 1, d, mode, chunk, &a) !=
       TTT_OK)
     return "none";
-  return ttt::scan_mfma_supports(a) ? "scan_mfma" : "scan_valu";
+  return runs_mfma(a) ? "scan_mfma" : "scan_valu";
 }
 
 extern "C" const char* ttt_status_string(int32_t status) {
@@ -507,9 +531,13 @@ extern "C" const char* ttt_status_string(int32_t status) {
     case TTT_ERR_UNSUPPORTED: return "unsupported (d must be 16, 32, 64 or 128; pointers must be aligned)";
     case TTT_ERR_ALIAS: return "out or W_final overlaps another argument";
     case TTT_ERR_HIP: return "HIP runtime error at launch";
-    case TTT_ERR_WORKSPACE: return "record buffer smaller than ttt_linear_record_bytes";
+    case TTT_ERR_WORKSPACE:
+      return "record or workspace smaller than ttt_linear_record_bytes / "
+             "ttt_linear_backward_workspace_bytes";
     default: return "unknown status";
   }
 }
 
-extern "C" const char* ttt_version(void) { return "ttt_linear 0.1.0 (gfx950)"; }
+extern "C" const char* ttt_version(void) {
+  return "ttt_linear 0.2.0 (gfx950) src=" TTT_SOURCE_DIGEST;
+}

@@ -78,9 +78,16 @@ def _f32(a64: np.ndarray) -> np.ndarray:
 def make_case(B: int, H: int, T: int, d: int, seed: int, *, ln: str = "st",
               dual: bool = False, chunk: int = 16, in_bf16: bool = False,
               l2norm_qkv: bool = False, random_affine: bool = False,
-              eta_mean: float = 0.0, w0_std: float = 0.02,
-              name: str | None = None) -> ScanInputs:
-    """Draw one problem following the recipe in the module docstring."""
+              eta_mean: float = 0.0, w0_std: float = 0.02, v_mean: float = 0.0,
+              w0_common_row: float = 0.0, name: str | None = None) -> ScanInputs:
+    """Draw one problem following the recipe in the module docstring.
+
+    Off-centre LayerNorm inputs (both off by default, and drawn after
+    everything else so that the other draws do not change): ``v_mean`` adds a
+    constant to every v (the targets, so the inner model's outputs drift to a
+    large common mean), and ``w0_common_row`` adds ``w0_common_row * r`` to
+    every row of W0, r ~ N(0,1)^d / sqrt(d) (so z = W0 k starts with a common
+    component r.k, large against its spread across the features)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     draw = lambda *shape: rng.standard_normal(shape, dtype=np.float32)
     W0 = _f32(draw(B, H, d, d).astype(np.float64) * w0_std)
@@ -100,13 +107,19 @@ def make_case(B: int, H: int, T: int, d: int, seed: int, *, ln: str = "st",
             a64 = a.astype(np.float64)
             return _f32(a64 / np.linalg.norm(a64, axis=-1, keepdims=True) * np.sqrt(d))
         q, k, v = nrm(q), nrm(k), nrm(v)
+    if v_mean != 0.0:
+        v = _f32(v.astype(np.float64) + v_mean)
+    if w0_common_row != 0.0:
+        r = draw(B, H, 1, d).astype(np.float64) / np.sqrt(d)
+        W0 = _f32(W0.astype(np.float64) + w0_common_row * r)
     if in_bf16:
         q, k, v, eta, gate = (round_to_bf16(a) for a in (q, k, v, eta, gate))
     return ScanInputs(name=name or f"B{B}_H{H}_T{T}_d{d}", q=q, k=k, v=v, eta_logit=eta,
                       gate_logit=gate, W0=W0, gamma=gamma, beta=beta, ln=ln, dual=dual,
                       chunk=chunk, in_bf16=in_bf16,
                       meta=dict(B=B, H=H, T=T, d=d, seed=seed, l2norm_qkv=l2norm_qkv,
-                                random_affine=random_affine, eta_mean=eta_mean))
+                                random_affine=random_affine, eta_mean=eta_mean, v_mean=v_mean,
+                                w0_common_row=w0_common_row))
 
 
 #: The five named workloads.  Sizes, distributions and seeds are the ones the

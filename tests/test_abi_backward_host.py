@@ -1,5 +1,6 @@
-"""Host-only checks of the training entry points of the C ABI: the record size
-query, and the argument checks of the recording forward and of the backward.
+"""Host-only checks of the training entry points of the C ABI: the record and
+workspace size queries, and the argument checks of the recording forward and
+of the backward.
 
 Every check runs before the first HIP call.  The rejected calls below are sent
 to the real entry points only where no device is visible (the fake addresses
@@ -25,7 +26,32 @@ def rec_bytes(B=B, H=H, T=T, d=D, mode=0):
 @pytest.mark.parametrize("B_,H_,T_", [(1, 1, 0), (1, 1, 1), (2, 3, 16), (2, 3, 17), (4, 32, 16384)])
 def test_record_bytes_formula(B_, H_, T_):
     ntiles = -(-T_ // 16)
-    assert rec_bytes(B_, H_, T_) == 4 * B_ * H_ * (T_ * 64 + ntiles * 64 * 64 + 2 * 64)
+    assert rec_bytes(B_, H_, T_) == 4 * B_ * H_ * (T_ * 64 + ntiles * 64 * 64)
+
+
+def ws_bytes(B=B, H=H, d=D, mode=0):
+    st, n = ttt.ttt_linear_backward_workspace_bytes(B, H, d, mode)
+    assert st == ttt.TTT_OK
+    return n
+
+
+@pytest.mark.parametrize("mode", [0, ttt.TTT_LN_EXACT, ttt.TTT_IN_BF16, ttt.TTT_DUAL,
+                                  ttt.TTT_SILU_QK])
+def test_workspace_bytes_formula(mode):
+    # per (b,h): dgamma and dbeta before their sum over the batch
+    assert ws_bytes(B, H, D, mode) == 4 * B * H * 2 * 64
+    assert ws_bytes(B, H, D, (mode & ~ttt.TTT_LN_EXACT) | ttt.TTT_NO_LN) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(d=32), ttt.TTT_ERR_UNSUPPORTED),
+    (dict(mode=1 << 10), ttt.TTT_ERR_MODE),
+    (dict(B=0), ttt.TTT_ERR_SHAPE),
+])
+def test_workspace_bytes_rejects(over, code):
+    a = dict(B=B, H=H, d=D, mode=0)
+    a.update(over)
+    assert ttt.ttt_linear_backward_workspace_bytes(a["B"], a["H"], a["d"], a["mode"])[0] == code
 
 
 @pytest.mark.parametrize("mode", [0, ttt.TTT_LN_EXACT, ttt.TTT_NO_LN, ttt.TTT_IN_BF16,
@@ -39,7 +65,7 @@ def test_record_bytes_independent_of_dtype_ln_and_form(mode):
 @pytest.mark.parametrize("over,code", [
     (dict(d=32), ttt.TTT_ERR_UNSUPPORTED),
     (dict(d=128), ttt.TTT_ERR_UNSUPPORTED),
-    (dict(mode=32), ttt.TTT_ERR_MODE),
+    (dict(mode=1 << 10), ttt.TTT_ERR_MODE),
     (dict(mode=ttt.TTT_LN_EXACT | ttt.TTT_NO_LN), ttt.TTT_ERR_MODE),
     (dict(B=0), ttt.TTT_ERR_SHAPE),
     (dict(T=-1), ttt.TTT_ERR_SHAPE),
@@ -89,6 +115,7 @@ needs_no_gpu = pytest.mark.skipif(_GPU, reason="sends unlaunchable arguments to 
     (dict(q=None), ttt.TTT_ERR_NULL),                       # the forward's own checks first
     (dict(out=A), ttt.TTT_ERR_ALIAS),
     (dict(mode=ttt.TTT_LN_EXACT | ttt.TTT_NO_LN), ttt.TTT_ERR_MODE),
+    (dict(mode=ttt.TTT_FORCE_VALU), ttt.TTT_ERR_UNSUPPORTED),   # records only on the MFMA scan
 ])
 def test_forward_record_rejects(over, code):
     assert fwd_call(**over) == code
@@ -98,7 +125,7 @@ def test_forward_record_rejects(over, code):
 # backward
 # ---------------------------------------------------------------------------
 BWD_FIELDS = ("q", "k", "v", "eta_logit", "gate_logit", "gamma", "beta", "record",
-              "record_bytes", "dout", "dW_final", "dq", "dk", "dv", "deta_logit", "dgate_logit",
+              "record_bytes", "workspace", "workspace_bytes", "dout", "dW_final", "dq", "dk", "dv", "deta_logit", "dgate_logit",
               "dW0", "dgamma", "dbeta", "B", "H", "T", "d", "mode", "chunk", "stream")
 
 
@@ -106,7 +133,8 @@ def bwd_args(**over):
     names = ("q", "k", "v", "eta_logit", "gate_logit", "gamma", "beta", "record", None, "dout",
              "dW_final", "dq", "dk", "dv", "deta_logit", "dgate_logit", "dW0", "dgamma", "dbeta")
     base = {n: A + i * S for i, n in enumerate(names) if n is not None}
-    base.update(record_bytes=rec_bytes(), B=B, H=H, T=T, d=D, mode=0, chunk=16, stream=None)
+    base.update(record_bytes=rec_bytes(), workspace=A + 19 * S, workspace_bytes=ws_bytes(),
+                B=B, H=H, T=T, d=D, mode=0, chunk=16, stream=None)
     base.update(over)
     return base
 
@@ -126,7 +154,7 @@ def test_backward_null(field):
 
 @needs_no_gpu
 @pytest.mark.parametrize("field", ["q", "dout", "dq", "dk", "dv", "dgate_logit", "dW0",
-                                   "dW_final", "record"])
+                                   "dW_final", "record", "workspace"])
 def test_backward_misaligned(field):
     assert bwd_call(**{field: bwd_args()[field] + 4}) == ttt.TTT_ERR_UNSUPPORTED
 
@@ -149,8 +177,13 @@ def test_backward_eta_alignment_follows_dtype():
     dict(dW0=A + 10 * S + 64),     # dW0 partially over dW_final
     dict(dgamma=A + 5 * S),        # dgamma == gamma
     dict(dbeta=A + 17 * S),        # dbeta == dgamma
-    dict(record=A + 9 * S),        # record == dout
-    dict(deta_logit=A + 7 * S + 1024),   # deta inside the record
+    dict(record=A + 17 * S),       # record == dgamma
+    dict(deta_logit=A + 7 * S + 1024),   # deta inside the record (an input)
+    dict(record=A + 11 * S),       # record == dq
+    dict(workspace=A + 7 * S),     # workspace == record
+    dict(workspace=A + 11 * S + 512),    # workspace inside dq
+    dict(workspace=A + 18 * S),    # workspace == dbeta
+    dict(workspace=A + 5 * S),     # workspace == gamma
 ])
 def test_backward_alias_rejected(over):
     assert bwd_call(**over) == ttt.TTT_ERR_ALIAS
@@ -163,7 +196,10 @@ def test_backward_alias_rejected(over):
     (dict(mode=ttt.TTT_DUAL, chunk=0), ttt.TTT_ERR_MODE),
     (dict(d=16), ttt.TTT_ERR_UNSUPPORTED),
     (dict(record_bytes=rec_bytes() - 4), ttt.TTT_ERR_WORKSPACE),
-    (dict(mode=32), ttt.TTT_ERR_MODE),
+    (dict(workspace_bytes=ws_bytes() - 4), ttt.TTT_ERR_WORKSPACE),
+    (dict(workspace_bytes=0), ttt.TTT_ERR_WORKSPACE),
+    (dict(workspace=None), ttt.TTT_ERR_NULL),
+    (dict(mode=1 << 10), ttt.TTT_ERR_MODE),
     (dict(H=0), ttt.TTT_ERR_SHAPE),
 ])
 def test_backward_rejects(over, code):
@@ -176,6 +212,10 @@ def test_backward_without_ln_ignores_affine_pointers():
     st = bwd_call(gamma=None, beta=None, dgamma=None, dbeta=None, mode=ttt.TTT_NO_LN,
                   record_bytes=1)
     assert st == ttt.TTT_ERR_WORKSPACE
+    # ... and the workspace is not needed at all
+    st = bwd_call(gamma=None, beta=None, dgamma=None, dbeta=None, mode=ttt.TTT_NO_LN,
+                  workspace=None, workspace_bytes=0, record_bytes=1)
+    assert st == ttt.TTT_ERR_WORKSPACE
 
 
 @needs_no_gpu
@@ -187,4 +227,5 @@ def test_backward_empty_sequence_allows_null_token_pointers():
 
 
 def test_status_string_of_workspace_error():
-    assert "record" in ttt.ttt_status_string(ttt.TTT_ERR_WORKSPACE)
+    s = ttt.ttt_status_string(ttt.TTT_ERR_WORKSPACE)
+    assert "record" in s and "workspace" in s

@@ -49,6 +49,9 @@ def test_binding_constants_match_header():
 
 def test_version_and_status_strings():
     assert "ttt_linear" in ttt.ttt_version()
+    # the library carries the digest of the sources it was built from
+    from test_rnn_layer_ttt_amd.build import source_digest
+    assert ttt.ttt_version().endswith("src=" + source_digest())
     for code in range(8):
         assert ttt.ttt_status_string(code)
     assert ttt.ttt_status_string(99) == "unknown status"
@@ -108,7 +111,7 @@ def test_bad_shape(over):
     assert call(**over) == ttt.TTT_ERR_SHAPE
 
 
-@pytest.mark.parametrize("mode", [32, 64, 0x80000000, ttt.TTT_LN_EXACT | ttt.TTT_NO_LN])
+@pytest.mark.parametrize("mode", [128, 1 << 10, 0x80000000, ttt.TTT_LN_EXACT | ttt.TTT_NO_LN])
 def test_bad_mode(mode):
     assert call(mode=mode) == ttt.TTT_ERR_MODE
 
@@ -168,9 +171,34 @@ def test_empty_sequence_allows_null_sequence_pointers():
 
 
 @pytest.mark.parametrize("d", [16, 32, 64, 128])
-@pytest.mark.parametrize("mode", [0, 1, 2, 4, 8, 5, 7, 13, 16, 23, 29])
+@pytest.mark.parametrize("mode", [0, 1, 2, 4, 8, 5, 7, 13, 16, 23, 29, 32, 37, 55, 61])
 def test_supported_combinations_validate(d, mode):
     assert call(d=d, mode=mode) == ttt.TTT_OK
+
+
+def test_kernel_choice():
+    # d = 64 runs on the matrix cores (per-token, and the dual form with chunks of 16) ...
+    assert ttt.ttt_linear_kernel(64, 0, 1) == "scan_mfma"
+    assert ttt.ttt_linear_kernel(64, ttt.TTT_DUAL | ttt.TTT_IN_BF16, 16) == "scan_mfma"
+    assert ttt.ttt_linear_kernel(64, ttt.TTT_DUAL, 8) == "scan_valu"
+    # ... unless the vector-ALU kernel is asked for
+    assert ttt.ttt_linear_kernel(64, ttt.TTT_FORCE_VALU, 1) == "scan_valu"
+    assert ttt.ttt_linear_kernel(64, ttt.TTT_FORCE_VALU | ttt.TTT_DUAL, 16) == "scan_valu"
+    for d in (16, 32, 128):
+        assert ttt.ttt_linear_kernel(d, 0, 1) == "scan_valu"
+    assert ttt.ttt_linear_kernel(48, 0, 1) == "none"
+
+
+def test_stale_library_is_refused(tmp_path, monkeypatch):
+    # a library whose digest does not match the sources must not load
+    from test_rnn_layer_ttt_amd import build as build_mod
+    monkeypatch.setattr(build_mod, "source_digest", lambda kernel=None: "0" * 16)
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="stale"):
+        binding.load_library()
+    monkeypatch.undo()
+    binding._lib = None
+    assert binding.load_library() is not None
 
 
 def test_error_codes_raise_from_check():
@@ -185,5 +213,6 @@ def test_mode_bits():
     assert ttt.mode_bits() == 0
     assert ttt.mode_bits("exact", True, True) == ttt.TTT_LN_EXACT | ttt.TTT_DUAL | ttt.TTT_IN_BF16
     assert ttt.mode_bits("none") == ttt.TTT_NO_LN
+    assert ttt.mode_bits(force_valu=True) == ttt.TTT_FORCE_VALU
     with pytest.raises(ValueError):
         ttt.mode_bits("bogus")

@@ -33,7 +33,7 @@ needs_no_gpu = pytest.mark.skipif(_GPU, reason="sends unlaunchable arguments to 
 
 @needs_no_gpu
 @pytest.mark.parametrize("over,code", [
-    (dict(mode=32), ttt.TTT_ERR_MODE),
+    (dict(mode=1 << 10), ttt.TTT_ERR_MODE),
     (dict(B=0), ttt.TTT_ERR_SHAPE),
     (dict(H=0), ttt.TTT_ERR_SHAPE),
     (dict(hidden=0), ttt.TTT_ERR_SHAPE),

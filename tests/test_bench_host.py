@@ -40,15 +40,46 @@ def test_mask_counts_skipped_chunks_as_cheaper():
     assert by_none < by_all and fl_none < fl_all
 
 
-def test_roofline_fraction_is_achieved_over_peak():
-    x = make_case(1, 2, 48, 64, seed=3, in_bf16=True)
-    _, nbytes, _ = bench.algorithmic_work(x)
-    name, roof = bench.roofline(x, kernel_ms=1e-6, traffic=None)   # ~1e5 GB/s: rounding is small
+def test_roofline_fraction_is_achieved_over_the_binding_peak():
+    # fp32 inputs: 1284 B and 6 d^2 flops per token-head; the HBM time is the larger
+    x = make_case(1, 2, 48, 64, seed=3)
+    _, nbytes, flops = bench.algorithmic_work(x)
+    assert nbytes / 8e12 > flops / 157.3e12
+    name, roof = bench.roofline(x, kernel_ms=1e-6, traffic=None, kernel="scan_mfma")
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s"
     assert roof["achieved"] == pytest.approx(nbytes / 1e-9 / 1e9, rel=1e-3)
     assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"], rel=1e-3)
+    assert roof["frac_hbm"] == roof["frac"]
+    assert roof["frac_compute"] == pytest.approx(flops / 1e-9 / 157.3e12, rel=1e-3)
+    # bf16 inputs halve the input bytes: the fp32 arithmetic is then the binding roof
+    xb = make_case(1, 2, 2048, 64, seed=3, in_bf16=True)   # long enough that W0 is minor
+    _, nb, fb = bench.algorithmic_work(xb)
+    _, rb = bench.roofline(xb, kernel_ms=1e-3, traffic=None, kernel="scan_mfma",
+                           hbm_measured_gbs=5000.0)
+    assert rb["bound"] == "alu" and rb["unit"] == "TFLOP/s" and rb["peak"] == 157.3
+    assert rb["frac"] == rb["frac_compute"]
+    assert rb["frac_hbm"] == pytest.approx(nb / 1e-6 / 8e12, rel=1e-3)
+    assert rb["frac_hbm_measured"] == pytest.approx(nb / 1e-6 / 5e12, rel=1e-3)
+    assert rb["t_compute_us"] > rb["t_hbm_us"]
+    # the dual form's contractions are priced on the bf16 matrix cores: HBM binds
+    xd = make_case(1, 2, 2048, 64, seed=3, in_bf16=True, dual=True, chunk=16)
+    _, rd = bench.roofline(xd, kernel_ms=1e-3, traffic=None, kernel="scan_mfma")
+    assert rd["bound"] == "hbm" and rd["compute_peak_tflops"] == 2500.0
     _, rt = bench.roofline(x, kernel_ms=2.0, traffic=123, train=True)
     assert rt["traffic"] == 123 and rt["bound"] == "hbm"
+
+
+def test_headline_workload_ceilings():
+    # the 256-scan per-token workload: 815,800,320 algorithmic bytes (102.0 us at
+    # 8 TB/s) and 25.77 GFLOP (163.8 us at 157.3 TFLOP/s), so fp32 arithmetic binds
+    from test_rnn_layer_ttt_amd.inputs import WORKLOADS
+    cfg = WORKLOADS["h1024_T4096_bf16"]
+    x = make_case(cfg["B"], cfg["H"], 16, cfg["d"], seed=0, in_bf16=True)
+    B, H, d, T = cfg["B"], cfg["H"], cfg["d"], cfg["T"]
+    nbytes = B * H * T * ((4 * d + 1) * 2 + 4 * d) + B * H * 8 * d * d + H * 8 * d
+    assert nbytes == 815_800_320
+    assert 6 * d * d * B * H * T / 157.3e12 * 1e6 == pytest.approx(163.8, abs=0.1)
+    del x
 
 
 def test_traffic_is_reported_only_for_the_measured_source(tmp_path, monkeypatch):
@@ -87,7 +118,14 @@ def test_projection_work_and_its_matrix_roofline():
     # 32 more tokens of 2 batches: their x rows in and their results out (bf16)
     assert by_b - by_a == 2 * 32 * (hidden * 2 + rows * 2)
     assert by_c - by_a == 2 * 32 * rows * 2          # fp32 results are twice as wide
+    # hidden 256 is below the bf16 ridge: the weights' and results' bytes bind
     name, roof = bench.roofline(a, kernel_ms=1e-3, traffic=None, project=True)
-    assert name == "proj_mfma" and roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s"
+    assert name == "proj_mfma" and roof["bound"] == "hbm"
+    assert roof["frac_compute"] == pytest.approx(fl_a / 1e-6 / 1e12 / 2500.0, abs=1e-4)
+    # hidden 1024 over 4096 tokens: the matrix cores bind
+    big = make_case(2, 16, 2048, 64, seed=4, in_bf16=True)
+    _, _, fl_big = bench.projection_work(big)
+    name, roof = bench.roofline(big, kernel_ms=1e-3, traffic=None, project=True)
+    assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s"
     assert roof["peak"] == bench.BF16_MATRIX_PEAK_TFLOPS
-    assert roof["achieved"] == pytest.approx(fl_a / 1e-6 / 1e12, rel=1e-3)
+    assert roof["achieved"] == pytest.approx(fl_big / 1e-6 / 1e12, rel=1e-3)

@@ -408,3 +408,42 @@ def test_empty_sequence_returns_initial_state():
     out, W = run(x)
     assert out.shape == (2, 3, 0, 5)
     assert np.array_equal(W, x.W0)
+
+
+@pytest.mark.parametrize("ln", ["st", "exact"])
+def test_ln_stats_diagnostic(ln):
+    # with eta = 0 the weight never moves, so z_t = W0 k_t: its feature mean and
+    # biased standard deviation are written out here in plain loops
+    x = small(19, T=6, d=7)
+    x.eta_logit[:] = -np.inf
+    out, W, st = run(x, ln=ln, return_ln_stats=True)
+    o2, W2 = run(x, ln=ln)
+    assert np.array_equal(out, o2) and np.array_equal(W, W2)
+    B, H, T, d = x.q.shape
+    for b in range(B):
+        for h in range(H):
+            for t in range(T):
+                z = [sum(float(x.W0[b, h, i, j]) * float(x.k[b, h, t, j]) for j in range(d))
+                     for i in range(d)]
+                m = sum(z) / d
+                sd = (sum((zi - m) ** 2 for zi in z) / d) ** 0.5
+                assert st["mean"][b, h, t] == pytest.approx(m, rel=1e-12, abs=1e-15)
+                assert st["std"][b, h, t] == pytest.approx(sd, rel=1e-12)
+                if ln == "st":
+                    # delta_t = gamma (z - m) / sqrt(sd^2 + eps) + beta - v_t
+                    want = [float(x.gamma[h, i]) * (z[i] - m) / (sd * sd + 1e-6) ** 0.5
+                            + float(x.beta[h, i]) - float(x.v[b, h, t, i]) for i in range(d)]
+                    assert np.allclose(st["delta"][b, h, t], want, rtol=1e-12, atol=1e-14)
+
+
+def test_off_centre_inputs_move_the_ln_mean():
+    # the generator's off-centre options do what they say: a common row of W0
+    # gives z a feature mean far above its spread at t = 0
+    x = make_case(1, 2, 3, 64, seed=20, w0_common_row=30.0)
+    _, _, st = run(x, return_ln_stats=True)
+    assert np.all(np.abs(st["mean"][..., 0]) / st["std"][..., 0] > 1.0)
+    assert np.max(np.abs(st["mean"][..., 0]) / st["std"][..., 0]) > 20.0
+    y = make_case(1, 2, 3, 64, seed=20, v_mean=3.0)
+    z = make_case(1, 2, 3, 64, seed=20)
+    assert np.allclose(y.v, z.v + 3.0, atol=1e-6)
+    assert np.array_equal(y.q, z.q) and np.array_equal(y.W0, z.W0)

@@ -178,15 +178,46 @@ def test_backward_repeatable_and_in_place_state_gradient():
     dW = cot(dWf).clone()
     out = {k: torch.empty_like(v) for k, v in g1.items()}
     p = lambda a: a.data_ptr()
+    st, nws = ttt.ttt_linear_backward_workspace_bytes(B, H, d, ttt.mode_bits("exact"))
+    assert st == ttt.TTT_OK and nws == B * H * 2 * d * 4
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
     st = ttt.ttt_linear_backward(
         p(t["q"]), p(t["k"]), p(t["v"]), p(t["eta_logit"]), p(t["gate_logit"]), p(t["gamma"]),
-        p(t["beta"]), p(rec), rec.numel(), p(cot(dout)), p(dW), p(out["dq"]), p(out["dk"]),
+        p(t["beta"]), p(rec), rec.numel(), p(ws), nws, p(cot(dout)), p(dW), p(out["dq"]),
+        p(out["dk"]),
         p(out["dv"]), p(out["deta_logit"]), p(out["dgate_logit"]), p(dW), p(out["dgamma"]),
         p(out["dbeta"]), B, H, T, d, ttt.mode_bits("exact"), 1,
         torch.cuda.current_stream().cuda_stream)
     assert st == ttt.TTT_OK
     torch.cuda.synchronize()
     assert torch.equal(dW, g1["dW0"])
+
+
+def test_concurrent_backward_calls_share_one_record():
+    # the record is read-only: two backward calls on one record, on two streams
+    # at once (each with its own workspace), give the bits of a lone call
+    say("case concurrent backward on one record")
+    x = make_case(4, 4, 300, 64, seed=372, ln="st", random_affine=True)
+    dout, dWf = make_cotangents(4, 4, 300, 64, seed=373)
+    t = dev(x)
+    _, _, rec = ttt.forward_record(t["q"], t["k"], t["v"], t["eta_logit"], t["gate_logit"],
+                                   t["W0"], t["gamma"], t["beta"], ln="st")
+    args = (t["q"], t["k"], t["v"], t["eta_logit"], t["gate_logit"], t["gamma"], t["beta"], rec)
+    ref = ttt.backward(*args, cot(dout), cot(dWf), ln="st")
+    torch.cuda.synchronize()
+    before = rec.clone()
+    d_o, d_w = cot(dout), cot(dWf)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s1):
+        g1 = ttt.backward(*args, d_o, d_w, ln="st", stream=s1)
+    with torch.cuda.stream(s2):
+        g2 = ttt.backward(*args, d_o, d_w, ln="st", stream=s2)
+    torch.cuda.synchronize()
+    assert torch.equal(rec, before)
+    for key in GRADS:
+        assert torch.equal(g1[key], ref[key]) and torch.equal(g2[key], ref[key]), key
 
 
 def test_autograd_function_matches_backward():

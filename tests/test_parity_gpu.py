@@ -82,6 +82,24 @@ def test_small_parity(d, ln, bf16, dual, chunk, T):
     assert_close(W, rW, TOL[bf16], "W_final")
 
 
+VALU64 = [(ln, bf16, dual, chunk) for ln in ("st", "exact", "none") for bf16 in (False, True)
+          for dual, chunk in ((False, 1), (True, 16), (True, 5))]
+
+
+@pytest.mark.parametrize("ln,bf16,dual,chunk", VALU64)
+def test_small_parity_vector_alu_d64(ln, bf16, dual, chunk):
+    # the vector-ALU kernel at d = 64, where a plain call runs the matrix-core one
+    say(f"case vector-ALU d=64 ln={ln} bf16={bf16} dual={dual} chunk={chunk}")
+    assert ttt.ttt_linear_kernel(64, ttt.mode_bits(ln, dual, bf16, force_valu=True),
+                                 chunk) == "scan_valu"
+    x = make_case(2, 3, 77, 64, seed=150, ln=ln, dual=dual, chunk=chunk, in_bf16=bf16,
+                  random_affine=True)
+    out, W = gpu_run(x, force_valu=True)
+    ro, rW = ref_run(x)
+    assert_close(out, ro, TOL[bf16], "out")
+    assert_close(W, rW, TOL[bf16], "W_final")
+
+
 @pytest.mark.parametrize("T", [1, 2, 31, 32, 33, 64, 65])
 @pytest.mark.parametrize("ln,dual", [("st", False), ("exact", False), ("st", True)])
 def test_short_and_ragged_sequences(T, ln, dual):
@@ -297,6 +315,20 @@ def test_named_workload(name):
         pairs = [(0, 0), (B - 1, H - 1), (B // 2, (H * 3) // 5)]
     s = x.subset(pairs)
     ro, rW = ref_run(s)
+    for n, (b, h) in enumerate(pairs):
+        assert_close(out[b, h], ro[0, n], TOL[x.in_bf16], f"out[{b},{h}]")
+        assert_close(W[b, h], rW[0, n], TOL[x.in_bf16], f"W_final[{b},{h}]")
+
+
+@pytest.mark.parametrize("name", ["h256_T2048_fp32", "h1024_T4096_bf16"])
+def test_named_workload_vector_alu(name):
+    # the per-token workloads on the vector-ALU kernel, as the benchmark times it beside
+    say(f"case workload {name} on the vector-ALU kernel")
+    x = make_inputs(name)
+    B, H, T, d = x.q.shape
+    out, W = gpu_run(x, force_valu=True)
+    pairs = [(0, 0), (B - 1, H - 1)]
+    ro, rW = ref_run(x.subset(pairs))
     for n, (b, h) in enumerate(pairs):
         assert_close(out[b, h], ro[0, n], TOL[x.in_bf16], f"out[{b},{h}]")
         assert_close(W[b, h], rW[0, n], TOL[x.in_bf16], f"W_final[{b},{h}]")
