@@ -181,7 +181,8 @@ int32_t ttt_linear_record_bytes(int64_t B, int64_t H, int64_t T, int64_t d, uint
  * ttt_linear_forward (same arguments, same results: out and W_final are
  * identical to its) that also fills `record` for ttt_linear_backward.
  * `record` is written, so it must not overlap any other argument.  T == 0
- * writes no record and copies W0 to W_final as the forward does.
+ * writes no record (its size is then 0 and it may be NULL) and copies W0 to
+ * W_final as the forward does.
  */
 int32_t ttt_linear_forward_record(const void* q, const void* k, const void* v,
                                   const void* eta_logit, const void* gate_logit,

@@ -66,6 +66,13 @@ def load_library(path: str = LIB_PATH, check_digest: bool = True) -> ctypes.CDLL
         raise RuntimeError(
             f"HIP library {path} is missing: build it first "
             "(python -c 'import __graft_entry__ as g; g.build()')")
+    # The library must share the HIP runtime of the framework that owns the
+    # device memory: PyTorch ships its own libamdhip64, so it is loaded first
+    # and the library's dependency then resolves to that copy.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     lib.ttt_version.restype = ctypes.c_char_p
     lib.ttt_version.argtypes = []

@@ -169,7 +169,8 @@ int32_t validate_record(const void* record, int64_t record_bytes, int64_t B, int
                         int64_t T, int64_t d, uint32_t mode, RecordLayout* r) {
   const int32_t st = record_layout(B, H, T, d, mode, r);
   if (st != TTT_OK) return st;
-  if (record == nullptr) return TTT_ERR_NULL;
+  // an empty sequence has an empty record, which may be NULL
+  if (T > 0 && record == nullptr) return TTT_ERR_NULL;
   if (!aligned(record, 16)) return TTT_ERR_UNSUPPORTED;
   if (record_bytes < r->bytes) return TTT_ERR_WORKSPACE;
   return TTT_OK;
@@ -228,7 +229,7 @@ int32_t validate_backward(const void* q, const void* k, const void* v, const voi
   const bool no_ln = (mode & TTT_NO_LN) != 0;
   const bool bf16 = (mode & TTT_IN_BF16) != 0;
   // pointers
-  if (record == nullptr || dW0 == nullptr) return TTT_ERR_NULL;
+  if ((T > 0 && record == nullptr) || dW0 == nullptr) return TTT_ERR_NULL;
   if (!no_ln && (gamma == nullptr || beta == nullptr || dgamma == nullptr || dbeta == nullptr))
     return TTT_ERR_NULL;
   if (T > 0 && (q == nullptr || k == nullptr || v == nullptr || eta_logit == nullptr ||

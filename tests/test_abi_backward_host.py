@@ -224,6 +224,14 @@ def test_backward_empty_sequence_allows_null_token_pointers():
                   dk=None, dv=None, deta_logit=None, dgate_logit=None, T=0,
                   record_bytes=rec_bytes(T=0) - 1)
     assert st == ttt.TTT_ERR_WORKSPACE
+    # the record of an empty sequence is empty and may be NULL (the check that
+    # trips is then the workspace size, after the pointer checks)
+    assert rec_bytes(T=0) == 0
+    st = bwd_call(q=None, k=None, v=None, eta_logit=None, gate_logit=None, dout=None, dq=None,
+                  dk=None, dv=None, deta_logit=None, dgate_logit=None, T=0, record=None,
+                  record_bytes=0, workspace_bytes=0)
+    assert st == ttt.TTT_ERR_WORKSPACE
+    assert bwd_call(T=1, record=None) == ttt.TTT_ERR_NULL
 
 
 def test_status_string_of_workspace_error():
