@@ -234,6 +234,32 @@ int32_t ttt_linear_backward_workspace_bytes(int64_t B, int64_t H, int64_t d, uin
                                             int64_t* bytes);
 
 /*
+ * ttt_linear_backward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and results, without the workspace.  The
+ * scratch is instead a static device array inside the library, of
+ * TTT_STATIC_SCRATCH_BYTES, that each GPU holds for the life of the process;
+ * its device address is looked up once per device, on the first call made with
+ * that device current.  Sizes whose workspace
+ * (ttt_linear_backward_workspace_bytes) exceeds it return TTT_ERR_WORKSPACE
+ * before any HIP call: at d = 64, B*H <= 4096.  The call allocates nothing.
+ * Every call on one GPU shares that GPU's array, so calls that overlap in time
+ * on one GPU (two streams, two threads) race and must be serialised by the
+ * caller; sequential calls are safe (nothing in the array needs clearing
+ * between calls).  Call it with the device of `stream` current.
+ */
+#define TTT_STATIC_SCRATCH_BYTES 2097152   /* 2 MiB */
+int32_t ttt_linear_backward_noalloc(const void* q, const void* k, const void* v,
+                                    const void* eta_logit, const void* gate_logit,
+                                    const float* gamma, const float* beta,
+                                    const void* record, int64_t record_bytes,
+                                    const float* dout, const float* dW_final,
+                                    float* dq, float* dk, float* dv, float* deta_logit,
+                                    float* dgate_logit, float* dW0, float* dgamma, float* dbeta,
+                                    int64_t B, int64_t H, int64_t T, int64_t d,
+                                    uint32_t mode, int64_t chunk, void* stream);
+
+/*
  * ---- The layer's input projections ----
  *
  * q_t = W_q x_t, k_t = W_k x_t, v_t = W_v x_t, and the learning-rate and gate

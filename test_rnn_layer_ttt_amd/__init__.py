@@ -11,7 +11,8 @@ from .binding import (TTT_DUAL, TTT_ERR_ALIAS, TTT_ERR_HIP, TTT_ERR_MODE, TTT_ER
                       TTT_FORCE_VALU, TTT_LN_EXACT, TTT_NO_LN, TTT_OK, TTT_SILU_QK, TTTArgumentError,
                       TTTError, backward,
                       check, forward, forward_record, load_library, mode_bits, project,
-                      ttt_linear, ttt_linear_backward, ttt_linear_backward_workspace_bytes,
+                      TTT_STATIC_SCRATCH_BYTES, ttt_linear, ttt_linear_backward,
+                      ttt_linear_backward_noalloc, ttt_linear_backward_workspace_bytes,
                       ttt_linear_forward,
                       ttt_linear_forward_masked, ttt_linear_forward_record, ttt_linear_project,
                       ttt_linear_kernel, ttt_linear_record_bytes, ttt_linear_validate,
@@ -22,7 +23,8 @@ __all__ = ["TTT_DUAL", "TTT_ERR_ALIAS", "TTT_ERR_HIP", "TTT_ERR_MODE", "TTT_ERR_
            "TTT_FORCE_VALU", "TTT_LN_EXACT", "TTT_NO_LN", "TTT_OK", "TTT_SILU_QK", "TTTArgumentError", "TTTError", "backward",
            "check", "forward", "forward_record", "load_library", "mode_bits", "project",
            "ttt_linear", "ttt_linear_project",
-           "ttt_linear_backward", "ttt_linear_backward_workspace_bytes", "ttt_linear_forward", "ttt_linear_forward_masked",
+           "TTT_STATIC_SCRATCH_BYTES", "ttt_linear_backward", "ttt_linear_backward_noalloc",
+           "ttt_linear_backward_workspace_bytes", "ttt_linear_forward", "ttt_linear_forward_masked",
            "ttt_linear_forward_record",
            "ttt_linear_kernel", "ttt_linear_record_bytes", "ttt_linear_validate",
            "ttt_status_string", "ttt_version"]

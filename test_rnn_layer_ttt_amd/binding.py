@@ -23,6 +23,9 @@ TTT_NO_LN = 8
 TTT_SILU_QK = 16
 TTT_FORCE_VALU = 32
 
+#: bytes of the static device scratch behind ttt_linear_backward_noalloc
+TTT_STATIC_SCRATCH_BYTES = 2097152
+
 TTT_OK = 0
 TTT_ERR_NULL = 1
 TTT_ERR_SHAPE = 2
@@ -36,7 +39,8 @@ TTT_ERR_WORKSPACE = 7
 RECORD_CHUNK = 16
 
 #: every symbol the header declares
-EXPORTED = ("ttt_linear_backward", "ttt_linear_backward_workspace_bytes",
+EXPORTED = ("ttt_linear_backward", "ttt_linear_backward_noalloc",
+            "ttt_linear_backward_workspace_bytes",
             "ttt_linear_forward", "ttt_linear_forward_masked",
             "ttt_linear_forward_record", "ttt_linear_project",
             "ttt_linear_kernel", "ttt_linear_record_bytes", "ttt_linear_validate",
@@ -108,6 +112,10 @@ def load_library(path: str = LIB_PATH, check_digest: bool = True) -> ctypes.CDLL
                                         [ctypes.c_void_p] + [ctypes.c_int64] +
                                         [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 4 +
                                         [ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p])
+    lib.ttt_linear_backward_noalloc.restype = ctypes.c_int32
+    lib.ttt_linear_backward_noalloc.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.c_int64] +
+                                                [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 4 +
+                                                [ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p])
     lib.ttt_linear_backward_workspace_bytes.restype = ctypes.c_int32
     lib.ttt_linear_backward_workspace_bytes.argtypes = [ctypes.c_int64] * 3 + [
         ctypes.c_uint32, ctypes.POINTER(ctypes.c_int64)]
@@ -203,6 +211,21 @@ def ttt_linear_backward(q, k, v, eta_logit, gate_logit, gamma, beta, record, rec
         p(q), p(k), p(v), p(eta_logit), p(gate_logit), p(gamma), p(beta), p(record),
         int(record_bytes), p(workspace), int(workspace_bytes), p(dout), p(dW_final), p(dq),
         p(dk), p(dv), p(deta_logit),
+        p(dgate_logit), p(dW0), p(dgamma), p(dbeta), int(B), int(H), int(T), int(d),
+        ctypes.c_uint32(int(mode)), int(chunk), p(stream)))
+
+
+def ttt_linear_backward_noalloc(q, k, v, eta_logit, gate_logit, gamma, beta, record,
+                                record_bytes, dout, dW_final, dq, dk, dv, deta_logit,
+                                dgate_logit, dW0, dgamma, dbeta, B, H, T, d, mode, chunk,
+                                stream) -> int:
+    """The backward with its scratch in the library's static device array
+    (no workspace argument; raw pointers); returns the status code."""
+    lib = load_library()
+    p = lambda x: None if x is None else ctypes.c_void_p(int(x))
+    return int(lib.ttt_linear_backward_noalloc(
+        p(q), p(k), p(v), p(eta_logit), p(gate_logit), p(gamma), p(beta), p(record),
+        int(record_bytes), p(dout), p(dW_final), p(dq), p(dk), p(dv), p(deta_logit),
         p(dgate_logit), p(dW0), p(dgamma), p(dbeta), int(B), int(H), int(T), int(d),
         ctypes.c_uint32(int(mode)), int(chunk), p(stream)))
 

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "scan_common.h"
 
@@ -216,7 +217,10 @@ int32_t validate_backward(const void* q, const void* k, const void* v, const voi
                           const float* dW_final, float* dq, float* dk, float* dv,
                           float* deta_logit, float* dgate_logit, float* dW0, float* dgamma,
                           float* dbeta, int64_t B, int64_t H, int64_t T, int64_t d,
-                          uint32_t mode, int64_t chunk, ttt::BwdArgs* a) {
+                          uint32_t mode, int64_t chunk, ttt::BwdArgs* a,
+                          bool internal_ws = false) {
+  // internal_ws: the scratch is the library's static device array (its size
+  // is workspace_bytes; the pointer is filled in later and overlaps nothing)
   // mode and shapes (the forward's rules, then the backward's coverage)
   if (mode & ~kKnownModes) return TTT_ERR_MODE;
   if ((mode & TTT_LN_EXACT) && (mode & TTT_NO_LN)) return TTT_ERR_MODE;
@@ -251,7 +255,8 @@ int32_t validate_backward(const void* q, const void* k, const void* v, const voi
       return TTT_ERR_UNSUPPORTED;
   }
   const int64_t ws_bytes = backward_workspace(B, H, d, mode);
-  if (ws_bytes > 0 && workspace == nullptr) return TTT_ERR_NULL;
+  if (internal_ws) workspace = nullptr;
+  if (!internal_ws && ws_bytes > 0 && workspace == nullptr) return TTT_ERR_NULL;
   if (ws_bytes > 0 && !aligned(workspace, 16)) return TTT_ERR_UNSUPPORTED;
   if (record_bytes < r.bytes || workspace_bytes < ws_bytes) return TTT_ERR_WORKSPACE;
   // aliasing: outputs (and the workspace) against one another and every input
@@ -452,6 +457,58 @@ extern "C" int32_t ttt_linear_record_bytes(int64_t B, int64_t H, int64_t T, int6
   const int32_t st = record_layout(B, H, T, d, mode, &r);
   if (st == TTT_OK) *bytes = r.bytes;
   return st;
+}
+
+// ---- the backward without a caller workspace ----
+// Its scratch (the per-(b,h) dgamma, dbeta before their sum over the batch)
+// is this static device array; every GPU the library runs on holds its own
+// copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr int64_t kStaticScratchBytes = TTT_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kStaticScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The device address of the current device's scratch array.
+hipError_t static_scratch(void** ptr) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  *ptr = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
+
+extern "C" int32_t ttt_linear_backward_noalloc(
+    const void* q, const void* k, const void* v, const void* eta_logit, const void* gate_logit,
+    const float* gamma, const float* beta, const void* record, int64_t record_bytes,
+    const float* dout, const float* dW_final, float* dq, float* dk, float* dv,
+    float* deta_logit, float* dgate_logit, float* dW0, float* dgamma, float* dbeta, int64_t B,
+    int64_t H, int64_t T, int64_t d, uint32_t mode, int64_t chunk, void* stream) {
+  ttt::BwdArgs a;
+  const int32_t st = validate_backward(q, k, v, eta_logit, gate_logit, gamma, beta, record,
+                                       record_bytes, nullptr, kStaticScratchBytes, dout,
+                                       dW_final, dq, dk, dv, deta_logit, dgate_logit, dW0,
+                                       dgamma, dbeta, B, H, T, d, mode, chunk, &a,
+                                       /*internal_ws=*/true);
+  if (st != TTT_OK) return st;
+  if (a.ln != ttt::kLnNone) {
+    void* p = nullptr;
+    if (static_scratch(&p) != hipSuccess || p == nullptr) return TTT_ERR_HIP;
+    a.gb_part = static_cast<float*>(p);
+  }
+  const hipError_t err = ttt::launch_bwd_mfma(a, static_cast<hipStream_t>(stream));
+  if (err == hipErrorNotSupported) return TTT_ERR_UNSUPPORTED;
+  return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
 extern "C" int32_t ttt_linear_backward_workspace_bytes(int64_t B, int64_t H, int64_t d,

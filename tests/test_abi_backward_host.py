@@ -234,6 +234,27 @@ def test_backward_empty_sequence_allows_null_token_pointers():
     assert bwd_call(T=1, record=None) == ttt.TTT_ERR_NULL
 
 
+@needs_no_gpu
+def test_noalloc_backward_checks_like_the_backward_and_bounds_its_scratch():
+    names = [f for f in BWD_FIELDS if f not in ("workspace", "workspace_bytes")]
+    nb = lambda **over: ttt.ttt_linear_backward_noalloc(*[bwd_args(**over)[f] for f in names])
+    # the argument checks of the backward ...
+    assert nb(dq=None) == ttt.TTT_ERR_NULL
+    assert nb(dq=A) == ttt.TTT_ERR_ALIAS
+    assert nb(mode=ttt.TTT_DUAL, chunk=8) == ttt.TTT_ERR_UNSUPPORTED
+    # ... and the static scratch's bound: 4096 scans at d = 64 fit, 4097 do not
+    assert ttt.TTT_STATIC_SCRATCH_BYTES == 2 * 1024 * 1024
+    big = dict(B=4097, H=1, T=1, record_bytes=rec_bytes(4097, 1, 1))
+    assert nb(**big) == ttt.TTT_ERR_WORKSPACE
+    big = dict(B=64, H=65, T=2, record_bytes=rec_bytes(64, 65, 2))
+    assert nb(**big) == ttt.TTT_ERR_WORKSPACE
+    # without the LayerNorm there is no scratch, so any size passes that check
+    # (and then stops at the size of the record)
+    assert nb(B=64, H=65, T=2, gamma=None, beta=None, dgamma=None, dbeta=None,
+              mode=ttt.TTT_NO_LN, record_bytes=1) == ttt.TTT_ERR_WORKSPACE
+    assert nb(B=64, H=65, T=2, record_bytes=1) == ttt.TTT_ERR_WORKSPACE
+
+
 def test_status_string_of_workspace_error():
     s = ttt.ttt_status_string(ttt.TTT_ERR_WORKSPACE)
     assert "record" in s and "workspace" in s
