@@ -69,6 +69,13 @@ def build(verbose: bool = False) -> str:
                 print(out)
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs])
+    # a kernel whose host-side stub was not emitted (the host pass can drop a
+    # kernel template without a diagnostic) would only fail when loaded
+    undef = [l for l in _run(["nm", "-D", "--undefined-only", tmp]).splitlines()
+             if "__device_stub__" in l]
+    if undef:
+        os.remove(tmp)
+        raise RuntimeError("kernels without a host stub:\n" + "\n".join(undef))
     os.replace(tmp, LIB)
     return LIB
 
