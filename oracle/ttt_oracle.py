@@ -35,8 +35,10 @@ weight, the loss is 0.5*||.||^2, the dual-mode causal sum is inclusive, and
 a final short chunk uses the same rule.
 
 Parity status of each public function is stated in its docstring; the
-forward functions are pinned by ``tests/test_oracle.py`` and the backward
-(``ttt_linear_backward`` and its helpers) by ``tests/test_oracle_backward.py``.
+forward functions are pinned by ``tests/test_oracle.py``, the backward
+(``ttt_linear_backward`` and its helpers) by ``tests/test_oracle_backward.py``
+and the two-layer inner model (``mlp_inner_grads``, ``ttt_mlp_forward``) by
+``tests/test_oracle_mlp.py``.
 """
 from __future__ import annotations
 
@@ -389,6 +391,85 @@ def ttt_linear_backward(q, k, v, eta_logit, gate_logit, W0, gamma, beta, dout, d
     g["dgamma"] = dgamma.sum(axis=0) if has_ln else None
     g["dbeta"] = dbeta.sum(axis=0) if has_ln else None
     return g
+
+
+def mlp_inner_grads(W1, W2, k, v, gamma, beta, ln: str, eps: float = EPS):
+    """Gradients of the two-layer inner model's loss for one token.
+
+    The inner model is f(x) = W2 silu(W1 x): a reading of "Edifice.Recurrent.TTT",
+    Options, `:variant`, which says the `:mlp` variant turns the hidden state
+    into a two-layer MLP with SiLU, and of "Error Correction in Trained TTT
+    Layers", abstract, which trains TTT-MLP under the same LayerNorm
+    squared-error objective as TTT-Linear.  With
+    h = W1 k, a = silu(h), z = W2 a and delta_z the gradient of the loss with
+    respect to z (``inner_grad_vector``: straight-through, exact or without
+    LayerNorm), the chain rule gives
+
+        dL/dW2 = delta_z a^T
+        dL/dW1 = ((W2^T delta_z) * silu'(h)) k^T
+
+    with W1, W2 the weights before the update.  Returns ``(dW1, dW2)``.
+    Pinned by torch autograd of the loss and by central finite differences
+    (tests/test_oracle_mlp.py).
+    """
+    mv = lambda M, x: np.matmul(M, x[..., None])[..., 0]
+    outer = lambda a, b: a[..., :, None] * b[..., None, :]
+    h = mv(W1, k)
+    a = silu(h)
+    z = mv(W2, a)
+    dz = inner_grad_vector(z, v, gamma, beta, ln, eps)
+    da = mv(np.swapaxes(W2, -1, -2), dz)
+    dh = da * silu_grad(h)
+    return outer(dh, k), outer(dz, a)
+
+
+def ttt_mlp_forward(q, k, v, eta_logit, gate_logit, W1_0, W2_0, gamma=None, beta=None,
+                    *, ln: str = LN_ST, dual: bool = False, chunk: int = 16,
+                    eps: float = EPS, dtype=np.float64):
+    """The scan with a two-layer inner model f(x) = W2 silu(W1 x), token by token.
+
+    Shapes: q, k, v, gate_logit [B,H,T,d]; eta_logit [B,H,T]; W1_0, W2_0
+    [B,H,d,d] (hidden width d); gamma, beta [H,d].  Returns ``(out, W1_final,
+    W2_final)``.  For each token t (the TTT-Linear steps of "Edifice.Recurrent.TTT",
+    "Equations (TTT-Linear)", with the inner model replaced):
+
+      eta_t = sigmoid(eta_logit_t) / d
+      (dW1, dW2) = mlp_inner_grads(P1, P2, k_t, v_t)   P = W (per-token) or the
+                                                        chunk-start W (dual form)
+      W1 = W1 - eta_t dW1,  W2 = W2 - eta_t dW2
+      o_t = (W2 silu(W1 q_t)) * sigmoid(gate_logit_t)   (updated weights)
+
+    Parity: pinned by tests/test_oracle_mlp.py (autograd of every inner step,
+    an independent torch scan, the eta -> 0 closed form, a hand-worked d = 1
+    case, dual with chunk 1 against per-token).
+    """
+    f = lambda a: None if a is None else np.asarray(a, dtype=dtype)
+    q, k, v, eta_logit, gate_logit, W1, W2 = map(f, (q, k, v, eta_logit, gate_logit, W1_0,
+                                                     W2_0))
+    B, H, T, d = q.shape
+    if ln != LN_NONE:
+        gamma = f(gamma)[None, :, :]
+        beta = f(beta)[None, :, :]
+    if dual and chunk < 1:
+        raise ValueError("chunk must be >= 1 in dual mode")
+    W1 = W1.copy()
+    W2 = W2.copy()
+    out = np.zeros((B, H, T, d), dtype=dtype)
+    eta_all = sigmoid(eta_logit) / dtype(d)
+    gate_all = sigmoid(gate_logit)
+    mv = lambda M, x: np.matmul(M, x[..., None])[..., 0]
+    P1, P2 = W1, W2
+    for t in range(T):
+        if dual and t % chunk == 0:
+            P1, P2 = W1.copy(), W2.copy()
+        if not dual:
+            P1, P2 = W1, W2
+        dW1, dW2 = mlp_inner_grads(P1, P2, k[:, :, t, :], v[:, :, t, :], gamma, beta, ln, eps)
+        eta = eta_all[:, :, t][..., None, None]
+        W1 = W1 - eta * dW1
+        W2 = W2 - eta * dW2
+        out[:, :, t, :] = mv(W2, silu(mv(W1, q[:, :, t, :]))) * gate_all[:, :, t, :]
+    return out, W1, W2
 
 
 def input_projections(x, w_proj, b_proj=None):

@@ -183,3 +183,21 @@ def make_projection_case(B: int, T: int, hidden: int, H: int, d: int, seed: int,
     if with_bias:
         b = _f32(rng.standard_normal((H, 4 * d + 1), dtype=np.float32).astype(np.float64) * 0.1)
     return x, w, b
+
+
+def make_mlp_case(B: int, H: int, T: int, d: int, seed: int, *, w1_std: float | None = None,
+                  **kw):
+    """Seeded problem for the two-layer inner model f(x) = W2 silu(W1 x).
+
+    Everything but W1 is ``make_case(B, H, T, d, seed, **kw)``, whose W0 serves
+    as W2 (N(0, 0.02^2), the pages' init of the inner weight).  W1 [B,H,d,d] is
+    drawn from its own generator, ``PCG64(SeedSequence([seed, 1]))``, as
+    N(0, w1_std^2) float32 with w1_std = 1/sqrt(d) by default (a fan-in scale,
+    so that W1 k is of order one and the SiLU works in its curved range; the
+    pages give no scale for it).  Returns ``(inputs, W1)``."""
+    case = make_case(B, H, T, d, seed, **kw)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 1])))
+    std = 1.0 / np.sqrt(d) if w1_std is None else w1_std
+    W1 = _f32(rng.standard_normal((B, H, d, d), dtype=np.float32).astype(np.float64) * std)
+    case.meta["w1_std"] = std
+    return case, W1
