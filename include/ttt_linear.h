@@ -290,6 +290,59 @@ int32_t ttt_linear_project(const void* x, const void* w_proj, const float* b_pro
                            int64_t B, int64_t T, int64_t hidden, int64_t H, int64_t d,
                            uint32_t mode, void* stream);
 
+/*
+ * ---- TTT-MLP: the scan with a two-layer inner model ----
+ *
+ * The inner model of every (batch, head) is f(x) = W2 silu(W1 x), with W1 and
+ * W2 both d x d fast weights and no biases ("Edifice.Recurrent.TTT", Options,
+ * `:variant`: the `:mlp` variant makes the hidden state a two-layer MLP with
+ * SiLU; "Error Correction in Trained TTT Layers", abstract: TTT-MLP is
+ * trained under the same LayerNorm squared-error objective as TTT-Linear).
+ * Per token t, with P1, P2 the weights the gradient is taken at (the current
+ * ones, or the chunk-start ones with TTT_DUAL):
+ *
+ *   h = P1 k_t,  a = silu(h),  z = P2 a
+ *   delta = LN(z) - v_t  (default),  J^T (LN(z) - v_t)  (TTT_LN_EXACT),
+ *           z - v_t  (TTT_NO_LN)
+ *   W1 -= (sigmoid(eta_logit_t)/d) ((P2^T delta) * silu'(h)) k_t^T
+ *   W2 -= (sigmoid(eta_logit_t)/d) delta a^T
+ *   out_t = (W2 silu(W1 q_t)) * sigmoid(gate_logit_t)      (updated weights)
+ *
+ * Arguments are those of ttt_linear_forward with W0 / W_final replaced by
+ * the two weights:
+ *   W1_0, W2_0           [B,H,d,d] fp32, row-major (h = W1 k, z = W2 a), read-only
+ *   W1_final, W2_final   [B,H,d,d] fp32 outputs, each NULL = not written; each
+ *                        may equal its own initial weight exactly (in place)
+ * Modes: TTT_DUAL, TTT_LN_EXACT, TTT_NO_LN, TTT_IN_BF16, TTT_FORCE_VALU as for
+ * the linear scan; TTT_SILU_QK (the other reading of `:mlp`) does not combine
+ * with this call (TTT_ERR_UNSUPPORTED).  d must be 16, 32 or 64.  Every check
+ * of ttt_linear_forward applies (W1 in the role of W), then: W2_0 non-NULL
+ * (TTT_ERR_NULL), W2_0 / W2_final 16-byte aligned (TTT_ERR_UNSUPPORTED), and
+ * no output overlapping another output or an input other than its own
+ * initial weight (TTT_ERR_ALIAS).  T == 0 copies W1_0 and W2_0 to the finals.
+ * Runs asynchronously on `stream`.
+ */
+int32_t ttt_mlp_forward(const void* q, const void* k, const void* v,
+                        const void* eta_logit, const void* gate_logit,
+                        const float* W1_0, const float* W2_0,
+                        const float* gamma, const float* beta,
+                        float* out, float* W1_final, float* W2_final,
+                        int64_t B, int64_t H, int64_t T, int64_t d,
+                        uint32_t mode, int64_t chunk, void* stream);
+
+/* The argument checks of ttt_mlp_forward alone (no HIP call, no memory read). */
+int32_t ttt_mlp_validate(const void* q, const void* k, const void* v,
+                         const void* eta_logit, const void* gate_logit,
+                         const float* W1_0, const float* W2_0,
+                         const float* gamma, const float* beta,
+                         float* out, float* W1_final, float* W2_final,
+                         int64_t B, int64_t H, int64_t T, int64_t d,
+                         uint32_t mode, int64_t chunk);
+
+/* The kernel a valid ttt_mlp_forward call with this d, mode and chunk runs:
+ * "mlp_mfma", "mlp_valu", or "none" if the combination is not supported. */
+const char* ttt_mlp_kernel(int64_t d, uint32_t mode, int64_t chunk);
+
 /* A static, human-readable description of a status code (never NULL). */
 const char* ttt_status_string(int32_t status);
 

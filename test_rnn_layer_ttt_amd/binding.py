@@ -44,6 +44,7 @@ EXPORTED = ("ttt_linear_backward", "ttt_linear_backward_noalloc",
             "ttt_linear_forward", "ttt_linear_forward_masked",
             "ttt_linear_forward_record", "ttt_linear_project",
             "ttt_linear_kernel", "ttt_linear_record_bytes", "ttt_linear_validate",
+            "ttt_mlp_forward", "ttt_mlp_kernel", "ttt_mlp_validate",
             "ttt_status_string", "ttt_version")
 
 _lib = None
@@ -98,6 +99,14 @@ def load_library(path: str = LIB_PATH, check_digest: bool = True) -> ctypes.CDLL
     lib.ttt_linear_kernel.argtypes = [ctypes.c_int64, ctypes.c_uint32, ctypes.c_int64]
     lib.ttt_status_string.restype = ctypes.c_char_p
     lib.ttt_status_string.argtypes = [ctypes.c_int32]
+    lib.ttt_mlp_forward.restype = ctypes.c_int32
+    lib.ttt_mlp_forward.argtypes = [ctypes.c_void_p] * 12 + [ctypes.c_int64] * 4 + [
+        ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p]
+    lib.ttt_mlp_validate.restype = ctypes.c_int32
+    lib.ttt_mlp_validate.argtypes = [ctypes.c_void_p] * 12 + [ctypes.c_int64] * 4 + [
+        ctypes.c_uint32, ctypes.c_int64]
+    lib.ttt_mlp_kernel.restype = ctypes.c_char_p
+    lib.ttt_mlp_kernel.argtypes = [ctypes.c_int64, ctypes.c_uint32, ctypes.c_int64]
     lib.ttt_linear_forward_masked.restype = ctypes.c_int32
     lib.ttt_linear_forward_masked.argtypes = [ctypes.c_void_p] * 11 + [ctypes.c_int64] * 4 + [
         ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p]
@@ -240,6 +249,34 @@ def ttt_linear_project(x, w_proj, b_proj, q, k, v, eta_logit, gate_logit, B, T, 
         int(T), int(hidden), int(H), int(d), ctypes.c_uint32(int(mode)), p(stream)))
 
 
+def ttt_mlp_forward(q, k, v, eta_logit, gate_logit, W1_0, W2_0, gamma, beta, out, W1_final,
+                    W2_final, B, H, T, d, mode, chunk, stream) -> int:
+    """The two-layer scan's C entry point with raw pointers (ints or None) and
+    sizes; returns the status code unchanged."""
+    lib = load_library()
+    p = lambda x: None if x is None else ctypes.c_void_p(int(x))
+    return int(lib.ttt_mlp_forward(
+        p(q), p(k), p(v), p(eta_logit), p(gate_logit), p(W1_0), p(W2_0), p(gamma), p(beta),
+        p(out), p(W1_final), p(W2_final), int(B), int(H), int(T), int(d),
+        ctypes.c_uint32(int(mode)), int(chunk), p(stream)))
+
+
+def ttt_mlp_validate(q, k, v, eta_logit, gate_logit, W1_0, W2_0, gamma, beta, out, W1_final,
+                     W2_final, B, H, T, d, mode, chunk) -> int:
+    """Only the argument checks of :func:`ttt_mlp_forward`; never launches."""
+    lib = load_library()
+    p = lambda x: None if x is None else ctypes.c_void_p(int(x))
+    return int(lib.ttt_mlp_validate(
+        p(q), p(k), p(v), p(eta_logit), p(gate_logit), p(W1_0), p(W2_0), p(gamma), p(beta),
+        p(out), p(W1_final), p(W2_final), int(B), int(H), int(T), int(d),
+        ctypes.c_uint32(int(mode)), int(chunk)))
+
+
+def ttt_mlp_kernel(d: int, mode: int, chunk: int) -> str:
+    """Name of the kernel a valid two-layer call with these settings launches."""
+    return load_library().ttt_mlp_kernel(int(d), ctypes.c_uint32(int(mode)), int(chunk)).decode()
+
+
 def check(status: int) -> None:
     """Raise for a non-OK status: ValueError-derived for argument errors."""
     if status == TTT_OK:
@@ -309,6 +346,39 @@ def forward(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln: st
             stream.cuda_stream)
     check(status)
     return out, W_final
+
+
+def mlp_forward(q, k, v, eta_logit, gate_logit, W1_0, W2_0, gamma=None, beta=None, *,
+                ln: str = "st", dual: bool = False, chunk: int = 16, out=None, W1_final=None,
+                W2_final=None, stream=None, force_valu: bool = False):
+    """The scan with the two-layer inner model W2 silu(W1 x) on torch device
+    tensors; returns ``(out, W1_final, W2_final)``.
+
+    Inputs as in :func:`forward`, with W1_0 and W2_0 float32 [B,H,d,d] in
+    place of W0.  Outputs are allocated when not given; ``W1_final=W1_0``
+    (and likewise for W2) updates a state in place."""
+    import torch
+
+    B, H, T, d = _check_inputs(q, k, v, eta_logit, gate_logit, W1_0, gamma, beta, ln)
+    if tuple(W2_0.shape) != (B, H, d, d) or W2_0.dtype != torch.float32 or not (
+            W2_0.is_cuda and W2_0.is_contiguous()):
+        raise ValueError("W2_0 must be a contiguous float32 device tensor [B,H,d,d]")
+    if out is None:
+        out = torch.empty((B, H, T, d), dtype=torch.float32, device=q.device)
+    if W1_final is None:
+        W1_final = torch.empty_like(W1_0)
+    if W2_final is None:
+        W2_final = torch.empty_like(W2_0)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    mode = mode_bits(ln, dual, q.dtype == torch.bfloat16, force_valu=force_valu)
+    gb = (_ptr(gamma) if ln != "none" else None, _ptr(beta) if ln != "none" else None)
+    status = ttt_mlp_forward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(eta_logit), _ptr(gate_logit), W1_0.data_ptr(),
+        W2_0.data_ptr(), *gb, _ptr(out), W1_final.data_ptr(), W2_final.data_ptr(), B, H, T, d,
+        mode, chunk if dual else 1, stream.cuda_stream)
+    check(status)
+    return out, W1_final, W2_final
 
 
 def _ptr(t):

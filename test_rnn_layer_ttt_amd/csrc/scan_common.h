@@ -38,6 +38,9 @@ struct ScanArgs {
   bool silu_qk = false;
   // run the vector-ALU kernel even where the matrix-core one applies
   bool force_valu = false;
+  // two-layer inner model W2 silu(W1 x): W0 / W_final above are W1's, these W2's
+  const float* W2_0 = nullptr;
+  float* W2_final = nullptr;   // nullptr: not written
 };
 
 // One validated backward call (d = 64, per-token modes).
@@ -77,6 +80,15 @@ constexpr int64_t kRecTile = 16;
 // Per-token VALU scan: one workgroup per (b,h), W in VGPRs, 4 lanes per row.
 // Handles every mode (including dual) for d in {16, 32, 64, 128}.
 hipError_t launch_scan_valu(const ScanArgs& a, hipStream_t stream);
+
+// Scan with the two-layer inner model on the vector ALUs: one workgroup per
+// (b,h), every mode (per-token and dual), d in {16, 32, 64}.
+hipError_t launch_mlp_valu(const ScanArgs& a, hipStream_t stream);
+
+// Matrix-core dual-form chunk scan with the two-layer inner model (d = 64,
+// chunk 16, bf16 inputs); hipErrorNotSupported for anything else.
+hipError_t launch_mlp_mfma(const ScanArgs& a, hipStream_t stream);
+bool mlp_mfma_supports(const ScanArgs& a);
 
 // MFMA chunk scan for d = 64: exact per-token modes through the chunked
 // (lookahead-corrected) form, and the dual form.  Returns hipErrorNotSupported

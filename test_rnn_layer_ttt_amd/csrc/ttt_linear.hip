@@ -368,7 +368,95 @@ int32_t validate_project(const void* x, const void* w_proj, const float* b_proj,
   return TTT_OK;
 }
 
+// Every argument check of ttt_mlp_forward; fills *a.  Makes no HIP call.
+int32_t validate_mlp(const void* q, const void* k, const void* v, const void* eta_logit,
+                     const void* gate_logit, const float* W1_0, const float* W2_0,
+                     const float* gamma, const float* beta, float* out, float* W1_final,
+                     float* W2_final, int64_t B, int64_t H, int64_t T, int64_t d, uint32_t mode,
+                     int64_t chunk, ttt::ScanArgs* a) {
+  // the linear scan's checks with W1 in the role of W
+  int32_t st = validate(q, k, v, eta_logit, gate_logit, W1_0, gamma, beta, out, W1_final, B, H,
+                        T, d, mode, chunk, a);
+  if (st != TTT_OK) return st;
+  if (W2_0 == nullptr) return TTT_ERR_NULL;
+  if (d > 64 || a->silu_qk) return TTT_ERR_UNSUPPORTED;
+  if (!aligned(W2_0, 16) || (W2_final && !aligned(W2_final, 16))) return TTT_ERR_UNSUPPORTED;
+  const bool bf16 = a->in_bf16;
+  const int64_t in_size = bf16 ? 2 : 4;
+  const int64_t seq = B * H * T * d, w = B * H * d * d, hd = a->gamma ? H * d * 4 : 0;
+  const int64_t ts = T > 0 ? 1 : 0;
+  const Range r_w2 = span(W2_0, w * 4);
+  const Range r_w2f = span(W2_final, W2_final ? w * 4 : 0);
+  const Range r_w1 = span(W1_0, w * 4);
+  const Range r_w1f = span(W1_final, W1_final ? w * 4 : 0);
+  const Range r_out = span(out, ts * seq * 4);
+  const Range ins[] = {span(q, ts * seq * in_size),        span(k, ts * seq * in_size),
+                       span(v, ts * seq * in_size),        span(gate_logit, ts * seq * in_size),
+                       span(eta_logit, ts * B * H * T * in_size), span(a->gamma, hd),
+                       span(a->beta, hd),                  r_w1};
+  for (const Range& r : ins)
+    if (overlaps(r_w2f, r)) return TTT_ERR_ALIAS;
+  if (overlaps(r_w2f, r_out) || overlaps(r_w2f, r_w1f)) return TTT_ERR_ALIAS;
+  if (overlaps(r_w2, r_out) || overlaps(r_w2, r_w1f)) return TTT_ERR_ALIAS;
+  if (W2_final && W2_final != W2_0 && overlaps(r_w2f, r_w2)) return TTT_ERR_ALIAS;
+  a->W2_0 = W2_0;
+  a->W2_final = W2_final;
+  return TTT_OK;
+}
+
+// the kernel a validated two-layer call runs
+bool runs_mlp_mfma(const ttt::ScanArgs& a) {
+  return !a.force_valu && ttt::mlp_mfma_supports(a);
+}
+
 }  // namespace
+
+extern "C" int32_t ttt_mlp_validate(const void* q, const void* k, const void* v,
+                                    const void* eta_logit, const void* gate_logit,
+                                    const float* W1_0, const float* W2_0, const float* gamma,
+                                    const float* beta, float* out, float* W1_final,
+                                    float* W2_final, int64_t B, int64_t H, int64_t T, int64_t d,
+                                    uint32_t mode, int64_t chunk) {
+  ttt::ScanArgs a;
+  return validate_mlp(q, k, v, eta_logit, gate_logit, W1_0, W2_0, gamma, beta, out, W1_final,
+                      W2_final, B, H, T, d, mode, chunk, &a);
+}
+
+extern "C" int32_t ttt_mlp_forward(const void* q, const void* k, const void* v,
+                                   const void* eta_logit, const void* gate_logit,
+                                   const float* W1_0, const float* W2_0, const float* gamma,
+                                   const float* beta, float* out, float* W1_final,
+                                   float* W2_final, int64_t B, int64_t H, int64_t T, int64_t d,
+                                   uint32_t mode, int64_t chunk, void* stream) {
+  ttt::ScanArgs a;
+  const int32_t st = validate_mlp(q, k, v, eta_logit, gate_logit, W1_0, W2_0, gamma, beta, out,
+                                  W1_final, W2_final, B, H, T, d, mode, chunk, &a);
+  if (st != TTT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    const size_t bytes = static_cast<size_t>(B * H * d * d) * sizeof(float);
+    if (W1_final && W1_final != W1_0 &&
+        hipMemcpyAsync(W1_final, W1_0, bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return TTT_ERR_HIP;
+    if (W2_final && W2_final != W2_0 &&
+        hipMemcpyAsync(W2_final, W2_0, bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return TTT_ERR_HIP;
+    return TTT_OK;
+  }
+  const hipError_t err = runs_mlp_mfma(a) ? ttt::launch_mlp_mfma(a, s) : ttt::launch_mlp_valu(a, s);
+  return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+extern "C" const char* ttt_mlp_kernel(int64_t d, uint32_t mode, int64_t chunk) {
+  alignas(16) static const float dummy[4] = {0, 0, 0, 0};
+  const void* p = dummy;
+  float* o = reinterpret_cast<float*>(0x100000);  // never dereferenced
+  ttt::ScanArgs a;
+  if (validate_mlp(p, p, p, p, p, dummy, dummy, dummy, dummy, o, nullptr, nullptr, 1, 1, 1, d,
+                   mode, chunk, &a) != TTT_OK)
+    return "none";
+  return runs_mlp_mfma(a) ? "mlp_mfma" : "mlp_valu";
+}
 
 extern "C" int32_t ttt_linear_project(const void* x, const void* w_proj, const float* b_proj,
                                       void* q, void* k, void* v, void* eta_logit,
