@@ -9,7 +9,9 @@ the recording forward (``ttt_linear_forward_record``) followed by the backward
 roofline is then that of the backward kernel.  With ``--pass project`` a step
 is the layer's input projections (``ttt_linear_project``, from a seeded bf16 x
 [B,T,H*d] and stacked weights) followed by the scan; the roofline is the
-projection kernel's (bf16 MFMA).  W warm-up steps run untimed; then exactly K steps are
+projection kernel's (bf16 MFMA).  With ``--mlp`` a step is one call of
+``ttt_mlp_forward``: the same scan with the two-layer inner model
+W2 silu(W1 x) (W2 is the workload's W0; W1 is drawn from the workload's seed).  W warm-up steps run untimed; then exactly K steps are
 timed between two device synchronisations, and each launch is also bracketed
 by events on its stream for the per-kernel duration.  Rank 0 prints one JSON
 line.
@@ -40,6 +42,8 @@ METRIC_PROJECT = ("TTT-Linear layer (input projections + scan) token-heads/s at 
                   "+ % of bf16 MFMA roofline of the projection kernel, 1 MI355X")
 METRIC_TRAIN = ("TTT-Linear training pass (recording forward + backward) token-heads/s at d=64 "
                 "+ % of HBM roofline of the backward kernel, 1 MI355X")
+METRIC_MLP = ("TTT-MLP scan (two-layer inner model) token-heads/s at d=64 "
+              "+ % of FP32/MFMA roofline, 1 MI355X")
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # 256 CU x 2.4 GHz x 256 flop/clk (packed FMA), published
 FP32_MATRIX_PEAK_TFLOPS = 157.3  # MFMA fp32, published
@@ -65,6 +69,23 @@ def algorithmic_work(x, mask=None):
     nbytes = ((n - n_skip) * per_tok_bytes + n_skip * skip_bytes + B * H * 8 * d * d + H * 8 * d
               + extra)
     flops = (n - n_skip) * per_tok_flops + n_skip * 2 * d * d
+    return n, nbytes, flops
+
+
+def mlp_work(x):
+    """Compulsory HBM bytes and flops of one two-layer launch (per token-head).
+
+    Bytes: those of the linear scan, with two d x d weights in and out per
+    scan.  Flops: seven d x d products per token (P1 k, P2 a, P2^T delta, the
+    two rank-one updates, W1 q and W2 silu(W1 q)), 14 d^2; the dual form adds
+    the in-chunk causal terms (the Gram matrices k.q and a.aq and their
+    corrections, 8 chunk d)."""
+    B, H, T, d = x.q.shape
+    n = B * H * T
+    s_in = 2 if x.in_bf16 else 4
+    per_tok_bytes = (4 * d + 1) * s_in + 4 * d
+    nbytes = n * per_tok_bytes + B * H * 16 * d * d + H * 8 * d
+    flops = n * (14 * d * d + (8 * x.chunk * d if x.dual else 0))
     return n, nbytes, flops
 
 
@@ -115,6 +136,16 @@ def precision(x, kernel):
             "fp32 state and output")
 
 
+def mlp_precision(x, kernel):
+    """What the arithmetic of a two-layer launch is, in words."""
+    if kernel == "mlp_valu":
+        return ("bf16 inputs widened to fp32; " if x.in_bf16 else "fp32 inputs; ") + \
+            "fp32 vector-ALU arithmetic, fp32 weights and output"
+    return ("bf16 inputs; d x d products on bf16 MFMA with the fp32 operands (weights, "
+            "activations, errors) split into bf16 hi + lo and only the lo*lo term dropped; "
+            "fp32 accumulation, fp32 LayerNorm, fp32 weights and output")
+
+
 def projection_work(x):
     """Flops and compulsory HBM bytes of one projection launch: x [B,T,hidden]
     and the weights [H,4d+1,hidden] in bf16, the five results out in the
@@ -127,7 +158,7 @@ def projection_work(x):
 
 
 def roofline(x, kernel_ms, traffic, train=False, mask=None, project=False,
-             hbm_measured_gbs=None, kernel=None):
+             hbm_measured_gbs=None, kernel=None, mlp=False):
     """Both ceilings of one launch and the fraction of the binding one.
 
     t_hbm = algorithmic bytes / the HBM peak and t_compute = algorithmic flops /
@@ -141,6 +172,13 @@ def roofline(x, kernel_ms, traffic, train=False, mask=None, project=False,
     if project:
         n, nbytes, flops = projection_work(x)
         name, cbound, cpeak = "proj_mfma", "mfma", BF16_MATRIX_PEAK_TFLOPS
+    elif mlp:
+        n, nbytes, flops = mlp_work(x)
+        name = kernel
+        if name == "mlp_mfma":
+            cbound, cpeak = "mfma", BF16_MATRIX_PEAK_TFLOPS
+        else:
+            cbound, cpeak = "alu", FP32_VECTOR_PEAK_TFLOPS
     elif train:
         n, nbytes, flops = backward_work(x)
         name, cbound, cpeak = "bwd_mfma", "alu", FP32_VECTOR_PEAK_TFLOPS
@@ -182,6 +220,7 @@ _CPU_TRAIN = False
 _CPU_MASK = None
 _CPU_PROJ = None   # (x, w_proj) of the layer-pass workload, float32 holding bf16 values
 _CPU_SILU = False
+_CPU_MLP_W1 = None   # W1 of the sampled scans (two-layer inner model)
 
 
 def _oracle_worker(idx):
@@ -205,6 +244,10 @@ def _oracle_worker(idx):
             args = (x.q[:, idx], x.k[:, idx], x.v[:, idx], x.eta_logit[:, idx],
                     x.gate_logit[:, idx], x.W0[:, idx], x.gamma[idx], x.beta[idx])
         m = None if _CPU_MASK is None else _CPU_MASK[:, idx]
+        if _CPU_MLP_W1 is not None:
+            oracle.ttt_mlp_forward(*args[:5], _CPU_MLP_W1[:, idx], *args[5:], ln=x.ln,
+                                   dual=x.dual, chunk=x.chunk)
+            return len(idx)
         oracle.ttt_linear_forward(*args, ln=x.ln, dual=x.dual, chunk=x.chunk, update_mask=m,
                                   silu_qk=_CPU_SILU)
         if _CPU_TRAIN:
@@ -220,12 +263,13 @@ def _cotangents(x):
     return make_cotangents(B, H, T, d, seed=x.meta.get("seed", 0) + 1000)
 
 
-def cpu_baseline(x, n_scans, workers, train=False, mask=None, proj=None):
+def cpu_baseline(x, n_scans, workers, train=False, mask=None, proj=None, mlp_W1=None):
     """Time the oracle on ``n_scans`` scans of ``x`` (full length) over ``workers``
     processes; with ``train`` its forward and its backward, as one training pass;
-    with ``proj`` = (x, w_proj) its input projections of each scan, then the scan."""
+    with ``proj`` = (x, w_proj) its input projections of each scan, then the scan;
+    with ``mlp_W1`` the two-layer scan (W2 = x.W0)."""
     import multiprocessing as mp
-    global _CPU_SAMPLE, _CPU_TRAIN, _CPU_MASK, _CPU_PROJ
+    global _CPU_SAMPLE, _CPU_TRAIN, _CPU_MASK, _CPU_PROJ, _CPU_MLP_W1
     _CPU_TRAIN = train
     _CPU_PROJ = proj
     B, H, T, d = x.q.shape
@@ -233,6 +277,8 @@ def cpu_baseline(x, n_scans, workers, train=False, mask=None, proj=None):
     step = max(1, (B * H) // n_scans)
     pairs = [(i // H, i % H) for i in range(0, B * H, step)][:n_scans]
     _CPU_SAMPLE = x.subset(pairs)
+    _CPU_MLP_W1 = None if mlp_W1 is None else np.ascontiguousarray(
+        mlp_W1[[p[0] for p in pairs], [p[1] for p in pairs]][None])
     _CPU_MASK = None if mask is None else np.ascontiguousarray(
         mask[[p[0] for p in pairs], [p[1] for p in pairs]][None])
     groups = [list(range(w, n_scans, workers)) for w in range(workers)]
@@ -244,8 +290,10 @@ def cpu_baseline(x, n_scans, workers, train=False, mask=None, proj=None):
     sec = time.perf_counter() - t0
     _CPU_SAMPLE = None
     _CPU_PROJ = None
+    _CPU_MLP_W1 = None
     what = (", forward and backward" if train else
-            ", input projections then the scan" if proj is not None else "")
+            ", input projections then the scan" if proj is not None else
+            ", two-layer inner model" if mlp_W1 is not None else "")
     return dict(value=round(done * T / sec, 1), unit="token-heads/s", cores=len(groups),
                 kind="oracle",
                 sample=f"{done} of {B * H} scans at full length T={T}"
@@ -291,6 +339,9 @@ def main():
                          "project: the layer's input projections from x, then the scan")
     ap.add_argument("--silu-qk", action="store_true",
                     help="the :mlp variant: SiLU on q and k before the inner model")
+    ap.add_argument("--mlp", action="store_true",
+                    help="the scan with the two-layer inner model W2 silu(W1 x) "
+                         "(ttt_mlp_forward)")
     ap.add_argument("--update-rate", type=float, default=None,
                     help="dual-form workloads: seeded SKIP/UPDATE decisions per chunk, each "
                          "UPDATE with this probability (ttt_linear_forward_masked)")
@@ -318,7 +369,15 @@ def main():
               "is produced.", file=sys.stderr)
         sys.exit(2)
 
-    x = make_inputs(args.workload)
+    W1_np = None
+    if args.mlp:
+        if args.pass_ != "forward" or args.silu_qk or args.update_rate is not None:
+            print("bench.py: --mlp times the two-layer forward alone", file=sys.stderr)
+            sys.exit(2)
+        from test_rnn_layer_ttt_amd.inputs import make_mlp_inputs
+        x, W1_np = make_mlp_inputs(args.workload)
+    else:
+        x = make_inputs(args.workload)
     B, H, T, d = x.q.shape
     train = args.pass_ == "train"
     project = args.pass_ == "project"
@@ -350,8 +409,8 @@ def main():
     # the CPU baseline runs before any GPU use (its workers are forked)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(x, args.cpu_scans, host_cores(), train, mask_np,
-                           proj_np if project else None)
+        cpu = cpu_baseline(x, args.cpu_scans if not args.mlp else min(args.cpu_scans, 64),
+                           host_cores(), train, mask_np, proj_np if project else None, W1_np)
 
     import torch
 
@@ -384,7 +443,18 @@ def main():
             if st != ttt.TTT_OK:
                 raise RuntimeError(f"ttt_linear_project: {ttt.ttt_status_string(st)}")
 
-    if mask_np is None:
+    if args.mlp:
+        W1 = torch.from_numpy(W1_np).to(dev)
+        W1f = torch.empty_like(W1)
+        mptrs = ptrs[:5] + (W1.data_ptr(), W0.data_ptr()) + ptrs[6:9] + (W1f.data_ptr(),
+                                                                         Wf.data_ptr())
+
+        def forward(extra_mode=0):
+            st = ttt.ttt_mlp_forward(*mptrs, B, H, T, d, mode | extra_mode, x.chunk,
+                                     stream.cuda_stream)
+            if st != ttt.TTT_OK:
+                raise RuntimeError(f"ttt_mlp_forward: {ttt.ttt_status_string(st)}")
+    elif mask_np is None:
         def forward():
             st = ttt.ttt_linear_forward(*ptrs, B, H, T, d, mode, x.chunk, stream.cuda_stream)
             if st != ttt.TTT_OK:
@@ -500,20 +570,23 @@ def main():
     copy_gbs = 2 * (1 << 30) / (float(np.median(copy_ms[1:])) / 1e3) / 1e9
 
     n_tok = B * H * T
-    kernel = "bwd_mfma" if train else "proj_mfma" if project else kernel_name(x)
-    traffic_key = args.workload + ("/backward" if train else "/project" if project else "")
+    kernel = ("bwd_mfma" if train else "proj_mfma" if project else
+              ttt.ttt_mlp_kernel(d, mode, x.chunk) if args.mlp else kernel_name(x))
+    traffic_key = args.workload + ("/backward" if train else "/project" if project else
+                                   "/mlp" if args.mlp else "")
     if mask_np is not None:
         traffic_key = args.workload + f"/update{args.update_rate:g}"
     if args.silu_qk:
         traffic_key += "/silu"
     kname, roof = roofline(x, avg_kernel_ms, load_traffic(kernel, traffic_key), train, mask_np,
-                           project, hbm_measured_gbs=copy_gbs)
+                           project, hbm_measured_gbs=copy_gbs, kernel=kernel, mlp=args.mlp)
 
     mode_name = ("dual-form chunk %d" % x.chunk if x.dual else "per-token") + \
         {"st": "", "exact": ", exact LN Jacobian", "none": ", no LN"}[x.ln]
     med = lambda a: round(float(np.median(a)), 4)
     line = {
-        "metric": METRIC_TRAIN if train else METRIC_PROJECT if project else METRIC,
+        "metric": (METRIC_TRAIN if train else METRIC_PROJECT if project else
+                   METRIC_MLP if args.mlp else METRIC),
         "value": round(n_tok / (ms_per_step / 1e3), 1),
         "unit": "token-heads/s",
         "n_gpus": 1,
@@ -529,7 +602,8 @@ def main():
         "config": {"workload": args.workload, "B": B, "H": H, "T": T, "d": d,
                    "hidden": H * d, "mode": mode_name,
                    "inputs": "bf16" if x.in_bf16 else "fp32", "state": "fp32",
-                   "precision": precision(x, kname) if not (train or project) else
+                   "precision": mlp_precision(x, kname) if args.mlp else
+                   precision(x, kname) if not (train or project) else
                    ("bf16 inputs" if x.in_bf16 else "fp32 inputs") +
                    "; fp32 accumulation, fp32 gradients",
                    "kernel": kname, "kernel_ms_avg": round(avg_kernel_ms, 4),
@@ -550,6 +624,8 @@ def main():
                                                              1)}
     if args.silu_qk:
         line["config"]["variant"] = "mlp (SiLU on q and k)"
+    if args.mlp:
+        line["config"]["variant"] = "two-layer inner model W2 silu(W1 x), both d x d"
     if mask_np is not None:
         line["config"]["update_rate"] = args.update_rate
         line["config"]["chunks_updated"] = float(np.mean(mask_np != 0))
@@ -561,10 +637,27 @@ def main():
                                   "then the scan")
         line["config"]["scan_ms_avg"] = round(float(np.mean(ms["scan"])), 4)
 
-    # ---- the vector-ALU per-token kernel on the same inputs, for comparison
-    # (the matrix-core kernel is what a call at d = 64 runs)
-    if (not train and not project and mask_np is None and args.valu_steps > 0
-            and kname == "scan_mfma"):
+    # ---- the vector-ALU kernel on the same inputs, for comparison (the
+    # matrix-core kernel is what a call at d = 64 runs)
+    if args.mlp and args.valu_steps > 0 and kname == "mlp_mfma":
+        forward(ttt.TTT_FORCE_VALU)
+        torch.cuda.synchronize()
+        vms = []
+        for _ in range(args.valu_steps):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            forward(ttt.TTT_FORCE_VALU)
+            b_.record(stream)
+            b_.synchronize()
+            vms.append(a_.elapsed_time(b_))
+        _, vroof = roofline(x, float(np.median(vms)), None, kernel="mlp_valu", mlp=True)
+        line["config"]["valu_kernel"] = {
+            "kernel": "mlp_valu", "kernel_ms_median": med(vms),
+            "token_heads_per_s": round(n_tok / (np.median(vms) / 1e3), 1),
+            "bound": vroof["bound"], "frac": vroof["frac"], "frac_hbm": vroof["frac_hbm"],
+            "frac_compute": vroof["frac_compute"], "precision": mlp_precision(x, "mlp_valu")}
+    if (not train and not project and not args.mlp and mask_np is None
+            and args.valu_steps > 0 and kname == "scan_mfma"):
         vmode = mode | ttt.TTT_FORCE_VALU
 
         def valu():

@@ -201,3 +201,13 @@ def make_mlp_case(B: int, H: int, T: int, d: int, seed: int, *, w1_std: float | 
     W1 = _f32(rng.standard_normal((B, H, d, d), dtype=np.float32).astype(np.float64) * std)
     case.meta["w1_std"] = std
     return case, W1
+
+
+def make_mlp_inputs(workload: str, **overrides):
+    """A named workload for the two-layer inner model: ``(inputs, W1)``, where
+    ``inputs`` is ``make_inputs(workload, **overrides)`` (its W0 serves as W2)
+    and W1 is drawn as in ``make_mlp_case`` from the workload's seed."""
+    cfg = dict(WORKLOADS[workload])
+    cfg.update(overrides)
+    B, H, T, d, seed = cfg.pop("B"), cfg.pop("H"), cfg.pop("T"), cfg.pop("d"), cfg.pop("seed")
+    return make_mlp_case(B, H, T, d, seed, name=workload, **cfg)
