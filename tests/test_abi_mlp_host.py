@@ -86,3 +86,10 @@ def test_kernel_query():
         assert ttt.ttt_mlp_kernel(d, 0, 1) == "mlp_valu"
     assert ttt.ttt_mlp_kernel(64, ttt.TTT_FORCE_VALU | ttt.TTT_DUAL | ttt.TTT_IN_BF16,
                               16) == "mlp_valu"
+    # the matrix-core kernel: dual form, chunks of 16, bf16 inputs, d = 64, every LN mode
+    for ln in (0, ttt.TTT_LN_EXACT, ttt.TTT_NO_LN):
+        assert ttt.ttt_mlp_kernel(64, ln | ttt.TTT_DUAL | ttt.TTT_IN_BF16, 16) == "mlp_mfma"
+    assert ttt.ttt_mlp_kernel(64, ttt.TTT_DUAL | ttt.TTT_IN_BF16, 8) == "mlp_valu"
+    assert ttt.ttt_mlp_kernel(64, ttt.TTT_DUAL, 16) == "mlp_valu"
+    assert ttt.ttt_mlp_kernel(32, ttt.TTT_DUAL | ttt.TTT_IN_BF16, 16) == "mlp_valu"
+    assert ttt.ttt_mlp_kernel(64, ttt.TTT_IN_BF16, 1) == "mlp_valu"
