@@ -141,6 +141,16 @@ def build(verbose: bool = False) -> str:
     if bad:
         raise RuntimeError("accumulator-input overwrite of an in-flight 16x16x16 MFMA:\n" +
                            "\n".join(f"  {s}: {m} | {w} ({n} wait states)" for s, m, w, n in bad))
+    # flat (generic-address) memory instructions count against the LDS wait
+    # counter as well, so every LDS wait after one waits for its memory
+    # round trip; device pointers here are global and LDS is addressed directly
+    flat = []
+    for s in SOURCES:
+        asm = os.path.join(BUILD_DIR, f"{os.path.splitext(s)[0]}-hip-amdgcn-amd-amdhsa-{ARCH}.s")
+        with open(asm) as f:
+            flat += [f"  {s}: {l.strip()}" for l in f if l.lstrip().startswith("flat_")]
+    if flat:
+        raise RuntimeError("flat memory instructions in device code:\n" + "\n".join(flat[:20]))
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs])
     # a kernel whose host-side stub was not emitted (the host pass can drop a

@@ -150,13 +150,13 @@ __device__ __forceinline__ void st4(uint16_t* p, const i16x4& v) {
 // 16x16x32 product (lane l = t + 16G holds, in slot e, feature
 // j = 32ks + 16(e/4) + 4G + e%4 of token t); KT: -K^T in the A layout of the
 // 16x16x16 product (lane l = j%16 + 16G of feature tile jb holds tokens
-// 4G + e of feature j); V and SG (sigmoid of the gate) by [token][feature].
+// 4G + e of feature j); V and SG (the gate logits) by [token][feature].
 struct alignas(16) Chunk {
   uint16_t KA[2][64][8];
   uint16_t QA[2][64][8];
   uint16_t KT[4][64][4];
   float V[BT][D];
-  float SG[BT][D];
+  float SG[BT][D];        // gate logits (the sigmoid is taken at the output)
   float ETA[BT];          // sigmoid(eta_logit)/d, 0 past the end
   float pad_[4];
 };
@@ -181,16 +181,18 @@ struct Stage {
 };
 
 // thread tid: array a = tid / 64 (q, k, v, gate), vectors (tid % 64) and
-// (tid % 64) + 64 of that array's 128 vectors in the chunk
-__device__ __forceinline__ void load_chunk(Stage& st, const uint16_t* const src[4],
-                                           const uint16_t* eta, int64_t t0, int64_t T, int tid) {
-  const int a = tid >> 6;
+// (tid % 64) + 64 of that array's 128 vectors in the chunk.  `src` is this
+// wave's array, chosen among the kernel's pointer arguments by a select, so
+// the loads stay global loads (an indexed array of pointers would make them
+// flat loads, which every LDS wait then waits for as well).
+__device__ __forceinline__ void load_chunk(Stage& st, const uint16_t* src, const uint16_t* eta,
+                                           int64_t t0, int64_t T, int tid) {
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int vid = (tid & 63) + 64 * r;
     const int t = vid >> 3;
     uint4 x = make_uint4(0, 0, 0, 0);
-    if (t0 + t < T) x = *reinterpret_cast<const uint4*>(src[a] + (t0 + t) * D + (vid & 7) * 8);
+    if (t0 + t < T) x = *reinterpret_cast<const uint4*>(src + (t0 + t) * D + (vid & 7) * 8);
     st.v[r] = x;
   }
   st.eta = 0u;
@@ -227,10 +229,6 @@ __device__ __forceinline__ void store_chunk(const Stage& st, Chunk& ck, int64_t 
       for (int i = 0; i < 4; ++i) {
         f[2 * i] = __uint_as_float(w[i] << 16);
         f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-      }
-      if (a == 3) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = fast_sigmoid(f[e]);
       }
       float* dst = (a == 2) ? &ck.V[t][j0] : &ck.SG[t][j0];
       *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
@@ -278,8 +276,8 @@ mlp_mfma_kernel(const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp
   const int h = static_cast<int>(bh % H);
   const int64_t nc = (T + BT - 1) / BT;
 
-  const uint16_t* src[4] = {qp + bh * T * D, kp + bh * T * D, vp + bh * T * D,
-                            gatep + bh * T * D};
+  const int a_ld = tid >> 6;   // the array this wave stages: q, k, v, gate
+  const uint16_t* src = (a_ld == 0 ? qp : a_ld == 1 ? kp : a_ld == 2 ? vp : gatep) + bh * T * D;
   const uint16_t* eta = etap + bh * T;
   float* dst_out = out + bh * T * D;
   const float* w1 = W1_0 + bh * D * D;
@@ -317,15 +315,16 @@ mlp_mfma_kernel(const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) p1[ks] = op32(p1t[2 * ks], p1t[2 * ks + 1]);
   };
+  // (two independent accumulation chains, the hi and the lo parts of W1)
   auto keys_times_w1 = [&](const uint16_t (*XA)[64][8], const Op32 (&p1)[2]) -> f32x4 {
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 ah = {0.0f, 0.0f, 0.0f, 0.0f}, al = ah;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const bf16x8 x = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(XA[ks][lane]));
-      acc = mfma32(x, p1[ks].hi, acc);
-      acc = mfma32(x, p1[ks].lo, acc);
+      ah = mfma32(x, p1[ks].hi, ah);
+      al = mfma32(x, p1[ks].lo, al);
     }
-    return acc;
+    return ah + al;
   };
   auto gram_kq = [&](const Chunk& ck) -> f32x4 {
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -361,14 +360,17 @@ mlp_mfma_kernel(const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp
   auto outputs = [&](int64_t cp, const Op32 (&p2)[2]) {
     const int par = static_cast<int>(cp & 1);
     const Chunk& ck = sm.ring[cp % RING];
-    f32x4 y = {0.0f, 0.0f, 0.0f, 0.0f}, g2 = {0.0f, 0.0f, 0.0f, 0.0f};
+    // one accumulation chain per half of the contraction
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 y2[2], g22[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const Op32 aq = act_op(sm.AQ, ks, n, g);
       const Op32 as = act_op(sm.A1[par], ks, n, g);
-      y = prod3(p2[ks], aq, y);
-      g2 = prod3(as, aq, g2);           // G2[s][t] = a_s . aq_t
+      y2[ks] = prod3(p2[ks], aq, zero);
+      g22[ks] = prod3(as, aq, zero);    // G2[s][t] = a_s . aq_t
     }
+    f32x4 y = y2[0] + y2[1], g2 = g22[0] + g22[1];
     // strictly later tokens only, negated (DT holds -eta delta)
 #pragma unroll
     for (int r = 0; r < 4; ++r) g2[r] = (4 * g + r > n) ? -g2[r] : 0.0f;
@@ -376,9 +378,10 @@ mlp_mfma_kernel(const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp
     y = prod3_16(dt, op16(g2), y);
     const int64_t t = cp * BT + n;
     if (t < T) {
-      const float4 sg = *reinterpret_cast<const float4*>(&ck.SG[n][16 * w + 4 * g]);
+      const float4 gl = *reinterpret_cast<const float4*>(&ck.SG[n][16 * w + 4 * g]);
       *reinterpret_cast<float4*>(dst_out + t * D + 16 * w + 4 * g) =
-          make_float4(y[0] * sg.x, y[1] * sg.y, y[2] * sg.z, y[3] * sg.w);
+          make_float4(y[0] * fast_sigmoid(gl.x), y[1] * fast_sigmoid(gl.y),
+                      y[2] * fast_sigmoid(gl.z), y[3] * fast_sigmoid(gl.w));
     }
   };
 
@@ -416,9 +419,9 @@ mlp_mfma_kernel(const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp
         // A operand of W2 (rows own outputs, contraction over hidden units)
         p2[ks] = op32(p2t[2 * ks], p2t[2 * ks + 1]);
       }
-      f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) z = prod3(p2[ks], act_op(sm.A1[par], ks, n, g), z);
+      const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+      const f32x4 z = prod3(p2[0], act_op(sm.A1[par], 0, n, g), zero) +
+                      prod3(p2[1], act_op(sm.A1[par], 1, n, g), zero);
       *reinterpret_cast<float4*>(&sm.Z[n][16 * w + 4 * g]) = make_float4(z[0], z[1], z[2], z[3]);
       if (c > 0) outputs(c - 1, p2);
     }
@@ -488,12 +491,9 @@ mlp_mfma_kernel(const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp
     // ---- D_c: back-propagation, updates, this chunk's aq, the next chunk's h
     {
       // DA^T = Delta^T P2 (rows tokens, cols own hidden units), at the chunk-start W2
-      f32x4 dat = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const Op32 d = act_op(sm.DS, ks, n, g);
-        dat = prod3(d, op32(p2n[2 * ks], p2n[2 * ks + 1]), dat);
-      }
+      const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+      const f32x4 dat = prod3(act_op(sm.DS, 0, n, g), op32(p2n[0], p2n[1]), zero) +
+                        prod3(act_op(sm.DS, 1, n, g), op32(p2n[2], p2n[3]), zero);
       // eta DH^T
       f32x4 edh;
 #pragma unroll
