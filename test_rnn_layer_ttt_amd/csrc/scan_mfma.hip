@@ -201,10 +201,13 @@ struct Stage {
 
 // The array loop is unrolled, so each base pointer is a kernel argument and
 // the loads issue as global loads (counted by vmcnt only).
+// skip: the tile is a skipped chunk (the dual form's chunk is the tile); it
+// needs only q and the gate, so its keys and values stay zero and are not
+// read from memory, and its eta_logit is -inf
 template <bool BF16>
 __device__ __forceinline__ void load_tile(Stage<BF16>& st, const void* const src[4],
                                           const void* etap, int64_t bhT, int64_t t0, int64_t T,
-                                          int lane, const uint8_t* mrow) {
+                                          int lane, bool skip) {
   using In = typename std::conditional<BF16, uint16_t, float>::type;
   using S = Stage<BF16>;
 #pragma unroll
@@ -214,20 +217,23 @@ __device__ __forceinline__ void load_tile(Stage<BF16>& st, const void* const src
     for (int r = 0; r < S::kPerLane; ++r) {
       const int vid = lane + 64 * r;
       uint4 x = make_uint4(0, 0, 0, 0);
-      if (t0 + (vid * S::kVE) / D < T) x = *reinterpret_cast<const uint4*>(base + vid * S::kVE);
+      if (t0 + (vid * S::kVE) / D < T && !(skip && (a == 1 || a == 2)))
+        x = *reinterpret_cast<const uint4*>(base + vid * S::kVE);
       st.v[a][r] = x;
     }
   }
   st.eta = 0u;
   if (lane < BT && t0 + lane < T) {
-    const In* e = static_cast<const In*>(etap) + bhT + t0 + lane;
-    if constexpr (BF16)
-      st.eta = *e;
-    else
-      st.eta = __float_as_uint(*e);
-    // a skipped chunk (the dual form's chunk is the tile): eta_logit = -inf,
-    // whose sigmoid is exactly 0
-    if (mrow != nullptr && mrow[t0 / BT] == 0) st.eta = BF16 ? 0xFF80u : 0xFF800000u;
+    // a skipped chunk: eta_logit = -inf, whose sigmoid is exactly 0
+    if (skip) {
+      st.eta = BF16 ? 0xFF80u : 0xFF800000u;
+    } else {
+      const In* e = static_cast<const In*>(etap) + bhT + t0 + lane;
+      if constexpr (BF16)
+        st.eta = *e;
+      else
+        st.eta = __float_as_uint(*e);
+    }
   }
 }
 
@@ -242,15 +248,17 @@ __device__ __forceinline__ uint32_t silu_bf16x2(uint32_t w) {
 
 // silu: the :mlp variant's SiLU on q and k (on the bf16 path the activated
 // values are rounded back to bf16, the matrix cores' operand type)
+// skip: a skipped chunk's keys and values are never read, so they are not stored
 template <bool BF16, int LN>
 __device__ __forceinline__ void store_tile(const Stage<BF16>& st,
                                            typename Smem<BF16>::Tile& tl, int64_t t0, int64_t T,
                                            int lane, const float (&sb)[Stage<BF16>::kVE],
-                                           bool silu) {
+                                           bool silu, bool skip = false) {
   using S = Stage<BF16>;
   auto vb = [&](float v, int e) { return LN == kLnNone ? v : sb[e] - v; };
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
+    if (skip && (a == 1 || a == 2)) continue;
 #pragma unroll
     for (int r = 0; r < S::kPerLane; ++r) {
       const int vid = lane + 64 * r;
@@ -668,8 +676,12 @@ __device__ __forceinline__ void write_tile_out(const float (*ob)[KPAD], float* o
 
 // ---------------------------------------------------------------------------
 // REC: also record delta_t and W at the start of every tile (for the backward;
-// in the dual form the tiles are the chunks)
-template <bool BF16, int LN, bool DUAL, bool REC>
+// in the dual form the tiles are the chunks).  MASK (dual form only): one
+// SKIP/UPDATE decision per chunk in upd_mask; a skipped chunk applies no
+// update (eta = 0), so only its outputs (W_c q_t) sigmoid(gate_t) are formed:
+// its keys, values and eta are not loaded, and its z, LayerNorm pass, key
+// Gram matrices, in-chunk correction and W update are left out.
+template <bool BF16, int LN, bool DUAL, bool REC, bool MASK = false>
 __global__ void __launch_bounds__(NT)
 scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
                  const void* __restrict__ vp, const void* __restrict__ etap,
@@ -690,7 +702,31 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   const void* const src[4] = {qp, kp, vp, gatep};
   const int64_t ntiles = (T + BT - 1) / BT;
   using R = Roles<BF16, DUAL>;
-  const uint8_t* mrow = (DUAL && upd_mask != nullptr) ? upd_mask + bh * ntiles : nullptr;
+  static_assert(!MASK || (DUAL && !REC), "the chunk mask is a dual-form forward option");
+  const uint8_t* mrow = MASK ? upd_mask + bh * ntiles : nullptr;
+  // The decisions of tiles wb .. wb+127 as two 64-bit words (bit i of mw0:
+  // tile wb + i is skipped; mw1: tile wb + 64 + i), formed by a ballot over
+  // the wave's lanes; moved on by 64 tiles once tile wb + 64 is the oldest
+  // one a period asks about.  No decision is read from memory inside a period.
+  int64_t wb = 0;
+  uint64_t mw0 = 0, mw1 = 0;
+  auto mask_bits = [&](int64_t base) -> uint64_t {
+    const int64_t u = base + lane;
+    return __ballot(u < ntiles && mrow[u] == 0);
+  };
+  if constexpr (MASK) {
+    mw0 = mask_bits(0);
+    mw1 = mask_bits(64);
+  }
+  // whether tile u (wb <= u < wb + 128) is a skipped chunk (never, without the mask)
+  auto skipped = [&](int64_t u) -> bool {
+    if constexpr (!MASK) {
+      return false;
+    } else {
+      const int64_t i = u - wb;
+      return i < 64 ? ((mw0 >> i) & 1) != 0 : ((mw1 >> (i - 64)) & 1) != 0;
+    }
+  };
   const int slice = R::slice_of(wave);
   const int irow = 16 * slice + l16;   // W row (feature i) held by this lane, slice waves
 
@@ -730,10 +766,11 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   if (stage_parity >= 0) {
     const int u = stage_parity;
     if (u < ntiles) {
-      load_tile<BF16>(st, src, etap, bhT, u * BT, T, lane, mrow);
-      store_tile<BF16, LN>(st, sm.ring[u], u * BT, T, lane, sb, silu != 0);
+      load_tile<BF16>(st, src, etap, bhT, u * BT, T, lane, skipped(u));
+      store_tile<BF16, LN>(st, sm.ring[u], u * BT, T, lane, sb, silu != 0, skipped(u));
     }
-    if (u + 2 < ntiles) load_tile<BF16>(st, src, etap, bhT, (u + 2) * BT, T, lane, mrow);
+    if (u + 2 < ntiles)
+      load_tile<BF16>(st, src, etap, bhT, (u + 2) * BT, T, lane, skipped(u + 2));
   }
   __syncthreads();
   // z of tile 0 and its coefficients
@@ -784,8 +821,17 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
 
   for (int64_t c = 0; c <= ntiles; ++c) {
     __syncthreads();   // S_c
+    if constexpr (MASK) {
+      // a period asks about tiles c-1 .. c+3
+      if (c - 1 == wb + 64) {
+        wb += 64;
+        mw0 = mw1;
+        mw1 = mask_bits(wb + 64);
+      }
+    }
     const bool live = c < ntiles;
-    if (DUAL && ln_half >= 0 && live) {
+    const bool skip_p = c >= 1 && skipped(c - 1), skip_c = skipped(c), skip_n = skipped(c + 1);
+    if (DUAL && ln_half >= 0 && live && !skip_c) {
       if (c == 0) dual_prefetch<BF16>(din, sm.ring[0], lane, ln_t0);
       dual_ln_pass<BF16, LN>(sm, din, sm.Dt[c & 1], lane, ln_t0, gam, eps);
     }
@@ -800,19 +846,21 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       if (c >= 1) {
         // outputs of tile c-1 and the update W_c = W_{c-1} - E_{c-1}^T K_{c-1}
         const auto& tp = sm.ring[(c - 1) % RING];
-        if (c == ntiles) Ereg = tok_e(c - 1);   // no z of a next tile was formed
-        if constexpr (!R::kTokInSlices) {
-          const float4 m4 = *reinterpret_cast<const float4*>(&sm.Mg[(c - 1) & 1][l16][4 * G]);
-          const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
-          make_tok(Mreg, mv);
+        if (c == ntiles && !skip_p) Ereg = tok_e(c - 1);   // no z of a next tile was formed
+        if (!skip_p) {
+          if constexpr (!R::kTokInSlices) {
+            const float4 m4 = *reinterpret_cast<const float4*>(&sm.Mg[(c - 1) & 1][l16][4 * G]);
+            const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
+            make_tok(Mreg, mv);
+          }
+          U = tok_mul(Mreg, Ereg, U);
         }
-        U = tok_mul(Mreg, Ereg, U);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 4 * G + r;
           sm.Ob[(c - 1) & 1][t][irow] = U[r] * tp.SG[t][irow];
         }
-        update_w(Wt, tp, Ereg, lane, l16, G);
+        if (!skip_p) update_w(Wt, tp, Ereg, lane, l16, G);
       }
       if (REC && live) {
         float* w = rec_W + ((bh * ntiles + c) * D + irow) * D + 4 * G;
@@ -827,17 +875,19 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         const auto& tn = sm.ring[(c + 1) % RING];
         if constexpr (BF16) {
           const WOps w = split_w(Wt);
-          if (c + 1 < ntiles) P = rows_times_wt(krows(tn), w, lane);
+          if (c + 1 < ntiles && !skip_n) P = rows_times_wt(krows(tn), w, lane);
           U = rows_times_wt(qrows(tc), w, lane);
         } else {
-          if (c + 1 < ntiles) P = rows_times_wt(krows(tn), Wt, l16, G);
+          if (c + 1 < ntiles && !skip_n) P = rows_times_wt(krows(tn), Wt, l16, G);
           U = rows_times_wt(qrows(tc), Wt, l16, G);
         }
         if constexpr (R::kTokInSlices) {
-          float m[4];
-          tok_m(tc, m);
-          make_tok(Mreg, m);
-          if (c + 1 < ntiles) {
+          if (!skip_c) {
+            float m[4];
+            tok_m(tc, m);
+            make_tok(Mreg, m);
+          }
+          if (c + 1 < ntiles && !skip_c && !skip_n) {
             float x[4];
             tok_x(tc, tn, x);
             make_tok(Xreg, x);
@@ -853,9 +903,9 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         if ((c & 1) == stage_parity) {
           if (c + 2 < ntiles)
             store_tile<BF16, LN>(st, sm.ring[(c + 2) % RING], (c + 2) * BT, T, lane, sb,
-                                 silu != 0);
+                                 silu != 0, skipped(c + 2));
         } else if (c + 3 < ntiles) {
-          load_tile<BF16>(st, src, etap, bhT, (c + 3) * BT, T, lane, mrow);
+          load_tile<BF16>(st, src, etap, bhT, (c + 3) * BT, T, lane, skipped(c + 3));
         }
       }
       if (wave == R::kOutWave && c >= 2)
@@ -867,13 +917,13 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         for (int t = 0; t < rows; ++t) dst[t * D] = sm.Dt[(c - 1) & 1][lane][t];
       }
       if constexpr (!R::kTokInSlices) {
-        if (wave == R::kStageEven && live) {
+        if (wave == R::kStageEven && live && !skip_c) {
           float m[4];
           tok_m(sm.ring[c % RING], m);
           *reinterpret_cast<float4*>(&sm.Mg[c & 1][l16][4 * G]) =
               make_float4(m[0], m[1], m[2], m[3]);
         }
-        if (wave == R::kStageOdd && c + 1 < ntiles) {
+        if (wave == R::kStageOdd && c + 1 < ntiles && !skip_c && !skip_n) {
           float x[4];
           tok_x(sm.ring[c % RING], sm.ring[(c + 1) % RING], x);
           *reinterpret_cast<float4*>(&sm.Xg[l16][4 * G]) = make_float4(x[0], x[1], x[2], x[3]);
@@ -895,22 +945,28 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
     }
     __syncthreads();   // G_c
     // the LayerNorm waves load their inputs of tile c+1 while the slices form z
-    if (ln_half >= 0 && c + 1 < ntiles) {
+    if (ln_half >= 0 && c + 1 < ntiles && !skip_n) {
       if constexpr (DUAL)
         dual_prefetch<BF16>(din, sm.ring[(c + 1) % RING], lane, ln_t0);
       else
         serial_prefetch<BF16>(sin, sm.ring[(c + 1) % RING], sm.Cd[(c + 1) & 1], lane);
     }
-    // z of tile c+1: K_{c+1} W_c^T - (K_{c+1} K_c^T) E_c
+    // z of tile c+1: K_{c+1} W_c^T - (K_{c+1} K_c^T) E_c (E_c of a skipped
+    // tile is zero; a skipped tile c+1 needs no z)
     if (slice >= 0 && c + 1 < ntiles) {
-      Ereg = tok_e(c);
-      if constexpr (!R::kTokInSlices) {
-        const float4 x4 = *reinterpret_cast<const float4*>(&sm.Xg[l16][4 * G]);
-        const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
-        make_tok(Xreg, xv);
+      if (!skip_c) Ereg = tok_e(c);
+      if (!skip_n) {
+        f32x4 Z = P;
+        if (!skip_c) {
+          if constexpr (!R::kTokInSlices) {
+            const float4 x4 = *reinterpret_cast<const float4*>(&sm.Xg[l16][4 * G]);
+            const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
+            make_tok(Xreg, xv);
+          }
+          Z = tok_mul(Xreg, Ereg, P);
+        }
+        *reinterpret_cast<float4*>(&sm.Zt[irow][4 * G]) = make_float4(Z[0], Z[1], Z[2], Z[3]);
       }
-      const f32x4 Z = tok_mul(Xreg, Ereg, P);
-      *reinterpret_cast<float4*>(&sm.Zt[irow][4 * G]) = make_float4(Z[0], Z[1], Z[2], Z[3]);
     }
   }
   __syncthreads();
@@ -935,6 +991,16 @@ hipError_t launch_one(const ScanArgs& a, hipStream_t s) {
                        static_cast<int>(a.H), a.T, a.eps, a.rec_delta, a.rec_W, a.upd_mask,
                        a.silu_qk ? 1 : 0);
     return hipGetLastError();
+  }
+  if constexpr (DUAL) {
+    if (a.upd_mask != nullptr) {
+      hipLaunchKernelGGL((scan_mfma_kernel<BF16, LN, true, false, true>),
+                         dim3(static_cast<unsigned>(a.B * a.H)), dim3(NT), 0, s, a.q, a.k, a.v,
+                         a.eta_logit, a.gate_logit, a.W0, a.gamma, a.beta, a.out, a.W_final,
+                         static_cast<int>(a.H), a.T, a.eps, static_cast<float*>(nullptr),
+                         static_cast<float*>(nullptr), a.upd_mask, a.silu_qk ? 1 : 0);
+      return hipGetLastError();
+    }
   }
   hipLaunchKernelGGL((scan_mfma_kernel<BF16, LN, DUAL, false>), dim3(static_cast<unsigned>(a.B * a.H)),
                      dim3(NT), 0, s, a.q, a.k, a.v, a.eta_logit, a.gate_logit, a.W0, a.gamma,
