@@ -75,17 +75,32 @@ proj_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                  void* __restrict__ v, void* __restrict__ gate, void* __restrict__ eta,
                  int64_t M, int64_t T, int hidden, int H, int ne, int64_t head_blocks) {
   __shared__ ProjSmem sm;
-  // Blocks [0, head_blocks) are (token tile, head) in token-tile-major order:
-  // blocks are dealt round-robin over the 8 XCDs, so when H is a multiple of
-  // 8 XCD x takes heads x, x + 8, ... of every token tile, its share of the
-  // weights stays in its L2 and consecutive blocks on it share their x rows.
+  // Blocks [0, head_blocks) are the (token tile, head) tiles.  Blocks are
+  // dealt round-robin over the 8 XCDs (block b to XCD b % 8), and an XCD runs
+  // one block per CU, about 32 at a time.  The tiles are listed in
+  // supertiles of 4 token tiles x 8 heads (smaller at the ragged edges) and
+  // XCD x takes one contiguous range of that list, so the blocks it runs
+  // together share 4 x tiles and 8 heads' weights through its L2: each x
+  // element is fetched about H/8 times chip-wide and each weight element
+  // about (token tiles)/4 times, instead of 8 and H/2-ish times with the
+  // tiles dealt one by one.  Any dealing still covers every tile once.
   // The eta tiles follow, (token tile, group of 256 heads).
   const bool eta_tile = int64_t(blockIdx.x) >= head_blocks;
   int64_t mt;
   int h = 0, e0 = 0;
   if (!eta_tile) {
-    mt = int64_t(blockIdx.x) / H;
-    h = static_cast<int>(int64_t(blockIdx.x) % H);
+    const int64_t b = blockIdx.x, n = head_blocks;
+    const int64_t xcd = b % 8, j = b / 8;
+    const int64_t wi = xcd * (n / 8) + min(xcd, n % 8) + j;   // position in the list
+    const int64_t nmt = n / H;
+    const int64_t ga = wi / (4 * int64_t(H));                  // token-tile group
+    const int64_t r = wi - ga * 4 * H;
+    const int na = static_cast<int>(min<int64_t>(4, nmt - 4 * ga));
+    const int64_t gb = r / (8 * na);                            // head group
+    const int r2 = static_cast<int>(r - gb * 8 * na);
+    const int nb = static_cast<int>(min<int64_t>(8, H - 8 * gb));
+    mt = 4 * ga + r2 / nb;
+    h = static_cast<int>(8 * gb) + r2 % nb;
   } else {
     const int64_t e = int64_t(blockIdx.x) - head_blocks;
     mt = e / ne;
