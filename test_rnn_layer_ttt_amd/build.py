@@ -29,14 +29,19 @@ CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
           "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
+#: kernel names (as the library reports them) whose source file is named otherwise
+KERNEL_SOURCES = {"mlp_mfma": "scan_mlp_mfma", "mlp_valu": "scan_mlp_valu"}
+
+
 def source_digest(kernel: str | None = None) -> str:
     """SHA-256 identifying a build: over one kernel's source and the shared
-    kernel header (``kernel`` = "scan_mfma", "bwd_mfma", "scan_valu"), or over
-    every source and the public header (``kernel`` = None)."""
+    kernel header (``kernel`` = "scan_mfma", "bwd_mfma", "scan_valu",
+    "mlp_mfma", ...), or over every source and the public header
+    (``kernel`` = None)."""
     import hashlib
     h = hashlib.sha256()
     if kernel is not None:
-        names = [kernel + ".hip", "scan_common.h"]
+        names = [KERNEL_SOURCES.get(kernel, kernel) + ".hip", "scan_common.h"]
     else:
         names = sorted(os.listdir(CSRC))
     for name in names:

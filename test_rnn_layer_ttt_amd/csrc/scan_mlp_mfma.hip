@@ -21,33 +21,37 @@
 // (the last line takes the chunk-end W2 and adds back the updates of the
 // chunk's later tokens, so the output product runs after the update).
 //
-// One workgroup of four waves owns one (batch, head) scan; wave w runs on
-// SIMD w and owns hidden units 16w..16w+15 and outputs 16w..16w+15.  The
-// weights stay fp32 in MFMA accumulator tiles: in the 16x16 accumulator
-// layout lane l holds X[4(l/16) + r][l % 16], r = 0..3, which is also the B
-// operand of X and the A operand of X^T for a 16x16x16 product whose
-// contraction runs over X's row index (and two such tiles side by side feed
-// a 16x16x32 product).  Each wave therefore holds W1 as W1^T tiles (rows:
-// inputs, contracted by P1 k and P1 q), and W2 twice: as W2^T tiles (rows:
-// hidden units, contracted by P2 a) and as W2 tiles (rows: outputs,
-// contracted by P2^T delta).  Both copies of W2 take the same update.
+// One workgroup owns one (batch, head) scan; block w covers hidden units
+// 16w..16w+15 and outputs 16w..16w+15.  The weights stay fp32 in MFMA
+// accumulator tiles: in the 16x16 accumulator layout lane l holds
+// X[4(l/16) + r][l % 16], r = 0..3, which is also the B operand of X and the
+// A operand of X^T for a 16-deep product whose contraction runs over X's row
+// index (and two such tiles side by side feed a 32-deep product).  W1 is held
+// as W1^T tiles (rows: inputs, contracted by P1 k and P1 q), and W2 twice: as
+// W2^T tiles (rows: hidden units, contracted by P2 a) and as W2 tiles (rows:
+// outputs, contracted by P2^T delta).  Both copies of W2 take the same update.
 // Activations are formed with the tokens as rows (H^T = K^T P1^T, DA^T =
 // Delta^T P2), the orientation the rank-16 updates contract over; what other
 // waves need crosses LDS, written once and read in the layout each product
 // wants.
 //
-// Precision: every product runs on bf16 MFMA (16x16x32, 16x16x16) with fp32
+// Precision: every product runs on the bf16 16x16x32 MFMA with fp32
 // accumulation; fp32 operands (weights, activations, errors, Gram entries)
 // are split into bf16 hi + lo parts and only the lo*lo term (~2^-17
 // relative) is dropped; the bf16 inputs are exact.  The LayerNorm, SiLU and
 // gating run in fp32 on the vector ALUs.
 //
-// Per chunk c, three barriers:
-//   X_c  A_c = silu(H_c) and aq_{c-1} in LDS: each wave forms Z_c for its
-//        outputs and the previous chunk's outputs Y_{c-1}
-//   Z_c  Z_c in LDS: each wave runs the LayerNorm of four tokens, writes Delta
-//   D_c  Delta_c in LDS: DA^T, DH, the three weight updates, HQ_c and aq_c,
-//        then H_{c+1} with the updated W1; inputs two chunks ahead are staged
+// Eight waves, two per SIMD: on SIMD w a hidden-side wave holds W1^T and W2
+// for hidden block w and runs the chain of a chunk, and an output-side wave
+// holds W2^T for output block w, forms z and the outputs, and stages the
+// inputs.  Per chunk c, three barriers:
+//   X_c  a_c and aq_{c-1} in LDS: output-side Z_c; hidden-side the W2 update
+//        of chunk c-1 (off the chain) and (P1 Q)^T, G1 of chunk c
+//   Z_c  Z_c in LDS: hidden-side the LayerNorm of four tokens each, Delta out;
+//        output-side the in-chunk output term of chunk c-1
+//   D_c  Delta_c in LDS: hidden-side DA^T, DH, the W1 update, the next chunk's
+//        a, HQ_c and aq_c; output-side the outputs of chunk c-1 (W2 before
+//        this chunk's update), the W2^T update, the staging two chunks ahead
 #include "scan_common.h"
 
 namespace ttt {
@@ -55,7 +59,7 @@ namespace {
 
 constexpr int D = 64;
 constexpr int BT = 16;       // tokens per chunk
-constexpr int NT = 256;      // four waves
+constexpr int NT = 512;      // eight waves, two per SIMD
 constexpr int RING = 3;      // staged input chunks in LDS
 constexpr int APAD = 72;     // padded bf16 row of the [token][unit] activation tiles
 
@@ -166,10 +170,10 @@ struct alignas(16) Smem {
   // activations a (and aq) by [token][unit] (hi, lo) and a by [unit][token]
   uint16_t A1[2][2][BT][APAD];   // [chunk parity][hi/lo]
   uint16_t A2[2][2][D][BT];      // [chunk parity][hi/lo]
-  uint16_t AQ[2][BT][APAD];      // [hi/lo]
+  uint16_t AQ[2][2][BT][APAD];   // [chunk parity][hi/lo]
   float Z[BT][D];                // z by [token][output]
   uint16_t DS[2][BT][APAD];      // delta by [token][output] (hi, lo)
-  uint16_t DT[2][D][BT];         // -eta delta by [output][token] (hi, lo)
+  uint16_t DT[2][2][D][BT];      // -eta delta by [output][token] ([chunk parity][hi/lo])
 };
 
 // ---------------------------------------------------------------------------
@@ -269,39 +273,47 @@ mlp_mfma_kernel(const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp
   __shared__ Smem sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;          // wave: hidden block and output block
+  const int wv = tid >> 6;
+  const int w = wv & 3;            // the block of hidden units and of outputs
+  const bool hid = wv < 4;         // hidden-side wave (else output-side), both on SIMD w
   const int n = lane & 15;
   const int g = lane >> 4;
   const int64_t bh = blockIdx.x;
   const int h = static_cast<int>(bh % H);
   const int64_t nc = (T + BT - 1) / BT;
 
-  const int a_ld = tid >> 6;   // the array this wave stages: q, k, v, gate
-  const uint16_t* src = (a_ld == 0 ? qp : a_ld == 1 ? kp : a_ld == 2 ? vp : gatep) + bh * T * D;
+  // output-side waves stage the inputs: wave 4 + a stages array a (q, k, v, gate)
+  const int stid = tid - 4 * 64;
+  const uint16_t* src = (w == 0 ? qp : w == 1 ? kp : w == 2 ? vp : gatep) + bh * T * D;
   const uint16_t* eta = etap + bh * T;
   float* dst_out = out + bh * T * D;
   const float* w1 = W1_0 + bh * D * D;
   const float* w2 = W2_0 + bh * D * D;
 
   // ---- weights in accumulator tiles
-  // p1t[jb][r] = W1[16w + n][16jb + 4g + r]   (W1^T: rows inputs, cols own hidden)
-  // p2t[ub][r] = W2[16w + n][16ub + 4g + r]   (W2^T: rows hidden, cols own outputs)
-  // p2n[ib][r] = W2[16ib + 4g + r][16w + n]   (W2: rows outputs, cols own hidden)
+  // hidden-side:  p1t[jb][r] = W1[16w + n][16jb + 4g + r]  (W1^T: rows inputs, own hidden cols)
+  //               p2n[ib][r] = W2[16ib + 4g + r][16w + n]  (W2: rows outputs, own hidden cols)
+  // output-side:  p2t[ub][r] = W2[16w + n][16ub + 4g + r]  (W2^T: rows hidden, own output cols)
   f32x4 p1t[4], p2t[4], p2n[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const float4 x = *reinterpret_cast<const float4*>(w1 + (16 * w + n) * D + 16 * b + 4 * g);
-    const float4 y = *reinterpret_cast<const float4*>(w2 + (16 * w + n) * D + 16 * b + 4 * g);
-    p1t[b] = f32x4{x.x, x.y, x.z, x.w};
-    p2t[b] = f32x4{y.x, y.y, y.z, y.w};
+    if (hid) {
+      const float4 x = *reinterpret_cast<const float4*>(w1 + (16 * w + n) * D + 16 * b + 4 * g);
+      p1t[b] = f32x4{x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p2n[b][r] = w2[(16 * b + 4 * g + r) * D + 16 * w + n];
+      for (int r = 0; r < 4; ++r) p2n[b][r] = w2[(16 * b + 4 * g + r) * D + 16 * w + n];
+      p2t[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    } else {
+      const float4 y = *reinterpret_cast<const float4*>(w2 + (16 * w + n) * D + 16 * b + 4 * g);
+      p2t[b] = f32x4{y.x, y.y, y.z, y.w};
+      p1t[b] = p2n[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
   }
 
   // LayerNorm affine of the four features a lane handles in the LayerNorm
   // pass (features 4n..4n+3)
   float gam[4] = {1.0f, 1.0f, 1.0f, 1.0f}, bet[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if constexpr (LN != kLnNone) {
+  if (LN != kLnNone && hid) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       gam[e] = gamma[h * D + 4 * n + e];
@@ -337,7 +349,8 @@ mlp_mfma_kernel(const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp
     return acc;
   };
   // a = silu(h) of this wave's hidden units, to LDS in both layouts; s' = silu'(h)
-  auto activate_and_share = [&](const f32x4& ht, f32x4& at, f32x4& spt, int par) {
+  auto activate_and_share = [&](const f32x4& ht, f32x4& spt, int par) {
+    f32x4 at;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float x = ht[r];
@@ -354,28 +367,34 @@ mlp_mfma_kernel(const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp
     st4(&sm.A2[par][0][16 * w + n][4 * g], o.hi);
     st4(&sm.A2[par][1][16 * w + n][4 * g], o.lo);
   };
-
-  // ---- the outputs of chunk cp (rows own outputs, cols tokens):
-  // Y = W2 aq + sum_{s>t} eta_s delta_s (a_s . aq_t), gated, stored
-  auto outputs = [&](int64_t cp, const Op32 (&p2)[2]) {
-    const int par = static_cast<int>(cp & 1);
-    const Chunk& ck = sm.ring[cp % RING];
-    // one accumulation chain per half of the contraction
-    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    f32x4 y2[2], g22[2];
+  // A operand of W2 for the own outputs (contraction over hidden units)
+  auto w2_operands = [&](Op32 (&p2)[2]) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const Op32 aq = act_op(sm.AQ, ks, n, g);
-      const Op32 as = act_op(sm.A1[par], ks, n, g);
-      y2[ks] = prod3(p2[ks], aq, zero);
-      g22[ks] = prod3(as, aq, zero);    // G2[s][t] = a_s . aq_t
-    }
-    f32x4 y = y2[0] + y2[1], g2 = g22[0] + g22[1];
+    for (int ks = 0; ks < 2; ++ks) p2[ks] = op32(p2t[2 * ks], p2t[2 * ks + 1]);
+  };
+
+  // ---- the outputs of chunk cp (rows own outputs, cols tokens), from W2 after
+  // chunk cp's update: Y = W2 aq + sum_{s>t} eta_s delta_s (a_s . aq_t), gated.
+  // The in-chunk term and the W2 product run in different stages.
+  auto outputs_inchunk = [&](int64_t cp) -> f32x4 {
+    const int par = static_cast<int>(cp & 1);
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 g22[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)       // G2[s][t] = a_s . aq_t
+      g22[ks] = prod3(act_op(sm.A1[par], ks, n, g), act_op(sm.AQ[par], ks, n, g), zero);
+    f32x4 g2 = g22[0] + g22[1];
     // strictly later tokens only, negated (DT holds -eta delta)
 #pragma unroll
     for (int r = 0; r < 4; ++r) g2[r] = (4 * g + r > n) ? -g2[r] : 0.0f;
-    const Op16 dt = col_op(sm.DT, w, n, g);
-    y = prod3_16(dt, op16(g2), y);
+    return prod3_16(col_op(sm.DT[par], w, n, g), op16(g2), zero);
+  };
+  auto outputs = [&](int64_t cp, const Op32 (&p2)[2], const f32x4& inchunk) {
+    const int par = static_cast<int>(cp & 1);
+    const Chunk& ck = sm.ring[cp % RING];
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4 y = prod3(p2[0], act_op(sm.AQ[par], 0, n, g), zero) +
+                    prod3(p2[1], act_op(sm.AQ[par], 1, n, g), zero) + inchunk;
     const int64_t t = cp * BT + n;
     if (t < T) {
       const float4 gl = *reinterpret_cast<const float4*>(&ck.SG[n][16 * w + 4 * g]);
@@ -385,25 +404,28 @@ mlp_mfma_kernel(const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp
     }
   };
 
-  // ---- prologue: chunks 0 and 1 staged, chunk 2 in flight
+  // ---- prologue: chunks 0 and 1 staged, chunk 2 in flight (output-side waves)
   Stage st;
-  load_chunk(st, src, eta, 0, T, tid);
-  store_chunk(st, sm.ring[0], 0, T, tid);
-  if (nc > 1) {
-    load_chunk(st, src, eta, BT, T, tid);
-    store_chunk(st, sm.ring[1], BT, T, tid);
+  if (!hid) {
+    load_chunk(st, src, eta, 0, T, stid);
+    store_chunk(st, sm.ring[0], 0, T, stid);
+    if (nc > 1) {
+      load_chunk(st, src, eta, BT, T, stid);
+      store_chunk(st, sm.ring[1], BT, T, stid);
+    }
+    if (nc > 2) load_chunk(st, src, eta, 2 * BT, T, stid);
   }
-  if (nc > 2) load_chunk(st, src, eta, 2 * BT, T, tid);
   __syncthreads();
 
-  f32x4 at, spt, hq0t, g1t;   // a^T, silu'(h)^T, (P1 Q)^T and G1^T of the current chunk
-  {
-    Op32 p1[2];
-    w1_operands(p1);
-    const f32x4 ht = keys_times_w1(sm.ring[0].KA, p1);
-    hq0t = keys_times_w1(sm.ring[0].QA, p1);
-    g1t = gram_kq(sm.ring[0]);
-    activate_and_share(ht, at, spt, 0);
+  // hidden-side state of the current chunk: silu'(h)^T, (P1 Q)^T and G1^T;
+  // output-side: W2's A operand, split once per update, and the in-chunk
+  // output term of the previous chunk
+  f32x4 spt = {0.0f, 0.0f, 0.0f, 0.0f}, hq0t = spt, g1t = spt, yin = spt;
+  Op32 p2op[2], p1op[2];   // W2's and W1's operands, split once per update
+  if (!hid) w2_operands(p2op);
+  if (hid) {
+    w1_operands(p1op);
+    activate_and_share(keys_times_w1(sm.ring[0].KA, p1op), spt, 0);
   }
   __syncthreads();
 
@@ -411,24 +433,29 @@ mlp_mfma_kernel(const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp
     const int par = static_cast<int>(c & 1);
     const Chunk& ck = sm.ring[c % RING];
 
-    // ---- X_c: Z_c for the own outputs; the previous chunk's outputs
-    {
-      Op32 p2[2];
+    // ---- X_c: a_c in LDS
+    if (hid) {
+      // W2 (rows outputs, own hidden cols) -= eta Delta A^T of the previous chunk
+      if (c > 0) {
+        const int pp = par ^ 1;
+        const Op16 oa = col_op(sm.A2[pp], w, n, g);   // a_{t}[own hidden], by token rows
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        // A operand of W2 (rows own outputs, contraction over hidden units)
-        p2[ks] = op32(p2t[2 * ks], p2t[2 * ks + 1]);
+        for (int b = 0; b < 4; ++b) p2n[b] = prod3_16(col_op(sm.DT[pp], b, n, g), oa, p2n[b]);
       }
+      // (P1 Q)^T and G1^T of this chunk, with W1 at its start
+      hq0t = keys_times_w1(ck.QA, p1op);
+      g1t = gram_kq(ck);
+    } else {
       const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-      const f32x4 z = prod3(p2[0], act_op(sm.A1[par], 0, n, g), zero) +
-                      prod3(p2[1], act_op(sm.A1[par], 1, n, g), zero);
+      const f32x4 z = prod3(p2op[0], act_op(sm.A1[par], 0, n, g), zero) +
+                      prod3(p2op[1], act_op(sm.A1[par], 1, n, g), zero);
       *reinterpret_cast<float4*>(&sm.Z[n][16 * w + 4 * g]) = make_float4(z[0], z[1], z[2], z[3]);
-      if (c > 0) outputs(c - 1, p2);
     }
     __syncthreads();
 
-    // ---- Z_c: LayerNorm of tokens 4w..4w+3 (lane: token 4w + g, features 4n..4n+3)
-    {
+    // ---- Z_c: the LayerNorm (hidden-side waves, tokens 4w..4w+3); the
+    // previous chunk's in-chunk output term (output-side waves)
+    if (hid) {
       const int t = 4 * w + g;
       const float4 z4 = *reinterpret_cast<const float4*>(&sm.Z[t][4 * n]);
       const float4 v4 = *reinterpret_cast<const float4*>(&ck.V[t][4 * n]);
@@ -482,15 +509,17 @@ mlp_mfma_kernel(const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp
       st4(&sm.DS[1][t][4 * n], od.lo);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sm.DT[0][4 * n + e][t] = static_cast<uint16_t>(oe.hi[e]);
-        sm.DT[1][4 * n + e][t] = static_cast<uint16_t>(oe.lo[e]);
+        sm.DT[par][0][4 * n + e][t] = static_cast<uint16_t>(oe.hi[e]);
+        sm.DT[par][1][4 * n + e][t] = static_cast<uint16_t>(oe.lo[e]);
       }
+    } else if (c > 0) {
+      yin = outputs_inchunk(c - 1);
     }
     __syncthreads();
 
-    // ---- D_c: back-propagation, updates, this chunk's aq, the next chunk's h
-    {
-      // DA^T = Delta^T P2 (rows tokens, cols own hidden units), at the chunk-start W2
+    // ---- D_c: Delta_c in LDS
+    if (hid) {
+      // DA^T = Delta^T P2 (rows tokens, own hidden cols), at the chunk-start W2
       const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
       const f32x4 dat = prod3(act_op(sm.DS, 0, n, g), op32(p2n[0], p2n[1]), zero) +
                         prod3(act_op(sm.DS, 1, n, g), op32(p2n[2], p2n[3]), zero);
@@ -499,6 +528,15 @@ mlp_mfma_kernel(const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp
 #pragma unroll
       for (int r = 0; r < 4; ++r) edh[r] = ck.ETA[4 * g + r] * (dat[r] * spt[r]);
       const Op16 oedh = op16(edh);
+      // W1^T (rows inputs, own hidden cols) -= K eta DH^T  (KT holds -K^T)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const i16x4 kt = ld4(ck.KT[b][lane]);
+        p1t[b] = mfma32(cat8(kt, kt), cat8(oedh.hi, oedh.lo), p1t[b]);
+      }
+      // the next chunk's a with the updated W1
+      w1_operands(p1op);
+      if (c + 1 < nc) activate_and_share(keys_times_w1(sm.ring[(c + 1) % RING].KA, p1op), spt, par ^ 1);
       // HQ^T = (P1 Q)^T - G1 (eta DH^T), s <= t; aq = silu(HQ)
       {
         f32x4 gm;
@@ -511,63 +549,37 @@ mlp_mfma_kernel(const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp
         const Op16 o = op16(aqt);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          sm.AQ[0][4 * g + r][16 * w + n] = static_cast<uint16_t>(o.hi[r]);
-          sm.AQ[1][4 * g + r][16 * w + n] = static_cast<uint16_t>(o.lo[r]);
+          sm.AQ[par][0][4 * g + r][16 * w + n] = static_cast<uint16_t>(o.hi[r]);
+          sm.AQ[par][1][4 * g + r][16 * w + n] = static_cast<uint16_t>(o.lo[r]);
         }
       }
-      // W2 (rows outputs, own hidden cols) -= eta Delta A^T
-      const Op16 oa = op16(at);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) p2n[b] = prod3_16(col_op(sm.DT, b, n, g), oa, p2n[b]);
+    } else {
+      // the previous chunk's outputs, from W2 before this chunk's update
+      if (c > 0) outputs(c - 1, p2op, yin);
       // W2^T (rows hidden, own output cols) -= A eta Delta^T
-      {
-        const Op16 od = col_op(sm.DT, w, n, g);
-        // B operand: -eta delta of the own outputs by token rows: lane holds
-        // [t = 4g + e][i = 16w + n], which is DT[16w + n][4g + e]
+      const Op16 od = col_op(sm.DT[par], w, n, g);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) p2t[b] = prod3_16(col_op(sm.A2[par], b, n, g), od, p2t[b]);
-      }
-      // W1^T (rows inputs, own hidden cols) -= K eta DH^T  (KT holds -K^T)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const i16x4 kt = ld4(ck.KT[b][lane]);
-        p1t[b] = mfma32(cat8(kt, kt), cat8(oedh.hi, oedh.lo), p1t[b]);
-      }
-      // the next chunk's h with the updated W1, and its (P1 Q)^T and G1^T
-      if (c + 1 < nc) {
-        const Chunk& cn = sm.ring[(c + 1) % RING];
-        Op32 p1[2];
-        w1_operands(p1);
-        const f32x4 ht = keys_times_w1(cn.KA, p1);
-        hq0t = keys_times_w1(cn.QA, p1);
-        g1t = gram_kq(cn);
-        activate_and_share(ht, at, spt, par ^ 1);
-      }
+      for (int b = 0; b < 4; ++b) p2t[b] = prod3_16(col_op(sm.A2[par], b, n, g), od, p2t[b]);
+      w2_operands(p2op);
       // stage chunk c + 2, load chunk c + 3
       if (c + 2 < nc) {
-        store_chunk(st, sm.ring[(c + 2) % RING], (c + 2) * BT, T, tid);
-        if (c + 3 < nc) load_chunk(st, src, eta, (c + 3) * BT, T, tid);
+        store_chunk(st, sm.ring[(c + 2) % RING], (c + 2) * BT, T, stid);
+        if (c + 3 < nc) load_chunk(st, src, eta, (c + 3) * BT, T, stid);
       }
     }
     __syncthreads();
   }
 
-  // ---- the last chunk's outputs
-  if (nc > 0) {
-    Op32 p2[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) p2[ks] = op32(p2t[2 * ks], p2t[2 * ks + 1]);
-    outputs(nc - 1, p2);
-  }
-
-  if (W1_final != nullptr) {
+  // ---- the last chunk's outputs, the final weights
+  if (!hid && nc > 0) outputs(nc - 1, p2op, outputs_inchunk(nc - 1));
+  if (hid && W1_final != nullptr) {
     float* o = W1_final + bh * D * D;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
       *reinterpret_cast<float4*>(o + (16 * w + n) * D + 16 * b + 4 * g) =
           make_float4(p1t[b][0], p1t[b][1], p1t[b][2], p1t[b][3]);
   }
-  if (W2_final != nullptr) {
+  if (!hid && W2_final != nullptr) {
     float* o = W2_final + bh * D * D;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
