@@ -71,7 +71,8 @@ extern "C" {
                              matrix-core kernel applies (d = 64): the kernel the
                              scan's specification names for the per-token mode,
                              kept callable for comparison; same results within
-                             rounding.  Not accepted by the recording forward */
+                             rounding.  Given to the recording forward and the
+                             backward, it selects their vector-ALU kernels too */
 
 /* status codes */
 #define TTT_OK               0
@@ -148,16 +149,20 @@ int32_t ttt_linear_forward_masked(const void* q, const void* k, const void* v,
  * differentiation through each step of the recurrence above (the models of
  * "Edifice.Recurrent.TTT" and "PonderTTT" train the layer end to end).  It
  * walks the sequence backwards in tiles of 16 tokens, from a record that the
- * forward leaves behind: delta_t for every token and W at the start of every
- * tile (16 KiB per tile and (b,h) at d = 64).
+ * forward leaves behind: delta_t for every token and the running W before
+ * every 16th token (16 KiB per tile and (b,h) at d = 64; in the dual form this
+ * W includes the updates of the chunk's tokens so far).
  *
- * Supported: d = 64, the per-token modes (straight-through, TTT_LN_EXACT,
- * TTT_NO_LN) and the dual form with chunk == 16 (its chunks are then the
- * tiles: every z of a chunk is taken at the chunk's first W, "TTT-Linear",
- * dual form), fp32 or bf16 inputs.  TTT_DUAL with another chunk gives
- * TTT_ERR_UNSUPPORTED.  A chunk that ttt_linear_forward_masked would skip is
- * trained by giving its tokens eta_logit = -inf in both calls: the step size
- * sigmoid(-inf) = 0 makes the forward identical, and its deta_logit is 0.
+ * Supported: every d and mode of ttt_linear_forward (d = 16, 32, 64, 128; the
+ * per-token modes straight-through, TTT_LN_EXACT and TTT_NO_LN, and the dual
+ * form with any chunk >= 1, where every z of a chunk is taken at the chunk's
+ * first W, "PonderTTT", dual-form updates), fp32 or bf16 inputs, with or
+ * without TTT_SILU_QK.  d = 64, per token or with chunk == 16, runs on the
+ * matrix cores, the rest on the vector ALUs (ttt_linear_backward_kernel says
+ * which); both record the same quantities, so a record of either forward
+ * serves either backward.  A chunk that ttt_linear_forward_masked would skip
+ * is trained by giving its tokens eta_logit = -inf in both calls: the step
+ * size sigmoid(-inf) = 0 makes the forward identical, and its deta_logit is 0.
  *
  * The record is one caller-owned device buffer of ttt_linear_record_bytes()
  * bytes, 16-byte aligned; its contents are private to the library.  The
@@ -179,7 +184,8 @@ int32_t ttt_linear_record_bytes(int64_t B, int64_t H, int64_t T, int64_t d, uint
 
 /*
  * ttt_linear_forward (same arguments, same results: out and W_final are
- * identical to its) that also fills `record` for ttt_linear_backward.
+ * identical to its, for the same mode) that also fills `record` for
+ * ttt_linear_backward.
  * `record` is written, so it must not overlap any other argument.  T == 0
  * writes no record (its size is then 0 and it may be NULL) and copies W0 to
  * W_final as the forward does.
@@ -232,6 +238,13 @@ int32_t ttt_linear_backward(const void* q, const void* k, const void* v,
  */
 int32_t ttt_linear_backward_workspace_bytes(int64_t B, int64_t H, int64_t d, uint32_t mode,
                                             int64_t* bytes);
+
+/*
+ * Which kernel ttt_linear_backward runs for this d, mode and chunk:
+ * "bwd_mfma" (matrix cores), "bwd_valu" (vector ALUs), or "none" when the
+ * combination is rejected.  A static string; makes no HIP call.
+ */
+const char* ttt_linear_backward_kernel(int64_t d, uint32_t mode, int64_t chunk);
 
 /*
  * ttt_linear_backward for callers that cannot allocate device memory (code

@@ -12,7 +12,8 @@ from .binding import (TTT_DUAL, TTT_ERR_ALIAS, TTT_ERR_HIP, TTT_ERR_MODE, TTT_ER
                       TTT_IN_BF16, TTT_LN_EXACT, TTT_NO_LN, TTT_OK, TTT_SILU_QK,
                       TTT_STATIC_SCRATCH_BYTES, TTTArgumentError, TTTError, backward, check,
                       forward, forward_record, load_library, mlp_forward, mode_bits, project,
-                      ttt_linear, ttt_linear_backward, ttt_linear_backward_noalloc,
+                      ttt_linear, ttt_linear_backward, ttt_linear_backward_kernel,
+                      ttt_linear_backward_noalloc,
                       ttt_linear_backward_workspace_bytes, ttt_linear_forward,
                       ttt_linear_forward_masked, ttt_linear_forward_record, ttt_linear_kernel,
                       ttt_linear_project, ttt_linear_record_bytes, ttt_linear_validate,
@@ -24,7 +25,8 @@ __all__ = ["TTT_DUAL", "TTT_ERR_ALIAS", "TTT_ERR_HIP", "TTT_ERR_MODE", "TTT_ERR_
            "TTT_IN_BF16", "TTT_LN_EXACT", "TTT_NO_LN", "TTT_OK", "TTT_SILU_QK",
            "TTT_STATIC_SCRATCH_BYTES", "TTTArgumentError", "TTTError", "backward", "check",
            "forward", "forward_record", "load_library", "mlp_forward", "mode_bits", "project",
-           "ttt_linear", "ttt_linear_backward", "ttt_linear_backward_noalloc",
+           "ttt_linear", "ttt_linear_backward", "ttt_linear_backward_kernel",
+           "ttt_linear_backward_noalloc",
            "ttt_linear_backward_workspace_bytes", "ttt_linear_forward",
            "ttt_linear_forward_masked", "ttt_linear_forward_record", "ttt_linear_kernel",
            "ttt_linear_project", "ttt_linear_record_bytes", "ttt_linear_validate",

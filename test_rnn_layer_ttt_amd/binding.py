@@ -39,7 +39,7 @@ TTT_ERR_WORKSPACE = 7
 RECORD_CHUNK = 16
 
 #: every symbol the header declares
-EXPORTED = ("ttt_linear_backward", "ttt_linear_backward_noalloc",
+EXPORTED = ("ttt_linear_backward", "ttt_linear_backward_kernel", "ttt_linear_backward_noalloc",
             "ttt_linear_backward_workspace_bytes",
             "ttt_linear_forward", "ttt_linear_forward_masked",
             "ttt_linear_forward_record", "ttt_linear_project",
@@ -97,6 +97,8 @@ def load_library(path: str = LIB_PATH, check_digest: bool = True) -> ctypes.CDLL
         ctypes.c_uint32, ctypes.c_int64]
     lib.ttt_linear_kernel.restype = ctypes.c_char_p
     lib.ttt_linear_kernel.argtypes = [ctypes.c_int64, ctypes.c_uint32, ctypes.c_int64]
+    lib.ttt_linear_backward_kernel.restype = ctypes.c_char_p
+    lib.ttt_linear_backward_kernel.argtypes = [ctypes.c_int64, ctypes.c_uint32, ctypes.c_int64]
     lib.ttt_status_string.restype = ctypes.c_char_p
     lib.ttt_status_string.argtypes = [ctypes.c_int32]
     lib.ttt_mlp_forward.restype = ctypes.c_int32
@@ -142,6 +144,12 @@ def ttt_status_string(status: int) -> str:
 def ttt_linear_kernel(d: int, mode: int, chunk: int) -> str:
     """Name of the kernel family a valid call with these settings launches."""
     return load_library().ttt_linear_kernel(int(d), ctypes.c_uint32(int(mode)), int(chunk)).decode()
+
+
+def ttt_linear_backward_kernel(d: int, mode: int, chunk: int) -> str:
+    """Name of the kernel ttt_linear_backward runs with these settings."""
+    return load_library().ttt_linear_backward_kernel(int(d), ctypes.c_uint32(int(mode)),
+                                                     int(chunk)).decode()
 
 
 def ttt_version() -> str:
@@ -452,14 +460,15 @@ def project(x, w_proj, b_proj=None, *, out_bf16: bool = True, stream=None):
 
 def forward_record(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *,
                    ln: str = "st", out=None, W_final=None, record=None, stream=None,
-                   silu_qk: bool = False, dual: bool = False):
-    """:func:`forward` (d = 64; per-token modes, or ``dual=True`` with chunks of
-    16) that also returns the record the backward reads: ``(out, W_final,
-    record)``, the record a uint8 device tensor."""
+                   silu_qk: bool = False, dual: bool = False, chunk: int = RECORD_CHUNK,
+                   force_valu: bool = False):
+    """:func:`forward` that also returns the record the backward reads:
+    ``(out, W_final, record)``, the record a uint8 device tensor.  Every d and
+    mode of :func:`forward` (``chunk`` is the dual form's)."""
     import torch
 
     B, H, T, d = _check_inputs(q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln)
-    mode = mode_bits(ln, dual, q.dtype == torch.bfloat16, silu_qk)
+    mode = mode_bits(ln, dual, q.dtype == torch.bfloat16, silu_qk, force_valu)
     st, nbytes = ttt_linear_record_bytes(B, H, T, d, mode)
     check(st)
     if out is None:
@@ -474,15 +483,16 @@ def forward_record(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *,
         _ptr(q), _ptr(k), _ptr(v), _ptr(eta_logit), _ptr(gate_logit), W0.data_ptr(),
         _ptr(gamma) if ln != "none" else None, _ptr(beta) if ln != "none" else None,
         _ptr(out), W_final.data_ptr(), record.data_ptr(), record.numel() * record.element_size(),
-        B, H, T, d, mode, RECORD_CHUNK if dual else 1, stream.cuda_stream))
+        B, H, T, d, mode, chunk if dual else 1, stream.cuda_stream))
     return out, W_final, record
 
 
 def backward(q, k, v, eta_logit, gate_logit, gamma, beta, record, dout, dW_final=None, *,
              ln: str = "st", stream=None, silu_qk: bool = False, dual: bool = False,
-             workspace=None):
+             chunk: int = RECORD_CHUNK, workspace=None, force_valu: bool = False):
     """Gradients from a record of :func:`forward_record` (same ``ln``,
-    ``silu_qk`` and ``dual``) and dL/dout (float32 [B,H,T,d]), dL/dW_final
+    ``silu_qk``, ``dual`` and ``chunk``; ``force_valu`` runs the vector-ALU
+    backward where the matrix-core one applies) and dL/dout (float32 [B,H,T,d]), dL/dW_final
     (float32 [B,H,d,d] or None).  Returns a dict with dq, dk, dv, dgate_logit,
     deta_logit, dW0, dgamma, dbeta (float32; the last two None with
     ``ln="none"``).  ``workspace``: a uint8 device tensor of at least
@@ -504,7 +514,7 @@ def backward(q, k, v, eta_logit, gate_logit, gamma, beta, record, dout, dW_final
              dbeta=None if ln == "none" else torch.empty((H, d), **f32))
     if stream is None:
         stream = torch.cuda.current_stream(dev)
-    mode = mode_bits(ln, dual, q.dtype == torch.bfloat16, silu_qk)
+    mode = mode_bits(ln, dual, q.dtype == torch.bfloat16, silu_qk, force_valu)
     st, ws_bytes = ttt_linear_backward_workspace_bytes(B, H, d, mode)
     check(st)
     if workspace is None:
@@ -516,7 +526,7 @@ def backward(q, k, v, eta_logit, gate_logit, gamma, beta, record, dout, dW_final
         workspace.numel() * workspace.element_size(), _ptr(dout),
         None if dW_final is None else dW_final.data_ptr(), _ptr(g["dq"]), _ptr(g["dk"]),
         _ptr(g["dv"]), _ptr(g["deta_logit"]), _ptr(g["dgate_logit"]), g["dW0"].data_ptr(),
-        _ptr(g["dgamma"]), _ptr(g["dbeta"]), B, H, T, d, mode, RECORD_CHUNK if dual else 1,
+        _ptr(g["dgamma"]), _ptr(g["dbeta"]), B, H, T, d, mode, chunk if dual else 1,
         stream.cuda_stream))
     return g
 
@@ -525,13 +535,12 @@ _autograd_fn = None
 
 
 def ttt_linear(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln: str = "st",
-               silu_qk: bool = False, dual: bool = False):
+               silu_qk: bool = False, dual: bool = False, chunk: int = RECORD_CHUNK):
     """Differentiable scan for torch autograd: ``(out, W_final)``.
 
     The forward is :func:`forward_record`; the backward is :func:`backward`
-    on the saved record.  d = 64: per-token modes, or the dual form with
-    chunks of 16 tokens.  Gradients come back in float32 (autograd casts them
-    to a bf16 input's dtype).
+    on the saved record.  Every d and mode of :func:`forward`.  Gradients come
+    back in float32 (autograd casts them to a bf16 input's dtype).
     """
     global _autograd_fn
     if _autograd_fn is None:
@@ -539,12 +548,15 @@ def ttt_linear(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln:
 
         class TTTLinearFunction(torch.autograd.Function):
             @staticmethod
-            def forward(ctx, q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln, silu_qk, dual):
+            def forward(ctx, q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln, silu_qk, dual,
+                        chunk):
                 out, W_final, record = forward_record(q, k, v, eta_logit, gate_logit, W0, gamma,
-                                                      beta, ln=ln, silu_qk=silu_qk, dual=dual)
+                                                      beta, ln=ln, silu_qk=silu_qk, dual=dual,
+                                                      chunk=chunk)
                 ctx.ln = ln
                 ctx.silu_qk = silu_qk
                 ctx.dual = dual
+                ctx.chunk = chunk
                 ctx.save_for_backward(q, k, v, eta_logit, gate_logit, gamma, beta, record)
                 return out, W_final
 
@@ -557,11 +569,12 @@ def ttt_linear(q, k, v, eta_logit, gate_logit, W0, gamma=None, beta=None, *, ln:
                 g = backward(q, k, v, eta_logit, gate_logit, gamma, beta, record,
                              dout.contiguous().float(),
                              None if dW_final is None else dW_final.contiguous().float(),
-                             ln=ctx.ln, silu_qk=ctx.silu_qk, dual=ctx.dual)
+                             ln=ctx.ln, silu_qk=ctx.silu_qk, dual=ctx.dual, chunk=ctx.chunk)
                 return (g["dq"], g["dk"], g["dv"], g["deta_logit"], g["dgate_logit"], g["dW0"],
-                        g["dgamma"], g["dbeta"], None, None, None)
+                        g["dgamma"], g["dbeta"], None, None, None, None)
 
         _autograd_fn = TTTLinearFunction
     if ln == "none":
         gamma = beta = None
-    return _autograd_fn.apply(q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln, silu_qk, dual)
+    return _autograd_fn.apply(q, k, v, eta_logit, gate_logit, W0, gamma, beta, ln, silu_qk, dual,
+                              chunk)

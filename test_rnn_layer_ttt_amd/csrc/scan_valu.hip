@@ -20,6 +20,11 @@
 // The output uses the updated weight through o = W_{t-1} q - eta*delta (k.q),
 // which equals W_t q exactly in real arithmetic and keeps the rank-1 update
 // off the output's dependency chain.
+//
+// The recording instantiation (REC) also writes what the backward replays:
+// delta_t of every token (staged in LDS with the outputs, written per tile)
+// and the running W before every 16th token (in the dual form too, where it
+// includes the chunk's updates so far).
 #include "scan_common.h"
 
 #include <type_traits>
@@ -77,7 +82,7 @@ __device__ __forceinline__ void unpack16(const uint4& w, float* f) {
   }
 }
 
-template <int D, bool BF16, int LN, bool DUAL>
+template <int D, bool BF16, int LN, bool DUAL, bool REC>
 __global__ void __launch_bounds__(4 * D)
 scan_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
                  const void* __restrict__ vp, const void* __restrict__ etap,
@@ -85,7 +90,8 @@ scan_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
                  const float* __restrict__ gamma, const float* __restrict__ beta,
                  float* __restrict__ out, float* __restrict__ W_final,
                  int H, int64_t T, int64_t chunk, float eps,
-                 const uint8_t* __restrict__ upd_mask, int silu) {
+                 const uint8_t* __restrict__ upd_mask, int silu,
+                 float* __restrict__ rec_delta, float* __restrict__ rec_W) {
   using In = typename std::conditional<BF16, uint16_t, float>::type;
   constexpr int NT = 4 * D;               // threads
   constexpr int NW = NT / 64;             // waves
@@ -96,12 +102,14 @@ scan_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   constexpr int NV = (NVEC + NT - 1) / NT;
   constexpr int NE = (TT + NT - 1) / NT;   // eta values per thread per tile
   constexpr float kInvD = 1.0f / D;
+  static_assert(TT % kRecTile == 0, "a tile must hold whole recorded-W intervals");
 
   __shared__ __align__(16) float sK[kTileElems];
   __shared__ __align__(16) float sQ[kTileElems];
   __shared__ __align__(16) float sV[kTileElems];
   __shared__ __align__(16) float sG[kTileElems];   // sigmoid(gate_logit)
   __shared__ __align__(16) float sO[kTileElems];
+  __shared__ __align__(16) float sDel[REC ? kTileElems : 4];   // delta_t, recorded
   __shared__ float sEta[TT];                       // sigmoid(eta_logit) / d
   __shared__ float2 sRed[2][2][NW];                // [reduction][token parity][wave]
 
@@ -122,6 +130,7 @@ scan_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
   const uint8_t* mrow =
       (DUAL && upd_mask != nullptr) ? upd_mask + bh * ((T + chunk - 1) / chunk) : nullptr;
   float* dst_out = out + bh * T * D;
+  const int64_t nrec = (T + kRecTile - 1) / kRecTile;   // recorded W per scan
 
   float W[C];
   float Wc[DUAL ? C : 1];
@@ -271,6 +280,16 @@ scan_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
     if (tile + 1 < ntiles) load_tile(tile + 1);
     const int nt = static_cast<int>(T - tile * TT < TT ? T - tile * TT : TT);
     for (int tt = 0; tt < nt; ++tt) {
+      if constexpr (REC) {
+        // W before token tile*TT + tt, at every 16th token (TT is a multiple of 16)
+        if (tt % kRecTile == 0) {
+          float4* w4 = reinterpret_cast<float4*>(
+              rec_W + ((bh * nrec + (tile * TT + tt) / kRecTile) * D + row) * D + seg * C);
+#pragma unroll
+          for (int c = 0; c < C / 4; ++c)
+            w4[c] = make_float4(W[4 * c], W[4 * c + 1], W[4 * c + 2], W[4 * c + 3]);
+        }
+      }
       if constexpr (DUAL) {
         if (ck == 0) {
 #pragma unroll
@@ -324,7 +343,10 @@ scan_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
 #pragma unroll
       for (int c = 0; c < C; ++c) W[c] = fmaf(-ci, kv[c], W[c]);
       const float o = fmaf(-ci, kq, u) * gi;
-      if (seg == 0) sO[tt * D + row] = o;
+      if (seg == 0) {
+        sO[tt * D + row] = o;
+        if constexpr (REC) sDel[tt * D + row] = delta;
+      }
       par ^= 1;
     }
     __syncthreads();
@@ -333,6 +355,11 @@ scan_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       float4* o4 = reinterpret_cast<float4*>(dst_out + tile * TT * D);
       const float4* s4 = reinterpret_cast<const float4*>(sO);
       for (int i = tid; i < nvec_out; i += NT) o4[i] = s4[i];
+      if constexpr (REC) {
+        float4* d4 = reinterpret_cast<float4*>(rec_delta + (bh * T + tile * TT) * D);
+        const float4* sd4 = reinterpret_cast<const float4*>(sDel);
+        for (int i = tid; i < nvec_out; i += NT) d4[i] = sd4[i];
+      }
     }
     if (tile + 1 < ntiles) store_tile();
     __syncthreads();
@@ -350,10 +377,16 @@ template <int D, bool BF16, int LN, bool DUAL>
 hipError_t launch_one(const ScanArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.B * a.H));
   const dim3 block(4 * D);
-  hipLaunchKernelGGL((scan_valu_kernel<D, BF16, LN, DUAL>), grid, block, 0, s, a.q, a.k, a.v,
-                     a.eta_logit, a.gate_logit, a.W0, a.gamma, a.beta, a.out, a.W_final,
-                     static_cast<int>(a.H), a.T, a.dual ? a.chunk : int64_t(1), a.eps,
-                     a.upd_mask, a.silu_qk ? 1 : 0);
+  if (a.rec_delta != nullptr)
+    hipLaunchKernelGGL((scan_valu_kernel<D, BF16, LN, DUAL, true>), grid, block, 0, s, a.q, a.k,
+                       a.v, a.eta_logit, a.gate_logit, a.W0, a.gamma, a.beta, a.out, a.W_final,
+                       static_cast<int>(a.H), a.T, a.dual ? a.chunk : int64_t(1), a.eps,
+                       a.upd_mask, a.silu_qk ? 1 : 0, a.rec_delta, a.rec_W);
+  else
+    hipLaunchKernelGGL((scan_valu_kernel<D, BF16, LN, DUAL, false>), grid, block, 0, s, a.q,
+                       a.k, a.v, a.eta_logit, a.gate_logit, a.W0, a.gamma, a.beta, a.out,
+                       a.W_final, static_cast<int>(a.H), a.T, a.dual ? a.chunk : int64_t(1),
+                       a.eps, a.upd_mask, a.silu_qk ? 1 : 0, nullptr, nullptr);
   return hipGetLastError();
 }
 

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <mutex>
 
+#include "bwd_valu.h"
 #include "scan_common.h"
 
 namespace {
@@ -145,7 +146,7 @@ int32_t record_layout(int64_t B, int64_t H, int64_t T, int64_t d, uint32_t mode,
   if (mode & ~kKnownModes) return TTT_ERR_MODE;
   if ((mode & TTT_LN_EXACT) && (mode & TTT_NO_LN)) return TTT_ERR_MODE;
   if (B < 1 || H < 1 || d < 1 || T < 0) return TTT_ERR_SHAPE;
-  if (d != 64) return TTT_ERR_UNSUPPORTED;
+  if (d != 16 && d != 32 && d != 64 && d != 128) return TTT_ERR_UNSUPPORTED;
   const int64_t ntiles = (T + ttt::kRecTile - 1) / ttt::kRecTile;
   int64_t BH, per_scan, a, b;
   if (!mul_ok(B, H, &BH) || BH > INT32_MAX) return TTT_ERR_SHAPE;
@@ -158,6 +159,17 @@ int32_t record_layout(int64_t B, int64_t H, int64_t T, int64_t d, uint32_t mode,
   r->w_off = BH * a * 4;
   r->bytes = elems * 4;
   return TTT_OK;
+}
+
+// the backward kernel of a validated call: the matrix-core one for d = 64, per
+// token or with chunks of kRecTile tokens; the vector-ALU one otherwise
+bool runs_bwd_mfma(int64_t d, uint32_t mode, int64_t chunk) {
+  return d == 64 && !(mode & TTT_FORCE_VALU) && (!(mode & TTT_DUAL) || chunk == ttt::kRecTile);
+}
+
+hipError_t launch_backward(const ttt::BwdArgs& a, uint32_t mode, hipStream_t s) {
+  return runs_bwd_mfma(a.d, mode, a.chunk) ? ttt::launch_bwd_mfma(a, s)
+                                           : ttt::launch_bwd_valu(a, s);
 }
 
 // bytes of the backward's scratch: per-(b,h) dgamma, dbeta before the batch sum
@@ -188,8 +200,6 @@ int32_t validate_forward_record(const void* q, const void* k, const void* v,
   if (st != TTT_OK) return st;
   st = validate_record(record, record_bytes, B, H, T, d, mode, r);
   if (st != TTT_OK) return st;
-  if (a->dual && a->chunk != ttt::kRecTile) return TTT_ERR_UNSUPPORTED;   // chunks = tiles
-  if (a->force_valu) return TTT_ERR_UNSUPPORTED;   // the record is the matrix-core kernel's
   const int64_t in_size = (mode & TTT_IN_BF16) ? 2 : 4;
   const int64_t seq = B * H * T * d, w = B * H * d * d;
   const Range rec = span(record, r->bytes);
@@ -229,7 +239,6 @@ int32_t validate_backward(const void* q, const void* k, const void* v, const voi
   int32_t st = record_layout(B, H, T, d, mode, &r);
   if (st != TTT_OK) return st;
   const bool dual = (mode & TTT_DUAL) != 0;
-  if (dual && chunk != ttt::kRecTile) return TTT_ERR_UNSUPPORTED;
   const bool no_ln = (mode & TTT_NO_LN) != 0;
   const bool bf16 = (mode & TTT_IN_BF16) != 0;
   // pointers
@@ -594,7 +603,7 @@ extern "C" int32_t ttt_linear_backward_noalloc(
     if (static_scratch(&p) != hipSuccess || p == nullptr) return TTT_ERR_HIP;
     a.gb_part = static_cast<float*>(p);
   }
-  const hipError_t err = ttt::launch_bwd_mfma(a, static_cast<hipStream_t>(stream));
+  const hipError_t err = launch_backward(a, mode, static_cast<hipStream_t>(stream));
   if (err == hipErrorNotSupported) return TTT_ERR_UNSUPPORTED;
   return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
@@ -630,8 +639,9 @@ extern "C" int32_t ttt_linear_forward_record(const void* q, const void* k, const
     }
     return TTT_OK;
   }
-  if (!ttt::scan_mfma_supports(a)) return TTT_ERR_UNSUPPORTED;
-  return ttt::launch_scan_mfma(a, s) == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+  // either kernel records the same quantities
+  const hipError_t err = runs_mfma(a) ? ttt::launch_scan_mfma(a, s) : ttt::launch_scan_valu(a, s);
+  return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }
 
 extern "C" int32_t ttt_linear_backward(const void* q, const void* k, const void* v,
@@ -651,9 +661,16 @@ extern "C" int32_t ttt_linear_backward(const void* q, const void* k, const void*
                                        dq, dk, dv, deta_logit, dgate_logit, dW0, dgamma, dbeta,
                                        B, H, T, d, mode, chunk, &a);
   if (st != TTT_OK) return st;
-  const hipError_t err = ttt::launch_bwd_mfma(a, static_cast<hipStream_t>(stream));
+  const hipError_t err = launch_backward(a, mode, static_cast<hipStream_t>(stream));
   if (err == hipErrorNotSupported) return TTT_ERR_UNSUPPORTED;
   return err == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+}
+
+extern "C" const char* ttt_linear_backward_kernel(int64_t d, uint32_t mode, int64_t chunk) {
+  RecordLayout r;
+  if (record_layout(1, 1, 1, d, mode, &r) != TTT_OK || ((mode & TTT_DUAL) && chunk < 1))
+    return "none";
+  return runs_bwd_mfma(d, mode, chunk) ? "bwd_mfma" : "bwd_valu";
 }
 
 extern "C" const char* ttt_linear_kernel(int64_t d, uint32_t mode, int64_t chunk) {

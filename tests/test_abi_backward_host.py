@@ -24,9 +24,10 @@ def rec_bytes(B=B, H=H, T=T, d=D, mode=0):
 
 
 @pytest.mark.parametrize("B_,H_,T_", [(1, 1, 0), (1, 1, 1), (2, 3, 16), (2, 3, 17), (4, 32, 16384)])
-def test_record_bytes_formula(B_, H_, T_):
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+def test_record_bytes_formula(B_, H_, T_, d):
     ntiles = -(-T_ // 16)
-    assert rec_bytes(B_, H_, T_) == 4 * B_ * H_ * (T_ * 64 + ntiles * 64 * 64)
+    assert rec_bytes(B_, H_, T_, d) == 4 * B_ * H_ * (T_ * d + ntiles * d * d)
 
 
 def ws_bytes(B=B, H=H, d=D, mode=0):
@@ -41,10 +42,12 @@ def test_workspace_bytes_formula(mode):
     # per (b,h): dgamma and dbeta before their sum over the batch
     assert ws_bytes(B, H, D, mode) == 4 * B * H * 2 * 64
     assert ws_bytes(B, H, D, (mode & ~ttt.TTT_LN_EXACT) | ttt.TTT_NO_LN) == 0
+    assert ws_bytes(B, H, 16, mode) == 4 * B * H * 2 * 16
 
 
 @pytest.mark.parametrize("over,code", [
-    (dict(d=32), ttt.TTT_ERR_UNSUPPORTED),
+    (dict(d=48), ttt.TTT_ERR_UNSUPPORTED),
+    (dict(d=256), ttt.TTT_ERR_UNSUPPORTED),
     (dict(mode=1 << 10), ttt.TTT_ERR_MODE),
     (dict(B=0), ttt.TTT_ERR_SHAPE),
 ])
@@ -63,8 +66,8 @@ def test_record_bytes_independent_of_dtype_ln_and_form(mode):
 
 
 @pytest.mark.parametrize("over,code", [
-    (dict(d=32), ttt.TTT_ERR_UNSUPPORTED),
-    (dict(d=128), ttt.TTT_ERR_UNSUPPORTED),
+    (dict(d=48), ttt.TTT_ERR_UNSUPPORTED),
+    (dict(d=8), ttt.TTT_ERR_UNSUPPORTED),
     (dict(mode=1 << 10), ttt.TTT_ERR_MODE),
     (dict(mode=ttt.TTT_LN_EXACT | ttt.TTT_NO_LN), ttt.TTT_ERR_MODE),
     (dict(B=0), ttt.TTT_ERR_SHAPE),
@@ -108,14 +111,16 @@ needs_no_gpu = pytest.mark.skipif(_GPU, reason="sends unlaunchable arguments to 
     (dict(record=A + 2 * S + 4096), ttt.TTT_ERR_ALIAS),     # record inside v
     (dict(record=A + 9 * S), ttt.TTT_ERR_ALIAS),            # record == W_final
     (dict(record=A + 5 * S), ttt.TTT_ERR_ALIAS),            # record == W0
-    (dict(mode=ttt.TTT_DUAL, chunk=8), ttt.TTT_ERR_UNSUPPORTED),    # chunks must be the tiles
-    (dict(mode=ttt.TTT_DUAL, chunk=32), ttt.TTT_ERR_UNSUPPORTED),
     (dict(mode=ttt.TTT_DUAL, chunk=0), ttt.TTT_ERR_MODE),
-    (dict(d=32), ttt.TTT_ERR_UNSUPPORTED),
+    (dict(d=48), ttt.TTT_ERR_UNSUPPORTED),
     (dict(q=None), ttt.TTT_ERR_NULL),                       # the forward's own checks first
     (dict(out=A), ttt.TTT_ERR_ALIAS),
     (dict(mode=ttt.TTT_LN_EXACT | ttt.TTT_NO_LN), ttt.TTT_ERR_MODE),
-    (dict(mode=ttt.TTT_FORCE_VALU), ttt.TTT_ERR_UNSUPPORTED),   # records only on the MFMA scan
+    # any chunk, d and the vector-ALU kernel record too: these reach the record's checks
+    (dict(mode=ttt.TTT_DUAL, chunk=8, record_bytes=1), ttt.TTT_ERR_WORKSPACE),
+    (dict(mode=ttt.TTT_DUAL, chunk=100, record_bytes=1), ttt.TTT_ERR_WORKSPACE),
+    (dict(d=16, record_bytes=rec_bytes(d=16) - 4), ttt.TTT_ERR_WORKSPACE),
+    (dict(mode=ttt.TTT_FORCE_VALU, record=A + 8 * S), ttt.TTT_ERR_ALIAS),
 ])
 def test_forward_record_rejects(over, code):
     assert fwd_call(**over) == code
@@ -191,10 +196,11 @@ def test_backward_alias_rejected(over):
 
 @needs_no_gpu
 @pytest.mark.parametrize("over,code", [
-    (dict(mode=ttt.TTT_DUAL, chunk=8), ttt.TTT_ERR_UNSUPPORTED),
-    (dict(mode=ttt.TTT_DUAL, chunk=1), ttt.TTT_ERR_UNSUPPORTED),
+    (dict(mode=ttt.TTT_DUAL, chunk=8, record_bytes=1), ttt.TTT_ERR_WORKSPACE),
+    (dict(mode=ttt.TTT_DUAL, chunk=1, workspace_bytes=0), ttt.TTT_ERR_WORKSPACE),
     (dict(mode=ttt.TTT_DUAL, chunk=0), ttt.TTT_ERR_MODE),
-    (dict(d=16), ttt.TTT_ERR_UNSUPPORTED),
+    (dict(d=48), ttt.TTT_ERR_UNSUPPORTED),
+    (dict(d=16, record_bytes=rec_bytes(d=16) - 4), ttt.TTT_ERR_WORKSPACE),
     (dict(record_bytes=rec_bytes() - 4), ttt.TTT_ERR_WORKSPACE),
     (dict(workspace_bytes=ws_bytes() - 4), ttt.TTT_ERR_WORKSPACE),
     (dict(workspace_bytes=0), ttt.TTT_ERR_WORKSPACE),
@@ -241,7 +247,8 @@ def test_noalloc_backward_checks_like_the_backward_and_bounds_its_scratch():
     # the argument checks of the backward ...
     assert nb(dq=None) == ttt.TTT_ERR_NULL
     assert nb(dq=A) == ttt.TTT_ERR_ALIAS
-    assert nb(mode=ttt.TTT_DUAL, chunk=8) == ttt.TTT_ERR_UNSUPPORTED
+    assert nb(d=48) == ttt.TTT_ERR_UNSUPPORTED
+    assert nb(mode=ttt.TTT_DUAL, chunk=0) == ttt.TTT_ERR_MODE
     # ... and the static scratch's bound: 4096 scans at d = 64 fit, 4097 do not
     assert ttt.TTT_STATIC_SCRATCH_BYTES == 2 * 1024 * 1024
     big = dict(B=4097, H=1, T=1, record_bytes=rec_bytes(4097, 1, 1))
@@ -258,3 +265,21 @@ def test_noalloc_backward_checks_like_the_backward_and_bounds_its_scratch():
 def test_status_string_of_workspace_error():
     s = ttt.ttt_status_string(ttt.TTT_ERR_WORKSPACE)
     assert "record" in s and "workspace" in s
+
+
+@pytest.mark.parametrize("d,mode,chunk,kernel", [
+    (64, 0, 1, "bwd_mfma"),
+    (64, ttt.TTT_LN_EXACT | ttt.TTT_IN_BF16, 1, "bwd_mfma"),
+    (64, ttt.TTT_DUAL, 16, "bwd_mfma"),
+    (64, ttt.TTT_DUAL, 8, "bwd_valu"),
+    (64, ttt.TTT_DUAL, 32, "bwd_valu"),
+    (64, ttt.TTT_FORCE_VALU, 1, "bwd_valu"),
+    (16, 0, 1, "bwd_valu"),
+    (32, ttt.TTT_NO_LN, 1, "bwd_valu"),
+    (128, ttt.TTT_DUAL | ttt.TTT_LN_EXACT, 5, "bwd_valu"),
+    (48, 0, 1, "none"),
+    (64, ttt.TTT_DUAL, 0, "none"),
+    (64, ttt.TTT_LN_EXACT | ttt.TTT_NO_LN, 1, "none"),
+])
+def test_backward_kernel_routing(d, mode, chunk, kernel):
+    assert ttt.ttt_linear_backward_kernel(d, mode, chunk) == kernel
