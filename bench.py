@@ -98,7 +98,8 @@ def backward_work(x):
     scan dL/dW_final in and dW0 out; per head gamma, beta in and their
     gradients out.  Flops: the 12 d^2 of the per-token gradient algebra
     (G_t k_t, G_t^T delta_t, W_{t-1}^T dz_t, W_t^T dy_t and the two rank-one
-    updates of G).
+    updates of G); the replays of W a backward kernel makes from the record
+    are its own choice and not counted.
     """
     B, H, T, d = x.q.shape
     n = B * H * T
@@ -106,12 +107,6 @@ def backward_work(x):
     per_tok_bytes = (4 * d + 1) * s_in + 4 * d + 4 * d + (d * d) // 4 + 16 * d + 4
     nbytes = n * per_tok_bytes + B * H * 8 * d * d + H * 16 * d
     return n, nbytes, n * 12 * d * d
-
-
-def ttt_record_chunk():
-    """Tokens per tile of the training record (the dual form's chunk must match)."""
-    from test_rnn_layer_ttt_amd.binding import RECORD_CHUNK
-    return RECORD_CHUNK
 
 
 def kernel_name(x, force_valu=False):
@@ -181,7 +176,7 @@ def roofline(x, kernel_ms, traffic, train=False, mask=None, project=False,
             cbound, cpeak = "alu", FP32_VECTOR_PEAK_TFLOPS
     elif train:
         n, nbytes, flops = backward_work(x)
-        name, cbound, cpeak = "bwd_mfma", "alu", FP32_VECTOR_PEAK_TFLOPS
+        name, cbound, cpeak = kernel or "bwd_mfma", "alu", FP32_VECTOR_PEAK_TFLOPS
     else:
         n, nbytes, flops = algorithmic_work(x, mask)
         name = kernel or kernel_name(x)
@@ -342,6 +337,11 @@ def main():
     ap.add_argument("--mlp", action="store_true",
                     help="the scan with the two-layer inner model W2 silu(W1 x) "
                          "(ttt_mlp_forward)")
+    ap.add_argument("--chunk", type=int, default=None,
+                    help="run the workload in the dual form with chunks of this many tokens")
+    ap.add_argument("--force-valu", action="store_true",
+                    help="run the vector-ALU kernels (TTT_FORCE_VALU) where the matrix-core "
+                         "ones would apply")
     ap.add_argument("--update-rate", type=float, default=None,
                     help="dual-form workloads: seeded SKIP/UPDATE decisions per chunk, each "
                          "UPDATE with this probability (ttt_linear_forward_masked)")
@@ -378,15 +378,17 @@ def main():
         x, W1_np = make_mlp_inputs(args.workload)
     else:
         x = make_inputs(args.workload)
+    if args.chunk is not None:
+        if args.chunk < 1 or args.mlp:
+            print("bench.py: --chunk takes a chunk >= 1 and the linear inner model",
+                  file=sys.stderr)
+            sys.exit(2)
+        x.dual, x.chunk = True, args.chunk
     B, H, T, d = x.q.shape
     train = args.pass_ == "train"
     project = args.pass_ == "project"
     if project and (d != 64 or args.update_rate is not None or args.silu_qk):
         print("bench.py: --pass project covers d = 64 and the plain scan", file=sys.stderr)
-        sys.exit(2)
-    if train and ((x.dual and x.chunk != ttt_record_chunk()) or d != 64):
-        print(f"bench.py: the backward covers d = 64, per-token or dual form with chunks of "
-              f"{ttt_record_chunk()}; workload {args.workload} is not one", file=sys.stderr)
         sys.exit(2)
     if args.cpu_scans is None:
         args.cpu_scans = 128 if train else 32 if project else 256
@@ -426,7 +428,7 @@ def main():
     out = torch.empty((B, H, T, d), dtype=torch.float32, device=dev)
     Wf = torch.empty_like(W0)
     stream = torch.cuda.current_stream(dev)
-    mode = ttt.mode_bits(x.ln, x.dual, x.in_bf16, args.silu_qk)
+    mode = ttt.mode_bits(x.ln, x.dual, x.in_bf16, args.silu_qk, args.force_valu)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), el.data_ptr(), gl.data_ptr(),
             W0.data_ptr(), gamma.data_ptr(), beta.data_ptr(), out.data_ptr(), Wf.data_ptr())
     if project:
@@ -570,10 +572,14 @@ def main():
     copy_gbs = 2 * (1 << 30) / (float(np.median(copy_ms[1:])) / 1e3) / 1e9
 
     n_tok = B * H * T
-    kernel = ("bwd_mfma" if train else "proj_mfma" if project else
-              ttt.ttt_mlp_kernel(d, mode, x.chunk) if args.mlp else kernel_name(x))
+    kernel = (ttt.ttt_linear_backward_kernel(d, mode, x.chunk if x.dual else 1) if train else
+              "proj_mfma" if project else
+              ttt.ttt_mlp_kernel(d, mode, x.chunk) if args.mlp else
+              kernel_name(x, args.force_valu))
     traffic_key = args.workload + ("/backward" if train else "/project" if project else
                                    "/mlp" if args.mlp else "")
+    if args.chunk is not None:
+        traffic_key += f"/chunk{args.chunk}"
     if mask_np is not None:
         traffic_key = args.workload + f"/update{args.update_rate:g}"
     if args.silu_qk:

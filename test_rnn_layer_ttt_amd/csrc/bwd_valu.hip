@@ -54,9 +54,13 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
-// DPP controls: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_ror:4, row_ror:8
+// DPP controls: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_shl:4, row_shr:4,
+// row_ror:4, row_ror:8 (row = 16 lanes; row_shl:n reads lane + n, row_shr:n
+// lane - n, row_ror:8 pairs each lane with lane ^ 8)
 constexpr int kQuadXor1 = 0xB1;
 constexpr int kQuadXor2 = 0x4E;
+constexpr int kRowShl4 = 0x104;
+constexpr int kRowShr4 = 0x114;
 constexpr int kRowRor4 = 0x124;
 constexpr int kRowRor8 = 0x128;
 
@@ -66,36 +70,65 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x;
 }
 
+// v_permlane32_swap / v_permlane16_swap (vector ALU, no LDS round trip): for
+// registers a, b the pair (a', b') with a' + b' = a of this lane plus a of
+// lane ^ 32 (resp. ^ 16) where that bit of the lane is clear, and b of this
+// lane plus b of lane ^ 32 (^ 16) where it is set.
+__device__ __forceinline__ float swap32_sum(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap16_sum(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum over the 16 quads of a wave of a value that is uniform within each quad.
 __device__ __forceinline__ float quads_sum(float x) {
   x += dpp<kRowRor4>(x);
   x += dpp<kRowRor8>(x);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  x = swap16_sum(x, x);
+  return swap32_sum(x, x);
 }
 
 // One step of the column butterfly over the wave's 16 quads (quad bit
-// 3 - STAGE, lane distance M).  While a lane carries more than one column it
-// keeps half (the upper half where its bit is set) and adds the partner's
-// partial sums of that half; with one column left it adds the partner's.
+// 3 - STAGE, lane distance M = 32 >> STAGE).  While a lane carries more than
+// one column it keeps half (the upper half where its bit is set) and adds the
+// partner's partial sums of that half; with one column left it adds the
+// partner's.  Lane distances 32 and 16 exchange through the lane swaps, 8 and
+// 4 through DPP within the row.
 template <int N, int STAGE>
 __device__ __forceinline__ void col_step(float (&v)[N], int lane, int& off) {
   constexpr int M = 32 >> STAGE;
   constexpr int HAVE = (N >> STAGE) > 0 ? (N >> STAGE) : 1;
-  if constexpr (HAVE > 1) {
-    constexpr int HALF = HAVE / 2;
-    const bool hi = (lane & M) != 0;
+  constexpr int HALF = HAVE > 1 ? HAVE / 2 : 1;
+  const bool hi = (lane & M) != 0;
 #pragma unroll
-    for (int i = 0; i < HALF; ++i) {
-      const float send = hi ? v[i] : v[i + HALF];
-      const float keep = hi ? v[i + HALF] : v[i];
-      v[i] = keep + __shfl_xor(send, M);
+  for (int i = 0; i < HALF; ++i) {
+    const float a = v[i];
+    const float b = HAVE > 1 ? v[i + HALF] : v[i];
+    if constexpr (M == 32) {
+      v[i] = swap32_sum(a, b);
+    } else if constexpr (M == 16) {
+      v[i] = swap16_sum(a, b);
+    } else {
+      // keep = the half this lane sums, send = the half its partner sums; the
+      // DPP moves run on every lane (a DPP read of a lane masked off by a
+      // branch would return zero), the choices are selects
+      const float keep = hi ? b : a;
+      const float send = hi ? a : b;
+      if constexpr (M == 8) {
+        v[i] = keep + dpp<kRowRor8>(send);
+      } else {
+        const float from_above = dpp<kRowShl4>(send);   // lane + 4
+        const float from_below = dpp<kRowShr4>(send);   // lane - 4
+        v[i] = keep + (hi ? from_below : from_above);
+      }
     }
-    if (hi) off += HALF;
-  } else {
-    v[0] += __shfl_xor(v[0], M);
   }
+  if (HAVE > 1 && hi) off += HALF;
 }
 
 template <bool BF16>
@@ -259,6 +292,51 @@ bwd_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       return make_float2(mu, m2 * kInvD);
     }
   };
+  // The straight-through mode's one exchange per token: the LayerNorm
+  // statistics of z and the two sums its vector-Jacobian product needs,
+  // sum gamma dd and sum gamma dd (z - mu), together with sum delta (G k) for
+  // d eta.  Each wave sums over its rows with z shifted by one of its own
+  // entries c; the parts combine exactly (the shifts enter only through
+  // c - mu, a few standard deviations at most).  Returns mu, var and the three
+  // sums in *st.
+  auto st_round = [&](float z, float gdd, float dgk, float4* st) {
+    const float c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(z)));
+    const float y = z - c;
+    const float sy = quads_sum(y);
+    const float syy = quads_sum(y * y);
+    const float sa = quads_sum(gdd);
+    const float sb = quads_sum(gdd * y);
+    const float sd = quads_sum(dgk);
+    const float mw = fmaf(sy, 1.0f / kRowsPerWave, c);
+    const float m2w = fmaxf(fmaf(-sy, sy * (1.0f / kRowsPerWave), syy), 0.0f);
+    if constexpr (NW == 1) {
+      st[0] = make_float4(mw, m2w * kInvD, sa, fmaf(c - mw, sa, sb));
+      st[1].x = sd;
+    } else {
+      if (lane == 0) {
+        sRed[0][par][wave] = make_float4(mw, m2w, sa, sb);
+        sRed[1][par][wave] = make_float4(c, sd, 0.0f, 0.0f);
+      }
+      __syncthreads();
+      float mu = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) mu += sRed[0][par][w].x;
+      mu *= 1.0f / NW;
+      float m2 = 0.0f, ta = 0.0f, tb = 0.0f, td = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float4 x = sRed[0][par][w];
+        const float4 u = sRed[1][par][w];
+        const float dm = x.x - mu;
+        m2 += fmaf(kRowsPerWave * dm, dm, x.y);
+        ta += x.z;
+        tb += fmaf(u.x - mu, x.z, x.w);
+        td += u.y;
+      }
+      st[0] = make_float4(mu, m2 * kInvD, ta, tb);
+      st[1].x = td;
+    }
+  };
   // The wave's column sums of part (this thread's row, its C columns) into
   // sCol[which][wave][slot]; the lanes of a quad group that share a column
   // after the butterfly write it once.
@@ -389,37 +467,45 @@ bwd_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
       const int ri = tt * D + row;
       const float a = sA[tt];
       const float sg = sSG[ri], dout_i = sDO[ri], del = sDel[ri], vi = sV[ri];
-      float kv[C], qv[C], part[C];
+      float kv[C], part[C];
       lds_cols(sK + tt * D, kv);
-      lds_cols(sQ + tt * D, qv);
-      // the output: y = W_t q, dy = dout sigmoid(g); dq = W_t^T dy
+      const float4* q4 = reinterpret_cast<const float4*>(sQ + tt * D + seg * C);
+      // the output: y = W_t q, dy = dout sigmoid(g); dq = W_t^T dy; and
+      // G = dL/dW_t = (the gradient after t) + dy q^T
+      const float u = dout_i * sg;
       float y = 0.0f;
 #pragma unroll
-      for (int c = 0; c < C; ++c) y = fmaf(W[c], qv[c], y);
+      for (int c = 0; c < C / 4; ++c) {
+        const float4 x = q4[c];
+        y = fmaf(W[4 * c], x.x, y);
+        y = fmaf(W[4 * c + 1], x.y, y);
+        y = fmaf(W[4 * c + 2], x.z, y);
+        y = fmaf(W[4 * c + 3], x.w, y);
+        G[4 * c] = fmaf(u, x.x, G[4 * c]);
+        G[4 * c + 1] = fmaf(u, x.y, G[4 * c + 1]);
+        G[4 * c + 2] = fmaf(u, x.z, G[4 * c + 2]);
+        G[4 * c + 3] = fmaf(u, x.w, G[4 * c + 3]);
+      }
       y = quad_sum(y);
-      const float u = dout_i * sg;
       const float dgt = dout_i * y * sg * (1.0f - sg);
 #pragma unroll
       for (int c = 0; c < C; ++c) part[c] = W[c] * u;
       store_cols(part, 0, tt % PT);
-      // G = dL/dW_t, then the update's gradients
-#pragma unroll
-      for (int c = 0; c < C; ++c) G[c] = fmaf(u, qv[c], G[c]);
+      // the update's gradients
       float gk = 0.0f;
 #pragma unroll
       for (int c = 0; c < C; ++c) gk = fmaf(G[c], kv[c], gk);
       gk = quad_sum(gk);
       const float dd = -a * gk;   // d delta_t
       const float cd = a * del;
-#pragma unroll
-      for (int c = 0; c < C; ++c) part[c] = -cd * G[c];
-      // W_{t-1}
-#pragma unroll
-      for (int c = 0; c < C; ++c) W[c] = fmaf(cd, kv[c], W[c]);
-      // z = P k with P = W_{t-1}, or the chunk-start W
+      // part: -a G^T delta; W_{t-1}; z = P k with P = W_{t-1}, or the chunk-start W
       float z = 0.0f;
 #pragma unroll
-      for (int c = 0; c < C; ++c) z = fmaf(DUAL ? Wc[c] : W[c], kv[c], z);
+      for (int c = 0; c < C; ++c) {
+        part[c] = -cd * G[c];
+        W[c] = fmaf(cd, kv[c], W[c]);
+        z = fmaf(DUAL ? Wc[c] : W[c], kv[c], z);
+      }
       z = quad_sum(z);
       // vector-Jacobian product of the inner gradient
       float dz, dvi, sdk;   // sdk = sum_i delta_i (G k)_i
@@ -428,18 +514,22 @@ bwd_valu_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
         dvi = -dd;
         sdk = rows_sum(make_float4(del * gk, 0.0f, 0.0f, 0.0f), 1, 1).x;
       } else {
-        const float2 st = ln_stats(z);
-        const float rs = __builtin_amdgcn_rsqf(st.y + eps);
-        const float xh = (z - st.x) * rs;
         if constexpr (LN == kLnST) {
+          // sum dxh = sum gamma dd; sum dxh xh = rs sum gamma dd (z - mu)
           const float dxh = gam * dd;
-          const float4 r = rows_sum(make_float4(dxh, dxh * xh, del * gk, 0.0f), 1, 3);
-          dz = rs * (dxh - r.x * kInvD - xh * (r.y * kInvD));
+          float4 r[2];
+          st_round(z, dxh, del * gk, r);
+          const float rs = __builtin_amdgcn_rsqf(r[0].y + eps);
+          const float xh = (z - r[0].x) * rs;
+          dz = rs * (dxh - r[0].z * kInvD - xh * (rs * r[0].w * kInvD));
           dvi = -dd;
           dgam = fmaf(dd, xh, dgam);
           dbet += dd;
-          sdk = r.z;
+          sdk = r[1].x;
         } else {
+          const float2 st = ln_stats(z);
+          const float rs = __builtin_amdgcn_rsqf(st.y + eps);
+          const float xh = (z - st.x) * rs;
           const float e = fmaf(gam, xh, bet) - vi;
           const float g = gam * e;
           const float4 ra = rows_sum(make_float4(g, g * xh, 0.0f, 0.0f), 1, 2);
