@@ -259,10 +259,17 @@ def test_full_size_backward_sampled(workload, head):
     xs, ds, dWs, (bs, hs) = _sampled(x, dout, dWf, head)
     r = ref_bwd(xs, ds, dWs)
     tol = TOL[x.in_bf16]
-    for key in ("dq", "dk", "dv", "dgate_logit", "deta_logit", "dW0"):
-        assert_close(g[key][bs, hs][None], r[key], tol, key)
+    per_scan(g, r, bs, hs, ("dq", "dk", "dv", "dgate_logit", "deta_logit", "dW0"), tol)
     assert_close(g["dgamma"][head], r["dgamma"].sum(axis=0), tol, "dgamma")
     assert_close(g["dbeta"][head], r["dbeta"].sum(axis=0), tol, "dbeta")
+
+
+def per_scan(g, r, bs, hs, keys, tol):
+    """Every sampled scan on its own (its error against its own largest
+    value), so that one scan's small gradients cannot hide behind another's."""
+    for key in keys:
+        for n, (b, h) in enumerate(zip(bs, hs)):
+            assert_close(g[key][b, h], r[key][0, n], tol, f"{key}[{b},{h}]")
 
 
 def test_full_size_exact_backward_tail():
@@ -398,7 +405,6 @@ def test_full_size_dual_backward_sampled():
     g = gpu_bwd(x, dout, dWf, dual=True)
     xs, ds, dWs, (bs, hs) = _sampled(x, dout, dWf, head)
     r = ref_bwd(xs, ds, dWs, dual=True)
-    for key in ("dq", "dk", "dv", "dgate_logit", "deta_logit", "dW0"):
-        assert_close(g[key][bs, hs][None], r[key], TOL[True], key)
+    per_scan(g, r, bs, hs, ("dq", "dk", "dv", "dgate_logit", "deta_logit", "dW0"), TOL[True])
     assert_close(g["dgamma"][head], r["dgamma"].sum(axis=0), TOL[True], "dgamma")
     assert_close(g["dbeta"][head], r["dbeta"].sum(axis=0), TOL[True], "dbeta")

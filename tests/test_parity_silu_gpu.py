@@ -126,11 +126,15 @@ def test_silu_full_size_sampled():
     cut = lambda a: np.ascontiguousarray(a[:, head][None])
     ro, rW = oracle.ttt_linear_forward(xs.q, xs.k, xs.v, xs.eta_logit, xs.gate_logit, xs.W0,
                                        xs.gamma, xs.beta, silu_qk=True)
-    close(cut(out.cpu().numpy()), ro, 2e-2, "out")
-    close(cut(W.cpu().numpy()), rW, 2e-2, "W_final")
+    o_np, W_np = out.cpu().numpy(), W.cpu().numpy()
+    for b in range(B):   # every sampled scan on its own
+        close(o_np[b, head], ro[0, b], 2e-2, f"out[{b},{head}]")
+        close(W_np[b, head], rW[0, b], 2e-2, f"W_final[{b},{head}]")
     r = oracle.ttt_linear_backward(xs.q, xs.k, xs.v, xs.eta_logit, xs.gate_logit, xs.W0,
                                    xs.gamma, xs.beta, cut(dout), cut(dWf), silu_qk=True)
     for key in ("dq", "dk", "dv", "dgate_logit", "deta_logit", "dW0"):
-        close(cut(g[key].cpu().numpy()), r[key], 2e-2, key)
+        gk = g[key].cpu().numpy()
+        for b in range(B):
+            close(gk[b, head], r[key][0, b], 2e-2, f"{key}[{b},{head}]")
     close(g["dgamma"][head].cpu().numpy(), r["dgamma"].sum(0), 2e-2, "dgamma")
     close(g["dbeta"][head].cpu().numpy(), r["dbeta"].sum(0), 2e-2, "dbeta")
