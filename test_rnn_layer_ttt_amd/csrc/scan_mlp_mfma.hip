@@ -37,9 +37,10 @@
 //
 // Precision: every product runs on the bf16 16x16x32 MFMA with fp32
 // accumulation; fp32 operands (weights, activations, errors, Gram entries)
-// are split into bf16 hi + lo parts and only the lo*lo term (~2^-17
-// relative) is dropped; the bf16 inputs are exact.  The LayerNorm, SiLU and
-// gating run in fp32 on the vector ALUs.
+// are split into bf16 hi + lo parts (x - hi - lo ~2^-17 relative); the
+// 32-deep products drop the lo*lo term (~2^-17 relative), the 16-deep ones
+// keep it; the bf16 inputs are exact.  The LayerNorm, SiLU and gating run in
+// fp32 on the vector ALUs.
 //
 // Eight waves, two per SIMD: on SIMD w a hidden-side wave holds W1^T and W2
 // for hidden block w and runs the chain of a chunk, and an output-side wave
@@ -78,14 +79,27 @@ __device__ __forceinline__ float bf16_val(unsigned short b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// x = hi + lo, both bf16 (round to nearest even each)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two fp32 values to two bf16 (round to nearest even each) in one register:
+// one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const f32x2 x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
+// x = hi + lo, both bf16 (round to nearest even each), two elements per
+// conversion; the residual x - hi is exact in fp32
 __device__ __forceinline__ void split4(const f32x4& x, i16x4& hi, i16x4& lo) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const unsigned short h = bf16_bits(x[e]);
-    hi[e] = static_cast<short>(h);
-    lo[e] = static_cast<short>(bf16_bits(x[e] - bf16_val(h)));
-  }
+  const uint32_t h01 = pack_bf16(x[0], x[1]);
+  const uint32_t h23 = pack_bf16(x[2], x[3]);
+  const uint32_t l01 = pack_bf16(x[0] - __uint_as_float(h01 << 16),
+                                 x[1] - __uint_as_float(h01 & 0xFFFF0000u));
+  const uint32_t l23 = pack_bf16(x[2] - __uint_as_float(h23 << 16),
+                                 x[3] - __uint_as_float(h23 & 0xFFFF0000u));
+  hi = __builtin_bit_cast(i16x4, make_uint2(h01, h23));
+  lo = __builtin_bit_cast(i16x4, make_uint2(l01, l23));
 }
 
 __device__ __forceinline__ bf16x8 cat8(const i16x4& a, const i16x4& b) {
@@ -132,12 +146,14 @@ __device__ __forceinline__ f32x4 prod3(const Op32& a, const Op32& b, f32x4 c) {
   c = mfma32(a.hi, b.lo, c);
   return mfma32(a.lo, b.hi, c);
 }
-// c + a b over a 16-deep contraction of two fp32 operands (lo*lo dropped):
-// one 32-deep product over (hi, hi) and (hi, lo), one over (lo, hi) and zeros
+// c + a b over a 16-deep contraction of two fp32 operands: two 32-deep
+// products that share the A operand (a.hi, a.lo), against (b.hi, b.hi) and
+// (b.lo, b.lo), so all four terms hi*hi, lo*hi, hi*lo and lo*lo are summed
+// (no zero padding to build, and the split operands are multiplied exactly)
 __device__ __forceinline__ f32x4 prod3_16(const Op16& a, const Op16& b, f32x4 c) {
-  const i16x4 z = {0, 0, 0, 0};
-  c = mfma32(cat8(a.hi, a.hi), cat8(b.hi, b.lo), c);
-  return mfma32(cat8(a.lo, z), cat8(b.hi, z), c);
+  const bf16x8 ah = cat8(a.hi, a.lo);
+  c = mfma32(ah, cat8(b.hi, b.hi), c);
+  return mfma32(ah, cat8(b.lo, b.lo), c);
 }
 
 __device__ __forceinline__ i16x4 ld4(const uint16_t* p) {
@@ -327,16 +343,16 @@ mlp_mfma_kernel(const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) p1[ks] = op32(p1t[2 * ks], p1t[2 * ks + 1]);
   };
-  // (two independent accumulation chains, the hi and the lo parts of W1)
+  // (one accumulation chain: no second zeroed accumulator and no adds)
   auto keys_times_w1 = [&](const uint16_t (*XA)[64][8], const Op32 (&p1)[2]) -> f32x4 {
-    f32x4 ah = {0.0f, 0.0f, 0.0f, 0.0f}, al = ah;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const bf16x8 x = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(XA[ks][lane]));
-      ah = mfma32(x, p1[ks].hi, ah);
-      al = mfma32(x, p1[ks].lo, al);
+      acc = mfma32(x, p1[ks].hi, acc);
+      acc = mfma32(x, p1[ks].lo, acc);
     }
-    return ah + al;
+    return acc;
   };
   auto gram_kq = [&](const Chunk& ck) -> f32x4 {
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -379,11 +395,9 @@ mlp_mfma_kernel(const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp
   auto outputs_inchunk = [&](int64_t cp) -> f32x4 {
     const int par = static_cast<int>(cp & 1);
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    f32x4 g22[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)       // G2[s][t] = a_s . aq_t
-      g22[ks] = prod3(act_op(sm.A1[par], ks, n, g), act_op(sm.AQ[par], ks, n, g), zero);
-    f32x4 g2 = g22[0] + g22[1];
+    // G2[s][t] = a_s . aq_t
+    f32x4 g2 = prod3(act_op(sm.A1[par], 0, n, g), act_op(sm.AQ[par], 0, n, g), zero);
+    g2 = prod3(act_op(sm.A1[par], 1, n, g), act_op(sm.AQ[par], 1, n, g), g2);
     // strictly later tokens only, negated (DT holds -eta delta)
 #pragma unroll
     for (int r = 0; r < 4; ++r) g2[r] = (4 * g + r > n) ? -g2[r] : 0.0f;
@@ -392,9 +406,8 @@ mlp_mfma_kernel(const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp
   auto outputs = [&](int64_t cp, const Op32 (&p2)[2], const f32x4& inchunk) {
     const int par = static_cast<int>(cp & 1);
     const Chunk& ck = sm.ring[cp % RING];
-    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    const f32x4 y = prod3(p2[0], act_op(sm.AQ[par], 0, n, g), zero) +
-                    prod3(p2[1], act_op(sm.AQ[par], 1, n, g), zero) + inchunk;
+    const f32x4 y = prod3(p2[1], act_op(sm.AQ[par], 1, n, g),
+                          prod3(p2[0], act_op(sm.AQ[par], 0, n, g), inchunk));
     const int64_t t = cp * BT + n;
     if (t < T) {
       const float4 gl = *reinterpret_cast<const float4*>(&ck.SG[n][16 * w + 4 * g]);
@@ -447,8 +460,8 @@ mlp_mfma_kernel(const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp
       g1t = gram_kq(ck);
     } else {
       const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-      const f32x4 z = prod3(p2op[0], act_op(sm.A1[par], 0, n, g), zero) +
-                      prod3(p2op[1], act_op(sm.A1[par], 1, n, g), zero);
+      const f32x4 z = prod3(p2op[1], act_op(sm.A1[par], 1, n, g),
+                            prod3(p2op[0], act_op(sm.A1[par], 0, n, g), zero));
       *reinterpret_cast<float4*>(&sm.Z[n][16 * w + 4 * g]) = make_float4(z[0], z[1], z[2], z[3]);
     }
     __syncthreads();
@@ -521,8 +534,8 @@ mlp_mfma_kernel(const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp
     if (hid) {
       // DA^T = Delta^T P2 (rows tokens, own hidden cols), at the chunk-start W2
       const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-      const f32x4 dat = prod3(act_op(sm.DS, 0, n, g), op32(p2n[0], p2n[1]), zero) +
-                        prod3(act_op(sm.DS, 1, n, g), op32(p2n[2], p2n[3]), zero);
+      const f32x4 dat = prod3(act_op(sm.DS, 1, n, g), op32(p2n[2], p2n[3]),
+                              prod3(act_op(sm.DS, 0, n, g), op32(p2n[0], p2n[1]), zero));
       // eta DH^T
       f32x4 edh;
 #pragma unroll
