@@ -76,16 +76,23 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 // into bf16 hi + lo (round to nearest each; |x - hi - lo| <= 2^-17 |x|), a
 // bf16-exact one (the bf16 inputs q, k) is taken as is
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ unsigned short bf16_rne(float x) {
-  return __builtin_bit_cast(unsigned short, static_cast<__bf16>(x));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// two fp32 values to two bf16 (round to nearest even each) in one register,
+// a in the low half: one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const f32x2 x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 __device__ __forceinline__ void split4(const float (&x)[4], i16x4& hi, i16x4& lo) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const unsigned short h = bf16_rne(x[e]);
-    hi[e] = static_cast<short>(h);
-    lo[e] = static_cast<short>(bf16_rne(x[e] - __uint_as_float(static_cast<uint32_t>(h) << 16)));
-  }
+  const uint32_t h01 = pack_bf16(x[0], x[1]);
+  const uint32_t h23 = pack_bf16(x[2], x[3]);
+  const uint32_t l01 = pack_bf16(x[0] - __uint_as_float(h01 << 16),
+                                 x[1] - __uint_as_float(h01 & 0xFFFF0000u));
+  const uint32_t l23 = pack_bf16(x[2] - __uint_as_float(h23 << 16),
+                                 x[3] - __uint_as_float(h23 & 0xFFFF0000u));
+  hi = __builtin_bit_cast(i16x4, make_uint2(h01, h23));
+  lo = __builtin_bit_cast(i16x4, make_uint2(l01, l23));
 }
 __device__ __forceinline__ i16x4 exact4(const float (&x)[4]) {
   i16x4 r;

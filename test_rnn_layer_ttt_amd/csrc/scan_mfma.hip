@@ -95,26 +95,26 @@ __device__ __forceinline__ float fast_sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
-__device__ __forceinline__ unsigned short bf16_bits(float x) {
-  const __bf16 b = static_cast<__bf16>(x);
-  return __builtin_bit_cast(unsigned short, b);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// two fp32 values to two bf16 (round to nearest even each) in one register,
+// a in the low half: one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const f32x2 x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
-__device__ __forceinline__ float bf16_val(unsigned short b) {
-  return __uint_as_float(static_cast<uint32_t>(b) << 16);
-}
-// x = hi + lo with hi, lo bf16 (round to nearest even each)
-__device__ __forceinline__ void split_bf16(float x, unsigned short& hi, unsigned short& lo) {
-  hi = bf16_bits(x);
-  lo = bf16_bits(x - bf16_val(hi));
+// (a, b) = hi + lo with hi, lo bf16 pairs (round to nearest even each; the
+// residual x - hi is exact in fp32)
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16(a, b);
+  lo = pack_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u));
 }
 __device__ __forceinline__ void split4(const float (&x)[4], i16x4& hi, i16x4& lo) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    unsigned short a, b;
-    split_bf16(x[e], a, b);
-    hi[e] = static_cast<short>(a);
-    lo[e] = static_cast<short>(b);
-  }
+  uint32_t h01, l01, h23, l23;
+  split2(x[0], x[1], h01, l01);
+  split2(x[2], x[3], h23, l23);
+  hi = __builtin_bit_cast(i16x4, make_uint2(h01, h23));
+  lo = __builtin_bit_cast(i16x4, make_uint2(l01, l23));
 }
 
 __device__ __forceinline__ f32x4 mfma_k32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -242,8 +242,7 @@ __device__ __forceinline__ void load_tile(Stage<BF16>& st, const void* const src
 // silu(x) = x sigmoid(x) on two packed bf16 values, each result rounded to bf16
 __device__ __forceinline__ uint32_t silu_bf16x2(uint32_t w) {
   const float a = __uint_as_float(w << 16), b = __uint_as_float(w & 0xFFFF0000u);
-  return static_cast<uint32_t>(bf16_bits(a * fast_sigmoid(a))) |
-         (static_cast<uint32_t>(bf16_bits(b * fast_sigmoid(b))) << 16);
+  return pack_bf16(a * fast_sigmoid(a), b * fast_sigmoid(b));
 }
 
 // silu: the :mlp variant's SiLU on q and k (on the bf16 path the activated
@@ -551,13 +550,14 @@ __device__ __forceinline__ WOps split_w(const f32x4 (&Wt)[4]) {
   WOps w;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
+    uint32_t h[4], l[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      unsigned short hi, lo;
-      split_bf16(Wt[2 * ks + e / 4][e % 4], hi, lo);
-      w.hi[ks][e] = __builtin_bit_cast(__bf16, hi);
-      w.lo[ks][e] = __builtin_bit_cast(__bf16, lo);
+    for (int p = 0; p < 4; ++p) {
+      const f32x4& x = Wt[2 * ks + p / 2];
+      split2(x[2 * (p % 2)], x[2 * (p % 2) + 1], h[p], l[p]);
     }
+    w.hi[ks] = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+    w.lo[ks] = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
   }
   return w;
 }
