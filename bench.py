@@ -137,8 +137,9 @@ def mlp_precision(x, kernel):
         return ("bf16 inputs widened to fp32; " if x.in_bf16 else "fp32 inputs; ") + \
             "fp32 vector-ALU arithmetic, fp32 weights and output"
     return ("bf16 inputs; d x d products on bf16 MFMA with the fp32 operands (weights, "
-            "activations, errors) split into bf16 hi + lo and only the lo*lo term dropped; "
-            "fp32 accumulation, fp32 LayerNorm, fp32 weights and output")
+            "activations, errors) split into bf16 hi + lo, the lo*lo term dropped in the "
+            "64-deep contractions and kept in the 16-deep ones; fp32 accumulation, fp32 "
+            "LayerNorm, fp32 weights and output")
 
 
 def projection_work(x):
