@@ -153,8 +153,50 @@ def projection_work(x):
     return B * H * T, nbytes, 2 * B * T * hidden * rows
 
 
+def measure_peaks(stream, launches=5):
+    """Measured compute ceilings on this GPU, TFLOP/s (median of ``launches``):
+    fp32 fused multiply-adds on the vector ALUs, compiled like the scan kernels
+    (no packed-FP32 instructions), and the bf16 MFMA in its 16x16x32 and
+    32x32x16 shapes (``bf16_mfma``: the faster).  None when the probe library
+    is not built."""
+    import ctypes
+
+    import torch
+
+    from test_rnn_layer_ttt_amd.build import PEAKS_LIB
+    if not os.path.exists(PEAKS_LIB):
+        return None
+    lib = ctypes.CDLL(PEAKS_LIB)
+    out = torch.empty(1024 * 256, dtype=torch.float32, device=stream.device)
+    res = {}
+    for name, fn, flops_fn, iters in (("fp32_vector", lib.ttt_peak_fp32, lib.ttt_peak_fp32_flops,
+                                       20000),
+                                      ("bf16_mfma_16x16x32", lib.ttt_peak_bf16_mfma,
+                                       lib.ttt_peak_bf16_mfma_flops, 4000),
+                                      ("bf16_mfma_32x32x16", lib.ttt_peak_bf16_mfma32,
+                                       lib.ttt_peak_bf16_mfma32_flops, 4000)):
+        fn.restype = ctypes.c_int32
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+        flops_fn.restype = ctypes.c_double
+        flops_fn.argtypes = [ctypes.c_int32, ctypes.c_int32]
+        blocks = 1024                     # 16 waves per CU on 256 CUs
+        ms = []
+        for i in range(launches + 1):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            if fn(out.data_ptr(), blocks, iters, stream.cuda_stream) != 0:
+                raise RuntimeError(f"peak probe {name} failed to launch")
+            b_.record(stream)
+            b_.synchronize()
+            if i > 0:
+                ms.append(a_.elapsed_time(b_))
+        res[name] = round(flops_fn(blocks, iters) / (float(np.median(ms)) / 1e3) / 1e12, 1)
+    res["bf16_mfma"] = max(res["bf16_mfma_16x16x32"], res["bf16_mfma_32x32x16"])
+    return res
+
+
 def roofline(x, kernel_ms, traffic, train=False, mask=None, project=False,
-             hbm_measured_gbs=None, kernel=None, mlp=False):
+             hbm_measured_gbs=None, kernel=None, mlp=False, peaks=None):
     """Both ceilings of one launch and the fraction of the binding one.
 
     t_hbm = algorithmic bytes / the HBM peak and t_compute = algorithmic flops /
@@ -203,6 +245,11 @@ def roofline(x, kernel_ms, traffic, train=False, mask=None, project=False,
     if hbm_measured_gbs:
         roof.update(hbm_measured_gbs=round(hbm_measured_gbs, 1),
                     frac_hbm_measured=round(gbs / hbm_measured_gbs, 4))
+    if peaks:
+        # the same arithmetic's ceiling measured on this GPU (fp32 without
+        # packed instructions, as the kernels are built; bf16 MFMA)
+        cm = peaks["bf16_mfma"] if cpeak == BF16_MATRIX_PEAK_TFLOPS else peaks["fp32_vector"]
+        roof.update(compute_measured_tflops=cm, frac_compute_measured=round(tfs / cm, 4))
     return name, roof
 
 
@@ -571,6 +618,7 @@ def main():
         copy_ms.append(a_.elapsed_time(b_))
     del src, dst
     copy_gbs = 2 * (1 << 30) / (float(np.median(copy_ms[1:])) / 1e3) / 1e9
+    peaks = measure_peaks(stream)
 
     n_tok = B * H * T
     kernel = (ttt.ttt_linear_backward_kernel(d, mode, x.chunk if x.dual else 1) if train else
@@ -586,7 +634,8 @@ def main():
     if args.silu_qk:
         traffic_key += "/silu"
     kname, roof = roofline(x, avg_kernel_ms, load_traffic(kernel, traffic_key), train, mask_np,
-                           project, hbm_measured_gbs=copy_gbs, kernel=kernel, mlp=args.mlp)
+                           project, hbm_measured_gbs=copy_gbs, kernel=kernel, mlp=args.mlp,
+                           peaks=peaks)
 
     mode_name = ("dual-form chunk %d" % x.chunk if x.dual else "per-token") + \
         {"st": "", "exact": ", exact LN Jacobian", "none": ", no LN"}[x.ln]
@@ -617,6 +666,7 @@ def main():
                    "kernel_ms_median": med(kernel_ms),
                    "kernel_ms_min": round(min(kernel_ms), 4),
                    "cu_occupied": f"{min(B * H, 256)}/256" if not project else "all",
+                   "peaks_measured": dict(peaks or {}, hbm_copy_gbs=round(copy_gbs, 1)),
                    "timing": "value from the wall clock of the K back-to-back steps (warm "
                              "caches); roofline from the events' average over them; cold = "
                              f"{args.flush_mib} MiB written between launches"},

@@ -17,11 +17,14 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libttt_linear.so")
+#: the throughput probes the benchmark measures its ceilings with (not the scan's ABI)
+PEAKS_LIB = os.path.join(HERE, "libttt_peaks.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
 SOURCES = ["ttt_linear.hip", "scan_valu.hip", "scan_mfma.hip", "bwd_mfma.hip", "bwd_valu.hip",
            "proj_mfma.hip", "scan_mlp_valu.hip", "scan_mlp_mfma.hip"]
+PEAK_SOURCES = ["peaks.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -124,20 +127,22 @@ def srcc_war_hazards(asm: str, min_wait: int = SRCC_WAR_MIN) -> list:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link the library; returns its path."""
+    """Compile every source, link the library and the probe library; returns
+    the library's path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    all_sources = SOURCES + PEAK_SOURCES
+    objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in all_sources]
     # the digest of the sources goes into ttt_version(), so a stale library can be told apart
     digest = [f'-DTTT_SOURCE_DIGEST="{source_digest()}"']
     # -save-temps=obj keeps the device assembly each object is assembled from
     cmds = [[HIPCC, *CFLAGS, *digest, "-save-temps=obj", "-c", os.path.join(CSRC, s), "-o", o]
-            for s, o in zip(SOURCES, objs)]
+            for s, o in zip(all_sources, objs)]
     with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out)
     bad = []
-    for s in SOURCES:
+    for s in all_sources:
         asm = os.path.join(BUILD_DIR, f"{os.path.splitext(s)[0]}-hip-amdgcn-amd-amdhsa-{ARCH}.s")
         if not os.path.exists(asm):
             raise RuntimeError(f"device assembly of {s} not found at {asm}")
@@ -150,14 +155,17 @@ def build(verbose: bool = False) -> str:
     # counter as well, so every LDS wait after one waits for its memory
     # round trip; device pointers here are global and LDS is addressed directly
     flat = []
-    for s in SOURCES:
+    for s in all_sources:
         asm = os.path.join(BUILD_DIR, f"{os.path.splitext(s)[0]}-hip-amdgcn-amd-amdhsa-{ARCH}.s")
         with open(asm) as f:
             flat += [f"  {s}: {l.strip()}" for l in f if l.lstrip().startswith("flat_")]
     if flat:
         raise RuntimeError("flat memory instructions in device code:\n" + "\n".join(flat[:20]))
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", PEAKS_LIB + ".tmp",
+          *objs[len(SOURCES):]])
+    os.replace(PEAKS_LIB + ".tmp", PEAKS_LIB)
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs])
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs[:len(SOURCES)]])
     # a kernel whose host-side stub was not emitted (the host pass can drop a
     # kernel template without a diagnostic) would only fail when loaded
     undef = [l for l in _run(["nm", "-D", "--undefined-only", tmp]).splitlines()

@@ -129,3 +129,39 @@ def test_projection_work_and_its_matrix_roofline():
     assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s"
     assert roof["peak"] == bench.BF16_MATRIX_PEAK_TFLOPS
     assert roof["achieved"] == pytest.approx(fl_big / 1e-6 / 1e12, rel=1e-3)
+
+
+def test_peak_probe_library_exports_and_flop_counts():
+    # the throughput probes bench.py measures its compute ceilings with: a
+    # separate library beside the scan's, with these four symbols; the flop
+    # counts follow the probes' loops (8 fp32 FMA chains per thread; 4
+    # 16x16x32 products per wave per iteration)
+    import ctypes
+
+    from test_rnn_layer_ttt_amd.build import PEAKS_LIB
+    if not os.path.exists(PEAKS_LIB):
+        pytest.skip("probe library not built")
+    out = subprocess.run(["nm", "-D", "--defined-only", PEAKS_LIB], capture_output=True,
+                         text=True, check=True).stdout
+    names = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    assert {"ttt_peak_fp32", "ttt_peak_bf16_mfma", "ttt_peak_bf16_mfma32", "ttt_peak_fp32_flops",
+            "ttt_peak_bf16_mfma_flops", "ttt_peak_bf16_mfma32_flops"} <= names
+    lib = ctypes.CDLL(PEAKS_LIB)
+    for fn in (lib.ttt_peak_fp32_flops, lib.ttt_peak_bf16_mfma_flops,
+               lib.ttt_peak_bf16_mfma32_flops):
+        fn.restype = ctypes.c_double
+        fn.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    assert lib.ttt_peak_fp32_flops(1024, 100) == 2 * 8 * 256 * 1024 * 100
+    assert lib.ttt_peak_bf16_mfma_flops(1024, 100) == 4 * 16384 * 4 * 1024 * 100
+    assert lib.ttt_peak_bf16_mfma32_flops(1024, 100) == 2 * 32768 * 4 * 1024 * 100
+
+
+def test_roofline_reports_measured_compute_ceiling():
+    x = make_case(2, 3, 64, 64, seed=0, in_bf16=True)
+    peaks = {"fp32_vector": 80.0, "bf16_mfma": 2000.0}
+    _, r = bench.roofline(x, kernel_ms=0.01, traffic=None, peaks=peaks, kernel="scan_mfma")
+    assert r["compute_measured_tflops"] == 80.0
+    assert r["frac_compute_measured"] == pytest.approx(r["frac_compute"] * 157.3 / 80.0, rel=1e-3)
+    xd = make_case(2, 3, 64, 64, seed=0, in_bf16=True, dual=True, chunk=16)
+    _, rd = bench.roofline(xd, kernel_ms=0.01, traffic=None, peaks=peaks, kernel="scan_mfma")
+    assert rd["compute_measured_tflops"] == 2000.0
