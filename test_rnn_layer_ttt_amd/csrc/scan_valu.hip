@@ -56,13 +56,26 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x;
 }
 
+// x of this lane plus x of lane ^ 16 (^ 32): v_permlane16_swap /
+// v_permlane32_swap of x with itself, on the vector ALU (no LDS round trip);
+// the two swapped registers hold the lane's own value and its partner's
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum over the 16 quads of a wave of a value that is uniform within each quad.
 __device__ __forceinline__ float quads_sum(float x) {
   x += dpp<kRowRor4>(x);
   x += dpp<kRowRor8>(x);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  x = xor16_sum(x);
+  return xor32_sum(x);
 }
 
 template <bool BF16>
