@@ -22,9 +22,9 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def setup(B, H, T, ln, bf16, seed):
-    x = make_case(B, H, T, 64, seed=seed, ln=ln, in_bf16=bf16, random_affine=True)
-    dout, dWf = make_cotangents(B, H, T, 64, seed=seed + 1)
+def setup(B, H, T, ln, bf16, seed, d=64, chunk=None):
+    x = make_case(B, H, T, d, seed=seed, ln=ln, in_bf16=bf16, random_affine=True)
+    dout, dWf = make_cotangents(B, H, T, d, seed=seed + 1)
     dt = torch.bfloat16 if bf16 else torch.float32
     f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(dt)
     g = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -33,31 +33,32 @@ def setup(B, H, T, ln, bf16, seed):
     gam = None if ln == "none" else t["gamma"]
     bet = None if ln == "none" else t["beta"]
     _, _, rec = ttt.forward_record(t["q"], t["k"], t["v"], t["eta_logit"], t["gate_logit"],
-                                   t["W0"], gam, bet, ln=ln)
+                                   t["W0"], gam, bet, ln=ln, dual=chunk is not None,
+                                   chunk=chunk or 16)
     return x, t, rec
 
 
-def outputs(B, H, T, ln):
+def outputs(B, H, T, ln, d=64):
     f32 = dict(dtype=torch.float32, device="cuda")
-    o = {n: torch.full((B, H, T, 64), float("nan"), **f32) for n in ("dq", "dk", "dv",
-                                                                     "dgate_logit")}
+    o = {n: torch.full((B, H, T, d), float("nan"), **f32) for n in ("dq", "dk", "dv",
+                                                                    "dgate_logit")}
     o["deta_logit"] = torch.full((B, H, T), float("nan"), **f32)
-    o["dW0"] = torch.full((B, H, 64, 64), float("nan"), **f32)
-    o["dgamma"] = None if ln == "none" else torch.full((H, 64), float("nan"), **f32)
-    o["dbeta"] = None if ln == "none" else torch.full((H, 64), float("nan"), **f32)
+    o["dW0"] = torch.full((B, H, d, d), float("nan"), **f32)
+    o["dgamma"] = None if ln == "none" else torch.full((H, d), float("nan"), **f32)
+    o["dbeta"] = None if ln == "none" else torch.full((H, d), float("nan"), **f32)
     return o
 
 
-def call(noalloc, t, rec, o, B, H, T, ln, bf16, ws=None):
+def call(noalloc, t, rec, o, B, H, T, ln, bf16, ws=None, d=64, chunk=None):
     p = lambda a: None if a is None else a.data_ptr()
     no_ln = ln == "none"
-    mode = ttt.mode_bits(ln, False, bf16)
+    mode = ttt.mode_bits(ln, chunk is not None, bf16)
     common = (p(t["q"]), p(t["k"]), p(t["v"]), p(t["eta_logit"]), p(t["gate_logit"]),
               None if no_ln else p(t["gamma"]), None if no_ln else p(t["beta"]), p(rec),
               rec.numel())
     grads = (p(t["dout"]), p(t["dWf"]), p(o["dq"]), p(o["dk"]), p(o["dv"]), p(o["deta_logit"]),
-             p(o["dgate_logit"]), p(o["dW0"]), p(o["dgamma"]), p(o["dbeta"]), B, H, T, 64,
-             mode, 1, torch.cuda.current_stream().cuda_stream)
+             p(o["dgate_logit"]), p(o["dW0"]), p(o["dgamma"]), p(o["dbeta"]), B, H, T, d,
+             mode, chunk or 1, torch.cuda.current_stream().cuda_stream)
     if noalloc:
         return ttt.ttt_linear_backward_noalloc(*common, *grads)
     return ttt.ttt_linear_backward(*common, p(ws), ws.numel(), *grads)
@@ -101,3 +102,25 @@ def test_noalloc_backward_at_its_largest_size():
     for key in GRADS:
         assert torch.isfinite(ref[key]).all(), key
         assert torch.equal(got[key], ref[key]), key
+
+
+def test_noalloc_backward_vector_alu_kernel():
+    # the vector-ALU backward (d other than 64, a dual chunk other than 16)
+    # through the same static scratch, two calls in a row, the second smaller
+    cases = ((4, 8, 70, "exact", False, 32, 5), (2, 3, 21, "st", True, 16, None))
+    for n, (B, H, T, ln, bf16, d, chunk) in enumerate(cases):
+        say(f"case no-alloc vector-ALU backward call {n + 1}: B={B} H={H} T={T} ln={ln} "
+            f"bf16={bf16} d={d} chunk={chunk}")
+        mode = ttt.mode_bits(ln, chunk is not None, bf16)
+        assert ttt.ttt_linear_backward_kernel(d, mode, chunk or 1) == "bwd_valu"
+        x, t, rec = setup(B, H, T, ln, bf16, seed=800 + n, d=d, chunk=chunk)
+        st, nws = ttt.ttt_linear_backward_workspace_bytes(B, H, d, mode)
+        assert st == ttt.TTT_OK and nws <= ttt.TTT_STATIC_SCRATCH_BYTES
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+        ref, got = outputs(B, H, T, ln, d), outputs(B, H, T, ln, d)
+        assert call(False, t, rec, ref, B, H, T, ln, bf16, ws, d=d, chunk=chunk) == ttt.TTT_OK
+        assert call(True, t, rec, got, B, H, T, ln, bf16, d=d, chunk=chunk) == ttt.TTT_OK
+        torch.cuda.synchronize()
+        for key in GRADS:
+            assert torch.isfinite(ref[key]).all(), key
+            assert torch.equal(got[key], ref[key]), key
