@@ -842,68 +842,44 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
           ln_pass<BF16, LN, DUAL>(sm, sin, sm.Cc[c & 1], sm.Dt[c & 1], lane, gam, eps);
         }
       }
-    } else if (slice >= 0 && !MASK && !REC) {
-      // one straight block up to the update, so the MFMA chains of its
-      // independent parts can interleave: at c = 0 there is no previous tile
-      // (the outputs written to Ob[1] are overwritten before they are read,
-      // and the update is skipped: its ring slot may not hold a tile yet, and
-      // a stale NaN times E = 0 would not be 0); in the last period the
-      // products run on a stale ring slot and are not used
-      if (c == ntiles) Ereg = tok_e(c - 1);   // no z of a next tile was formed
+    } else if (slice >= 0) {
+      // One straight block, so the MFMA chains of its independent parts can
+      // interleave: the token Gram matrices of tile c, the outputs of tile
+      // c-1 and the update W_c = W_{c-1} - E_{c-1}^T K_{c-1}, then
+      // K_{c+1} W_c^T (for z of the next tile) and Q_c W_c^T.  At c = 0 there
+      // is no previous tile: the outputs written to Ob[1] are overwritten
+      // before they are read, and the update is skipped (its ring slot may
+      // not hold a tile yet, and a stale NaN times E = 0 would not be 0).  In
+      // the last period the products run on a stale ring slot and are not
+      // used.  With the mask, a skipped tile's parts are left out.
+      if (c == ntiles && !skip_p) Ereg = tok_e(c - 1);   // no z of a next tile was formed
       const auto& tp = sm.ring[(c + RING - 1) % RING];
       const auto& tc = sm.ring[c % RING];
       const auto& tn = sm.ring[(c + 1) % RING];
       TokReg<BF16> Mn{}, Xn{};
       if constexpr (R::kTokInSlices) {
-        float m[4], x[4];
-        tok_m(tc, m);
-        make_tok(Mn, m);
-        tok_x(tc, tn, x);
-        make_tok(Xn, x);
-      } else {
+        if (!skip_c) {
+          float m[4];
+          tok_m(tc, m);
+          make_tok(Mn, m);
+        }
+        if (!skip_c && !skip_n) {
+          float x[4];
+          tok_x(tc, tn, x);
+          make_tok(Xn, x);
+        }
+      } else if (!skip_p) {
         const float4 m4 = *reinterpret_cast<const float4*>(&sm.Mg[(c + 1) & 1][l16][4 * G]);
         const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
         make_tok(Mreg, mv);
       }
-      U = tok_mul(Mreg, Ereg, U);
+      if (!skip_p) U = tok_mul(Mreg, Ereg, U);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 4 * G + r;
         sm.Ob[(c + 1) & 1][t][irow] = U[r] * tp.SG[t][irow];
       }
-      if (c >= 1) update_w(Wt, tp, Ereg, lane, l16, G);
-      if constexpr (BF16) {
-        const WOps w = split_w(Wt);
-        P = rows_times_wt(krows(tn), w, lane);
-        U = rows_times_wt(qrows(tc), w, lane);
-      } else {
-        P = rows_times_wt(krows(tn), Wt, l16, G);
-        U = rows_times_wt(qrows(tc), Wt, l16, G);
-      }
-      if constexpr (R::kTokInSlices) {
-        Mreg = Mn;
-        Xreg = Xn;
-      }
-    } else if (slice >= 0) {
-      if (c >= 1) {
-        // outputs of tile c-1 and the update W_c = W_{c-1} - E_{c-1}^T K_{c-1}
-        const auto& tp = sm.ring[(c - 1) % RING];
-        if (c == ntiles && !skip_p) Ereg = tok_e(c - 1);   // no z of a next tile was formed
-        if (!skip_p) {
-          if constexpr (!R::kTokInSlices) {
-            const float4 m4 = *reinterpret_cast<const float4*>(&sm.Mg[(c - 1) & 1][l16][4 * G]);
-            const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
-            make_tok(Mreg, mv);
-          }
-          U = tok_mul(Mreg, Ereg, U);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 4 * G + r;
-          sm.Ob[(c - 1) & 1][t][irow] = U[r] * tp.SG[t][irow];
-        }
-        if (!skip_p) update_w(Wt, tp, Ereg, lane, l16, G);
-      }
+      if (c >= 1 && !skip_p) update_w(Wt, tp, Ereg, lane, l16, G);
       if (REC && live) {
         float* w = rec_W + ((bh * ntiles + c) * D + irow) * D + 4 * G;
 #pragma unroll
@@ -911,30 +887,17 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
           *reinterpret_cast<float4*>(w + 16 * jt) =
               make_float4(Wt[jt][0], Wt[jt][1], Wt[jt][2], Wt[jt][3]);
       }
-      if (live) {
-        // K_{c+1} W_c^T (for z of the next tile) and Q_c W_c^T
-        const auto& tc = sm.ring[c % RING];
-        const auto& tn = sm.ring[(c + 1) % RING];
-        if constexpr (BF16) {
-          const WOps w = split_w(Wt);
-          if (c + 1 < ntiles && !skip_n) P = rows_times_wt(krows(tn), w, lane);
-          U = rows_times_wt(qrows(tc), w, lane);
-        } else {
-          if (c + 1 < ntiles && !skip_n) P = rows_times_wt(krows(tn), Wt, l16, G);
-          U = rows_times_wt(qrows(tc), Wt, l16, G);
-        }
-        if constexpr (R::kTokInSlices) {
-          if (!skip_c) {
-            float m[4];
-            tok_m(tc, m);
-            make_tok(Mreg, m);
-          }
-          if (c + 1 < ntiles && !skip_c && !skip_n) {
-            float x[4];
-            tok_x(tc, tn, x);
-            make_tok(Xreg, x);
-          }
-        }
+      if constexpr (BF16) {
+        const WOps w = split_w(Wt);
+        if (!skip_n) P = rows_times_wt(krows(tn), w, lane);
+        U = rows_times_wt(qrows(tc), w, lane);
+      } else {
+        if (!skip_n) P = rows_times_wt(krows(tn), Wt, l16, G);
+        U = rows_times_wt(qrows(tc), Wt, l16, G);
+      }
+      if constexpr (R::kTokInSlices) {
+        Mreg = Mn;
+        Xreg = Xn;
       }
     } else {
       if (stage_parity >= 0) {
