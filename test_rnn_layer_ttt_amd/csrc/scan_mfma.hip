@@ -351,6 +351,29 @@ __device__ __forceinline__ float shift_by_lane0(float x) {
   return x - __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }
 
+// The two sums of the straight-through LayerNorm in one register: a
+// v_permlane32_swap of (a, b) plus an add leaves a of lanes l and l + 32 in
+// lane l < 32 and b of lanes l - 32 and l in lane l >= 32; the row scans and
+// row_bcast:15 (steps 0 .. 4 above) then sum each half, so that lane 31 holds
+// the total of a and lane 63 that of b.  Seven instructions on the chain
+// instead of twelve for two interleaved full sums.
+__device__ __forceinline__ float pair_step0(float a, float b) {
+#pragma clang fp contract(off)
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float lane31(float x) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+}
+__device__ __forceinline__ void wave_pair_total(float& a, float& b) {
+  float r = pair_step0(a, b);
+  r = red_step<0>(r); r = red_step<1>(r); r = red_step<2>(r); r = red_step<3>(r);
+  r = red_step<4>(r);
+  a = lane31(r);
+  b = lane63(r);
+}
+
 // Two independent wave sums, interleaved step by step; wave-uniform results.
 __device__ __forceinline__ void wave_total2(float& a, float& b) {
   a = red_step<0>(a); b = red_step<0>(b);
@@ -365,19 +388,26 @@ __device__ __forceinline__ void wave_total2(float& a, float& b) {
 
 // delta for one token from y (lane = feature i) and the wave sums s1 = sum y,
 // s2 = sum y^2, where y = z - c is z shifted by one of its own entries c (the
-// LayerNorm of y equals that of z); gz = gamma_i y, bv = beta_i - v_t[i].  With
-// a = s1/d (the mean of y) and b = s2/d + eps, var + eps = b - a^2, and |a| is
-// a few standard deviations at most, so the difference does not cancel; the
-// terms that do not depend on the sums (gz, b) are formed off the critical path.
+// LayerNorm of y equals that of z); bv = beta_i - v_t[i].  With a = s1/d (the
+// mean of y) and b = s2/d + eps, var + eps = b - a^2, and |a| is a few standard
+// deviations at most, so the difference does not cancel; the terms that do not
+// depend on the sums are formed off the critical path.
+// Straight-through form: gz = d gamma_i y, and with the exact power-of-two
+// scalings d^2 (var + eps) = d s2 - s1^2 + d^2 eps =: Q,
+// delta = rsqrt(Q) (d gamma_i y - gamma_i s1) + bv; Q >= d^2 eps up to
+// rounding (the shifted sums do not cancel), so |Q| guards the square root
+// at no cost (a source modifier).  Exact form: gz = gamma_i y.
 template <int LN>
 __device__ __forceinline__ float delta_from_sums(float z, float gz, float s1, float s2, float bv,
                                                  float gam, float eps) {
-  const float a = s1 * (1.0f / D);
-  const float b = fmaf(s2, 1.0f / D, eps);
-  const float rs = __builtin_amdgcn_rsqf(fmaxf(fmaf(-a, a, b), eps));
   if constexpr (LN == kLnST) {
-    return fmaf(rs, fmaf(-gam, a, gz), bv);
+    const float c = fmaf(-s1, s1, float(D * D) * eps);
+    const float q = fmaf(s2, float(D), c);
+    return fmaf(__builtin_amdgcn_rsqf(fabsf(q)), fmaf(-gam, s1, gz), bv);
   } else {
+    const float a = s1 * (1.0f / D);
+    const float b = fmaf(s2, 1.0f / D, eps);
+    const float rs = __builtin_amdgcn_rsqf(fmaxf(fmaf(-a, a, b), eps));
     const float xh = (z - a) * rs;
     const float g = gam * fmaf(gam, xh, bv);
     float sg = g, sgx = g * xh;
@@ -395,8 +425,13 @@ __device__ __forceinline__ float token_delta(float z, float bv, float gam, float
   } else {
     const float y = shift_by_lane0(z);
     float s1 = y, s2 = y * y;
-    wave_total2(s1, s2);
-    return delta_from_sums<LN>(y, gam * y, s1, s2, bv, gam, eps);
+    if constexpr (LN == kLnST) {
+      wave_pair_total(s1, s2);
+      return delta_from_sums<LN>(y, (gam * float(D)) * y, s1, s2, bv, gam, eps);
+    } else {
+      wave_total2(s1, s2);
+      return delta_from_sums<LN>(y, gam * y, s1, s2, bv, gam, eps);
+    }
   }
 }
 
@@ -425,6 +460,7 @@ __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[B
   };
   load_row(0);
   load_row(1);
+  const float gam_d = gam * float(D);
   if constexpr (LN != kLnNone) zr[0] = shift_by_lane0(zr[0]);
   float dprev = 0.0f;
 #pragma unroll
@@ -451,15 +487,27 @@ __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[B
       dl = z - bv[s];
     } else {
       float a = z, b = z * z;
-      const float gz = gam * z;
-      a = red_step<0>(a); b = red_step<0>(b); fill(0);
-      a = red_step<1>(a); b = red_step<1>(b); fill(1);
-      a = red_step<2>(a); b = red_step<2>(b); fill(2);
-      a = red_step<3>(a); b = red_step<3>(b); fill(3);
-      a = red_step<4>(a); b = red_step<4>(b); fill(4);
-      a = red_step<5>(a); b = red_step<5>(b); fill(5);
-      if (s + 1 < BT) zr[s + 1] = shift_by_lane0(zr[s + 1]);
-      dl = delta_from_sums<LN>(z, gz, lane63(a), lane63(b), bv[s], gam, eps);
+      if constexpr (LN == kLnST) {
+        const float gz = gam_d * z;
+        float r = pair_step0(a, b); fill(0);
+        r = red_step<0>(r); fill(1);
+        r = red_step<1>(r); fill(2);
+        r = red_step<2>(r); fill(3);
+        r = red_step<3>(r); fill(4);
+        r = red_step<4>(r); fill(5);
+        if (s + 1 < BT) zr[s + 1] = shift_by_lane0(zr[s + 1]);
+        dl = delta_from_sums<LN>(z, gz, lane31(r), lane63(r), bv[s], gam, eps);
+      } else {
+        const float gz = gam * z;
+        a = red_step<0>(a); b = red_step<0>(b); fill(0);
+        a = red_step<1>(a); b = red_step<1>(b); fill(1);
+        a = red_step<2>(a); b = red_step<2>(b); fill(2);
+        a = red_step<3>(a); b = red_step<3>(b); fill(3);
+        a = red_step<4>(a); b = red_step<4>(b); fill(4);
+        a = red_step<5>(a); b = red_step<5>(b); fill(5);
+        if (s + 1 < BT) zr[s + 1] = shift_by_lane0(zr[s + 1]);
+        dl = delta_from_sums<LN>(z, gz, lane63(a), lane63(b), bv[s], gam, eps);
+      }
     }
     dr[s] = dl;
     if (s + 1 < BT) zr[s + 1] = fmaf(-cd[s], dl, zr[s + 1]);
