@@ -388,15 +388,18 @@ __device__ __forceinline__ void wave_total2(float& a, float& b) {
 
 // delta for one token from y (lane = feature i) and the wave sums s1 = sum y,
 // s2 = sum y^2, where y = z - c is z shifted by one of its own entries c (the
-// LayerNorm of y equals that of z); bv = beta_i - v_t[i].  With a = s1/d (the
-// mean of y) and b = s2/d + eps, var + eps = b - a^2, and |a| is a few standard
-// deviations at most, so the difference does not cancel; the terms that do not
-// depend on the sums are formed off the critical path.
-// Straight-through form: gz = d gamma_i y, and with the exact power-of-two
-// scalings d^2 (var + eps) = d s2 - s1^2 + d^2 eps =: Q,
-// delta = rsqrt(Q) (d gamma_i y - gamma_i s1) + bv; Q >= d^2 eps up to
-// rounding (the shifted sums do not cancel), so |Q| guards the square root
-// at no cost (a source modifier).  Exact form: gz = gamma_i y.
+// LayerNorm of y equals that of z).  The mean of y, s1/d, is a few standard
+// deviations at most, so with the exact power-of-two scalings
+// Q := d s2 - s1^2 + d^2 eps = d^2 (var + eps) the difference does not cancel,
+// and Q >= d^2 eps up to rounding, so |Q| guards the square root at no cost (a
+// source modifier).  The terms that do not depend on the sums are formed off
+// the critical path.
+// Straight-through form: gz = d gamma_i y, bv = beta_i - v_t[i], and
+// delta = rsqrt(Q) (d gamma_i y - gamma_i s1) + bv.
+// Exact form: gz = gamma_i^2, bv = gamma_i (beta_i - v_t[i]); with
+// x = (y - s1/d) rsqrt(var + eps) and g = gamma_i (gamma_i x + beta_i - v_t[i])
+// = gz x + bv, delta = rsqrt(var + eps) (g - mean(g) - x mean(g x)), the two
+// means from a second round of wave sums.
 template <int LN>
 __device__ __forceinline__ float delta_from_sums(float z, float gz, float s1, float s2, float bv,
                                                  float gam, float eps) {
@@ -406,13 +409,14 @@ __device__ __forceinline__ float delta_from_sums(float z, float gz, float s1, fl
     return fmaf(__builtin_amdgcn_rsqf(fabsf(q)), fmaf(-gam, s1, gz), bv);
   } else {
     const float a = s1 * (1.0f / D);
-    const float b = fmaf(s2, 1.0f / D, eps);
-    const float rs = __builtin_amdgcn_rsqf(fmaxf(fmaf(-a, a, b), eps));
+    const float c = fmaf(-s1, s1, float(D * D) * eps);
+    const float q = fmaf(s2, float(D), c);
+    const float rs = float(D) * __builtin_amdgcn_rsqf(fabsf(q));
     const float xh = (z - a) * rs;
-    const float g = gam * fmaf(gam, xh, bv);
+    const float g = fmaf(gz, xh, bv);
     float sg = g, sgx = g * xh;
     wave_total2(sg, sgx);
-    return rs * (g - sg * (1.0f / D) - xh * (sgx * (1.0f / D)));
+    return rs * fmaf(-xh, sgx * (1.0f / D), fmaf(sg, -1.0f / D, g));
   }
 }
 
@@ -430,7 +434,7 @@ __device__ __forceinline__ float token_delta(float z, float bv, float gam, float
       return delta_from_sums<LN>(y, (gam * float(D)) * y, s1, s2, bv, gam, eps);
     } else {
       wave_total2(s1, s2);
-      return delta_from_sums<LN>(y, gam * y, s1, s2, bv, gam, eps);
+      return delta_from_sums<LN>(y, gam * gam, s1, s2, gam * bv, gam, eps);
     }
   }
 }
@@ -498,7 +502,8 @@ __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[B
         if (s + 1 < BT) zr[s + 1] = shift_by_lane0(zr[s + 1]);
         dl = delta_from_sums<LN>(z, gz, lane31(r), lane63(r), bv[s], gam, eps);
       } else {
-        const float gz = gam * z;
+        const float g2 = gam * gam;
+        const float gbv = gam * bv[s];
         a = red_step<0>(a); b = red_step<0>(b); fill(0);
         a = red_step<1>(a); b = red_step<1>(b); fill(1);
         a = red_step<2>(a); b = red_step<2>(b); fill(2);
@@ -506,7 +511,7 @@ __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[B
         a = red_step<4>(a); b = red_step<4>(b); fill(4);
         a = red_step<5>(a); b = red_step<5>(b); fill(5);
         if (s + 1 < BT) zr[s + 1] = shift_by_lane0(zr[s + 1]);
-        dl = delta_from_sums<LN>(z, gz, lane63(a), lane63(b), bv[s], gam, eps);
+        dl = delta_from_sums<LN>(z, g2, lane63(a), lane63(b), gbv, gam, eps);
       }
     }
     dr[s] = dl;
