@@ -444,10 +444,13 @@ __device__ __forceinline__ float token_delta(float z, float bv, float gam, float
 // eta_s (k_s . k_{s+1}) in registers.  Token s's delta is applied to row s+1 at
 // once; its updates of rows s+2.. are spread over the reduction steps of token
 // s+1, where they fill the DPP wait states, with coefficient rows read two
-// tokens ahead of their use.  Row s+1 is shifted by its lane-0 entry (before
-// token s's own correction, so off the dependency chain) once every earlier
-// delta but token s's has reached it; the LayerNorm of token s+1 then runs on
-// the shifted row.
+// tokens ahead of their use.  Row s+1 is shifted by its lane-0 entry before
+// token s's own correction, so off the dependency chain (with the
+// straight-through form, possibly before the last of the deferred updates
+// reach it: any common shift leaves the LayerNorm unchanged, and a lane-0
+// entry a few updates old still keeps the mean of the shifted row within a few
+// standard deviations); the LayerNorm of token s+1 then runs on the shifted
+// row.
 template <int LN>
 __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[BT],
                                             const float (*cc)[BT],
@@ -492,26 +495,57 @@ __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[B
     } else {
       float a = z, b = z * z;
       if constexpr (LN == kLnST) {
+        // half the deferred rows go into the reduction's gaps, half into
+        // the waits of the tail (delta_from_sums written out), and row s+1
+        // is shifted early, so that its correction by delta_s below waits
+        // for delta_s alone
         const float gz = gam_d * z;
         float r = pair_step0(a, b); fill(0);
-        r = red_step<0>(r); fill(1);
-        r = red_step<1>(r); fill(2);
-        r = red_step<2>(r); fill(3);
-        r = red_step<3>(r); fill(4);
-        r = red_step<4>(r); fill(5);
+        r = red_step<0>(r);
+        r = red_step<1>(r); fill(1);
+        r = red_step<2>(r);
+        r = red_step<3>(r); fill(2);
+        r = red_step<4>(r);
         if (s + 1 < BT) zr[s + 1] = shift_by_lane0(zr[s + 1]);
-        dl = delta_from_sums<LN>(z, gz, lane31(r), lane63(r), bv[s], gam, eps);
+        const float s1 = lane31(r), s2 = lane63(r);
+        fill(3);
+        const float c = fmaf(-s1, s1, float(D * D) * eps);
+        const float q = fmaf(s2, float(D), c);
+        fill(4);
+        const float rq = __builtin_amdgcn_rsqf(fabsf(q));
+        fill(5);
+        dl = fmaf(rq, fmaf(-gam, s1, gz), bv[s]);
       } else {
         const float g2 = gam * gam;
         const float gbv = gam * bv[s];
+        // the exact form's two rounds of sums (delta_from_sums written out),
+        // the deferred rows spread over both
         a = red_step<0>(a); b = red_step<0>(b); fill(0);
-        a = red_step<1>(a); b = red_step<1>(b); fill(1);
-        a = red_step<2>(a); b = red_step<2>(b); fill(2);
-        a = red_step<3>(a); b = red_step<3>(b); fill(3);
-        a = red_step<4>(a); b = red_step<4>(b); fill(4);
-        a = red_step<5>(a); b = red_step<5>(b); fill(5);
+        a = red_step<1>(a); b = red_step<1>(b);
         if (s + 1 < BT) zr[s + 1] = shift_by_lane0(zr[s + 1]);
-        dl = delta_from_sums<LN>(z, g2, lane63(a), lane63(b), gbv, gam, eps);
+        a = red_step<2>(a); b = red_step<2>(b); fill(1);
+        a = red_step<3>(a); b = red_step<3>(b);
+        a = red_step<4>(a); b = red_step<4>(b); fill(2);
+        a = red_step<5>(a); b = red_step<5>(b);
+        const float s1 = lane63(a), s2 = lane63(b);
+        const float am = s1 * (1.0f / D);
+        const float c = fmaf(-s1, s1, float(D * D) * eps);
+        const float q = fmaf(s2, float(D), c);
+        const float rs = float(D) * __builtin_amdgcn_rsqf(fabsf(q));
+        const float xh = (z - am) * rs;
+        const float g = fmaf(g2, xh, gbv);
+        float sg = g, sgx = g * xh;
+        sg = red_step<0>(sg); sgx = red_step<0>(sgx); fill(3);
+        sg = red_step<1>(sg); sgx = red_step<1>(sgx);
+        sg = red_step<2>(sg); sgx = red_step<2>(sgx); fill(4);
+        sg = red_step<3>(sg); sgx = red_step<3>(sgx);
+        sg = red_step<4>(sg); sgx = red_step<4>(sgx); fill(5);
+        sg = red_step<5>(sg); sgx = red_step<5>(sgx);
+        // both lane reads first (two scalar registers: a read used at once
+        // stalls the chain on its hazard)
+        sg = lane63(sg);
+        sgx = lane63(sgx);
+        dl = rs * fmaf(-xh, sgx * (1.0f / D), fmaf(sg, -1.0f / D, g));
       }
     }
     dr[s] = dl;
