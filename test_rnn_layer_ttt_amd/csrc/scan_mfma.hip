@@ -181,7 +181,7 @@ struct alignas(16) Smem {
   Tile ring[RING];
   float Zt[D][ZPAD];       // z of the next serial pass, by feature
   float Dt[2][D][ZPAD];    // delta of a tile, by feature
-  float Cc[2][BT][BT];     // eta_s (k_s . k_t) of a tile
+  float Cc[2][BT][BT];     // -eta_s (k_s . k_t) of a tile (negated: the serial pass adds)
   float Cd[2][BT];         // its superdiagonal eta_s (k_s . k_{s+1})
   float Mg[2][BT][ZPAD];   // -(k_s . q_t), s <= t, of a tile, at [t][s]
   float Xg[BT][ZPAD];      // -(k_s . k'_t) of a tile and the next one, at [t][s]
@@ -439,11 +439,20 @@ __device__ __forceinline__ float token_delta(float z, float bv, float gam, float
   }
 }
 
-// The serial pass over one tile.  zr[t] = (W_c k_t)_i on entry; cc points at
-// eta_s (k_s . k_t) (t > s) in LDS and cd[s] holds its superdiagonal
-// eta_s (k_s . k_{s+1}) in registers.  Token s's delta is applied to row s+1 at
-// once; its updates of rows s+2.. are spread over the reduction steps of token
-// s+1, where they fill the DPP wait states, with coefficient rows read two
+// The serial pass over one tile.  zq[t / 4][t % 4] = (W_c k_t)_i on entry
+// (lane = feature i; the 16 rows as four 4-row groups); cc points at the
+// negated coefficients -eta_s (k_s . k_t) in LDS (row s, column t) and cd[s]
+// holds the superdiagonal eta_s (k_s . k_{s+1}) in registers.  Token s's delta
+// is applied to row s+1 at once.  Its updates of rows s+2.. are made during
+// token s+1: the rows of the 4-row group that holds row s+2 on the vector ALU
+// (coefficients broadcast from LDS), and each later group with one
+// v_mfma_f32_4x4x1f32.  That product's 16 blocks put lane 4b + j in block b,
+// column j, so with A = the lane pattern -eta_s (k_s . k_{4g + lane % 4}),
+// B = delta_s (lane = feature) and C = D = the group's four row registers it
+// is exactly the four updates zq[g][i] += A[4g + i] delta_s[lane], one issue
+// slot instead of four.  A group is a product target only while every row in
+// it lies two or more tokens ahead, so the vector ALU touches its rows no
+// sooner than a token after its last product.  Coefficient rows are read two
 // tokens ahead of their use.  Row s+1 is shifted by its lane-0 entry before
 // token s's own correction, so off the dependency chain (with the
 // straight-through form, possibly before the last of the deferred updates
@@ -452,23 +461,26 @@ __device__ __forceinline__ float token_delta(float z, float bv, float gam, float
 // standard deviations); the LayerNorm of token s+1 then runs on the shifted
 // row.
 template <int LN>
-__device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[BT],
-                                            const float (*cc)[BT],
+__device__ __forceinline__ void serial_tile(f32x4 (&zq)[4], const float (&bv)[BT],
+                                            const float* cc, int lane,
                                             const float (&cd)[BT], float gam, float eps,
                                             float (&dr)[BT]) {
-  float crow[4][BT];   // rows s-1 (in use), s, s+1, s+2 (in flight); ring by row % 4
+  // Row r of the coefficients (used in token r + 1, for the rows r + 2 ..):
+  // cq = its entries in the group g0 = (r + 2) / 4 (broadcast), cp[g - g0 - 1]
+  // = its lane pattern for each later group g.  Rows r - 1 .. r + 2 in a ring.
+  float4 cq[4];
+  float cp[4][3];
+  const float* ap = cc + (lane & 3);
   auto load_row = [&](int r) {
+    const int g0 = (r + 2) >> 2;
+    cq[r % 4] = *reinterpret_cast<const float4*>(&cc[r * BT + 4 * g0]);
 #pragma unroll
-    for (int q4 = (r + 2) / 4; q4 < BT / 4; ++q4) {
-      const float4 x = *reinterpret_cast<const float4*>(&cc[r][4 * q4]);
-      float* d = crow[r % 4];
-      d[4 * q4] = x.x; d[4 * q4 + 1] = x.y; d[4 * q4 + 2] = x.z; d[4 * q4 + 3] = x.w;
-    }
+    for (int g = g0 + 1; g < 4; ++g) cp[r % 4][g - g0 - 1] = ap[r * BT + 4 * g];
   };
   load_row(0);
   load_row(1);
   const float gam_d = gam * float(D);
-  if constexpr (LN != kLnNone) zr[0] = shift_by_lane0(zr[0]);
+  if constexpr (LN != kLnNone) zq[0][0] = shift_by_lane0(zq[0][0]);
   float dprev = 0.0f;
 #pragma unroll
   for (int s = 0; s < BT; ++s) {
@@ -477,15 +489,24 @@ __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[B
     __builtin_amdgcn_sched_barrier(0);
     if (s + 2 < BT - 2) load_row(s + 2);
     __builtin_amdgcn_sched_barrier(0);
-    const float z = zr[s];
-    // deferred rows s+1 .. BT-1 of the previous token, split into six slices
+    const float z = zq[s >> 2][s & 3];
+    // the deferred updates of delta_{s-1} (rows s+1 ..), in six slots: slot 0
+    // takes row s+1 (needed first) and the group products, slots 1 .. 3 the
+    // other vector-ALU rows of row s+1's group
     constexpr int kSlots = 6;
-    const int n = BT - 1 - s;
     auto fill = [&](int k) {
-      if (s == 0) return;
+      if (s == 0 || s + 1 >= BT) return;
+      const int r = s - 1, g0 = (s + 1) >> 2;
+      const float4 c4 = cq[r % 4];
+      const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+      const int t = s + 1 + k;
+      if (k < 4 && t <= 4 * g0 + 3) zq[g0][t & 3] = fmaf(cv[t & 3], dprev, zq[g0][t & 3]);
+      if (k == 0) {
 #pragma unroll
-      for (int t = s + 1 + (k * n) / kSlots; t < s + 1 + ((k + 1) * n) / kSlots; ++t)
-        zr[t] = fmaf(-crow[(s - 1) % 4][t], dprev, zr[t]);
+        for (int g = g0 + 1; g < 4; ++g)
+          zq[g] = __builtin_amdgcn_mfma_f32_4x4x1f32(cp[r % 4][g - g0 - 1], dprev, zq[g], 0, 0,
+                                                     0);
+      }
     };
     float dl;
     if constexpr (LN == kLnNone) {
@@ -495,10 +516,9 @@ __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[B
     } else {
       float a = z, b = z * z;
       if constexpr (LN == kLnST) {
-        // half the deferred rows go into the reduction's gaps, half into
-        // the waits of the tail (delta_from_sums written out), and row s+1
-        // is shifted early, so that its correction by delta_s below waits
-        // for delta_s alone
+        // the deferred updates go into the reduction's gaps, and row s+1 is
+        // shifted early, so that its correction by delta_s below waits for
+        // delta_s alone
         const float gz = gam_d * z;
         float r = pair_step0(a, b); fill(0);
         r = red_step<0>(r);
@@ -506,7 +526,7 @@ __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[B
         r = red_step<2>(r);
         r = red_step<3>(r); fill(2);
         r = red_step<4>(r);
-        if (s + 1 < BT) zr[s + 1] = shift_by_lane0(zr[s + 1]);
+        if (s + 1 < BT) zq[(s + 1) >> 2][(s + 1) & 3] = shift_by_lane0(zq[(s + 1) >> 2][(s + 1) & 3]);
         const float s1 = lane31(r), s2 = lane63(r);
         fill(3);
         const float c = fmaf(-s1, s1, float(D * D) * eps);
@@ -519,10 +539,10 @@ __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[B
         const float g2 = gam * gam;
         const float gbv = gam * bv[s];
         // the exact form's two rounds of sums (delta_from_sums written out),
-        // the deferred rows spread over both
+        // the deferred updates spread over both
         a = red_step<0>(a); b = red_step<0>(b); fill(0);
         a = red_step<1>(a); b = red_step<1>(b);
-        if (s + 1 < BT) zr[s + 1] = shift_by_lane0(zr[s + 1]);
+        if (s + 1 < BT) zq[(s + 1) >> 2][(s + 1) & 3] = shift_by_lane0(zq[(s + 1) >> 2][(s + 1) & 3]);
         a = red_step<2>(a); b = red_step<2>(b); fill(1);
         a = red_step<3>(a); b = red_step<3>(b);
         a = red_step<4>(a); b = red_step<4>(b); fill(2);
@@ -549,7 +569,8 @@ __device__ __forceinline__ void serial_tile(float (&zr)[BT], const float (&bv)[B
       }
     }
     dr[s] = dl;
-    if (s + 1 < BT) zr[s + 1] = fmaf(-cd[s], dl, zr[s + 1]);
+    if (s + 1 < BT)
+      zq[(s + 1) >> 2][(s + 1) & 3] = fmaf(-cd[s], dl, zq[(s + 1) >> 2][(s + 1) & 3]);
     dprev = dl;
   }
 }
@@ -579,14 +600,15 @@ __device__ __forceinline__ void serial_prefetch(SerialIn& in, const typename Sme
 template <bool BF16, int LN, bool DUAL>
 __device__ __forceinline__ void ln_pass(Smem<BF16>& sm, const SerialIn& in, const float (*cc)[BT],
                                         float (*dt)[ZPAD], int lane, float gam, float eps) {
-  float zr[BT], dr[BT];
+  f32x4 zq[BT / 4];
+  float dr[BT];
 #pragma unroll
   for (int q4 = 0; q4 < BT / 4; ++q4) {
     const float4 x = *reinterpret_cast<const float4*>(&sm.Zt[lane][4 * q4]);
-    zr[4 * q4] = x.x; zr[4 * q4 + 1] = x.y; zr[4 * q4 + 2] = x.z; zr[4 * q4 + 3] = x.w;
+    zq[q4] = f32x4{x.x, x.y, x.z, x.w};
   }
   static_assert(!DUAL, "the dual form runs dual_ln_pass");
-  serial_tile<LN>(zr, in.bv, cc, in.cd, gam, eps, dr);
+  serial_tile<LN>(zq, in.bv, &cc[0][0], lane, in.cd, gam, eps, dr);
 #pragma unroll
   for (int q4 = 0; q4 < BT / 4; ++q4)
     *reinterpret_cast<float4*>(&dt[lane][4 * q4]) =
@@ -875,7 +897,7 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float cv = t0.ETA[4 * G + r] * g[r];
-      sm.Cc[0][4 * G + r][l16] = cv;
+      sm.Cc[0][4 * G + r][l16] = -cv;
       if (4 * G + r + 1 == l16) sm.Cd[0][4 * G + r] = cv;
     }
   }
@@ -1030,7 +1052,7 @@ scan_mfma_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float cv = fe[r] * g[r];
-          sm.Cc[(c + 1) & 1][4 * G + r][l16] = cv;
+          sm.Cc[(c + 1) & 1][4 * G + r][l16] = -cv;
           if (4 * G + r + 1 == l16) sm.Cd[(c + 1) & 1][4 * G + r] = cv;
         }
       }
