@@ -516,18 +516,21 @@ __device__ __forceinline__ void serial_tile(f32x4 (&zq)[4], const float (&bv)[BT
     } else {
       float a = z, b = z * z;
       if constexpr (LN == kLnST) {
-        // the deferred updates go into the reduction's gaps, and row s+1 is
-        // shifted early, so that its correction by delta_s below waits for
+        // two interleaved sums (each fills the other's DPP wait states; the
+        // pairing through one lane-half swap that the dual form uses is two
+        // dependent steps longer, which shows here, where the chain's latency
+        // sets the pace), the deferred updates in the remaining gaps, and row
+        // s+1 shifted early, so that its correction by delta_s below waits for
         // delta_s alone
         const float gz = gam_d * z;
-        float r = pair_step0(a, b); fill(0);
-        r = red_step<0>(r);
-        r = red_step<1>(r); fill(1);
-        r = red_step<2>(r);
-        r = red_step<3>(r); fill(2);
-        r = red_step<4>(r);
+        a = red_step<0>(a); b = red_step<0>(b); fill(0);
+        a = red_step<1>(a); b = red_step<1>(b);
+        a = red_step<2>(a); b = red_step<2>(b); fill(1);
+        a = red_step<3>(a); b = red_step<3>(b);
+        a = red_step<4>(a); b = red_step<4>(b); fill(2);
         if (s + 1 < BT) zq[(s + 1) >> 2][(s + 1) & 3] = shift_by_lane0(zq[(s + 1) >> 2][(s + 1) & 3]);
-        const float s1 = lane31(r), s2 = lane63(r);
+        a = red_step<5>(a); b = red_step<5>(b);
+        const float s1 = lane63(a), s2 = lane63(b);
         fill(3);
         const float c = fmaf(-s1, s1, float(D * D) * eps);
         const float q = fmaf(s2, float(D), c);
