@@ -693,6 +693,25 @@ def main():
         line["config"]["pass"] = ("layer: input projections from x [B,T,hidden] bf16, "
                                   "then the scan")
         line["config"]["scan_ms_avg"] = round(float(np.mean(ms["scan"])), 4)
+        # for scale: the same product as one plain library GEMM (torch.matmul,
+        # hipBLASLt) into a [B*T, H*(4d+1)] bf16 result, no bias and none of the
+        # projection kernel's five scattered output layouts; both operands
+        # contiguous (the weights transposed once, outside the timing)
+        x2 = xt.reshape(B * T, H * d)
+        w2t = wt.reshape(H * (4 * d + 1), H * d).t().contiguous()
+        y2 = torch.matmul(x2, w2t)
+        torch.cuda.synchronize()
+        lms = []
+        for _ in range(max(3, min(args.steps, 20))):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            torch.matmul(x2, w2t, out=y2)
+            b_.record(stream)
+            b_.synchronize()
+            lms.append(a_.elapsed_time(b_))
+        line["config"]["library_gemm_ms_median"] = med(lms)
+        line["config"]["projection_ms_median"] = med(ms["main"])
+        del x2, w2t, y2
 
     # ---- the vector-ALU kernel on the same inputs, for comparison (the
     # matrix-core kernel is what a call at d = 64 runs)
