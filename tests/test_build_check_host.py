@@ -56,3 +56,20 @@ def test_vgpr_accumulator_inputs_are_tracked():
 \tv_cvt_pk_bf16_f32 v12, v1, v2
 """
     assert len(srcc_war_hazards(vg)) == 1
+
+
+def test_the_serial_pass_products_are_checked_too():
+    # the serial pass's 4x4x1 fp32 products (in-tile updates of the row
+    # groups) are held to the same rule: a rotated accumulator whose input
+    # register is overwritten at once is found, an in-place one passes
+    rotated = """
+\tv_mfma_f32_4x4x1_16b_f32 v[138:141], v183, v127, v[224:227]
+\tv_add_f32_dpp v224, v236, v236 row_shr:1 row_mask:0xf bank_mask:0xf bound_ctrl:1
+"""
+    h = srcc_war_hazards(rotated)
+    assert len(h) == 1 and "4x4x1" in h[0][0] and h[0][2] == 0
+    in_place = """
+\tv_mfma_f32_4x4x1_16b_f32 v[98:101], v188, v94, v[98:101]
+\tv_add_f32_dpp v188, v206, v206 row_shr:1 row_mask:0xf bank_mask:0xf bound_ctrl:1
+"""
+    assert srcc_war_hazards(in_place) == []
